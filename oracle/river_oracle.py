@@ -1,0 +1,356 @@
+"""Plain CPU oracle of the KV-shared early-exit decoder (River-LLM).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this module.  It shares no code with the HIP path
+and must never be used as a fallback for it.
+
+What it computes follows the lead page ("River-LLM: Large Language Model
+Seamless Exit Based on KV Share", arXiv:2604.18396):
+
+* section 3 (KV-shared exit river): beside each decoder layer sits an *exit
+  layer*, a full copy of that layer's parameters that is then quantised to
+  4-bit weights with 16-bit activations (W4A16), built without training; the
+  exit layer writes its K/V into the slot of the shared cache that belongs to
+  the original layer, so later tokens never find a missing entry;
+* section 4 (exit decision): at each layer the state-transition similarity
+  between that layer's input and output is taken per token; if its minimum
+  over the batch exceeds tau, the rest of the layers run as exit layers, and
+  no deeper layer checks again;
+* section 5 (prefill / generation): prefill takes one sequence-level decision
+  for all prompt tokens, generation decides once per generated position.
+
+Arithmetic: float64 for the forward pass.  Activations that the method keeps
+in 16 bits (the "A16" of W4A16) are rounded to bf16 at the points where the
+decoder stores them: the RMSNorm outputs that feed a linear layer, q/k/v
+after RoPE (k and v are what the cache holds), the attention output, and the
+SwiGLU product.  The residual stream stays wide.  The quantiser follows its
+definition in float32, because its result is an integer code that both sides
+must reach in the same precision.
+
+Readings where the pages are silent (all stated again where they are used):
+the similarity is the cosine between the residual stream entering a layer and
+the one leaving it; "exceeds" is a strict ``>``; the test runs after each
+backbone layer except the last; the quantiser is asymmetric min-max
+round-to-nearest with a float zero point per (output row, group of G inputs),
+the parameter form of HQQ, without HQQ's refinement step.
+"""
+import math
+
+import numpy as np
+
+EXIT_INT4 = "int4"
+EXIT_COPY = "copy"
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding (round to nearest, ties to even)
+# --------------------------------------------------------------------------
+def bf16_from_f32(x):
+    """Round float32 values to the nearest bf16 value (ties to even); float32 out."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    out = r.view(np.float32)
+    return np.where(np.isnan(x), x, out)
+
+
+def bf16_from_f64(x):
+    """Round float64 values to the nearest bf16 value in one step (no double
+    rounding through float32); float64 out.  Exact for results in the normal
+    range of bf16, which is all this decoder produces."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    u = x.view(np.uint64)
+    drop = np.uint64(45)  # 52 fraction bits of float64 minus 7 of bf16
+    lsb = (u >> drop) & np.uint64(1)
+    half = np.uint64((1 << 44) - 1)
+    mask = ~np.uint64((1 << 45) - 1)
+    r = ((u + half + lsb) & mask).view(np.float64)
+    # beyond bf16's largest finite value the rounding goes to infinity
+    r = np.where(np.abs(r) > 3.3895313892515355e38, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+# --------------------------------------------------------------------------
+# Exit-layer construction: copy, then 4-bit quantisation
+# (lead page, section 3: copy the layer's parameters in full, then quantise
+#  to W4A16; the page names HQQ as the default quantiser)
+# --------------------------------------------------------------------------
+def quantize_int4(w, group):
+    """Asymmetric 4-bit quantisation of a row-major weight matrix.
+
+    For each output row and each group of ``group`` consecutive input columns
+    (all float32, every operation separately rounded):
+        lo, hi = min, max of the group
+        s = bf16(fl(hi - lo) / 15), and s = 1 when that is 0
+        z = bf16(fl(-lo / s))
+        q = clamp(round_half_even(fl(fl(w / s) + z)), 0, 15)
+    Returns (q uint8 [N,K], s float32 [N,K/G], z float32 [N,K/G]); s and z hold
+    bf16 values.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    if k % group:
+        raise ValueError("group size must divide the number of columns")
+    wg = w.reshape(n, k // group, group)
+    lo = wg.min(axis=-1)
+    hi = wg.max(axis=-1)
+    s = bf16_from_f32((hi - lo) / np.float32(15.0))
+    s = np.where(s == np.float32(0.0), np.float32(1.0), s).astype(np.float32)
+    z = bf16_from_f32(-lo / s)
+    t = wg / s[..., None]
+    t = t + z[..., None]
+    q = np.clip(np.rint(t), 0, 15).astype(np.uint8)
+    return q.reshape(n, k), s, z
+
+
+def dequantize_int4(q, s, z, group):
+    """w_hat = fl(fl(q - z) * s) in float32 (the W ~ s (q - z) form)."""
+    n, k = q.shape
+    qg = q.reshape(n, k // group, group).astype(np.float32)
+    wh = (qg - z[..., None]) * s[..., None]
+    return wh.reshape(n, k).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Decoder pieces (Llama-style layer: pre-norm attention and SwiGLU MLP)
+# --------------------------------------------------------------------------
+def rmsnorm(h, gain, eps):
+    """h / sqrt(mean(h^2) + eps) * gain, over the last axis, float64."""
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
+
+
+def rope_tables(positions, head_dim, theta):
+    """cos/sin [n, head_dim/2] of angle pos * theta^(-2i/head_dim), float64."""
+    half = head_dim // 2
+    inv = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(x, cos, sin):
+    """Rotate-half RoPE: pair (i, i + D/2) turned by the angle of index i.
+    x [..., n, H, D]; cos/sin [n, D/2]."""
+    half = x.shape[-1] // 2
+    a, b = x[..., :half], x[..., half:]
+    c = cos[:, None, :]
+    s = sin[:, None, :]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def cosine_rows(a, b):
+    """Per-row cosine a.b / max(|a||b|, 1e-8), clamped to [-1, 1], float64."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    num = np.sum(a * b, axis=-1)
+    den = np.maximum(np.sqrt(np.sum(a * a, axis=-1)) * np.sqrt(np.sum(b * b, axis=-1)), 1e-8)
+    return np.clip(num / den, -1.0, 1.0)
+
+
+def linear(x, w):
+    """x @ w^T in float64 (w is a row-major [N][K] matrix)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+class Shape:
+    """Decoder hyper-parameters (names follow the usual Llama notation)."""
+
+    def __init__(self, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim,
+                 vocab, group_size, tied_embeddings, rms_eps=1e-5, rope_theta=500000.0, **_):
+        self.L, self.d, self.Hq, self.Hkv, self.Dh = n_layers, d_model, n_q_heads, n_kv_heads, head_dim
+        self.F, self.V, self.G = ffn_dim, vocab, group_size
+        self.tied = bool(tied_embeddings)
+        self.eps, self.theta = float(rms_eps), float(rope_theta)
+
+
+def attention(q, kc, vc, start, n):
+    """Causal GQA attention for n new rows at positions start..start+n-1.
+
+    q [B, n, Hq, D]; kc/vc [B, Hkv, S, D] already hold the new keys/values.
+    Query head h reads kv head floor(h * Hkv / Hq).  Scores q.k / sqrt(D),
+    softmax with its maximum subtracted, float64.  Returns [B, n, Hq, D].
+    """
+    B, _, Hq, D = q.shape
+    Hkv = kc.shape[1]
+    end = start + n
+    out = np.empty((B, n, Hq, D), dtype=np.float64)
+    rows = np.arange(n)[:, None] + start
+    cols = np.arange(end)[None, :]
+    masked = cols > rows
+    for b in range(B):
+        for h in range(Hq):
+            j = (h * Hkv) // Hq
+            k = kc[b, j, :end].astype(np.float64)
+            v = vc[b, j, :end].astype(np.float64)
+            sc = (q[b, :, h].astype(np.float64) @ k.T) / math.sqrt(D)
+            sc = np.where(masked, -np.inf, sc)
+            sc = sc - sc.max(axis=-1, keepdims=True)
+            p = np.exp(sc)
+            p = p / p.sum(axis=-1, keepdims=True)
+            out[b, :, h] = p @ v
+    return out
+
+
+def decoder_layer(shape, lw, h, start, kc, vc):
+    """One decoder layer on h [B, n, d] at positions start..start+n-1.
+
+    ``lw`` holds float32 copies of the layer weights (backbone or exit copy).
+    Writes the new K/V into kc/vc [B, Hkv, S, D] (this layer's slots of the
+    shared cache) and returns the residual stream after the layer (float64).
+    """
+    B, n, d = h.shape
+    Hq, Hkv, D = shape.Hq, shape.Hkv, shape.Dh
+    x = bf16_from_f64(rmsnorm(h, lw["attn_norm"], shape.eps))
+    q = linear(x, lw["wq"]).reshape(B, n, Hq, D)
+    k = linear(x, lw["wk"]).reshape(B, n, Hkv, D)
+    v = linear(x, lw["wv"]).reshape(B, n, Hkv, D)
+    cos, sin = rope_tables(np.arange(start, start + n), D, shape.theta)
+    q = bf16_from_f64(apply_rope(q, cos, sin))
+    k = bf16_from_f64(apply_rope(k, cos, sin))
+    v = bf16_from_f64(v)
+    kc[:, :, start:start + n] = k.transpose(0, 2, 1, 3)
+    vc[:, :, start:start + n] = v.transpose(0, 2, 1, 3)
+    o = bf16_from_f64(attention(q, kc, vc, start, n)).reshape(B, n, Hq * D)
+    h1 = h + linear(o, lw["wo"])
+    x2 = bf16_from_f64(rmsnorm(h1, lw["mlp_norm"], shape.eps))
+    u = bf16_from_f64(silu(linear(x2, lw["w_gate"])) * linear(x2, lw["w_up"]))
+    return h1 + linear(u, lw["w_down"])
+
+
+def lm_head(shape, h, final_norm, w_lm):
+    """logits = bf16(rmsnorm(h, final_norm)) @ W_lm^T, float64 [.., V]."""
+    x = bf16_from_f64(rmsnorm(h, final_norm, shape.eps))
+    return linear(x, w_lm)
+
+
+def greedy(logits):
+    """argmax over the vocabulary; the lowest index wins ties."""
+    return np.argmax(logits, axis=-1).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# The river: backbone layers, exit layers, shared cache, exit controller
+# --------------------------------------------------------------------------
+class RiverOracle:
+    """KV-shared early-exit decoder on the CPU.
+
+    weights: dict with float32 numpy arrays (bf16 values):
+      embed [V,d], final_norm [d], lm_head [V,d] or None (tied to embed),
+      layers: list of dicts attn_norm, wq, wk, wv, wo, mlp_norm, w_gate, w_up, w_down.
+    """
+
+    LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+    def __init__(self, shape, weights, max_batch, max_seq):
+        self.s = shape if isinstance(shape, Shape) else Shape(**shape)
+        self.w = weights
+        self.max_batch, self.max_seq = int(max_batch), int(max_seq)
+        self.exit_layers = None
+        self.exit_codes = None   # per layer: name -> (q, s, z) in int4 mode
+        s = self.s
+        kv_shape = (s.L, self.max_batch, s.Hkv, self.max_seq, s.Dh)
+        self.k_cache = np.zeros(kv_shape, dtype=np.float64)
+        self.v_cache = np.zeros(kv_shape, dtype=np.float64)
+        self.pos = 0
+        self.batch = None
+
+    # -- build ------------------------------------------------------------
+    def build_exit_layers(self, mode=EXIT_INT4):
+        """One exit layer per decoder layer: a copy of all its parameters,
+        with the seven linear matrices quantised in int4 mode (norm gains are
+        copied as they are).  Embedding, final norm and LM head get no copy."""
+        if mode not in (EXIT_INT4, EXIT_COPY):
+            raise ValueError(mode)
+        self.exit_layers, self.exit_codes = [], []
+        for lw in self.w["layers"]:
+            ex, codes = {}, {}
+            for name, arr in lw.items():
+                if name in self.LINEARS and mode == EXIT_INT4:
+                    q, sc, z = quantize_int4(arr, self.s.G)
+                    codes[name] = (q, sc, z)
+                    ex[name] = dequantize_int4(q, sc, z, self.s.G)
+                else:
+                    ex[name] = np.array(arr, dtype=np.float32, copy=True)
+            self.exit_layers.append(ex)
+            self.exit_codes.append(codes)
+
+    def reset(self):
+        self.pos = 0
+        self.batch = None
+
+    # -- one pass over all layers ------------------------------------------
+    def _run(self, tokens, start, tau, force_E, record):
+        s = self.s
+        B, n = tokens.shape
+        h = self.w["embed"][tokens].astype(np.float64)        # [B, n, d]
+        exited = False
+        E = s.L
+        trace = []
+        inputs = []
+        for l in range(s.L):
+            if force_E is not None:
+                use_exit = l >= force_E
+            else:
+                use_exit = exited
+            lw = self.exit_layers[l] if use_exit else self.w["layers"][l]
+            if record:
+                inputs.append(h.copy())
+            h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B])
+            if force_E is None:
+                if not exited and l < s.L - 1:
+                    # batch minimum of the per-token state-transition similarity
+                    m = float(cosine_rows(h.reshape(-1, s.d), h_out.reshape(-1, s.d)).min())
+                    trace.append(m)
+                    # the decision is taken in float32, like the device's
+                    if np.float32(m) > np.float32(tau):
+                        exited = True
+                        E = l + 1
+            h = h_out
+        if force_E is not None:
+            E = int(force_E)
+        w_lm = self.w["embed"] if self.w["lm_head"] is None else self.w["lm_head"]
+        logits = lm_head(s, h[:, -1], self.w["final_norm"], w_lm)
+        res = {"logits": logits, "next": greedy(logits), "E": E, "trace": trace, "h_final": h}
+        if record:
+            res["layer_inputs"] = inputs
+        return res
+
+    def prefill(self, tokens, tau, force_E=None, record=False):
+        """Sequence-level exit: one decision per layer for all B*T prompt rows
+        (the minimum runs over every row).  Logits of each row's last position."""
+        if self.exit_layers is None:
+            raise RuntimeError("build_exit_layers first")
+        tokens = np.asarray(tokens, dtype=np.int64)
+        B, T = tokens.shape
+        if B > self.max_batch or T > self.max_seq:
+            raise ValueError("prefill exceeds the cache")
+        self.reset()
+        res = self._run(tokens, 0, tau, force_E, record)
+        self.pos = T
+        self.batch = B
+        return res
+
+    def decode_step(self, tokens, tau, force_E=None, record=False):
+        """Token-level exit for one generated position (all B rows share it)."""
+        if self.exit_layers is None or self.batch is None:
+            raise RuntimeError("prefill first")
+        tokens = np.asarray(tokens, dtype=np.int64).reshape(-1, 1)
+        if tokens.shape[0] != self.batch:
+            raise ValueError("batch size differs from the prefill's")
+        if self.pos + 1 > self.max_seq:
+            raise ValueError("cache full")
+        res = self._run(tokens, self.pos, tau, force_E, record)
+        res["pos"] = self.pos
+        self.pos += 1
+        return res
+
+    def kv_bytes_per_token(self, dtype_bytes=2):
+        """Bytes the single shared cache holds per token (K and V, all layers)."""
+        s = self.s
+        return s.L * 2 * s.Hkv * s.Dh * dtype_bytes
