@@ -1,0 +1,68 @@
+// Exit-layer construction on gfx950: copy + 4-bit group quantisation of one
+// linear matrix ("River-LLM: Large Language Model Seamless Exit Based on KV
+// Share", section 3: exit layers are copies of each layer quantised to W4A16,
+// made without training).
+//
+// Per (row, group of G columns), float32 with every operation rounded on its
+// own (IEEE division, no contraction) so that the codes are reproducible
+// bit for bit:
+//   s = bf16((hi - lo) / 15), s = 1 if that is 0;  z = bf16(-lo / s);
+//   code = clamp(round_half_even(w / s + z), 0, 15).
+// One thread packs one 32-bit word (8 columns); the G/8 threads of a group sit
+// in adjacent lanes and find the group's min and max with lane shuffles.
+#include "device_common.h"
+
+#pragma clang fp contract(off)
+
+namespace river {
+
+__device__ __forceinline__ float bf16_round(float f) { return bf2f(f2bf(f)); }
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ w, int64_t words,
+                                                       int KW, int G, uint32_t *__restrict__ codes,
+                                                       uint32_t *__restrict__ sz) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = i < words;
+  const int gw = G / 8;  // threads (words) per group, a power of two <= 64
+  float v[8];
+  float lo = INFINITY, hi = -INFINITY;
+  if (live) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(w + i * 8);
+    v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+    v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { lo = fminf(lo, v[j]); hi = fmaxf(hi, v[j]); }
+  }
+  for (int o = gw >> 1; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+  }
+  if (!live) return;
+  float s = bf16_round(__fdiv_rn(__fsub_rn(hi, lo), 15.0f));
+  if (s == 0.0f) s = 1.0f;
+  const float z = bf16_round(__fdiv_rn(-lo, s));
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float q = rintf(__fadd_rn(__fdiv_rn(v[j], s), z));
+    q = fminf(fmaxf(q, 0.0f), 15.0f);
+    word |= (uint32_t)q << (4 * (j & 3) + 16 * (j >> 2));
+  }
+  codes[i] = word;
+  const int64_t row = i / KW;
+  const int wi = (int)(i % KW);
+  if (wi % gw == 0)
+    sz[row * (KW / gw) + wi / gw] = (uint32_t)f2bf(s) | ((uint32_t)f2bf(z) << 16);
+}
+
+hipError_t launch_quantize(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
+                           hipStream_t s) {
+  if (G < 32 || G > 512 || (G & (G - 1)) || K % G) return hipErrorInvalidValue;
+  const int64_t words = (int64_t)N * (K / 8);
+  const int64_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, words, K / 8, G,
+                     codes, sz);
+  return hipGetLastError();
+}
+
+}  // namespace river

@@ -1,0 +1,562 @@
+// Host side of the KV-shared early-exit decoder: argument validation, buffer
+// layouts, the layer scheduler for prefill and decode, and HIP-graph replay of
+// decode steps.  Every decision of the method (the batch-minimum cosine against
+// tau, the sticky exit flag) is taken on the device; the host only enqueues.
+//
+// Method: "River-LLM: Large Language Model Seamless Exit Based on KV Share"
+// (section 3: shared-KV exit layers; section 4: exit rule; section 5:
+// sequence-level exit in prefill, token-level exit in generation).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <new>
+#include <tuple>
+#include <vector>
+
+#include "river_internal.h"
+
+namespace river {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+void linear_shapes(const river_config &c, LinearShape o[7]) {
+  const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  o[0] = {qd, c.d_model};
+  o[1] = {kd, c.d_model};
+  o[2] = {kd, c.d_model};
+  o[3] = {c.d_model, qd};
+  o[4] = {c.ffn_dim, c.d_model};
+  o[5] = {c.ffn_dim, c.d_model};
+  o[6] = {c.d_model, c.ffn_dim};
+}
+
+static size_t linear_region(const river_config &c, const LinearShape &s, bool copy, size_t *sz_off) {
+  if (copy) {
+    *sz_off = 0;
+    return align256((size_t)s.N * s.K * 2);
+  }
+  const size_t codes = align256((size_t)s.N * (s.K / 8) * 4);
+  *sz_off = codes;
+  return codes + align256((size_t)s.N * (s.K / c.group_size) * 4);
+}
+
+static size_t layer_region(const river_config &c, bool copy) {
+  LinearShape sh[7];
+  linear_shapes(c, sh);
+  size_t t = 0, dummy;
+  for (int i = 0; i < 7; ++i) t += linear_region(c, sh[i], copy, &dummy);
+  return t;
+}
+
+void bank_offsets(const river_config &c, int layer, int linear, bool copy, size_t *codes, size_t *sz) {
+  LinearShape sh[7];
+  linear_shapes(c, sh);
+  size_t off = (size_t)layer * layer_region(c, copy), szo = 0;
+  for (int i = 0; i < linear; ++i) off += linear_region(c, sh[i], copy, &szo);
+  linear_region(c, sh[linear], copy, &szo);
+  *codes = off;
+  *sz = copy ? 0 : off + szo;
+}
+
+size_t bank_bytes(const river_config &c, bool copy) { return (size_t)c.n_layers * layer_region(c, copy); }
+
+Workspace workspace_layout(const river_config &c) {
+  Workspace w{};
+  const int64_t R = (int64_t)c.max_batch * c.max_seq;
+  const int qd = c.n_q_heads * c.head_dim;
+  w.rows = R;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.hA = take((size_t)R * c.d_model * 4);
+  w.hB = take((size_t)R * c.d_model * 4);
+  w.x = take((size_t)R * c.d_model * 2);
+  w.q = take((size_t)R * qd * 2);
+  w.attn = take((size_t)R * qd * 2);
+  w.u = take((size_t)R * c.ffn_dim * 2);
+  const int64_t gemv_wgs = c.d_model / 4 + 1;
+  const int64_t cos_wgs = (R + 3) / 4;
+  w.part_floats = (int)std::max<int64_t>(gemv_wgs * kPartFloatsPerWG, cos_wgs);
+  w.part = take((size_t)w.part_floats * 4);
+  w.attn_splits = (c.max_seq + kAttnChunk - 1) / kAttnChunk;
+  w.attn_part = take((size_t)c.max_batch * c.n_q_heads * w.attn_splits * (c.head_dim + 2) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace river
+
+using namespace river;
+
+// ---------------------------------------------------------------------------
+struct river_ctx {
+  river_config cfg;
+  std::vector<river_layer_w> layers;
+  const uint16_t *embed, *final_norm, *lm_head;
+  char *bank;
+  size_t bank_size;
+  uint16_t *kv;
+  char *ws;
+  Control *ctrl;
+  hipStream_t stream;
+  Workspace wl;
+  bool built = false;
+  int exit_mode = 0;
+  int pos = 0;
+  int batch = 0;
+  bool use_graph = true;
+  int force_E = -1;
+  struct GraphKey {
+    const void *tok, *logits, *next;
+    int B, force_E;
+    uint32_t tau_bits;
+    bool operator<(const GraphKey &o) const {
+      return std::tie(tok, logits, next, B, force_E, tau_bits) <
+             std::tie(o.tok, o.logits, o.next, o.B, o.force_E, o.tau_bits);
+    }
+  };
+  std::map<GraphKey, hipGraphExec_t> graphs;
+};
+
+namespace {
+
+bool valid_config(const river_config *c) {
+  if (!c) return false;
+  if (c->n_layers < 1 || c->n_layers > RIVER_MAX_LAYERS) return false;
+  if (c->d_model < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 2 ||
+      c->ffn_dim < 8 || c->vocab < 1 || c->group_size < 1 || c->max_batch < 1 || c->max_seq < 1)
+    return false;
+  if (!std::isfinite(c->rms_eps) || c->rms_eps < 0.f || !std::isfinite(c->rope_theta) ||
+      c->rope_theta <= 0.f)
+    return false;
+  if (c->n_q_heads % c->n_kv_heads) return false;
+  return true;
+}
+
+// shapes the kernels handle; RIVER_OK or RIVER_E_UNIMPLEMENTED
+int supported(const river_config *c) {
+  const int G = c->group_size;
+  const int qd = c->n_q_heads * c->head_dim;
+  if (G < 32 || G > 512 || (G & (G - 1))) return RIVER_E_UNIMPLEMENTED;
+  if (c->d_model % G || c->ffn_dim % G || qd % G) return RIVER_E_UNIMPLEMENTED;
+  if (c->d_model % 256 || c->ffn_dim % 256 || qd % 256) return RIVER_E_UNIMPLEMENTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return RIVER_E_UNIMPLEMENTED;
+  const int gq = c->n_q_heads / c->n_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4) return RIVER_E_UNIMPLEMENTED;
+  if (c->max_batch > 64) return RIVER_E_UNIMPLEMENTED;
+  if (c->ffn_dim % 32) return RIVER_E_UNIMPLEMENTED;
+  return RIVER_OK;
+}
+
+template <class T>
+T *at(char *base, size_t off) { return reinterpret_cast<T *>(base + off); }
+
+void fill_weights(river_ctx *ctx, int l, int lin_first, int count, LinearWeights &w) {
+  const river_layer_w &L = ctx->layers[l];
+  const void *bb[7] = {L.wq, L.wk, L.wv, L.wo, L.w_gate, L.w_up, L.w_down};
+  LinearShape sh[7];
+  linear_shapes(ctx->cfg, sh);
+  std::memset(&w, 0, sizeof(w));
+  w.nseg = count;
+  const bool copy = ctx->exit_mode == RIVER_EXIT_COPY;
+  for (int i = 0; i < count; ++i) {
+    const int lin = lin_first + i;
+    w.bf[i] = static_cast<const uint16_t *>(bb[lin]);
+    w.seg_rows[i] = sh[lin].N;
+    size_t co, so;
+    bank_offsets(ctx->cfg, l, lin, copy, &co, &so);
+    if (copy) {
+      w.ex_bf[i] = at<const uint16_t>(ctx->bank, co);
+    } else {
+      w.q4[i] = at<const uint32_t>(ctx->bank, co);
+      w.sz[i] = at<const uint32_t>(ctx->bank, so);
+    }
+  }
+}
+
+uint16_t *k_layer(river_ctx *ctx, int l) {
+  const river_config &c = ctx->cfg;
+  return ctx->kv + (size_t)l * c.max_batch * c.n_kv_heads * c.max_seq * c.head_dim;
+}
+uint16_t *v_layer(river_ctx *ctx, int l) {
+  const river_config &c = ctx->cfg;
+  const size_t half = (size_t)c.n_layers * c.max_batch * c.n_kv_heads * c.max_seq * c.head_dim;
+  return ctx->kv + half + (size_t)l * c.max_batch * c.n_kv_heads * c.max_seq * c.head_dim;
+}
+
+#define RV_TRY(expr)                         \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return RIVER_E_HIP; \
+  } while (0)
+
+// Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
+int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next) {
+  const river_config &c = ctx->cfg;
+  const int B = ctx->batch;
+  hipStream_t s = ctx->stream;
+  float *hA = at<float>(ctx->ws, ctx->wl.hA), *hB = at<float>(ctx->ws, ctx->wl.hB);
+  const int qd = c.n_q_heads * c.head_dim;
+
+  BeginParams bp{};
+  bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
+  bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
+  bp.tau = tau; bp.is_prefill = 0; bp.set_pos = -1;
+  RV_TRY(launch_begin(bp, s));
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const river_layer_w &L = ctx->layers[l];
+    GemvParams g{};
+    g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl; g.B = B;
+    g.eps = c.rms_eps; g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim;
+    g.max_seq = c.max_seq; g.max_batch = c.max_batch; g.rope_theta = c.rope_theta;
+    g.n_layers = c.n_layers;
+
+    // attention RMSNorm + fused q|k|v + RoPE + write into the shared slot
+    GemvParams q = g;
+    fill_weights(ctx, l, 0, 3, q.w);
+    q.N = qd + 2 * c.n_kv_heads * c.head_dim; q.K = c.d_model;
+    q.h_src = hA; q.h_stride = c.d_model; q.gain = static_cast<const uint16_t *>(L.attn_norm);
+    q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
+    q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
+    RV_TRY(launch_gemv(kXNorm, kEpQKV, q, s));
+
+    AttnParams a{};
+    a.q = q.q_out; a.k_cache = q.k_cache; a.v_cache = q.v_cache;
+    a.out = at<uint16_t>(ctx->ws, ctx->wl.attn); a.part = at<float>(ctx->ws, ctx->wl.attn_part);
+    a.counters = control_attn_counters(ctx->ctrl, c.max_batch); a.ctrl = ctx->ctrl;
+    a.B = B; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.Dh = c.head_dim; a.S = c.max_seq;
+    a.splits = ctx->wl.attn_splits; a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    RV_TRY(launch_attn_decode(a, s));
+
+    GemvParams o = g;
+    fill_weights(ctx, l, 3, 1, o.w);
+    o.N = c.d_model; o.K = qd; o.x_src = a.out; o.x_stride = qd;
+    o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
+    RV_TRY(launch_gemv(kXBf16, kEpResid, o, s));
+
+    GemvParams gu = g;
+    fill_weights(ctx, l, 4, 2, gu.w);
+    gu.N = 2 * c.ffn_dim; gu.K = c.d_model;
+    gu.h_src = hB; gu.h_stride = c.d_model; gu.gain = static_cast<const uint16_t *>(L.mlp_norm);
+    gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u); gu.u_stride = c.ffn_dim;
+    RV_TRY(launch_gemv(kXNorm, kEpSwiGLU, gu, s));
+
+    GemvParams dn = g;
+    fill_weights(ctx, l, 6, 1, dn.w);
+    dn.N = c.d_model; dn.K = c.ffn_dim; dn.x_src = gu.u_out; dn.x_stride = c.ffn_dim;
+    dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model; dn.h_src = hA;
+    dn.part = at<float>(ctx->ws, ctx->wl.part);
+    dn.test_exit = l < c.n_layers - 1;
+    RV_TRY(launch_gemv(kXBf16, kEpResidExit, dn, s));
+    std::swap(hA, hB);
+  }
+  GemvParams lm{};
+  lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
+  lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
+  lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
+  lm.h_src = hA; lm.h_stride = c.d_model; lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
+  lm.logits = logits; lm.next = next; lm.is_prefill = 0; lm.vocab = c.vocab;
+  RV_TRY(launch_gemv(kXNorm, kEpLogits, lm, s));
+  return RIVER_OK;
+}
+
+int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau, float *logits,
+                    int32_t *next) {
+  const river_config &c = ctx->cfg;
+  hipStream_t s = ctx->stream;
+  const int64_t R = (int64_t)B * T;
+  float *hA = at<float>(ctx->ws, ctx->wl.hA), *hB = at<float>(ctx->ws, ctx->wl.hB);
+  uint16_t *x = at<uint16_t>(ctx->ws, ctx->wl.x);
+  const int qd = c.n_q_heads * c.head_dim;
+
+  BeginParams bp{};
+  bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = R; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
+  bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
+  bp.tau = tau; bp.is_prefill = 1; bp.set_pos = T;
+  RV_TRY(launch_begin(bp, s));
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const river_layer_w &L = ctx->layers[l];
+    GemmParams g{};
+    g.M = (int)R; g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl;
+    g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim; g.max_seq = c.max_seq;
+    g.max_batch = c.max_batch; g.T = T; g.rope_theta = c.rope_theta;
+
+    RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), R, c.d_model, c.rms_eps};
+    RV_TRY(launch_rows_norm(rn, s));
+
+    GemmParams q = g;
+    fill_weights(ctx, l, 0, 3, q.w);
+    q.N = qd + 2 * c.n_kv_heads * c.head_dim; q.K = c.d_model; q.x = x; q.ldx = c.d_model;
+    q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
+    q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
+    RV_TRY(launch_gemm(kEpQKV, q, s));
+
+    AttnPrefillParams ap{};
+    ap.q = q.q_out; ap.k_cache = q.k_cache; ap.v_cache = q.v_cache;
+    ap.out = at<uint16_t>(ctx->ws, ctx->wl.attn); ap.B = B; ap.T = T; ap.Hq = c.n_q_heads;
+    ap.Hkv = c.n_kv_heads; ap.Dh = c.head_dim; ap.S = c.max_seq;
+    ap.scale = 1.0f / std::sqrt((float)c.head_dim);
+    RV_TRY(launch_attn_prefill(ap, s));
+
+    GemmParams o = g;
+    fill_weights(ctx, l, 3, 1, o.w);
+    o.N = c.d_model; o.K = qd; o.x = ap.out; o.ldx = qd;
+    o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
+    RV_TRY(launch_gemm(kEpResid, o, s));
+
+    RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), R, c.d_model, c.rms_eps};
+    RV_TRY(launch_rows_norm(rn2, s));
+
+    GemmParams gu = g;
+    fill_weights(ctx, l, 4, 2, gu.w);
+    gu.N = 2 * c.ffn_dim; gu.K = c.d_model; gu.x = x; gu.ldx = c.d_model;
+    gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u);
+    RV_TRY(launch_gemm(kEpSwiGLU, gu, s));
+
+    GemmParams dn = g;
+    fill_weights(ctx, l, 6, 1, dn.w);
+    dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
+    dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
+    RV_TRY(launch_gemm(kEpResid, dn, s));
+
+    if (l < c.n_layers - 1 && ctx->force_E < 0) {
+      RowsCosParams rc{hA, hB, R, c.d_model, at<float>(ctx->ws, ctx->wl.part), ctx->ctrl, l,
+                       c.n_layers};
+      RV_TRY(launch_rows_cos_exit(rc, s));
+    }
+    std::swap(hA, hB);
+  }
+  GemvParams lm{};
+  lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
+  lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
+  lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
+  lm.h_src = hA + (int64_t)(T - 1) * c.d_model; lm.h_stride = (int64_t)T * c.d_model;
+  lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
+  lm.logits = logits; lm.next = next; lm.is_prefill = 1; lm.vocab = c.vocab;
+  RV_TRY(launch_gemv(kXNorm, kEpLogits, lm, s));
+  return RIVER_OK;
+}
+
+void drop_graphs(river_ctx *ctx) {
+  for (auto &kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  ctx->graphs.clear();
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char *river_strerror(int code) {
+  switch (code) {
+    case RIVER_OK: return "ok";
+    case RIVER_E_INVALID_ARG: return "invalid argument";
+    case RIVER_E_BAD_SIZE: return "buffer smaller than required";
+    case RIVER_E_STATE: return "call out of order";
+    case RIVER_E_RANGE: return "batch or position out of range";
+    case RIVER_E_HIP: return "HIP runtime error";
+    case RIVER_E_UNIMPLEMENTED: return "shape not supported by the kernels";
+  }
+  return "unknown status";
+}
+
+int river_query_sizes(const river_config *cfg, river_sizes *out) {
+  if (!cfg || !out) return RIVER_E_INVALID_ARG;
+  if (!valid_config(cfg)) return RIVER_E_INVALID_ARG;
+  const int sup = supported(cfg);
+  if (sup != RIVER_OK) return sup;
+  out->exit_bank_bytes = bank_bytes(*cfg, false);
+  out->exit_bank_copy_bytes = bank_bytes(*cfg, true);
+  out->kv_cache_bytes = (size_t)2 * cfg->n_layers * cfg->max_batch * cfg->n_kv_heads *
+                        cfg->max_seq * cfg->head_dim * 2;
+  out->workspace_bytes = workspace_layout(*cfg).total;
+  out->control_bytes = control_bytes(cfg->max_batch, cfg->n_kv_heads);
+  return RIVER_OK;
+}
+
+int river_exit_bank_offsets(const river_config *cfg, int32_t layer, int32_t linear,
+                            int32_t copy_layout, size_t *codes_off, size_t *sz_off) {
+  if (!cfg || !codes_off || !sz_off || !valid_config(cfg)) return RIVER_E_INVALID_ARG;
+  if (layer < 0 || layer >= cfg->n_layers || linear < 0 || linear >= 7) return RIVER_E_RANGE;
+  const int sup = supported(cfg);
+  if (sup != RIVER_OK) return sup;
+  bank_offsets(*cfg, layer, linear, copy_layout != 0, codes_off, sz_off);
+  return RIVER_OK;
+}
+
+int river_init(const river_config *cfg, const river_weights *w, void *exit_bank, void *kv_cache,
+               void *workspace, void *control, const river_sizes *given, void *hip_stream,
+               river_ctx **out) {
+  if (!cfg || !w || !exit_bank || !kv_cache || !workspace || !control || !given || !out)
+    return RIVER_E_INVALID_ARG;
+  if (!valid_config(cfg)) return RIVER_E_INVALID_ARG;
+  river_sizes need;
+  const int q = river_query_sizes(cfg, &need);
+  if (q != RIVER_OK) return q;
+  if (given->exit_bank_bytes < need.exit_bank_bytes || given->kv_cache_bytes < need.kv_cache_bytes ||
+      given->workspace_bytes < need.workspace_bytes || given->control_bytes < need.control_bytes)
+    return RIVER_E_BAD_SIZE;
+  if (!w->embed || !w->final_norm || !w->layers) return RIVER_E_INVALID_ARG;
+  if (!cfg->tied_embeddings && !w->lm_head) return RIVER_E_INVALID_ARG;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const river_layer_w &L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up ||
+        !L.w_down)
+      return RIVER_E_INVALID_ARG;
+  }
+  river_ctx *ctx = new (std::nothrow) river_ctx();
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  ctx->cfg = *cfg;
+  ctx->layers.assign(w->layers, w->layers + cfg->n_layers);
+  ctx->embed = static_cast<const uint16_t *>(w->embed);
+  ctx->final_norm = static_cast<const uint16_t *>(w->final_norm);
+  ctx->lm_head = static_cast<const uint16_t *>(cfg->tied_embeddings ? w->embed : w->lm_head);
+  ctx->bank = static_cast<char *>(exit_bank);
+  ctx->bank_size = given->exit_bank_bytes;
+  ctx->kv = static_cast<uint16_t *>(kv_cache);
+  ctx->ws = static_cast<char *>(workspace);
+  ctx->ctrl = static_cast<Control *>(control);
+  ctx->stream = static_cast<hipStream_t>(hip_stream);
+  ctx->wl = workspace_layout(*cfg);
+  *out = ctx;
+  return RIVER_OK;
+}
+
+int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  if (mode != RIVER_EXIT_INT4 && mode != RIVER_EXIT_COPY) return RIVER_E_INVALID_ARG;
+  const bool copy = mode == RIVER_EXIT_COPY;
+  if (ctx->bank_size < bank_bytes(ctx->cfg, copy)) return RIVER_E_BAD_SIZE;
+  const river_config &c = ctx->cfg;
+  drop_graphs(ctx);
+  ctx->built = false;
+  RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads), ctx->stream));
+  LinearShape sh[7];
+  linear_shapes(c, sh);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const river_layer_w &L = ctx->layers[l];
+    const void *src[7] = {L.wq, L.wk, L.wv, L.wo, L.w_gate, L.w_up, L.w_down};
+    for (int i = 0; i < 7; ++i) {
+      size_t co, so;
+      bank_offsets(c, l, i, copy, &co, &so);
+      if (copy) {
+        RV_TRY(hipMemcpyAsync(ctx->bank + co, src[i], (size_t)sh[i].N * sh[i].K * 2,
+                              hipMemcpyDeviceToDevice, ctx->stream));
+      } else {
+        RV_TRY(launch_quantize(static_cast<const uint16_t *>(src[i]), sh[i].N, sh[i].K,
+                               c.group_size, at<uint32_t>(ctx->bank, co), at<uint32_t>(ctx->bank, so),
+                               ctx->stream));
+      }
+    }
+  }
+  ctx->built = true;
+  ctx->exit_mode = mode;
+  ctx->pos = 0;
+  ctx->batch = 0;
+  return RIVER_OK;
+}
+
+int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T, float tau,
+                  float *d_logits, int32_t *d_next) {
+  if (!ctx || !d_tokens) return RIVER_E_INVALID_ARG;
+  if (!std::isfinite(tau)) return RIVER_E_INVALID_ARG;
+  if (!ctx->built) return RIVER_E_STATE;
+  if (B < 1 || T < 1 || B > ctx->cfg.max_batch || T > ctx->cfg.max_seq) return RIVER_E_RANGE;
+  if (B > 8) return RIVER_E_UNIMPLEMENTED;
+  const int st = enqueue_prefill(ctx, d_tokens, B, T, tau, d_logits, d_next);
+  if (st != RIVER_OK) return st;
+  ctx->pos = T;
+  ctx->batch = B;
+  return RIVER_OK;
+}
+
+int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float *d_logits,
+                      int32_t *d_next) {
+  if (!ctx || !d_tokens) return RIVER_E_INVALID_ARG;
+  if (!std::isfinite(tau)) return RIVER_E_INVALID_ARG;
+  if (!ctx->built || ctx->batch == 0) return RIVER_E_STATE;
+  if (ctx->pos + 1 > ctx->cfg.max_seq) return RIVER_E_RANGE;
+  if (ctx->use_graph && ctx->stream != nullptr) {
+    river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E, 0};
+    std::memcpy(&key.tau_bits, &tau, 4);
+    auto it = ctx->graphs.find(key);
+    if (it == ctx->graphs.end()) {
+      hipGraph_t graph;
+      RV_TRY(hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
+      const int st = enqueue_decode(ctx, d_tokens, tau, d_logits, d_next);
+      hipError_t e = hipStreamEndCapture(ctx->stream, &graph);
+      if (st != RIVER_OK) return st;
+      if (e != hipSuccess) return RIVER_E_HIP;
+      hipGraphExec_t exec;
+      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (e != hipSuccess) return RIVER_E_HIP;
+      it = ctx->graphs.emplace(key, exec).first;
+    }
+    RV_TRY(hipGraphLaunch(it->second, ctx->stream));
+  } else {
+    const int st = enqueue_decode(ctx, d_tokens, tau, d_logits, d_next);
+    if (st != RIVER_OK) return st;
+  }
+  ctx->pos += 1;
+  return RIVER_OK;
+}
+
+int river_exit_stats(river_ctx *ctx, river_exit_stats_t *out) {
+  if (!ctx || !out) return RIVER_E_INVALID_ARG;
+  if (!ctx->built) return RIVER_E_STATE;
+  Control h;
+  RV_TRY(hipMemcpyAsync(&h, ctx->ctrl, sizeof(Control), hipMemcpyDeviceToHost, ctx->stream));
+  RV_TRY(hipStreamSynchronize(ctx->stream));
+  std::memset(out, 0, sizeof(*out));
+  const int L = ctx->cfg.n_layers;
+  double sum = 0.0;
+  for (int e = 0; e <= L; ++e) {
+    out->decode_hist[e] = h.decode_hist[e];
+    out->prefill_hist[e] = h.prefill_hist[e];
+    sum += (double)e * (double)h.decode_hist[e];
+  }
+  out->n_decode_steps = h.n_decode;
+  out->n_prefill = h.n_prefill;
+  out->mean_exit_layer = h.n_decode ? sum / (double)h.n_decode : 0.0;
+  out->last_E = h.last_E;
+  out->pos = h.pos;
+  out->token_errors = h.bad_token;
+  for (int l = 0; l < RIVER_MAX_LAYERS; ++l) out->last_trace[l] = l < L ? h.trace[l] : NAN;
+  return RIVER_OK;
+}
+
+int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  switch (option) {
+    case RIVER_OPT_GRAPH:
+      if (value != 0 && value != 1) return RIVER_E_INVALID_ARG;
+      ctx->use_graph = value != 0;
+      return RIVER_OK;
+    case RIVER_OPT_FORCE_E:
+      if (value < -1 || value > ctx->cfg.n_layers) return RIVER_E_RANGE;
+      ctx->force_E = (int)value;
+      return RIVER_OK;
+  }
+  return RIVER_E_INVALID_ARG;
+}
+
+int river_reset(river_ctx *ctx) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  ctx->pos = 0;
+  ctx->batch = 0;
+  return RIVER_OK;
+}
+
+void river_destroy(river_ctx *ctx) {
+  if (!ctx) return;
+  drop_graphs(ctx);
+  delete ctx;
+}
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+// Internal declarations shared by the host scheduler and the HIP kernels of
+// the KV-shared early-exit decoder.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/river.h"
+
+namespace river {
+
+// ---------------------------------------------------------------------------
+// Device control block.  It lives at the start of the caller's control buffer
+// and carries everything a pass decides on the device: the sticky exit flag,
+// the number of backbone layers run, tau, the cache position, the per-layer
+// trace of batch-minimum cosines, histograms of E, and the counters of the
+// "last workgroup finishes the reduction" pattern.  Counters are zero between
+// kernels: the workgroup that finds itself last resets its counter.
+// ---------------------------------------------------------------------------
+constexpr int kMaxLayers = RIVER_MAX_LAYERS;
+constexpr int kNumCounters = 16;
+
+enum CounterId {
+  kCtrExit = 0,       // decode down-projection: exit test after the layer
+  kCtrLogits = 1,     // LM head: argmax hand-off and bookkeeping
+  kCtrRowsCos = 2,    // prefill: cosine minimum over all rows
+};
+
+struct Control {
+  int32_t flag;      // 1 once the exit fired in the current pass
+  int32_t E;         // backbone layers run in the current pass
+  float tau;
+  int32_t pos;       // position the current decode step writes
+  int32_t force_E;   // -1: decide with tau; e >= 0: layers >= e are exit layers
+  int32_t bad_token; // a token id outside [0, vocab) was seen (and clamped)
+  int32_t last_E;
+  int32_t pad0;
+  int64_t n_decode, n_prefill;
+  int64_t decode_hist[kMaxLayers + 1];
+  int64_t prefill_hist[kMaxLayers + 1];
+  float trace[kMaxLayers];
+  uint32_t counters[kNumCounters];
+  // followed by: uint64_t argmax_key[max_batch];
+  //              uint32_t attn_counters[max_batch * n_kv_heads];
+};
+
+__host__ __device__ inline size_t control_bytes(int max_batch, int n_kv_heads) {
+  size_t b = sizeof(Control);
+  b = (b + 7) & ~size_t(7);
+  b += sizeof(uint64_t) * (size_t)max_batch;
+  b += sizeof(uint32_t) * (size_t)max_batch * n_kv_heads;
+  return (b + 255) & ~size_t(255);
+}
+__host__ __device__ inline uint64_t *control_keys(Control *c) {
+  size_t off = (sizeof(Control) + 7) & ~size_t(7);
+  return reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(c) + off);
+}
+__host__ __device__ inline uint32_t *control_attn_counters(Control *c, int max_batch) {
+  return reinterpret_cast<uint32_t *>(control_keys(c) + max_batch);
+}
+
+// ---------------------------------------------------------------------------
+// Exit-bank layout: per layer, per linear (q, k, v, o, gate, up, down), the
+// packed codes then the packed scale/zero words, each region 256-byte aligned.
+// ---------------------------------------------------------------------------
+struct LinearShape {
+  int N, K;
+};
+void linear_shapes(const river_config &c, LinearShape out[7]);
+size_t align256(size_t x);
+// offsets of (layer, linear) in the int4 bank or in the bf16 copy bank
+void bank_offsets(const river_config &c, int layer, int linear, bool copy, size_t *codes,
+                  size_t *sz);
+size_t bank_bytes(const river_config &c, bool copy);
+
+// ---------------------------------------------------------------------------
+// Workspace layout (byte offsets into the caller's workspace buffer).
+// ---------------------------------------------------------------------------
+struct Workspace {
+  size_t hA, hB;       // fp32 residual stream [R][d], layer input / output
+  size_t x;            // bf16 normalised activations [R][max(d, F)] (prefill)
+  size_t q;            // bf16 queries [R][Hq*Dh]
+  size_t attn;         // bf16 attention output [R][Hq*Dh]
+  size_t u;            // bf16 SwiGLU product [R][F]
+  size_t part;         // fp32 per-workgroup partial sums for the exit test
+  size_t attn_part;    // fp32 split-K attention partials
+  size_t total;
+  int64_t rows;        // R: rows the buffers hold
+  int part_floats;
+  int attn_splits;     // split count the decode attention is sized for
+};
+Workspace workspace_layout(const river_config &c);
+
+constexpr int kAttnChunk = 256;   // positions per decode-attention workgroup
+constexpr int kPartFloatsPerWG = 3 * 64;  // B <= 64 rows x (dot, |a|^2, |b|^2)
+
+// ---------------------------------------------------------------------------
+// Kernel launch parameters
+// ---------------------------------------------------------------------------
+enum XSource { kXNorm = 0, kXBf16 = 1 };
+enum Epilogue { kEpQKV = 0, kEpResid = 1, kEpResidExit = 2, kEpSwiGLU = 3, kEpLogits = 4 };
+
+struct LinearWeights {
+  const uint16_t *bf[3];   // backbone bf16 segments (or exit bf16 copies)
+  const uint32_t *q4[3];   // exit int4 code segments
+  const uint32_t *sz[3];   // exit scale/zero segments
+  const uint16_t *ex_bf[3];// exit bf16 copy segments (copy mode)
+  int seg_rows[3];         // physical rows of each segment
+  int nseg;
+};
+
+struct GemvParams {
+  LinearWeights w;
+  int N;            // logical output rows
+  int K;            // input columns
+  int G;            // group size
+  int layer;        // layer index (exit choice); -1: always backbone (LM head)
+  int exit_mode;    // RIVER_EXIT_INT4 or RIVER_EXIT_COPY
+  Control *ctrl;
+  int B;            // batch rows
+  // x source
+  const float *h_src; int64_t h_stride;   // kXNorm: fp32 rows, stride in floats
+  const uint16_t *gain; float eps;
+  const uint16_t *x_src; int64_t x_stride; // kXBf16
+  // epilogues
+  const float *h_in; float *h_out; int64_t h_io_stride;   // residual
+  // (kEpResidExit also reads the layer input through h_src, same stride)
+  uint16_t *q_out; uint16_t *k_cache; uint16_t *v_cache;  // QKV
+  int Hq, Hkv, Dh, max_seq, max_batch; float rope_theta;
+  uint16_t *u_out; int64_t u_stride;                      // SwiGLU
+  float *part;                                            // exit test partials
+  int test_exit; int n_layers;                            // exit test enabled?
+  float *logits; int32_t *next; int is_prefill; int vocab;// LM head
+};
+
+struct AttnParams {
+  const uint16_t *q;      // [B][Hq*Dh]
+  const uint16_t *k_cache, *v_cache;  // layer base: [max_batch][Hkv][S][Dh]
+  uint16_t *out;          // [B][Hq*Dh]
+  float *part;            // [B][Hq][splits][Dh + 2]
+  uint32_t *counters;     // [B][Hkv]
+  Control *ctrl;
+  int B, Hq, Hkv, Dh, S, splits;
+  float scale;
+};
+
+struct BeginParams {
+  Control *ctrl;
+  const int32_t *tokens;
+  int64_t rows;       // tokens to embed
+  int B;              // batch rows (argmax keys to clear)
+  const uint16_t *embed;
+  float *h;
+  int d, vocab, n_layers, force_E;
+  float tau;
+  int is_prefill;
+  int set_pos;        // >= 0: write this position into the control block
+};
+
+// ---- launchers (each returns hipGetLastError() after the launch) ----------
+hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_quantize(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
+                           hipStream_t s);
+hipError_t launch_begin(const BeginParams &p, hipStream_t s);
+hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s);
+hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
+
+// prefill
+struct RowsNormParams {
+  const float *h; uint16_t *x; const uint16_t *gain; int64_t rows; int d; float eps;
+};
+hipError_t launch_rows_norm(const RowsNormParams &p, hipStream_t s);
+
+struct GemmParams {
+  LinearWeights w;
+  int M, N, K, G;
+  int layer, exit_mode;
+  Control *ctrl;
+  const uint16_t *x; int64_t ldx;  // bf16 [M][K]
+  // epilogues (same meaning as GemvParams)
+  const float *h_in; float *h_out; int64_t h_io_stride;
+  uint16_t *q_out; uint16_t *k_cache; uint16_t *v_cache;
+  int Hq, Hkv, Dh, max_seq, max_batch, T; float rope_theta;
+  uint16_t *u_out;
+};
+hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s);
+
+struct AttnPrefillParams {
+  const uint16_t *q;       // [B*T][Hq*Dh]
+  const uint16_t *k_cache, *v_cache;  // layer base [max_batch][Hkv][S][Dh]
+  uint16_t *out;           // [B*T][Hq*Dh]
+  int B, T, Hq, Hkv, Dh, S;
+  float scale;
+};
+hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s);
+
+struct RowsCosParams {
+  const float *a, *b; int64_t rows; int d;
+  float *part; Control *ctrl; int layer; int n_layers;
+};
+hipError_t launch_rows_cos_exit(const RowsCosParams &p, hipStream_t s);
+
+}  // namespace river

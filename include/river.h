@@ -1,0 +1,201 @@
+/*
+ * river.h -- C ABI of the KV-shared early-exit decoder for MI355X (gfx950).
+ *
+ * The method is the one of the page "River-LLM: Large Language Model Seamless
+ * Exit Based on KV Share" (arXiv:2604.18396):
+ *   - section 3: beside every decoder layer sits an exit layer, a full copy of
+ *     the layer's parameters quantised to 4-bit weights with 16-bit activations
+ *     (W4A16), built without training; exit layers write their K/V into the
+ *     cache slot of the original layer, so there is a single shared KV cache
+ *     and later tokens never miss an entry;
+ *   - section 4: after a layer, the state-transition similarity (cosine
+ *     between the layer's input and output residual stream) is taken for every
+ *     token of the batch; if its minimum exceeds tau, all remaining layers run
+ *     as exit layers and no deeper layer tests again;
+ *   - section 5: prefill takes one sequence-level decision for all prompt
+ *     tokens, generation one decision per generated position.
+ *
+ * Conventions shared by every entry point
+ *   - Every device buffer is allocated by the caller and only borrowed by the
+ *     library; it must stay alive until river_destroy().  The library owns only
+ *     its host-side context (and the HIP graphs it records for decode steps).
+ *   - All GPU work is enqueued on the HIP stream given to river_init(); no call
+ *     synchronises except river_exit_stats().  A kernel fault surfaces at the
+ *     next synchronisation, as usual for HIP.
+ *   - Every call returns a river status code.  Arguments and state are checked
+ *     on the host before anything is enqueued; a call that fails enqueues
+ *     nothing and leaves the context unchanged.  No C++ exception crosses the
+ *     ABI.
+ *   - bf16 means bfloat16 stored as 16-bit words; matrices are row-major
+ *     [rows][cols], a linear layer's weight is [out N][in K] (y = x W^T).
+ *   - The context is not thread-safe: calls on one context must not overlap.
+ */
+#ifndef RIVER_H
+#define RIVER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct river_ctx river_ctx; /* opaque, owned by the library */
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  RIVER_OK = 0,
+  RIVER_E_INVALID_ARG = 1,   /* null pointer, bad enum, non-finite tau, ...   */
+  RIVER_E_BAD_SIZE = 2,      /* a buffer smaller than river_query_sizes says  */
+  RIVER_E_STATE = 3,         /* call out of order (e.g. prefill before build) */
+  RIVER_E_RANGE = 4,         /* batch > max_batch, position beyond max_seq    */
+  RIVER_E_HIP = 5,           /* a HIP runtime call or kernel launch failed    */
+  RIVER_E_UNIMPLEMENTED = 6  /* a shape the kernels do not support            */
+};
+
+/* ---- exit-bank construction modes -------------------------------------- */
+enum {
+  RIVER_EXIT_INT4 = 1, /* copy + 4-bit group quantisation (the method)         */
+  RIVER_EXIT_COPY = 2  /* exact bf16 copy: exit layers equal the backbone; used
+                          to check that the exit plumbing changes nothing      */
+};
+
+#define RIVER_MAX_LAYERS 256
+
+/* Decoder shape (Llama-style: pre-norm RMSNorm, GQA attention with rotate-half
+ * RoPE, SwiGLU MLP) and the capacity of the shared KV cache.
+ *   head_dim must be even and at most 128; d_model, head_dim, ffn_dim multiples
+ *   of 8; group_size a multiple of 32 dividing d_model, ffn_dim and
+ *   n_q_heads*head_dim; n_q_heads a multiple of n_kv_heads. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rms_eps, rope_theta;
+  int32_t tied_embeddings; /* 1: the LM head is the embedding matrix          */
+  int32_t group_size;      /* G: input columns sharing one scale/zero          */
+  int32_t max_batch;       /* rows of one decode step (and prefill batch)      */
+  int32_t max_seq;         /* positions the shared cache holds per row         */
+} river_config;
+
+/* One decoder layer's backbone weights, device pointers to bf16:
+ *   attn_norm, mlp_norm [d_model]; wq [Hq*Dh][d]; wk, wv [Hkv*Dh][d];
+ *   wo [d][Hq*Dh]; w_gate, w_up [F][d]; w_down [d][F]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} river_layer_w;
+
+/* Whole-model weights: embed [V][d] bf16, final_norm [d] bf16, lm_head [V][d]
+ * bf16 (NULL when tied_embeddings), layers: HOST array of n_layers entries
+ * (copied by river_init, so it may be freed afterwards). */
+typedef struct {
+  const void *embed, *final_norm, *lm_head;
+  const river_layer_w *layers;
+} river_weights;
+
+/* Device-buffer sizes in bytes, from river_query_sizes(). */
+typedef struct {
+  size_t exit_bank_bytes; /* packed int4 exit layers (river_exit_bank_offsets)    */
+  size_t exit_bank_copy_bytes; /* bank size RIVER_EXIT_COPY needs (bf16 copies)    */
+  size_t kv_cache_bytes;  /* the single shared cache, see below                    */
+  size_t workspace_bytes; /* activations and reduction scratch                     */
+  size_t control_bytes;   /* decision flag, tau, position, histograms, trace       */
+} river_sizes;
+
+/* Statistics read back by river_exit_stats().  E is the number of backbone
+ * layers a pass ran (1..n_layers; n_layers means no exit). */
+typedef struct {
+  int64_t prefill_hist[RIVER_MAX_LAYERS + 1]; /* count of prefills per E        */
+  int64_t decode_hist[RIVER_MAX_LAYERS + 1];  /* count of decode steps per E    */
+  int64_t n_prefill, n_decode_steps;
+  double mean_exit_layer;                     /* mean E over decode steps       */
+  int32_t last_E;                             /* E of the latest pass           */
+  int32_t pos;                                /* next position to be written    */
+  int32_t token_errors;                       /* 1 if a token id outside
+                                                 [0, vocab) was seen; it was
+                                                 replaced by 0                  */
+  float last_trace[RIVER_MAX_LAYERS];         /* latest pass: batch-min cosine
+                                                 after layer l, NaN if untested */
+} river_exit_stats_t;
+
+/* Sizes of the four device buffers the caller must allocate for cfg.
+ * Shared KV cache layout (bf16): K then V, each [L][max_batch][Hkv][max_seq][Dh],
+ * i.e. L*2*Hkv*Dh*2 bytes per token and row; exit layers add no KV bytes.
+ * Returns RIVER_E_INVALID_ARG / RIVER_E_UNIMPLEMENTED for unusable shapes. */
+int river_query_sizes(const river_config *cfg, river_sizes *out);
+
+/* Byte offsets, inside the exit bank, of one exit linear of one layer.
+ * linear: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down.
+ * Packed int4 layout of a linear with N rows and K columns:
+ *   codes: uint32 [N][K/8]; word w of row n holds the codes of columns
+ *          8w..8w+7, column 8w+j in bits 4*(j%4) + 16*(j/4) .. +3;
+ *   sz:    uint32 [N][K/G]; bf16 scale in bits 0..15, bf16 zero in 16..31;
+ *   w_hat = (code - zero) * scale.
+ * In RIVER_EXIT_COPY mode the bank holds bf16 [N][K] copies instead, each
+ * starting at codes_off of the copy layout (pass copy_layout = 1); sz_off is
+ * then unused and set to 0. */
+int river_exit_bank_offsets(const river_config *cfg, int32_t layer, int32_t linear,
+                            int32_t copy_layout, size_t *codes_off, size_t *sz_off);
+
+/* Create a context.  exit_bank, kv_cache, workspace, control: device buffers
+ * of at least the sizes in `given`, which must be no smaller than what
+ * river_query_sizes(cfg) reports (else RIVER_E_BAD_SIZE).  w: backbone weights,
+ * borrowed.  hip_stream: a hipStream_t (NULL = the null stream).  Touches no
+ * device memory and launches nothing; *out receives the new context. */
+int river_init(const river_config *cfg, const river_weights *w, void *exit_bank,
+               void *kv_cache, void *workspace, void *control, const river_sizes *given,
+               void *hip_stream, river_ctx **out);
+
+/* Build the exit layers (section 3 of the lead page: copy every layer's
+ * parameters, then quantise its seven linear matrices to int4; the norm gains
+ * stay as they are and are read from the backbone).  Per (row, group of G
+ * columns), in float32 with every operation separately rounded:
+ *   s = bf16((max - min) / 15), s = 1 if that is 0;  z = bf16(-min / s);
+ *   code = clamp(round_half_even(w / s + z), 0, 15).
+ * mode RIVER_EXIT_COPY stores exact bf16 copies instead and needs a bank of
+ * exit_bank_copy_bytes (else RIVER_E_BAD_SIZE).  Clears the control block and
+ * resets the cache position to 0.  May be called again to rebuild. */
+int river_build_exit_layers(river_ctx *ctx, int32_t mode);
+
+/* Prefill B prompts of T tokens each (d_tokens: device int32 [B][T]) into
+ * positions 0..T-1 of the shared cache, with ONE sequence-level exit decision
+ * per layer: the cosine minimum runs over all B*T rows (section 5).  Writes
+ * fp32 logits of each row's last position to d_logits [B][vocab] and the greedy
+ * token (lowest index on ties) to d_next [B] (int32); either may be NULL.
+ * tau must be finite.  1 <= B <= max_batch, 1 <= T <= max_seq; fixes the batch
+ * size for the following decode steps.  Requires river_build_exit_layers. */
+int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T, float tau,
+                  float *d_logits, int32_t *d_next);
+
+/* One token-level-exit decode step (section 4): d_tokens device int32 [B]
+ * (B from the last prefill) are written at the next position; after each
+ * backbone layer l < L-1 the batch-minimum cosine is compared with tau on the
+ * device and, once it exceeds tau, layers l+1.. run as exit layers.  Outputs
+ * as in river_prefill.  RIVER_E_RANGE when the cache is full. */
+int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float *d_logits,
+                      int32_t *d_next);
+
+/* Copy the statistics to host memory; synchronises the stream. */
+int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
+
+/* Options.
+ *   RIVER_OPT_GRAPH   0/1: record each decode-step configuration once as a HIP
+ *                     graph and replay it (default 1);
+ *   RIVER_OPT_FORCE_E -1 (default) to decide with tau, or e in 0..n_layers to
+ *                     run layers < e on the backbone and the rest as exit
+ *                     layers without testing (e = n_layers: original model,
+ *                     e = 0: every layer quantised). */
+enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2 };
+int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
+
+/* Start a new sequence: position back to 0 (statistics are kept). */
+int river_reset(river_ctx *ctx);
+
+/* Release the host context and its graphs (never the borrowed buffers). */
+void river_destroy(river_ctx *ctx);
+
+/* Text of a status code (static storage). */
+const char *river_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
