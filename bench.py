@@ -1,0 +1,261 @@
+#!/usr/bin/env python
+"""Decode throughput of the KV-shared early-exit decoder on one MI355X.
+
+One "step" is one token-level-exit decode step of the whole decoder (embedding,
+every layer as backbone or exit layer, the exit test after each backbone
+layer, LM head and argmax) for the batch, on synthetic seeded inputs resident
+in HBM.  Default workload: the Llama-3.1-8B shape at batch 1 after a
+512-token prompt, tau = 0.5.
+
+Prints one JSON line with the throughput, a roofline object for the kernel
+class that takes the most time (algorithmic bytes per launch over its mean
+launch duration, timed with HIP events on the library's stream), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s, 8B-shape KV-shared exit, τ=0.5; HBM GB/s as % of peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="8b")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic bytes per launch (what each kernel must move, nothing it avoids)
+# ----------------------------------------------------------------------------
+def linear_bytes(N, K, G, exit_int4):
+    if exit_int4:
+        return N * K // 2 + N * (K // G) * 4   # packed codes + bf16 scale/zero
+    return N * K * 2
+
+
+def kind_bytes(shape, B, kind, exit_path, ctx_len):
+    s = shape
+    d, F, G = s.d_model, s.ffn_dim, s.group_size
+    qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    if kind == "qkv":
+        return (linear_bytes(qd + 2 * kd, d, G, exit_path) + B * d * 4 + B * (qd + 2 * kd) * 2)
+    if kind == "attn":
+        return B * kd * 2 * 2 * ctx_len + B * qd * 2 * 2
+    if kind == "o":
+        return linear_bytes(d, qd, G, exit_path) + B * qd * 2 + B * d * 4 * 2
+    if kind == "gateup":
+        return linear_bytes(2 * F, d, G, exit_path) + B * d * 4 + B * F * 2
+    if kind == "down":
+        return linear_bytes(d, F, G, exit_path) + B * F * 2 + B * d * 4 * 3
+    if kind == "lm_head":
+        return s.vocab * d * 2 + B * d * 4 + B * s.vocab * 4
+    if kind == "begin":
+        return B * d * 2 + B * d * 4
+    return 0
+
+
+def step_bytes(shape, B, E, ctx_len):
+    tot = kind_bytes(shape, B, "begin", False, 0) + kind_bytes(shape, B, "lm_head", False, 0)
+    for layer in range(shape.n_layers):
+        ex = layer >= E
+        for k in ("qkv", "attn", "o", "gateup", "down"):
+            tot += kind_bytes(shape, B, k, ex, ctx_len)
+    return tot
+
+
+def mean_kind_bytes(shape, B, kind, hist, positions):
+    """Mean algorithmic bytes per launch of `kind` over steps whose E values
+    are given by `hist` (count per E) and whose context lengths are `positions`."""
+    L = shape.n_layers
+    steps = sum(hist)
+    if steps == 0:
+        return 0.0
+    mean_ctx = sum(positions) / len(positions)
+    if kind in ("lm_head", "begin"):
+        return float(kind_bytes(shape, B, kind, False, mean_ctx))
+    tot = 0.0
+    for E, n in enumerate(hist):
+        if n == 0:
+            continue
+        for layer in range(L):
+            tot += n * kind_bytes(shape, B, kind, layer >= E, mean_ctx)
+    return tot / (steps * L)
+
+
+# ----------------------------------------------------------------------------
+def cpu_baseline(shape, weights, B, T, mean_E):
+    """The oracle, as it stands, on a bounded sample: one backbone layer, one
+    exit layer (quantised by the oracle itself) and the LM head of the same
+    workload, for one decode position after a T-token context; the step time is
+    assembled as mean_E backbone layers + (L - mean_E) exit layers + LM head."""
+    import numpy as np
+    from oracle import river_oracle as ro
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    s = ro.Shape(**shape.as_dict())
+    lw = {k: v.float().cpu().numpy() for k, v in weights["layers"][0].items()}
+    ex = dict(lw)
+    for name in ro.RiverOracle.LINEARS:
+        q, sc, z = ro.quantize_int4(lw[name], s.G)
+        ex[name] = ro.dequantize_int4(q, sc, z, s.G)
+    lm = (weights["lm_head"] if weights["lm_head"] is not None else weights["embed"]).float().cpu().numpy()
+    fn = weights["final_norm"].float().cpu().numpy()
+    rng = np.random.default_rng(0)
+    S = T + 1
+    kc = ro.bf16_from_f64(rng.standard_normal((B, s.Hkv, S, s.Dh)))
+    vc = ro.bf16_from_f64(rng.standard_normal((B, s.Hkv, S, s.Dh)))
+    h = rng.standard_normal((B, 1, s.d)) * 0.5
+    t0 = time.perf_counter()
+    ro.decoder_layer(s, lw, h, T, kc, vc)
+    t_bb = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ro.decoder_layer(s, ex, h, T, kc, vc)
+    t_ex = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ro.lm_head(s, h[:, -1], fn, lm)
+    t_lm = time.perf_counter() - t0
+    step = mean_E * t_bb + (s.L - mean_E) * t_ex + t_lm
+    return {
+        "value": round(B / step, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"one decode position at context {T}: 1 backbone layer ({t_bb:.2f} s), 1 int4 exit "
+                   f"layer ({t_ex:.2f} s), LM head ({t_lm:.2f} s); step = {mean_E:.2f} x backbone + "
+                   f"{s.L - mean_E:.2f} x exit + LM head = {step:.2f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the decode path is single-GPU; see the sharding design note).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from early_exit_kv_amd import river as rv
+
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    B, T = wl.batch, wl.prompt
+    tau = args.tau if args.tau is not None else wl.taus[len(wl.taus) // 2 if len(wl.taus) > 1 else 0]
+    if args.workload == "8b":
+        tau = 0.5 if args.tau is None else args.tau
+    K, W = args.steps, args.warmup
+    max_seq = T + W + K
+    print(f"[bench] workload {wl.name} B={B} T={T} steps={K} warmup={W} tau={tau}", file=sys.stderr,
+          flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = synth.make_weights(shape, seed=0, device=dev)
+    tokens = synth.make_tokens(shape, B, T, seed=0).to(dev)
+    r = rv.River(shape, weights, B, max_seq)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r.build_exit_layers("int4")
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    _, nxt = r.prefill(tokens, tau, want_logits=False)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    st0 = r.exit_stats()
+    prefill_E = st0["last_E"]
+
+    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    bufs[0].copy_(nxt)
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+
+    def run(n, start):
+        for i in range(n):
+            j = start + i
+            r.decode_step(bufs[j % 2], tau, logits=logits, next_tok=bufs[(j + 1) % 2])
+
+    run(W, 0)
+    torch.cuda.synchronize()
+    hist0 = r.exit_stats()["decode_hist"]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(K, W)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    hist1 = r.exit_stats()["decode_hist"]
+    hist = [a - b for a, b in zip(hist1, hist0)]
+    mean_E = sum(e * n for e, n in enumerate(hist)) / max(1, sum(hist))
+    positions = [T + W + i + 1 for i in range(K)]
+    tok_s = B * K / elapsed
+    ms_step = elapsed / K * 1e3
+    avg_step_bytes = sum(n * step_bytes(shape, B, e, sum(positions) / K) for e, n in enumerate(hist)) / K
+    step_gbs = avg_step_bytes / (elapsed / K) / 1e9
+
+    roofline = None
+    kinds = {}
+    if not args.no_profile:
+        # same workload again, eager launches with HIP events around every kernel
+        r.reset()
+        _, nxt = r.prefill(tokens, tau, want_logits=False)
+        bufs[0].copy_(nxt)
+        run(W, 0)
+        r.profile(True)
+        h0 = r.exit_stats()["decode_hist"]
+        r.profile_read()
+        run(K, W)
+        times = r.profile_read()
+        h1 = r.exit_stats()["decode_hist"]
+        r.profile(False)
+        phist = [a - b for a, b in zip(h1, h0)]
+        for kind, (n, ms) in times.items():
+            if n == 0 or kind.startswith("p_"):
+                continue
+            mb = mean_kind_bytes(shape, B, kind, phist, positions)
+            avg_us = ms / n * 1e3
+            kinds[kind] = {"launches": n, "avg_us": round(avg_us, 3), "total_ms": round(ms, 3),
+                           "avg_bytes": int(mb), "gbs": round(mb / (avg_us * 1e-6) / 1e9, 1)}
+        dom = max(kinds, key=lambda k: kinds[k]["total_ms"])
+        dk = kinds[dom]
+        achieved = dk["avg_bytes"] / (dk["avg_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, weights, B, T, mean_E)
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, uniform tokens)",
+        "config": {"workload": wl.name, "shape": shape.name, "batch": B, "prompt": T, "tau": tau,
+                   "exit_layers": "int4 g%d" % shape.group_size},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_hbm_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "mean_exit_layer": round(mean_E, 3), "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
+        "prefill_tok_s": round(B * T / prefill_s, 1), "prefill_E": prefill_E,
+        "build_exit_layers_s": round(build_s, 4), "kernels": kinds,
+    }
+    r.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

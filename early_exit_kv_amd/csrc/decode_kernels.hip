@@ -73,22 +73,35 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
 }
 
 // ===========================================================================
-// Row mapping of the fused linears.
-//   QKV: logical rows come in RoPE pairs: logical 2P, 2P+1 are rows i and
-//        i + Dh/2 of head hh, with P = hh*(Dh/2) + i, heads ordered q, k, v.
-//   SwiGLU: each workgroup's first half of rows are gate rows, second half the
-//        up rows with the same indices.
+// GEMV: y[b][n] = sum_k x[b][k] W[n][k] for B <= M batch rows.
+//
+// Work split: a workgroup is 4 wavefronts; each wavefront owns R consecutive
+// logical rows and splits K across its 64 lanes in 16-byte chunks (8 bf16
+// weights or 32 int4 codes), with U chunks per lane issued before any of them
+// is used.  Workgroups stride over row blocks, so the activation vector is
+// staged into LDS once per workgroup.  Logical rows are mapped per fused
+// linear: QKV rows come in RoPE pairs (rows i and i + Dh/2 of one head), and
+// each wavefront of the gate|up linear owns R/2 gate rows and the R/2 up rows
+// with the same indices, so every epilogue is local to its wavefront.
+//
+// Activations sit in LDS as bf16 pairs, laid out for the weight format:
+// natural order for bf16 weights, nibble order for int4 (pair j of word w =
+// columns 8w+j and 8w+4+j).  An int4 code pair becomes the bf16 pair
+// (128+q_a, 128+q_b) with one and-or, so
+//   sum_k x_k (q_k - z) s = s * (dot(x, 128+q) - (128 + z) * sum_k x_k)
+// and each 32-code chunk lies inside one quantisation group.
 // ===========================================================================
+constexpr int kXLdsBytes = 64 * 1024;
+
 struct RowRef {
   int seg, row;
   bool valid;
 };
 
 template <int EP>
-__device__ __forceinline__ RowRef map_row(const GemvParams &p, int blk, int RW, int j) {
+__device__ __forceinline__ RowRef map_row(const GemvParams &p, int L, int wave_first, int R) {
   RowRef r;
   if constexpr (EP == kEpQKV) {
-    const int L = blk * RW + j;
     const int half = p.Dh >> 1;
     const int P = L >> 1;
     const int hh = P / half, i = P % half;
@@ -99,502 +112,780 @@ __device__ __forceinline__ RowRef map_row(const GemvParams &p, int blk, int RW, 
     else if (fused < qrows + krows) { r.seg = 1; r.row = fused - qrows; }
     else { r.seg = 2; r.row = fused - qrows - krows; }
   } else if constexpr (EP == kEpSwiGLU) {
-    const int hw = RW >> 1;
+    const int hw = R >> 1, j = L - wave_first;
     r.seg = j < hw ? 0 : 1;
-    r.row = blk * hw + (j < hw ? j : j - hw);
+    r.row = (wave_first >> 1) + (j < hw ? j : j - hw);
     r.valid = r.row < p.w.seg_rows[0];
   } else {
     r.seg = 0;
-    r.row = blk * RW + j;
-    r.valid = r.row < p.N;
+    r.row = L;
+    r.valid = L < p.N;
   }
   return r;
 }
 
-// ===========================================================================
-// GEMV: y[b][n] = sum_k x[b][k] W[n][k] for B <= M rows.
-//   Threads of a workgroup form 256/tpr groups of tpr threads; each group owns
-//   R output rows and splits K into 16-byte chunks (8 bf16 weights or 32 int4
-//   codes).  The activation slab sits in LDS as bf16 pairs, laid out for the
-//   weight format: natural order for bf16, nibble order for int4 (pair j of
-//   word w = columns 8w+j and 8w+4+j).
-//   int4: a code pair is turned into the bf16 pair (128+q_a, 128+q_b) with one
-//   and-or, so sum x(q - z) = dot(x, 128+q) - (128 + z) * sum(x); each 32-code
-//   chunk lies in one quantisation group, whose (s, z) finishes the chunk.
-// ===========================================================================
-constexpr int kXLdsBytes = 48 * 1024;
+// int4 codes of one 32-bit word (column 8w+j in bits 4j..4j+3) as the four
+// bf16 pairs (128+q_a, 128+q_b) for the column pairs (0,2) (4,6) (1,3) (5,7)
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&pr)[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  pr[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x05010400u);
+  pr[1] = __builtin_amdgcn_perm(0x43434343u, lo, 0x05030402u);
+  pr[2] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05010400u);
+  pr[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05030402u);
+}
 
-template <int M, int R, int XS, int EP>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int tpr, int kslab) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t *xl = reinterpret_cast<uint32_t *>(smem);                      // [M][kslab/2]
-  float *xs = reinterpret_cast<float *>(smem + (size_t)M * kslab * 2);     // [M][kslab/32]
-  __shared__ float red[4][R * M];
-  __shared__ float outv[16][M];   // RW <= 16 rows
-  __shared__ float rstd_s[M];
-  __shared__ float bred[8];
+// Row groups, chunks per lane and activation layout of one GEMV launch.
+//   R rows per wavefront task; UQ int4 chunks or UB bf16 chunks per lane are
+//   loaded together (16 loads of 16 bytes in flight per lane in the common
+//   shapes), so the chip keeps tens of MB of weight reads outstanding.
+template <int EP> struct GemvTile;
+template <> struct GemvTile<kEpQKV> { static constexpr int R = 4, UQ = 2, UB = 2; };
+template <> struct GemvTile<kEpResid> { static constexpr int R = 4, UQ = 2, UB = 2; };
+template <> struct GemvTile<kEpSwiGLU> { static constexpr int R = 8, UQ = 2, UB = 2; };
+template <> struct GemvTile<kEpResidExit> { static constexpr int R = 2, UQ = 8, UB = 8; };
+template <> struct GemvTile<kEpLogits> { static constexpr int R = 2, UQ = 8, UB = 8; };
+
+template <int M, int XS, int EP>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int ntask) {
+  constexpr int R = GemvTile<EP>::R, UQ = GemvTile<EP>::UQ, UB = GemvTile<EP>::UB;
+  constexpr int UMAX = UQ > UB ? UQ : UB;
+  extern __shared__ uint4 smem4[];
+  uint32_t *xl = reinterpret_cast<uint32_t *>(smem4);            // [M][kslab/2] bf16 pairs
+  float *xs = reinterpret_cast<float *>(xl + M * (kslab >> 1));  // [M][kslab/32] chunk sums
+  constexpr int NS = 4 * M;   // prologue sums: M norms, then 3 exit sums per batch row
+  __shared__ float pred[4][NS];
+  __shared__ float wred[4][R * M][3];
+  __shared__ uint64_t wkey[4][R * M];
   __shared__ int last_flag;
 
-  const bool ex = layer_uses_exit(p.ctrl, p.layer);
-  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
-  const int groups = 256 / tpr;
-  const int RW = groups * R;
-  const int g = threadIdx.x / tpr, tl = threadIdx.x % tpr;
-  const int blk = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  // the wavefront index is uniform: keep it (and all row addresses) in SGPRs
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = p.K, KW = K >> 3, KG = K >> p.gshift;
+  Control *ctl = p.ctrl;
+  const int half = kslab >> 1;
+  const bool single = K <= kslab;
+  const int wstride = gridDim.x * 4;   // wavefront tasks are strided over all wavefronts
 
-  const uint16_t *wrow_bf[R];
-  const uint32_t *wrow_q4[R];
-  const uint32_t *wrow_sz[R];
-  bool rvalid[R];
-  const int KW = p.K / 8;        // code words per row
-  const int KG = p.K / p.G;      // groups per row
+  // ---- exit choice as far as it is known before the pending test (if any)
+  const int flag0 = __hip_atomic_load(&ctl->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool pending = EP == kEpQKV && p.test_prev && ctl->force_E < 0 && flag0 == 0;
+  bool ex = (EP == kEpQKV && flag0 != 0) || layer_uses_exit(ctl, p.layer);
+  bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+
+  const uint16_t *wbf[R];
+  const uint32_t *wq[R];
+  const uint32_t *wz[R];
+  bool rv[R];
+  auto setup_rows = [&](int task) {
+    const int first = task * R;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    RowRef rr = map_row<EP>(p, blk, RW, g * R + r);
-    rvalid[r] = rr.valid;
-    const int row = rr.valid ? rr.row : 0;
-    const uint16_t *bf = ex ? p.w.ex_bf[rr.seg] : p.w.bf[rr.seg];
-    wrow_bf[r] = bf ? bf + (int64_t)row * p.K : nullptr;
-    wrow_q4[r] = q4 ? p.w.q4[rr.seg] + (int64_t)row * KW : nullptr;
-    wrow_sz[r] = q4 ? p.w.sz[rr.seg] + (int64_t)row * KG : nullptr;
-  }
-
-  // RMSNorm prologue: 1/sqrt(mean(h^2) + eps) per batch row
-  if constexpr (XS == kXNorm) {
-    for (int b = 0; b < M; ++b) {
-      float ss = 0.f;
-      if (b < p.B) {
-        const float *h = p.h_src + (int64_t)b * p.h_stride;
-        for (int k = threadIdx.x * 4; k < p.K; k += 1024) {
-          float4 v = *reinterpret_cast<const float4 *>(h + k);
-          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-      }
-      ss = block_sum(ss, bred);
-      if (threadIdx.x == 0) rstd_s[b] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+    for (int r = 0; r < R; ++r) {
+      const RowRef rr = map_row<EP>(p, first + r, first, R);
+      rv[r] = rr.valid;
+      const int row = rr.valid ? rr.row : 0;
+      const uint16_t *bf = ex ? p.w.ex_bf[rr.seg] : p.w.bf[rr.seg];
+      wbf[r] = q4 ? nullptr : bf + (int64_t)row * K;
+      wq[r] = q4 ? p.w.q4[rr.seg] + (int64_t)row * KW : nullptr;
+      wz[r] = q4 ? p.w.sz[rr.seg] + (int64_t)row * KG : nullptr;
     }
-    __syncthreads();
-  }
-
-  float acc[R][M];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int b = 0; b < M; ++b) acc[r][b] = 0.f;
-
-  for (int k0 = 0; k0 < p.K; k0 += kslab) {
-    const int ks = min(kslab, p.K - k0);
-    __syncthreads();
-    // ---- stage the activation slab as bf16 pairs
-    const int npair = ks >> 1;
-    for (int idx = threadIdx.x; idx < M * npair; idx += 256) {
-      const int b = idx / npair, pr = idx % npair;
-      int c0, c1;
-      if (q4) { const int w = pr >> 2, j = pr & 3; c0 = 8 * w + j; c1 = c0 + 4; }
-      else { c0 = 2 * pr; c1 = c0 + 1; }
-      uint32_t v = 0;
-      if (b < p.B) {
-        if constexpr (XS == kXNorm) {
-          const float *h = p.h_src + (int64_t)b * p.h_stride + k0;
-          const float rs = rstd_s[b];
-          v = pack_bf2(h[c0] * rs * bf2f(p.gain[k0 + c0]), h[c1] * rs * bf2f(p.gain[k0 + c1]));
-        } else {
-          const uint16_t *x = p.x_src + (int64_t)b * p.x_stride + k0;
-          v = (uint32_t)x[c0] | ((uint32_t)x[c1] << 16);
-        }
-      }
-      xl[b * npair + pr] = v;
-    }
+  };
+  uint4 wv[UMAX][R];
+  uint32_t zv[UQ][R];
+  auto load_batch = [&](int k0, int nch, int c0) {
     if (q4) {
-      __syncthreads();
-      const int nch = ks >> 5;
-      for (int idx = threadIdx.x; idx < M * nch; idx += 256) {
-        const int b = idx / nch, ch = idx % nch;
-        const uint32_t *src = xl + b * npair + ch * 16;
-        float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s += bf_lo(src[i]) + bf_hi(src[i]);
-        xs[b * (kslab >> 5) + ch] = s;
-      }
-    }
-    __syncthreads();
-
-    if (q4) {
-      // ---- int4 exit layer: 32 codes per 16-byte chunk
-      const int nch = ks >> 5;
-      for (int c = tl; c < nch; c += tpr) {
-        uint4 wv[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          wv[r] = rvalid[r] ? *reinterpret_cast<const uint4 *>(wrow_q4[r] + (k0 >> 3) + 4 * c)
-                            : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        const int grp = (k0 + 32 * c) / p.G;
-        float sc[R], zz[R];
+      for (int u = 0; u < UQ; ++u) {
+        const int c = c0 + 64 * u;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const uint32_t szw = rvalid[r] ? wrow_sz[r][grp] : 0u;
-          sc[r] = bf_lo(szw);
-          zz[r] = 128.0f + bf_hi(szw);
+          const bool ok = c < nch && rv[r];
+          wv[u][r] = ok ? *reinterpret_cast<const uint4 *>(wq[r] + (k0 >> 3) + 4 * c)
+                        : make_uint4(0, 0, 0, 0);
+          zv[u][r] = ok ? wz[r][(k0 + 32 * c) >> p.gshift] : 0u;
         }
+      }
+    } else {
 #pragma unroll
-        for (int b = 0; b < M; ++b) {
-          const uint4 *xp = reinterpret_cast<const uint4 *>(xl + b * npair + c * 16);
-          const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
-          const float xsum = xs[b * (kslab >> 5) + c];
-          const uint32_t xa[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                   x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+      for (int u = 0; u < UB; ++u) {
+        const int c = c0 + 64 * u;
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const uint32_t wd[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
-            float d = 0.f;
+        for (int r = 0; r < R; ++r) {
+          const bool ok = c < nch && rv[r];
+          wv[u][r] = ok ? *reinterpret_cast<const uint4 *>(wbf[r] + k0 + 8 * c)
+                        : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto nchunks = [&](int ks) { return q4 ? (ks >> 5) : (ks >> 3); };
+  auto per_iter = [&]() { return 64 * (q4 ? UQ : UB); };
+  float acc[R][M];
+  auto compute_batch = [&](int nch, int c0) {
+    if (q4) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+      for (int u = 0; u < UQ; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nch) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t pairw = ((wd[i] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
-                d = dot2_bf16(pairw, xa[i * 4 + j], d);
-              }
+          for (int b = 0; b < M; ++b) {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(xl + b * half + c * 16);
+            const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+            const float xsum = xs[b * (kslab >> 5) + c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              uint32_t pr[4];
+              float d = 0.f;
+              unpack_word(wv[u][r].x, pr);
+              d = dot2_bf16(pr[0], x0.x, d); d = dot2_bf16(pr[1], x0.y, d);
+              d = dot2_bf16(pr[2], x0.z, d); d = dot2_bf16(pr[3], x0.w, d);
+              unpack_word(wv[u][r].y, pr);
+              d = dot2_bf16(pr[0], x1.x, d); d = dot2_bf16(pr[1], x1.y, d);
+              d = dot2_bf16(pr[2], x1.z, d); d = dot2_bf16(pr[3], x1.w, d);
+              unpack_word(wv[u][r].z, pr);
+              d = dot2_bf16(pr[0], x2.x, d); d = dot2_bf16(pr[1], x2.y, d);
+              d = dot2_bf16(pr[2], x2.z, d); d = dot2_bf16(pr[3], x2.w, d);
+              unpack_word(wv[u][r].w, pr);
+              d = dot2_bf16(pr[0], x3.x, d); d = dot2_bf16(pr[1], x3.y, d);
+              d = dot2_bf16(pr[2], x3.z, d); d = dot2_bf16(pr[3], x3.w, d);
+              const float sc = bf_lo(zv[u][r]);
+              const float zo = 128.0f + bf_hi(zv[u][r]);
+              acc[r][b] = fmaf(sc, d - zo * xsum, acc[r][b]);
             }
-            acc[r][b] = fmaf(sc[r], d - zz[r] * xsum, acc[r][b]);
           }
         }
       }
     } else {
-      // ---- bf16 weights (backbone, LM head, or exit copies)
-      const int nch = ks >> 3;
-      for (int c = tl; c < nch; c += tpr) {
-        uint4 wv[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          wv[r] = rvalid[r] ? *reinterpret_cast<const uint4 *>(wrow_bf[r] + k0 + 8 * c)
-                            : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < UB; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nch) {
 #pragma unroll
-        for (int b = 0; b < M; ++b) {
-          const uint4 xv = *reinterpret_cast<const uint4 *>(xl + b * npair + 4 * c);
+          for (int b = 0; b < M; ++b) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xl + b * half + 4 * c);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            float d = acc[r][b];
-            d = dot2_bf16(wv[r].x, xv.x, d);
-            d = dot2_bf16(wv[r].y, xv.y, d);
-            d = dot2_bf16(wv[r].z, xv.z, d);
-            d = dot2_bf16(wv[r].w, xv.w, d);
-            acc[r][b] = d;
+            for (int r = 0; r < R; ++r) {
+              float d = acc[r][b];
+              d = dot2_bf16(wv[u][r].x, xv.x, d);
+              d = dot2_bf16(wv[u][r].y, xv.y, d);
+              d = dot2_bf16(wv[u][r].z, xv.z, d);
+              d = dot2_bf16(wv[u][r].w, xv.w, d);
+              acc[r][b] = d;
+            }
           }
         }
       }
     }
-  }
+  };
 
-  // ---- reduce over the tpr threads of each group
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // ---- prologue.  Its own loads go first (RMSNorm statistics; for the first
+  // kernel of a layer also the previous layer's exit sums); the first weight
+  // batch is issued right behind them, so the weights stream in while the
+  // prologue reduces and stages the activations.
+  const int n8 = K >> 3;
+  float sums[NS];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int i = 0; i < NS; ++i) sums[i] = 0.f;
+  if constexpr (XS == kXNorm) {
+    for (int idx = threadIdx.x; idx < M * n8; idx += 256) {
+      const int b = idx / n8, g8 = idx - b * n8;
+      if (b < p.B) {
+        const float *h = p.h_src + (int64_t)b * p.h_stride + 8 * g8;
+        const float4 a0 = *reinterpret_cast<const float4 *>(h);
+        const float4 a1 = *reinterpret_cast<const float4 *>(h + 4);
+        const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
+                         a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+#pragma unroll
+        for (int bb = 0; bb < M; ++bb) sums[bb] += bb == b ? ss : 0.f;
+      }
+    }
+  }
+  if (pending) {
+    for (int wg = threadIdx.x; wg < p.part_wgs; wg += 256) {
+      const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
+#pragma unroll
+      for (int b = 0; b < M; ++b) {
+        if (b < p.B) {
+          sums[M + 3 * b] += pp[3 * b];
+          sums[M + 3 * b + 1] += pp[3 * b + 1];
+          sums[M + 3 * b + 2] += pp[3 * b + 2];
+        }
+      }
+    }
+  }
+  int task = blockIdx.x * 4 + wid;
+  setup_rows(task);
+  load_batch(0, nchunks(min(kslab, K)), lane);
+
+  if (XS == kXNorm || pending) {
+    if (XS == kXNorm) {
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const float v = wave_sum_uniform(sums[i]);
+        if (lane == 0) pred[wid][i] = v;
+      }
+    }
+    if (pending) {
+#pragma unroll
+      for (int i = M; i < NS; ++i) {
+        const float v = wave_sum_uniform(sums[i]);
+        if (lane == 0) pred[wid][i] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sums[i] = (pred[0][i] + pred[1][i]) + (pred[2][i] + pred[3][i]);
+  }
+  if (pending) {
+    // exit decision of the previous layer (lead page, section 4): the minimum
+    // over the batch of cos(layer input, layer output) must exceed tau.  Every
+    // workgroup reaches the same result from the same sums; workgroup 0
+    // records it.
+    float mcos = 2.0f;
 #pragma unroll
     for (int b = 0; b < M; ++b) {
-      float v = wave_sum(acc[r][b]);
-      if (lane == 0) red[wid][r * M + b] = v;
+      if (b < p.B) {
+        const float sd = sums[M + 3 * b], sa = sums[M + 3 * b + 1], sb = sums[M + 3 * b + 2];
+        float cs = sd / fmaxf(sqrtf(sa) * sqrtf(sb), 1e-8f);
+        cs = fminf(fmaxf(cs, -1.0f), 1.0f);
+        mcos = fminf(mcos, cs);
+      }
     }
-  __syncthreads();
-  const int wpg = tpr >> 6;  // waves per group
-  for (int idx = threadIdx.x; idx < RW * M; idx += 256) {
-    const int j = idx / M, b = idx % M;
-    const int gg = j / R, r = j % R;
-    float s = 0.f;
-    for (int w = 0; w < wpg; ++w) s += red[gg * wpg + w][r * M + b];
-    outv[j][b] = s;
+    const bool fired = mcos > ctl->tau;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      ctl->trace[p.layer - 1] = mcos;
+      if (fired) {
+        ctl->E = p.layer;
+        __hip_atomic_store(&ctl->flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (fired) {  // the guess was the backbone: fetch the exit layer instead
+      ex = true;
+      q4 = p.exit_mode == RIVER_EXIT_INT4;
+      setup_rows(task);
+      load_batch(0, nchunks(min(kslab, K)), lane);
+    }
   }
-  __syncthreads();
 
-  // ---- epilogues
-  if constexpr (EP == kEpQKV) {
-    const int pos = p.ctrl->pos;
-    const int half = p.Dh >> 1;
-    for (int idx = threadIdx.x; idx < (RW >> 1) * M; idx += 256) {
-      const int pp = idx / M, b = idx % M;
-      if (b >= p.B) continue;
-      const int L0 = blk * RW + 2 * pp;
-      if (L0 >= p.N) continue;
-      const int P = L0 >> 1;
-      const int hh = P / half, i = P % half;
-      float y0 = outv[2 * pp][b], y1 = outv[2 * pp + 1][b];
-      if (hh < p.Hq + p.Hkv) {
-        const double ang = (double)pos * pow((double)p.rope_theta, -2.0 * i / (double)p.Dh);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        const float c = (float)cs, s = (float)sn;
-        const float a = y0 * c - y1 * s;
-        const float bb = y1 * c + y0 * s;
-        y0 = a;
-        y1 = bb;
+  // ---- stage x[:, k0:k0+ks] as bf16 pairs in the order of the weight format,
+  //      and the sum of every 32-column chunk for the int4 fold
+  auto stage = [&](int k0, int ks) {
+    const int m8 = ks >> 3;
+    for (int idx = threadIdx.x; idx < M * m8; idx += 256) {
+      const int b = idx / m8, g8 = idx - b * m8;
+      const int col = k0 + 8 * g8;
+      uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;   // natural pairs (0,1) (2,3) (4,5) (6,7)
+      float csum = 0.f;
+      if (b < p.B) {
+        if constexpr (XS == kXNorm) {
+          const float *h = p.h_src + (int64_t)b * p.h_stride + col;
+          const float4 h0 = *reinterpret_cast<const float4 *>(h);
+          const float4 h1 = *reinterpret_cast<const float4 *>(h + 4);
+          const uint4 g = *reinterpret_cast<const uint4 *>(p.gain + col);
+          float ssb = 0.f;
+#pragma unroll
+          for (int bb = 0; bb < M; ++bb) ssb = bb == b ? sums[bb] : ssb;
+          const float rs = 1.0f / sqrtf(ssb / (float)K + p.eps);
+          a0 = pack_bf2(h0.x * rs * bf_lo(g.x), h0.y * rs * bf_hi(g.x));
+          a1 = pack_bf2(h0.z * rs * bf_lo(g.y), h0.w * rs * bf_hi(g.y));
+          a2 = pack_bf2(h1.x * rs * bf_lo(g.z), h1.y * rs * bf_hi(g.z));
+          a3 = pack_bf2(h1.z * rs * bf_lo(g.w), h1.w * rs * bf_hi(g.w));
+        } else {
+          const uint4 v = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)b * p.x_stride + col);
+          a0 = v.x; a1 = v.y; a2 = v.z; a3 = v.w;
+        }
+        csum = (bf_lo(a0) + bf_hi(a0)) + (bf_lo(a1) + bf_hi(a1)) + (bf_lo(a2) + bf_hi(a2)) +
+               (bf_lo(a3) + bf_hi(a3));
       }
-      if (hh < p.Hq) {
-        uint16_t *q = p.q_out + (int64_t)b * p.Hq * p.Dh + hh * p.Dh;
-        q[i] = f2bf(y0);
-        q[i + half] = f2bf(y1);
+      uint4 o;
+      if (q4) {  // column pairs (0,2) (4,6) (1,3) (5,7), as unpack_word makes them
+        o.x = (a0 & 0xFFFFu) | (a1 << 16);
+        o.y = (a2 & 0xFFFFu) | (a3 << 16);
+        o.z = (a0 >> 16) | (a1 & 0xFFFF0000u);
+        o.w = (a2 >> 16) | (a3 & 0xFFFF0000u);
+        // the four items of a 32-column chunk sit in four adjacent lanes
+        csum += dpp<kDppXor1>(csum);
+        csum += dpp<kDppXor2>(csum);
+        if ((g8 & 3) == 0) xs[b * (kslab >> 5) + (g8 >> 2)] = csum;
       } else {
-        const bool isk = hh < p.Hq + p.Hkv;
-        const int kvh = isk ? hh - p.Hq : hh - p.Hq - p.Hkv;
-        uint16_t *base = isk ? p.k_cache : p.v_cache;
-        uint16_t *dst = base + (((int64_t)b * p.Hkv + kvh) * p.max_seq + pos) * p.Dh;
-        dst[i] = f2bf(y0);
-        dst[i + half] = f2bf(y1);
+        o = make_uint4(a0, a1, a2, a3);
+      }
+      *reinterpret_cast<uint4 *>(xl + b * half + 4 * g8) = o;
+    }
+    __syncthreads();
+  };
+
+  // lane-local epilogue state kept across tasks
+  float ed = 0.f, ea = 0.f, eb = 0.f;
+  uint64_t best = 0;
+  const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && ctl->force_E < 0;
+
+  auto finish_task = [&](int first) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < M; ++b) acc[r][b] = wave_sum_uniform(acc[r][b]);
+    auto pick = [&](int r, int b) {
+      float v = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int bb = 0; bb < M; ++bb)
+          if (rr == r && bb == b) v = acc[rr][bb];
+      return v;
+    };
+    if constexpr (EP == kEpQKV) {
+      if (lane < (R / 2) * M) {
+        const int pp = lane / M, b = lane % M;
+        const int L0 = first + 2 * pp;
+        if (b < p.B && L0 < p.N) {
+          const int hd = p.Dh >> 1;
+          const int P = L0 >> 1;
+          const int hh = P / hd, i = P % hd;
+          float y0 = pick(2 * pp, b), y1 = pick(2 * pp + 1, b);
+          const int pos = ctl->pos;
+          if (hh < p.Hq + p.Hkv) {
+            const float2 cs = p.rope[(int64_t)pos * hd + i];
+            const float a = y0 * cs.x - y1 * cs.y;
+            y1 = y1 * cs.x + y0 * cs.y;
+            y0 = a;
+          }
+          if (hh < p.Hq) {
+            uint16_t *q = p.q_out + (int64_t)b * p.Hq * p.Dh + hh * p.Dh;
+            q[i] = f2bf(y0);
+            q[i + hd] = f2bf(y1);
+          } else {
+            const bool isk = hh < p.Hq + p.Hkv;
+            const int kvh = isk ? hh - p.Hq : hh - p.Hq - p.Hkv;
+            uint16_t *dst = (isk ? p.k_cache : p.v_cache) +
+                            (((int64_t)b * p.Hkv + kvh) * p.max_seq + pos) * p.Dh;
+            dst[i] = f2bf(y0);
+            dst[i + hd] = f2bf(y1);
+          }
+        }
+      }
+    } else if constexpr (EP == kEpSwiGLU) {
+      if (lane < (R / 2) * M) {
+        const int jj = lane / M, b = lane % M;
+        const int n = (first >> 1) + jj;
+        if (b < p.B && n < p.w.seg_rows[0]) {
+          const float gt = pick(jj, b), up = pick(R / 2 + jj, b);
+          p.u_out[(int64_t)b * p.u_stride + n] = f2bf(gt / (1.0f + expf(-gt)) * up);
+        }
+      }
+    } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
+      if (lane < R * M) {
+        const int r = lane / M, b = lane % M;
+        const int n = first + r;
+        if (b < p.B && n < p.N) {
+          const int64_t o = (int64_t)b * p.h_io_stride + n;
+          const float v = p.h_in[o] + pick(r, b);
+          p.h_out[o] = v;
+          if (exit_sums) {
+            const float a = p.h_src[o];
+            ed += a * v;
+            ea += a * a;
+            eb += v * v;
+          }
+        }
+      }
+    } else if constexpr (EP == kEpLogits) {
+      if (lane < R * M) {
+        const int r = lane / M, b = lane % M;
+        const int n = first + r;
+        if (b < p.B && n < p.N) {
+          const float v = pick(r, b);
+          if (p.logits) p.logits[(int64_t)b * p.vocab + n] = v;
+          const uint64_t key = ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+          best = key > best ? key : best;
+        }
       }
     }
-  } else if constexpr (EP == kEpSwiGLU) {
-    const int hw = RW >> 1;
-    for (int idx = threadIdx.x; idx < hw * M; idx += 256) {
-      const int jj = idx / M, b = idx % M;
-      const int n = blk * hw + jj;
-      if (b >= p.B || n >= p.w.seg_rows[0]) continue;
-      const float gt = outv[jj][b], up = outv[hw + jj][b];
-      const float si = gt / (1.0f + expf(-gt));
-      p.u_out[(int64_t)b * p.u_stride + n] = f2bf(si * up);
-    }
-  } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
-    for (int idx = threadIdx.x; idx < RW * M; idx += 256) {
-      const int j = idx % RW, b = idx / RW;
-      const int n = blk * RW + j;
-      if (b >= p.B || n >= p.N) continue;
-      const int64_t o = (int64_t)b * p.h_io_stride + n;
-      const float v = p.h_in[o] + outv[j][b];
-      p.h_out[o] = v;
-      outv[j][b] = v;   // kept for the exit sums below (same thread, same slot)
-    }
-    if constexpr (EP == kEpResidExit) {
-      // every workgroup read the same flag at its start, so all of them agree
-      // on whether this layer is tested (no re-check once the exit fired)
-      if (p.test_exit && !ex && p.ctrl->force_E < 0) {
-        // per-workgroup partial sums of <a,b>, |a|^2, |b|^2 for each batch row,
-        // a = layer input, b = layer output, over this workgroup's rows
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < M; ++b) acc[r][b] = 0.f;
+  };
+
+  bool prefetched = true;
+  if (single) stage(0, K);
+  for (; task < ntask; task += wstride) {
+    if (!prefetched) setup_rows(task);
+    zero_acc();
+    for (int k0 = 0; k0 < K; k0 += kslab) {
+      const int ks = min(kslab, K - k0);
+      if (!single) {
         __syncthreads();
-        for (int b = 0; b < M; ++b) {
-          float sd = 0.f, sa = 0.f, sb = 0.f;
-          if (b < p.B && threadIdx.x < RW) {
-            const int n = blk * RW + threadIdx.x;
-            if (n < p.N) {
-              const float a = p.h_src[(int64_t)b * p.h_io_stride + n];
-              const float v = outv[threadIdx.x][b];
-              sd = a * v; sa = a * a; sb = v * v;
-            }
-          }
-          sd = block_sum(sd, bred);
-          sa = block_sum(sa, bred);
-          sb = block_sum(sb, bred);
-          if (threadIdx.x == 0 && b < p.B) {
-            float *pp = p.part + (int64_t)blk * kPartFloatsPerWG + 3 * b;
-            pp[0] = sd; pp[1] = sa; pp[2] = sb;
-          }
-        }
-        if (arrive_last(&p.ctrl->counters[kCtrExit], gridDim.x, &last_flag)) {
-          float mcos = 2.0f;
-          for (int b = 0; b < p.B; ++b) {
-            float sd = 0.f, sa = 0.f, sb = 0.f;
-            for (int w = threadIdx.x; w < (int)gridDim.x; w += 256) {
-              const float *pp = p.part + (int64_t)w * kPartFloatsPerWG + 3 * b;
-              sd += pp[0]; sa += pp[1]; sb += pp[2];
-            }
-            sd = block_sum(sd, bred);
-            sa = block_sum(sa, bred);
-            sb = block_sum(sb, bred);
-            const float den = fmaxf(sqrtf(sa) * sqrtf(sb), 1e-8f);
-            float cs = sd / den;
-            cs = fminf(fmaxf(cs, -1.0f), 1.0f);
-            mcos = fminf(mcos, cs);
-          }
-          if (threadIdx.x == 0) {
-            Control *c = p.ctrl;
-            if (c->force_E < 0 && c->flag == 0) {
-              c->trace[p.layer] = mcos;
-              if (mcos > c->tau) {
-                c->flag = 1;
-                c->E = p.layer + 1;
-              }
-            }
-          }
-        }
+        stage(k0, ks);
+      }
+      const int nch = nchunks(ks);
+      for (int c0 = lane; c0 - lane < nch; c0 += per_iter()) {
+        if (!prefetched) load_batch(k0, nch, c0);
+        prefetched = false;
+        compute_batch(nch, c0);
+      }
+    }
+    finish_task(task * R);
+  }
+
+  // ---- per-workgroup tails
+  if constexpr (EP == kEpResidExit) {
+    if (exit_sums) {
+      // partial sums of this workgroup's rows, summed in a fixed order; the next
+      // layer's first kernel reads them after the kernel boundary
+      if (lane < R * M) {
+        wred[wid][lane][0] = ed;
+        wred[wid][lane][1] = ea;
+        wred[wid][lane][2] = eb;
+      }
+      __syncthreads();
+      if (threadIdx.x < 3 * M) {
+        const int b = threadIdx.x / 3, k = threadIdx.x % 3;
+        float s = 0.f;
+        for (int w = 0; w < 4; ++w)
+          for (int r = 0; r < R; ++r) s += wred[w][r * M + b][k];
+        if (b < p.B) p.part[(int64_t)blockIdx.x * kPartFloatsPerWG + 3 * b + k] = s;
       }
     }
   } else if constexpr (EP == kEpLogits) {
-    for (int idx = threadIdx.x; idx < RW * M; idx += 256) {
-      const int j = idx % RW, b = idx / RW;
-      const int n = blk * RW + j;
-      if (b >= p.B || n >= p.N) continue;
-      const float v = outv[j][b];
-      if (p.logits) p.logits[(int64_t)b * p.vocab + n] = v;
-    }
+    if (lane < R * M) wkey[wid][lane] = best;
+    __syncthreads();
     if (threadIdx.x < M && threadIdx.x < p.B) {
       const int b = threadIdx.x;
-      uint64_t best = 0;
-      for (int j = 0; j < RW; ++j) {
-        const int n = blk * RW + j;
-        if (n >= p.N) break;
-        const uint64_t key = ((uint64_t)float_order(outv[j][b]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
-        best = key > best ? key : best;
-      }
-      __hip_atomic_fetch_max(control_keys(p.ctrl) + b, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint64_t m = 0;
+      for (int w = 0; w < 4; ++w)
+        for (int r = 0; r < R; ++r) m = wkey[w][r * M + b] > m ? wkey[w][r * M + b] : m;
+      __hip_atomic_fetch_max(control_keys(ctl) + b, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (arrive_last(&p.ctrl->counters[kCtrLogits], gridDim.x, &last_flag)) {
-      Control *c = p.ctrl;
+    if (arrive_last(&ctl->counters[kCtrLogits], gridDim.x, &last_flag)) {
       if (threadIdx.x < p.B && p.next) {
-        const uint64_t key = __hip_atomic_load(control_keys(c) + threadIdx.x, __ATOMIC_RELAXED,
+        const uint64_t key = __hip_atomic_load(control_keys(ctl) + threadIdx.x, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
         p.next[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
       }
       if (threadIdx.x == 0) {
-        const int E = c->E;
-        c->last_E = E;
+        const int E = ctl->E;
+        ctl->last_E = E;
         if (p.is_prefill) {
-          c->prefill_hist[E] += 1;
-          c->n_prefill += 1;
+          ctl->prefill_hist[E] += 1;
+          ctl->n_prefill += 1;
         } else {
-          c->decode_hist[E] += 1;
-          c->n_decode += 1;
-          c->pos += 1;
+          ctl->decode_hist[E] += 1;
+          ctl->n_decode += 1;
+          ctl->pos += 1;
         }
       }
     }
   }
 }
 
-template <int M, int XS, int EP>
-static hipError_t gemv_launch_m(const GemvParams &p, hipStream_t s) {
-  constexpr int R = 4;
-  const int nch4 = p.K / 32;  // int4 chunks per row decide the thread split
-  const int tpr = nch4 >= 256 ? 256 : (nch4 >= 128 ? 128 : 64);
-  const int RW = (256 / tpr) * R;
+static int gemv_kslab(int M, int K) {
   int kslab = kXLdsBytes / (M * 2);
   kslab = kslab / 256 * 256;
-  if (kslab > p.K) kslab = p.K;
-  const size_t lds = (size_t)M * kslab * 2 + (size_t)M * (kslab / 32) * 4;
-  int rows = p.N;
-  if (EP == kEpSwiGLU) rows = 2 * p.w.seg_rows[0];
-  const int grid = (rows + RW - 1) / RW;
-  hipLaunchKernelGGL((gemv_kernel<M, R, XS, EP>), dim3(grid), dim3(256), lds, s, p, tpr, kslab);
-  return hipGetLastError();
+  return kslab >= K ? K : kslab;
+}
+
+static int mpad(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+static int num_cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+  }
+  return n;
+}
+
+struct GemvPlan {
+  int grid, ntask, kslab;
+  size_t lds;
+  const void *fn;
+};
+
+// Wavefront tasks (R rows each) are spread over at most one residency wave of
+// workgroups; with several K slabs (large batch) every workgroup takes one
+// task group of 4 tasks.
+template <int M, int XS, int EP>
+static GemvPlan gemv_plan(const GemvParams &p) {
+  constexpr int R = GemvTile<EP>::R;
+  GemvPlan g;
+  g.kslab = gemv_kslab(M, p.K);
+  g.lds = (size_t)M * g.kslab * 2 + (size_t)M * (g.kslab / 32) * 4;
+  const int rows = EP == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
+  g.ntask = (rows + R - 1) / R;
+  g.fn = (const void *)gemv_kernel<M, XS, EP>;
+  const int wgs = (g.ntask + 3) / 4;
+  if (p.K > g.kslab) {
+    g.grid = wgs;
+    return g;
+  }
+  static int resident = 0;
+  if (!resident) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g.fn, 256, g.lds) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 2;
+    resident = per_cu * num_cus();
+  }
+  const int per = (wgs + resident - 1) / resident;   // task groups per workgroup
+  g.grid = (wgs + per - 1) / per;
+  return g;
 }
 
 template <int XS, int EP>
-static hipError_t gemv_launch_xe(const GemvParams &p, hipStream_t s) {
-  if (p.B <= 1) return gemv_launch_m<1, XS, EP>(p, s);
-  if (p.B <= 2) return gemv_launch_m<2, XS, EP>(p, s);
-  if (p.B <= 4) return gemv_launch_m<4, XS, EP>(p, s);
-  return gemv_launch_m<8, XS, EP>(p, s);
+static GemvPlan gemv_plan_m(const GemvParams &p) {
+  switch (mpad(p.B)) {
+    case 1: return gemv_plan<1, XS, EP>(p);
+    case 2: return gemv_plan<2, XS, EP>(p);
+    case 4: return gemv_plan<4, XS, EP>(p);
+    default: return gemv_plan<8, XS, EP>(p);
+  }
 }
 
-hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s) {
-  if (p.B < 1 || p.B > 8) return hipErrorInvalidValue;
+static GemvPlan plan_for(Epilogue ep, const GemvParams &p) {
   switch (ep) {
-    case kEpQKV: return gemv_launch_xe<kXNorm, kEpQKV>(p, s);
-    case kEpSwiGLU: return gemv_launch_xe<kXNorm, kEpSwiGLU>(p, s);
-    case kEpResid: return gemv_launch_xe<kXBf16, kEpResid>(p, s);
-    case kEpResidExit: return gemv_launch_xe<kXBf16, kEpResidExit>(p, s);
-    case kEpLogits: return gemv_launch_xe<kXNorm, kEpLogits>(p, s);
+    case kEpQKV: return gemv_plan_m<kXNorm, kEpQKV>(p);
+    case kEpSwiGLU: return gemv_plan_m<kXNorm, kEpSwiGLU>(p);
+    case kEpResid: return gemv_plan_m<kXBf16, kEpResid>(p);
+    case kEpResidExit: return gemv_plan_m<kXBf16, kEpResidExit>(p);
+    default: return gemv_plan_m<kXNorm, kEpLogits>(p);
   }
+}
+
+int gemv_grid(Epilogue ep, const GemvParams &p) { return plan_for(ep, p).grid; }
+
+hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s) {
   (void)xs;
-  return hipErrorInvalidValue;
+  if (p.B < 1 || p.B > 8 || ep > kEpLogits) return hipErrorInvalidValue;
+  const GemvPlan g = plan_for(ep, p);
+  int kslab = g.kslab, ntask = g.ntask;
+  GemvParams pc = p;
+  void *args[] = {&pc, &kslab, &ntask};
+  return hipLaunchKernel(g.fn, dim3(g.grid), dim3(256), args, g.lds, s);
+}
+
+// ===========================================================================
+// RoPE table (float64 angles, rounded once to float32)
+// ===========================================================================
+__global__ void rope_table_kernel(float2 *rope, int max_seq, int head_dim, double theta) {
+  const int hd = head_dim / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)max_seq * hd) return;
+  const int t = (int)(i / hd), j = (int)(i % hd);
+  const double ang = (double)t * pow(theta, -2.0 * j / (double)head_dim);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  rope[i] = make_float2((float)cs, (float)sn);
+}
+
+hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float theta, hipStream_t s) {
+  const int64_t n = (int64_t)max_seq * (head_dim / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, rope,
+                     max_seq, head_dim, (double)theta);
+  return hipGetLastError();
 }
 
 // ===========================================================================
 // Decode attention (GQA, split over positions).  Workgroup (split, kv head, b)
-// scores its chunk of positions for the Hq/Hkv query heads that share the kv
-// head (one K/V read serves all of them), keeps the chunk's max and sum, and
-// the last workgroup of each (b, kv head) merges the chunks.
+// covers `chunk` positions in sub-chunks of 64: all K and V loads of a
+// sub-chunk are issued before any is used, one K/V read serves the Hq/Hkv
+// query heads that share the kv head, and each wavefront keeps its own online
+// softmax (running max and sum).  The four wavefronts merge at the end; with
+// several splits the last workgroup of each (b, kv head) merges the splits.
 // ===========================================================================
+int attn_chunk(int max_seq, int batch, int n_kv_heads) {
+  const int pairs = batch * n_kv_heads;
+  const int target = (2048 + pairs - 1) / pairs;           // splits per (b, kv head)
+  int chunk = (max_seq + target - 1) / target;
+  chunk = (chunk + kAttnSub - 1) / kAttnSub * kAttnSub;
+  return chunk < kAttnSub ? kAttnSub : chunk;
+}
+
 template <int DH, int GQ>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
-  constexpr int LPP = DH / 8;          // lanes per position (8 bf16 each)
-  constexpr int PPP = 256 / LPP;       // positions per pass
-  __shared__ float sc[GQ][kAttnChunk];
-  __shared__ float accs[PPP][GQ][DH];
-  __shared__ float bred[8];
-  __shared__ float mstat[GQ], lstat[GQ];
+  constexpr int LPP = DH / 8;        // lanes per position (8 bf16 each)
+  constexpr int PPW = 64 / LPP;      // positions per wavefront per pass (slots)
+  constexpr int PPP = 4 * PPW;       // positions per workgroup per pass
+  constexpr int NP = kAttnSub / PPP; // passes per sub-chunk
+  __shared__ float wm[4][GQ];
+  __shared__ float wl[4][PPW][GQ];
+  __shared__ __align__(16) float wo[4][PPW][GQ][DH];
+  __shared__ float sm[kMaxAttnSplits][GQ][2];
   __shared__ int last_flag;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int slot = lane / LPP, ln = lane % LPP;
   const int n = p.ctrl->pos + 1;
-  const int t0 = split * kAttnChunk;
-  const int cnt = min(kAttnChunk, n - t0);
-  const int slot = threadIdx.x / LPP, ln = threadIdx.x % LPP;
-  const int64_t kvbase = (((int64_t)b * p.Hkv + kvh) * p.S) * DH;
+  const int t0 = split * p.chunk;
+  const int t1 = min(n, t0 + p.chunk);
+  const int64_t kvbase = (((int64_t)b * p.Hkv + kvh) * p.S) * DH + ln * 8;
   const uint16_t *K = p.k_cache + kvbase;
   const uint16_t *V = p.v_cache + kvbase;
 
-  if (cnt > 0) {
-    float qv[GQ][8];
+  float qv[GQ][8];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(p.q + ((int64_t)b * p.Hq + kvh * GQ + h) * DH + ln * 8);
-      qv[h][0] = bf_lo(u.x); qv[h][1] = bf_hi(u.x); qv[h][2] = bf_lo(u.y); qv[h][3] = bf_hi(u.y);
-      qv[h][4] = bf_lo(u.z); qv[h][5] = bf_hi(u.z); qv[h][6] = bf_lo(u.w); qv[h][7] = bf_hi(u.w);
+  for (int h = 0; h < GQ; ++h) {
+    const uint4 u =
+        *reinterpret_cast<const uint4 *>(p.q + ((int64_t)b * p.Hq + kvh * GQ + h) * DH + ln * 8);
+    qv[h][0] = bf_lo(u.x); qv[h][1] = bf_hi(u.x); qv[h][2] = bf_lo(u.y); qv[h][3] = bf_hi(u.y);
+    qv[h][4] = bf_lo(u.z); qv[h][5] = bf_hi(u.z); qv[h][6] = bf_lo(u.w); qv[h][7] = bf_hi(u.w);
+  }
+  float m[GQ], l[GQ], acc[GQ][8];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  for (int sb = t0; sb < t1; sb += kAttnSub) {
+    uint4 kr[NP], vr[NP];
+    bool ok[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = sb + i * PPP + wid * PPW + slot;
+      ok[i] = t < t1;
+      kr[i] = ok[i] ? *reinterpret_cast<const uint4 *>(K + (int64_t)t * DH) : make_uint4(0, 0, 0, 0);
+      vr[i] = ok[i] ? *reinterpret_cast<const uint4 *>(V + (int64_t)t * DH) : make_uint4(0, 0, 0, 0);
     }
-    for (int tt = slot; tt < cnt; tt += PPP) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(K + (int64_t)(t0 + tt) * DH + ln * 8);
-      const float kf[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
-                           bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
+    float s[NP][GQ];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const float kf[8] = {bf_lo(kr[i].x), bf_hi(kr[i].x), bf_lo(kr[i].y), bf_hi(kr[i].y),
+                           bf_lo(kr[i].z), bf_hi(kr[i].z), bf_lo(kr[i].w), bf_hi(kr[i].w)};
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = fmaf(qv[h][e], kf[e], d);
-        d = group_sum(d, LPP);
-        if (ln == 0) sc[h][tt] = d * p.scale;
+        d = LPP == 16 ? sum16(d) : sum8(d);   // the lanes of one position
+        s[i][h] = ok[i] ? d * p.scale : -INFINITY;
       }
     }
-    __syncthreads();
+#pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      float v = threadIdx.x < cnt ? sc[h][threadIdx.x] : -INFINITY;
-      const float m = block_min(-v, bred);   // max via min of negatives
-      const float mx = -m;
-      const float e = threadIdx.x < cnt ? expf(v - mx) : 0.f;
-      if (threadIdx.x < cnt) sc[h][threadIdx.x] = e;
-      const float l = block_sum(e, bred);
-      if (threadIdx.x == 0) { mstat[h] = mx; lstat[h] = l; }
-    }
-    __syncthreads();
-    float acc[GQ][8];
+      // running max over every position this wavefront has seen
+      float mx = s[0][h];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
+      for (int i = 1; i < NP; ++i) mx = fmaxf(mx, s[i][h]);
+      if (LPP == 8) mx = fmaxf(mx, dpp<kDppRor8>(mx));
+      const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
+      const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 16));
+      const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 32));
+      const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 48));
+      mx = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+      const float mnew = fmaxf(m[h], mx);
+      if (mnew == -INFINITY) continue;   // nothing visible yet in this wavefront
+      const float corr = expf(m[h] - mnew);
+      l[h] *= corr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    for (int tt = slot; tt < cnt; tt += PPP) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(V + (int64_t)(t0 + tt) * DH + ln * 8);
-      const float vf[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
-                           bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
+      for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
+      m[h] = mnew;
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        const float pr = sc[h][tt];
+      for (int i = 0; i < NP; ++i) {
+        const float pr = ok[i] ? expf(s[i][h] - mnew) : 0.f;
+        l[h] += pr;
+        const float vf[8] = {bf_lo(vr[i].x), bf_hi(vr[i].x), bf_lo(vr[i].y), bf_hi(vr[i].y),
+                             bf_lo(vr[i].z), bf_hi(vr[i].z), bf_lo(vr[i].w), bf_hi(vr[i].w)};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
       }
     }
+  }
+  // per-slot results to LDS; m is uniform over the wavefront
+  if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
+    for (int h = 0; h < GQ; ++h) wm[wid][h] = m[h];
+  }
+  if (ln == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) accs[slot][h][ln * 8 + e] = acc[h][e];
+    for (int h = 0; h < GQ; ++h) wl[wid][slot][h] = l[h];
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float4 *dst = reinterpret_cast<float4 *>(&wo[wid][slot][h][ln * 8]);
+    dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+    dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+  }
+  __syncthreads();
+  const bool direct = p.splits == 1;
+  float *part_base = p.part + ((int64_t)b * p.Hq + kvh * GQ) * p.splits * (DH + 2);
+  for (int idx = threadIdx.x; idx < GQ * DH; idx += 256) {
+    const int h = idx / DH, e = idx % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, wm[wv][h]);
+    float L = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        const float f = expf(wm[wv][h] - M);
+        float lw = 0.f, ow = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < PPW; ++sl) {
+          lw += wl[wv][sl][h];
+          ow += wo[wv][sl][h][e];
+        }
+        L += f * lw;
+        o += f * ow;
+      }
+    }
+    if (direct) {
+      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(o / L);
+    } else {
+      float *pp = part_base + ((int64_t)h * p.splits + split) * (DH + 2);
+      st_coherent(pp + e, o);
+      if (e == 0) {
+        st_coherent(pp + DH, M);
+        st_coherent(pp + DH + 1, L);
+      }
+    }
+  }
+  if (direct) return;
+  if (arrive_last(&p.counters[b * p.Hkv + kvh], gridDim.x, &last_flag)) {
+    // merge the splits that hold positions: scale factors first, then the
+    // weighted sum with every load of a thread issued together
+    const int nval = (n + p.chunk - 1) / p.chunk;
+    for (int idx = threadIdx.x; idx < nval * GQ; idx += 256) {
+      const int sp = idx / GQ, h = idx % GQ;
+      const float *pp = part_base + ((int64_t)h * p.splits + sp) * (DH + 2);
+      sm[sp][h][0] = ld_coherent(pp + DH);
+      sm[sp][h][1] = ld_coherent(pp + DH + 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < GQ) {
+      const int h = threadIdx.x;
+      float mx = -INFINITY;
+      for (int sp = 0; sp < nval; ++sp) mx = fmaxf(mx, sm[sp][h][0]);
+      float L = 0.f;
+      for (int sp = 0; sp < nval; ++sp) {
+        const float f = sm[sp][h][0] == -INFINITY ? 0.f : expf(sm[sp][h][0] - mx);
+        sm[sp][h][0] = f;
+        L += f * sm[sp][h][1];
+      }
+      wm[0][h] = 1.0f / L;
+    }
     __syncthreads();
     for (int idx = threadIdx.x; idx < GQ * DH; idx += 256) {
       const int h = idx / DH, e = idx % DH;
-      float s = 0.f;
-      for (int sl = 0; sl < PPP; ++sl) s += accs[sl][h][e];
-      float *pp = p.part + (((int64_t)b * p.Hq + kvh * GQ + h) * p.splits + split) * (DH + 2);
-      pp[e] = s;
-      if (e == 0) { pp[DH] = mstat[h]; pp[DH + 1] = lstat[h]; }
-    }
-  }
-  if (arrive_last(&p.counters[b * p.Hkv + kvh], gridDim.x, &last_flag)) {
-    const int nval = (n + kAttnChunk - 1) / kAttnChunk;
-    for (int idx = threadIdx.x; idx < GQ * DH; idx += 256) {
-      const int h = idx / DH, e = idx % DH;
-      const float *base = p.part + (((int64_t)b * p.Hq + kvh * GQ + h) * p.splits) * (DH + 2);
-      float mx = -INFINITY;
-      for (int sp = 0; sp < nval; ++sp) mx = fmaxf(mx, base[sp * (DH + 2) + DH]);
-      float l = 0.f, o = 0.f;
-      for (int sp = 0; sp < nval; ++sp) {
-        const float f = expf(base[sp * (DH + 2) + DH] - mx);
-        l += f * base[sp * (DH + 2) + DH + 1];
-        o += f * base[sp * (DH + 2) + e];
+      const float *base = part_base + (int64_t)h * p.splits * (DH + 2) + e;
+      float o = 0.f;
+      int sp = 0;
+      for (; sp + 8 <= nval; sp += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ld_coherent(base + (sp + u) * (DH + 2));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o = fmaf(sm[sp + u][h][0], v[u], o);
       }
-      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(o / l);
+      for (; sp < nval; ++sp) o = fmaf(sm[sp][h][0], ld_coherent(base + sp * (DH + 2)), o);
+      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(o * wm[0][h]);
     }
   }
 }
@@ -613,6 +904,7 @@ static hipError_t attn_launch_dh(const AttnParams &p, hipStream_t s) {
 }
 
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
+  if (p.chunk % kAttnSub || p.splits < 1 || p.splits > kMaxAttnSplits) return hipErrorInvalidValue;
   switch (p.Dh) {
     case 64: return attn_launch_dh<64>(p, s);
     case 128: return attn_launch_dh<128>(p, s);

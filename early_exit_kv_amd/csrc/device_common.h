@@ -32,6 +32,47 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// DPP cross-lane moves (no LDS traffic).  row_ror:n rotates within each row
+// of 16 lanes; quad_perm permutes within each group of 4; half_mirror reverses
+// each half-row of 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppRor1 = 0x121, kDppRor2 = 0x122, kDppRor4 = 0x124, kDppRor8 = 0x128;
+constexpr int kDppHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+
+// all-reduce within aligned groups of 16 (sum16) or 8 (sum8) lanes
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<kDppRor8>(v);
+  v += dpp<kDppRor4>(v);
+  v += dpp<kDppRor2>(v);
+  v += dpp<kDppRor1>(v);
+  return v;
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<kDppRor8>(v));
+  v = fmaxf(v, dpp<kDppRor4>(v));
+  v = fmaxf(v, dpp<kDppRor2>(v));
+  v = fmaxf(v, dpp<kDppRor1>(v));
+  return v;
+}
+// wavefront sum, returned as a wave-uniform value
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v = sum16(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -77,22 +118,35 @@ __device__ __forceinline__ float block_min(float v, float *red) {
 // Last-workgroup hand-off: every workgroup publishes its results, then thread
 // 0 counts itself in; the workgroup that brings the count to `total` sees all
 // published data (release/acquire at agent scope) and resets the counter.
+//
+// Data handed across workgroups inside one kernel travels only through
+// relaxed agent-scope atomics (coherent at device scope on their own: they are
+// not kept dirty in one XCD's L2), so no release/acquire fence is needed --
+// on gfx950 those fences write back / invalidate the whole L2.  Ordering:
+// each thread waits for its own coherent stores to complete (s_waitcnt, also
+// a compiler barrier) before the workgroup barrier, and only then does thread
+// 0 count the workgroup in.
+__device__ __forceinline__ void st_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t total, int *smem_flag) {
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (old == total - 1);
-    if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const uint32_t old =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (old == total - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *smem_flag = last;
   }
   __syncthreads();
-  bool last = *smem_flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  asm volatile("" ::: "memory");
+  return *smem_flag != 0;
 }
 
 // Exit choice of a layer, read at the start of every kernel of that layer.

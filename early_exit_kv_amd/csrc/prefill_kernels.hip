@@ -74,10 +74,10 @@ __global__ __launch_bounds__(256) void rows_cos_kernel(RowsCosParams p) {
     c = fminf(fmaxf(c, -1.0f), 1.0f);
   }
   const float m = block_min(c, bred);
-  if (threadIdx.x == 0) p.part[blockIdx.x] = m;
+  if (threadIdx.x == 0) st_coherent(&p.part[blockIdx.x], m);
   if (arrive_last(&p.ctrl->counters[kCtrRowsCos], gridDim.x, &last_flag)) {
     float mm = 2.0f;
-    for (int i = threadIdx.x; i < (int)gridDim.x; i += 256) mm = fminf(mm, p.part[i]);
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += 256) mm = fminf(mm, ld_coherent(&p.part[i]));
     mm = block_min(mm, bred);
     if (threadIdx.x == 0) {
       Control *ct = p.ctrl;
@@ -198,15 +198,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         uint4 cw = bvalid ? *reinterpret_cast<const uint4 *>(qrow + (k0 >> 3))
                           : make_uint4(0, 0, 0, 0);
         const uint32_t wd[4] = {cw.x, cw.y, cw.z, cw.w};
-        // word i covers columns 8i..8i+7; column 8i+j sits in nibble 4(j%4)+16(j/4)
+        // word i covers columns 8i..8i+7; column 8i+j sits in bits 4j..4j+3
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t o[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int j0 = 2 * jj, j1 = 2 * jj + 1;
-            const uint32_t c0 = (wd[i] >> (4 * (j0 & 3) + 16 * (j0 >> 2))) & 0xF;
-            const uint32_t c1 = (wd[i] >> (4 * (j1 & 3) + 16 * (j1 >> 2))) & 0xF;
+            const uint32_t c0 = (wd[i] >> (8 * jj)) & 0xF;
+            const uint32_t c1 = (wd[i] >> (8 * jj + 4)) & 0xF;
             o[jj] = (0x4300u | c0) | ((0x4300u | c1) << 16);
           }
           *reinterpret_cast<uint4 *>(&Bs[tid][i * 8]) = make_uint4(o[0], o[1], o[2], o[3]);

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
   for (int j = 0; j < 8; ++j) {
     float q = rintf(__fadd_rn(__fdiv_rn(v[j], s), z));
     q = fminf(fmaxf(q, 0.0f), 15.0f);
-    word |= (uint32_t)q << (4 * (j & 3) + 16 * (j >> 2));
+    word |= (uint32_t)q << (4 * j);   // column 8w+j in bits 4j..4j+3
   }
   codes[i] = word;
   const int64_t row = i / KW;

@@ -79,8 +79,9 @@ Workspace workspace_layout(const river_config &c) {
   const int64_t cos_wgs = (R + 3) / 4;
   w.part_floats = (int)std::max<int64_t>(gemv_wgs * kPartFloatsPerWG, cos_wgs);
   w.part = take((size_t)w.part_floats * 4);
-  w.attn_splits = (c.max_seq + kAttnChunk - 1) / kAttnChunk;
+  w.attn_splits = (c.max_seq + kAttnSub - 1) / kAttnSub;  // the most any batch size uses
   w.attn_part = take((size_t)c.max_batch * c.n_q_heads * w.attn_splits * (c.head_dim + 2) * 4);
+  w.rope = take((size_t)c.max_seq * (c.head_dim / 2) * 8);
   w.total = off;
   return w;
 }
@@ -117,6 +118,14 @@ struct river_ctx {
     }
   };
   std::map<GraphKey, hipGraphExec_t> graphs;
+  // profiling: events around every launch, folded into per-class totals on read
+  bool profiling = false;
+  struct Timed {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Timed> timed;
+  std::vector<hipEvent_t> event_pool;
 };
 
 namespace {
@@ -191,6 +200,40 @@ uint16_t *v_layer(river_ctx *ctx, int l) {
     if (e_ != hipSuccess) return RIVER_E_HIP; \
   } while (0)
 
+hipEvent_t take_event(river_ctx *ctx) {
+  if (!ctx->event_pool.empty()) {
+    hipEvent_t e = ctx->event_pool.back();
+    ctx->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event before the launch and one after it when profiling.
+struct TimedLaunch {
+  river_ctx *ctx;
+  int kind;
+  hipEvent_t a = nullptr;
+  TimedLaunch(river_ctx *c, int k) : ctx(c), kind(k) {
+    if (ctx->profiling && (a = take_event(ctx))) (void)hipEventRecord(a, ctx->stream);
+  }
+  hipError_t done(hipError_t e) {
+    if (a) {
+      hipEvent_t b = take_event(ctx);
+      if (b) {
+        (void)hipEventRecord(b, ctx->stream);
+        ctx->timed.push_back({kind, a, b});
+      } else {
+        ctx->event_pool.push_back(a);
+      }
+    }
+    return e;
+  }
+};
+#define TIMED(kind, expr) RV_TRY(TimedLaunch(ctx, kind).done(expr))
+
 // Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
 int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next) {
   const river_config &c = ctx->cfg;
@@ -203,14 +246,17 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
   bp.tau = tau; bp.is_prefill = 0; bp.set_pos = -1;
-  RV_TRY(launch_begin(bp, s));
+  TIMED(RIVER_K_BEGIN, launch_begin(bp, s));
 
+  int down_wgs = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     const river_layer_w &L = ctx->layers[l];
     GemvParams g{};
     g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl; g.B = B;
+    g.gshift = __builtin_ctz((unsigned)c.group_size);
     g.eps = c.rms_eps; g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim;
     g.max_seq = c.max_seq; g.max_batch = c.max_batch; g.rope_theta = c.rope_theta;
+    g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
     g.n_layers = c.n_layers;
 
     // attention RMSNorm + fused q|k|v + RoPE + write into the shared slot
@@ -220,28 +266,32 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     q.h_src = hA; q.h_stride = c.d_model; q.gain = static_cast<const uint16_t *>(L.attn_norm);
     q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
     q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
-    RV_TRY(launch_gemv(kXNorm, kEpQKV, q, s));
+    // the exit test after layer l-1 is decided at the start of this kernel
+    q.test_prev = l > 0; q.part = at<float>(ctx->ws, ctx->wl.part); q.part_wgs = down_wgs;
+    TIMED(RIVER_K_QKV, launch_gemv(kXNorm, kEpQKV, q, s));
 
     AttnParams a{};
     a.q = q.q_out; a.k_cache = q.k_cache; a.v_cache = q.v_cache;
     a.out = at<uint16_t>(ctx->ws, ctx->wl.attn); a.part = at<float>(ctx->ws, ctx->wl.attn_part);
     a.counters = control_attn_counters(ctx->ctrl, c.max_batch); a.ctrl = ctx->ctrl;
     a.B = B; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.Dh = c.head_dim; a.S = c.max_seq;
-    a.splits = ctx->wl.attn_splits; a.scale = 1.0f / std::sqrt((float)c.head_dim);
-    RV_TRY(launch_attn_decode(a, s));
+    a.chunk = attn_chunk(c.max_seq, B, c.n_kv_heads);
+    a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    TIMED(RIVER_K_ATTN, launch_attn_decode(a, s));
 
     GemvParams o = g;
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x_src = a.out; o.x_stride = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
-    RV_TRY(launch_gemv(kXBf16, kEpResid, o, s));
+    TIMED(RIVER_K_O, launch_gemv(kXBf16, kEpResid, o, s));
 
     GemvParams gu = g;
     fill_weights(ctx, l, 4, 2, gu.w);
     gu.N = 2 * c.ffn_dim; gu.K = c.d_model;
     gu.h_src = hB; gu.h_stride = c.d_model; gu.gain = static_cast<const uint16_t *>(L.mlp_norm);
     gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u); gu.u_stride = c.ffn_dim;
-    RV_TRY(launch_gemv(kXNorm, kEpSwiGLU, gu, s));
+    TIMED(RIVER_K_GATEUP, launch_gemv(kXNorm, kEpSwiGLU, gu, s));
 
     GemvParams dn = g;
     fill_weights(ctx, l, 6, 1, dn.w);
@@ -249,16 +299,18 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model; dn.h_src = hA;
     dn.part = at<float>(ctx->ws, ctx->wl.part);
     dn.test_exit = l < c.n_layers - 1;
-    RV_TRY(launch_gemv(kXBf16, kEpResidExit, dn, s));
+    down_wgs = gemv_grid(kEpResidExit, dn);
+    TIMED(RIVER_K_DOWN, launch_gemv(kXBf16, kEpResidExit, dn, s));
     std::swap(hA, hB);
   }
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
+  lm.gshift = __builtin_ctz((unsigned)c.group_size);
   lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
   lm.h_src = hA; lm.h_stride = c.d_model; lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
   lm.logits = logits; lm.next = next; lm.is_prefill = 0; lm.vocab = c.vocab;
-  RV_TRY(launch_gemv(kXNorm, kEpLogits, lm, s));
+  TIMED(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
   return RIVER_OK;
 }
 
@@ -275,7 +327,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = R; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
   bp.tau = tau; bp.is_prefill = 1; bp.set_pos = T;
-  RV_TRY(launch_begin(bp, s));
+  TIMED(RIVER_K_BEGIN, launch_begin(bp, s));
 
   for (int l = 0; l < c.n_layers; ++l) {
     const river_layer_w &L = ctx->layers[l];
@@ -283,66 +335,78 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     g.M = (int)R; g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl;
     g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim; g.max_seq = c.max_seq;
     g.max_batch = c.max_batch; g.T = T; g.rope_theta = c.rope_theta;
+    g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
 
     RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), R, c.d_model, c.rms_eps};
-    RV_TRY(launch_rows_norm(rn, s));
+    TIMED(RIVER_K_P_NORM, launch_rows_norm(rn, s));
 
     GemmParams q = g;
     fill_weights(ctx, l, 0, 3, q.w);
     q.N = qd + 2 * c.n_kv_heads * c.head_dim; q.K = c.d_model; q.x = x; q.ldx = c.d_model;
     q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
     q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
-    RV_TRY(launch_gemm(kEpQKV, q, s));
+    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpQKV, q, s));
 
     AttnPrefillParams ap{};
     ap.q = q.q_out; ap.k_cache = q.k_cache; ap.v_cache = q.v_cache;
     ap.out = at<uint16_t>(ctx->ws, ctx->wl.attn); ap.B = B; ap.T = T; ap.Hq = c.n_q_heads;
     ap.Hkv = c.n_kv_heads; ap.Dh = c.head_dim; ap.S = c.max_seq;
     ap.scale = 1.0f / std::sqrt((float)c.head_dim);
-    RV_TRY(launch_attn_prefill(ap, s));
+    TIMED(RIVER_K_P_ATTN, launch_attn_prefill(ap, s));
 
     GemmParams o = g;
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x = ap.out; o.ldx = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
-    RV_TRY(launch_gemm(kEpResid, o, s));
+    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpResid, o, s));
 
     RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), R, c.d_model, c.rms_eps};
-    RV_TRY(launch_rows_norm(rn2, s));
+    TIMED(RIVER_K_P_NORM, launch_rows_norm(rn2, s));
 
     GemmParams gu = g;
     fill_weights(ctx, l, 4, 2, gu.w);
     gu.N = 2 * c.ffn_dim; gu.K = c.d_model; gu.x = x; gu.ldx = c.d_model;
     gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u);
-    RV_TRY(launch_gemm(kEpSwiGLU, gu, s));
+    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpSwiGLU, gu, s));
 
     GemmParams dn = g;
     fill_weights(ctx, l, 6, 1, dn.w);
     dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
     dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
-    RV_TRY(launch_gemm(kEpResid, dn, s));
+    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpResid, dn, s));
 
     if (l < c.n_layers - 1 && ctx->force_E < 0) {
       RowsCosParams rc{hA, hB, R, c.d_model, at<float>(ctx->ws, ctx->wl.part), ctx->ctrl, l,
                        c.n_layers};
-      RV_TRY(launch_rows_cos_exit(rc, s));
+      TIMED(RIVER_K_P_COS, launch_rows_cos_exit(rc, s));
     }
     std::swap(hA, hB);
   }
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
+  lm.gshift = __builtin_ctz((unsigned)c.group_size);
   lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
   lm.h_src = hA + (int64_t)(T - 1) * c.d_model; lm.h_stride = (int64_t)T * c.d_model;
   lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
   lm.logits = logits; lm.next = next; lm.is_prefill = 1; lm.vocab = c.vocab;
-  RV_TRY(launch_gemv(kXNorm, kEpLogits, lm, s));
+  TIMED(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
   return RIVER_OK;
 }
 
 void drop_graphs(river_ctx *ctx) {
   for (auto &kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
   ctx->graphs.clear();
+}
+
+void drop_events(river_ctx *ctx) {
+  for (auto &t : ctx->timed) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  ctx->timed.clear();
+  for (auto e : ctx->event_pool) (void)hipEventDestroy(e);
+  ctx->event_pool.clear();
 }
 
 }  // namespace
@@ -436,6 +500,8 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
   drop_graphs(ctx);
   ctx->built = false;
   RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads), ctx->stream));
+  RV_TRY(launch_rope_table(at<float2>(ctx->ws, ctx->wl.rope), c.max_seq, c.head_dim, c.rope_theta,
+                           ctx->stream));
   LinearShape sh[7];
   linear_shapes(c, sh);
   for (int l = 0; l < c.n_layers; ++l) {
@@ -481,7 +547,7 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
   if (!std::isfinite(tau)) return RIVER_E_INVALID_ARG;
   if (!ctx->built || ctx->batch == 0) return RIVER_E_STATE;
   if (ctx->pos + 1 > ctx->cfg.max_seq) return RIVER_E_RANGE;
-  if (ctx->use_graph && ctx->stream != nullptr) {
+  if (ctx->use_graph && !ctx->profiling && ctx->stream != nullptr) {
     river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E, 0};
     std::memcpy(&key.tau_bits, &tau, 4);
     auto it = ctx->graphs.find(key);
@@ -542,6 +608,11 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
       if (value < -1 || value > ctx->cfg.n_layers) return RIVER_E_RANGE;
       ctx->force_E = (int)value;
       return RIVER_OK;
+    case RIVER_OPT_PROFILE:
+      if (value != 0 && value != 1) return RIVER_E_INVALID_ARG;
+      if (!value) drop_events(ctx);
+      ctx->profiling = value != 0;
+      return RIVER_OK;
   }
   return RIVER_E_INVALID_ARG;
 }
@@ -553,9 +624,28 @@ int river_reset(river_ctx *ctx) {
   return RIVER_OK;
 }
 
+int river_profile_read(river_ctx *ctx, river_kernel_time_t *out) {
+  if (!ctx || !out) return RIVER_E_INVALID_ARG;
+  if (!ctx->profiling) return RIVER_E_STATE;
+  RV_TRY(hipStreamSynchronize(ctx->stream));
+  for (int k = 0; k < RIVER_K_NKINDS; ++k) out[k] = {0, 0.0};
+  for (auto &t : ctx->timed) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess && t.kind >= 0 && t.kind < RIVER_K_NKINDS) {
+      out[t.kind].launches += 1;
+      out[t.kind].total_ms += ms;
+    }
+    ctx->event_pool.push_back(t.a);
+    ctx->event_pool.push_back(t.b);
+  }
+  ctx->timed.clear();
+  return RIVER_OK;
+}
+
 void river_destroy(river_ctx *ctx) {
   if (!ctx) return;
   drop_graphs(ctx);
+  drop_events(ctx);
   delete ctx;
 }
 

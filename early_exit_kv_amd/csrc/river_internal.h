@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/river.h"
+#include "river.h"
 
 namespace river {
 
@@ -85,6 +85,7 @@ struct Workspace {
   size_t u;            // bf16 SwiGLU product [R][F]
   size_t part;         // fp32 per-workgroup partial sums for the exit test
   size_t attn_part;    // fp32 split-K attention partials
+  size_t rope;         // fp32 (cos, sin) of pos * theta^(-2i/Dh), [max_seq][Dh/2]
   size_t total;
   int64_t rows;        // R: rows the buffers hold
   int part_floats;
@@ -92,7 +93,8 @@ struct Workspace {
 };
 Workspace workspace_layout(const river_config &c);
 
-constexpr int kAttnChunk = 256;   // positions per decode-attention workgroup
+constexpr int kAttnSub = 64;      // positions per decode-attention sub-chunk
+constexpr int kMaxAttnSplits = 512;  // splits one (b, kv head) may use
 constexpr int kPartFloatsPerWG = 3 * 64;  // B <= 64 rows x (dot, |a|^2, |b|^2)
 
 // ---------------------------------------------------------------------------
@@ -128,11 +130,15 @@ struct GemvParams {
   // (kEpResidExit also reads the layer input through h_src, same stride)
   uint16_t *q_out; uint16_t *k_cache; uint16_t *v_cache;  // QKV
   int Hq, Hkv, Dh, max_seq, max_batch; float rope_theta;
+  const float2 *rope;                                     // (cos, sin) table
   uint16_t *u_out; int64_t u_stride;                      // SwiGLU
   float *part;                                            // exit test partials
-  int test_exit; int n_layers;                            // exit test enabled?
+  int test_exit; int n_layers;                            // down: write the partials
+  int test_prev; int part_wgs;    // QKV: decide the previous layer's test first
+  int gshift;                     // log2(group size)
   float *logits; int32_t *next; int is_prefill; int vocab;// LM head
 };
+
 
 struct AttnParams {
   const uint16_t *q;      // [B][Hq*Dh]
@@ -141,9 +147,11 @@ struct AttnParams {
   float *part;            // [B][Hq][splits][Dh + 2]
   uint32_t *counters;     // [B][Hkv]
   Control *ctrl;
-  int B, Hq, Hkv, Dh, S, splits;
+  int B, Hq, Hkv, Dh, S, splits, chunk;
   float scale;
 };
+// positions per decode-attention workgroup for a cache of max_seq positions
+int attn_chunk(int max_seq, int batch, int n_kv_heads);
 
 struct BeginParams {
   Control *ctrl;
@@ -163,7 +171,12 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
                            hipStream_t s);
 hipError_t launch_begin(const BeginParams &p, hipStream_t s);
+// RoPE table: rope[t][i] = (cos, sin)(t * theta^(-2i/Dh)), angles in float64
+hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float theta, hipStream_t s);
 hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s);
+// workgroups launch_gemv uses for these parameters (the QKV launch reads that
+// many partials left by the previous layer's down projection)
+int gemv_grid(Epilogue ep, const GemvParams &p);
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 
 // prefill
@@ -182,6 +195,7 @@ struct GemmParams {
   const float *h_in; float *h_out; int64_t h_io_stride;
   uint16_t *q_out; uint16_t *k_cache; uint16_t *v_cache;
   int Hq, Hkv, Dh, max_seq, max_batch, T; float rope_theta;
+  const float2 *rope;
   uint16_t *u_out;
 };
 hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s);

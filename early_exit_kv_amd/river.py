@@ -16,7 +16,9 @@ LIB_PATH = os.path.join(_HERE, "libriver.so")
 RIVER_OK, RIVER_E_INVALID_ARG, RIVER_E_BAD_SIZE, RIVER_E_STATE = 0, 1, 2, 3
 RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
 RIVER_EXIT_INT4, RIVER_EXIT_COPY = 1, 2
-RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E = 1, 2
+RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE = 1, 2, 3
+KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
+                "p_norm", "p_gemm", "p_attn", "p_cos")
 RIVER_MAX_LAYERS = 256
 LINEAR_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
@@ -24,7 +26,7 @@ LINEAR_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 EXPORTS = (
     "river_query_sizes", "river_exit_bank_offsets", "river_init", "river_build_exit_layers",
     "river_prefill", "river_decode_step", "river_exit_stats", "river_set_option",
-    "river_reset", "river_destroy", "river_strerror",
+    "river_reset", "river_destroy", "river_strerror", "river_profile_read",
 )
 
 
@@ -58,6 +60,10 @@ class RiverSizes(ctypes.Structure):
     _fields_ = [("exit_bank_bytes", ctypes.c_size_t), ("exit_bank_copy_bytes", ctypes.c_size_t),
                 ("kv_cache_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
                 ("control_bytes", ctypes.c_size_t)]
+
+
+class RiverKernelTime(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class RiverExitStats(ctypes.Structure):
@@ -99,6 +105,7 @@ def load_library(path=LIB_PATH):
         "river_reset": (ctypes.c_int, [P]),
         "river_destroy": (None, [P]),
         "river_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "river_profile_read": (ctypes.c_int, [P, ctypes.POINTER(RiverKernelTime)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -263,6 +270,16 @@ class River:
         """-1: decide with tau; e in 0..L: layers < e backbone, the rest exit layers."""
         self.set_option(RIVER_OPT_FORCE_E, e)
 
+    def profile(self, on=True):
+        """Time every kernel with HIP events (decode steps then launch eagerly)."""
+        self.set_option(RIVER_OPT_PROFILE, 1 if on else 0)
+
+    def profile_read(self):
+        """{kind: (launches, total_ms)} accumulated since the previous read."""
+        arr = (RiverKernelTime * len(KERNEL_KINDS))()
+        self._call(self.lib.river_profile_read, "river_profile_read", arr)
+        return {k: (arr[i].launches, arr[i].total_ms) for i, k in enumerate(KERNEL_KINDS)}
+
     def reset(self):
         _check(self.lib.river_reset(self.ctx), "river_reset")
 
@@ -307,8 +324,7 @@ def unpack_int4(words, sz, group):
     N, KW = w.shape
     codes = np.empty((N, KW * 8), dtype=np.uint8)
     for j in range(8):
-        shift = 4 * (j % 4) + 16 * (j // 4)
-        codes[:, j::8] = ((w >> shift) & 0xF).astype(np.uint8)
+        codes[:, j::8] = ((w >> (4 * j)) & 0xF).astype(np.uint8)
     z32 = np.asarray(sz, dtype=np.int64) & 0xFFFFFFFF
     s = ((z32 & 0xFFFF).astype(np.uint32) << 16).view(np.float32)
     z = ((z32 >> 16).astype(np.uint32) << 16).view(np.float32)

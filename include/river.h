@@ -126,7 +126,7 @@ int river_query_sizes(const river_config *cfg, river_sizes *out);
  * linear: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down.
  * Packed int4 layout of a linear with N rows and K columns:
  *   codes: uint32 [N][K/8]; word w of row n holds the codes of columns
- *          8w..8w+7, column 8w+j in bits 4*(j%4) + 16*(j/4) .. +3;
+ *          8w..8w+7, column 8w+j in bits 4j..4j+3;
  *   sz:    uint32 [N][K/G]; bf16 scale in bits 0..15, bf16 zero in 16..31;
  *   w_hat = (code - zero) * scale.
  * In RIVER_EXIT_COPY mode the bank holds bf16 [N][K] copies instead, each
@@ -183,8 +183,35 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     run layers < e on the backbone and the rest as exit
  *                     layers without testing (e = n_layers: original model,
  *                     e = 0: every layer quantised). */
-enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2 };
+enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
+
+/* Kernel classes timed when RIVER_OPT_PROFILE is 1 (decode steps then launch
+ * eagerly, with a HIP event recorded on the context's stream before and after
+ * every kernel). */
+enum {
+  RIVER_K_BEGIN = 0,   /* control reset + embedding gather               */
+  RIVER_K_QKV = 1,     /* decode: RMSNorm + q|k|v GEMV + RoPE + KV write  */
+  RIVER_K_ATTN = 2,    /* decode: split-K GQA attention                   */
+  RIVER_K_O = 3,       /* decode: o GEMV + residual                       */
+  RIVER_K_GATEUP = 4,  /* decode: RMSNorm + gate|up GEMV + SwiGLU         */
+  RIVER_K_DOWN = 5,    /* decode: down GEMV + residual + exit test        */
+  RIVER_K_LMHEAD = 6,  /* final RMSNorm + LM head GEMV + argmax           */
+  RIVER_K_P_NORM = 7,  /* prefill: RMSNorm rows                           */
+  RIVER_K_P_GEMM = 8,  /* prefill: MFMA GEMMs                             */
+  RIVER_K_P_ATTN = 9,  /* prefill: causal attention                       */
+  RIVER_K_P_COS = 10,  /* prefill: sequence-level exit test               */
+  RIVER_K_NKINDS = 11
+};
+typedef struct {
+  int64_t launches;    /* kernels of this class timed since the last read  */
+  double total_ms;     /* their summed durations (event to event)          */
+} river_kernel_time_t;
+
+/* Per-class kernel times accumulated since the previous call (or since
+ * profiling was switched on); out has RIVER_K_NKINDS entries.  Synchronises
+ * the stream.  RIVER_E_STATE when profiling is off. */
+int river_profile_read(river_ctx *ctx, river_kernel_time_t *out);
 
 /* Start a new sequence: position back to 0 (statistics are kept). */
 int river_reset(river_ctx *ctx);
