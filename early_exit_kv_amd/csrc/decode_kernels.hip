@@ -146,7 +146,8 @@ template <> struct GemvTile<kEpResidExit> { static constexpr int R = 2, UQ = 8, 
 template <> struct GemvTile<kEpLogits> { static constexpr int R = 2, UQ = 8, UB = 8; };
 
 template <int M, int XS, int EP>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int ntask) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M == 1 ? 4 : 1, 8)))
+void gemv_kernel(GemvParams p, int kslab, int ntask) {
   constexpr int R = GemvTile<EP>::R, UQ = GemvTile<EP>::UQ, UB = GemvTile<EP>::UB;
   constexpr int UMAX = UQ > UB ? UQ : UB;
   extern __shared__ uint4 smem4[];
@@ -164,56 +165,73 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
   const int K = p.K, KW = K >> 3, KG = K >> p.gshift;
   Control *ctl = p.ctrl;
   const int half = kslab >> 1;
-  const bool single = K <= kslab;
+  // one LDS stage holds all of K for one or two batch rows (K <= 16384)
+  const bool single = M <= 2 || K <= kslab;
   const int wstride = gridDim.x * 4;   // wavefront tasks are strided over all wavefronts
 
-  // ---- exit choice as far as it is known before the pending test (if any)
-  const int flag0 = __hip_atomic_load(&ctl->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool pending = EP == kEpQKV && p.test_prev && ctl->force_E < 0 && flag0 == 0;
-  bool ex = (EP == kEpQKV && flag0 != 0) || layer_uses_exit(ctl, p.layer);
+  // ---- exit choice as far as it is known before the pending test (if any).
+  // Plain loads of uniform addresses: they go through the scalar cache and do
+  // not hold up the vector loads issued below.  (Workgroup 0 of a QKV launch
+  // may set the flag while others read it; both values lead to the same
+  // choice, because every workgroup also takes the pending decision itself.)
+  const int flag0 = ctl->flag;
+  const int force0 = ctl->force_E;
+  const bool pending = EP == kEpQKV && p.test_prev && force0 < 0 && flag0 == 0;
+  bool ex = flag0 != 0 || (p.layer >= 0 && force0 >= 0 && p.layer >= force0);
+  if (p.layer < 0) ex = false;
   bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
 
-  const uint16_t *wbf[R];
-  const uint32_t *wq[R];
-  const uint32_t *wz[R];
+  // Rows of the current task: row indices plus at most two segment bases (the
+  // first half of a gate|up task reads gate rows, the second half up rows; the
+  // RoPE pairs of a QKV task belong to one head and so to one segment).
+  int rowi[R];
   bool rv[R];
+  const uint16_t *bfA = nullptr, *bfB = nullptr;
+  const uint32_t *qA = nullptr, *qB = nullptr, *zA = nullptr, *zB = nullptr;
+  auto seg_base = [&](int sg, const uint16_t *&bf, const uint32_t *&q, const uint32_t *&z) {
+    if (sg == 0) { bf = ex ? p.w.ex_bf[0] : p.w.bf[0]; q = p.w.q4[0]; z = p.w.sz[0]; }
+    else if (sg == 1) { bf = ex ? p.w.ex_bf[1] : p.w.bf[1]; q = p.w.q4[1]; z = p.w.sz[1]; }
+    else { bf = ex ? p.w.ex_bf[2] : p.w.bf[2]; q = p.w.q4[2]; z = p.w.sz[2]; }
+  };
   auto setup_rows = [&](int task) {
     const int first = task * R;
+    const int seg0 = map_row<EP>(p, first, first, R).seg;
+    seg_base(EP == kEpSwiGLU ? 0 : seg0, bfA, qA, zA);
+    seg_base(EP == kEpSwiGLU ? 1 : seg0, bfB, qB, zB);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const RowRef rr = map_row<EP>(p, first + r, first, R);
       rv[r] = rr.valid;
-      const int row = rr.valid ? rr.row : 0;
-      const uint16_t *bf = ex ? p.w.ex_bf[rr.seg] : p.w.bf[rr.seg];
-      wbf[r] = q4 ? nullptr : bf + (int64_t)row * K;
-      wq[r] = q4 ? p.w.q4[rr.seg] + (int64_t)row * KW : nullptr;
-      wz[r] = q4 ? p.w.sz[rr.seg] + (int64_t)row * KG : nullptr;
+      rowi[r] = rr.valid ? rr.row : 0;
     }
   };
-  uint4 wv[UMAX][R];
+  auto second_half = [&](int r) { return EP == kEpSwiGLU && r >= R / 2; };
+  v4u wv[UMAX][R];
   uint32_t zv[UQ][R];
+  // Every load is issued unconditionally (straight-line code, one batch in
+  // flight): chunks past the end of a row are clamped to its last chunk and
+  // rows past the end of the matrix read row 0; neither result is used.
   auto load_batch = [&](int k0, int nch, int c0) {
     if (q4) {
 #pragma unroll
       for (int u = 0; u < UQ; ++u) {
-        const int c = c0 + 64 * u;
+        const int c = min(c0 + 64 * u, nch - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const bool ok = c < nch && rv[r];
-          wv[u][r] = ok ? *reinterpret_cast<const uint4 *>(wq[r] + (k0 >> 3) + 4 * c)
-                        : make_uint4(0, 0, 0, 0);
-          zv[u][r] = ok ? wz[r][(k0 + 32 * c) >> p.gshift] : 0u;
+          const uint32_t *q = (second_half(r) ? qB : qA) + (int64_t)rowi[r] * KW + (k0 >> 3) + 4 * c;
+          const uint32_t *z = (second_half(r) ? zB : zA) + (int64_t)rowi[r] * KG + ((k0 + 32 * c) >> p.gshift);
+          wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(q));
+          zv[u][r] = *z;
         }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        const int c = c0 + 64 * u;
+        const int c = min(c0 + 64 * u, nch - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const bool ok = c < nch && rv[r];
-          wv[u][r] = ok ? *reinterpret_cast<const uint4 *>(wbf[r] + k0 + 8 * c)
-                        : make_uint4(0, 0, 0, 0);
+          const uint16_t *w = (second_half(r) ? bfB : bfA) + (int64_t)rowi[r] * K + k0 + 8 * c;
+          wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(w));
         }
       }
     }
@@ -236,16 +254,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
             for (int r = 0; r < R; ++r) {
               uint32_t pr[4];
               float d = 0.f;
-              unpack_word(wv[u][r].x, pr);
+              unpack_word(wv[u][r][0], pr);
               d = dot2_bf16(pr[0], x0.x, d); d = dot2_bf16(pr[1], x0.y, d);
               d = dot2_bf16(pr[2], x0.z, d); d = dot2_bf16(pr[3], x0.w, d);
-              unpack_word(wv[u][r].y, pr);
+              unpack_word(wv[u][r][1], pr);
               d = dot2_bf16(pr[0], x1.x, d); d = dot2_bf16(pr[1], x1.y, d);
               d = dot2_bf16(pr[2], x1.z, d); d = dot2_bf16(pr[3], x1.w, d);
-              unpack_word(wv[u][r].z, pr);
+              unpack_word(wv[u][r][2], pr);
               d = dot2_bf16(pr[0], x2.x, d); d = dot2_bf16(pr[1], x2.y, d);
               d = dot2_bf16(pr[2], x2.z, d); d = dot2_bf16(pr[3], x2.w, d);
-              unpack_word(wv[u][r].w, pr);
+              unpack_word(wv[u][r][3], pr);
               d = dot2_bf16(pr[0], x3.x, d); d = dot2_bf16(pr[1], x3.y, d);
               d = dot2_bf16(pr[2], x3.z, d); d = dot2_bf16(pr[3], x3.w, d);
               const float sc = bf_lo(zv[u][r]);
@@ -266,10 +284,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               float d = acc[r][b];
-              d = dot2_bf16(wv[u][r].x, xv.x, d);
-              d = dot2_bf16(wv[u][r].y, xv.y, d);
-              d = dot2_bf16(wv[u][r].z, xv.z, d);
-              d = dot2_bf16(wv[u][r].w, xv.w, d);
+              d = dot2_bf16(wv[u][r][0], xv.x, d);
+              d = dot2_bf16(wv[u][r][1], xv.y, d);
+              d = dot2_bf16(wv[u][r][2], xv.z, d);
+              d = dot2_bf16(wv[u][r][3], xv.w, d);
               acc[r][b] = d;
             }
           }
@@ -278,30 +296,89 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
     }
   };
 
-  // ---- prologue.  Its own loads go first (RMSNorm statistics; for the first
-  // kernel of a layer also the previous layer's exit sums); the first weight
-  // batch is issued right behind them, so the weights stream in while the
-  // prologue reduces and stages the activations.
+  // ---- prologue.  Its own loads go first (RMSNorm input rows; for the first
+  // kernel of a layer also the previous layer's exit sums), the first weight
+  // batch right behind them, and only then does anything wait: the weights
+  // stream in while the prologue reduces and stages the activations.
   const int n8 = K >> 3;
   float sums[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) sums[i] = 0.f;
-  if constexpr (XS == kXNorm) {
-    for (int idx = threadIdx.x; idx < M * n8; idx += 256) {
-      const int b = idx / n8, g8 = idx - b * n8;
-      if (b < p.B) {
-        const float *h = p.h_src + (int64_t)b * p.h_stride + 8 * g8;
-        const float4 a0 = *reinterpret_cast<const float4 *>(h);
-        const float4 a1 = *reinterpret_cast<const float4 *>(h + 4);
-        const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
-                         a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+  // the normalised rows are held in registers when M*K/8 <= 256*kHeld
+  constexpr int kHeld = 2;
+  const bool held = XS == kXNorm && M * n8 <= 256 * kHeld;
+  float4 hv[kHeld][2];
+  uint4 gv[kHeld];
+  if (XS == kXNorm && held) {
 #pragma unroll
-        for (int bb = 0; bb < M; ++bb) sums[bb] += bb == b ? ss : 0.f;
+    for (int j = 0; j < kHeld; ++j) {
+      const int idx = min((int)threadIdx.x + 256 * j, M * n8 - 1);
+      const int b = min(idx / n8, p.B - 1), g8 = idx % n8;
+      const float *h = p.h_src + (int64_t)b * p.h_stride + 8 * g8;
+      hv[j][0] = *reinterpret_cast<const float4 *>(h);
+      hv[j][1] = *reinterpret_cast<const float4 *>(h + 4);
+      gv[j] = *reinterpret_cast<const uint4 *>(p.gain + 8 * g8);
+    }
+  }
+  constexpr int kPartHeld = 4;   // exit partials per thread held in registers
+  float pv[kPartHeld][3 * M];
+  if (pending) {
+#pragma unroll
+    for (int j = 0; j < kPartHeld; ++j) {
+      const int wg = min((int)threadIdx.x + 256 * j, p.part_wgs - 1);
+      const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
+#pragma unroll
+      for (int i = 0; i < 3 * M; ++i) pv[j][i] = pp[i];
+    }
+  }
+  int task = blockIdx.x * 4 + wid;
+  setup_rows(task);
+  load_batch(0, nchunks(min(kslab, K)), lane);
+
+  if constexpr (XS == kXNorm) {
+    if (held) {
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j) {
+        const int idx = threadIdx.x + 256 * j;
+        if (idx < M * n8 && idx / n8 < p.B) {
+          const int b = idx / n8;
+          const float4 a0 = hv[j][0], a1 = hv[j][1];
+          const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
+                           a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+#pragma unroll
+          for (int bb = 0; bb < M; ++bb) sums[bb] += bb == b ? ss : 0.f;
+        }
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < M * n8; idx += 256) {
+        const int b = idx / n8, g8 = idx - b * n8;
+        if (b < p.B) {
+          const float *h = p.h_src + (int64_t)b * p.h_stride + 8 * g8;
+          const float4 a0 = *reinterpret_cast<const float4 *>(h);
+          const float4 a1 = *reinterpret_cast<const float4 *>(h + 4);
+          const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
+                           a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+#pragma unroll
+          for (int bb = 0; bb < M; ++bb) sums[bb] += bb == b ? ss : 0.f;
+        }
       }
     }
   }
   if (pending) {
-    for (int wg = threadIdx.x; wg < p.part_wgs; wg += 256) {
+#pragma unroll
+    for (int j = 0; j < kPartHeld; ++j) {
+      if ((int)threadIdx.x + 256 * j < p.part_wgs) {
+#pragma unroll
+        for (int b = 0; b < M; ++b) {
+          if (b < p.B) {
+            sums[M + 3 * b] += pv[j][3 * b];
+            sums[M + 3 * b + 1] += pv[j][3 * b + 1];
+            sums[M + 3 * b + 2] += pv[j][3 * b + 2];
+          }
+        }
+      }
+    }
+    for (int wg = threadIdx.x + 256 * kPartHeld; wg < p.part_wgs; wg += 256) {
       const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
 #pragma unroll
       for (int b = 0; b < M; ++b) {
@@ -313,10 +390,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
       }
     }
   }
-  int task = blockIdx.x * 4 + wid;
-  setup_rows(task);
-  load_batch(0, nchunks(min(kslab, K)), lane);
-
   if (XS == kXNorm || pending) {
     if (XS == kXNorm) {
 #pragma unroll
@@ -378,10 +451,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
       float csum = 0.f;
       if (b < p.B) {
         if constexpr (XS == kXNorm) {
-          const float *h = p.h_src + (int64_t)b * p.h_stride + col;
-          const float4 h0 = *reinterpret_cast<const float4 *>(h);
-          const float4 h1 = *reinterpret_cast<const float4 *>(h + 4);
-          const uint4 g = *reinterpret_cast<const uint4 *>(p.gain + col);
+          float4 h0, h1;
+          uint4 g;
+          const int j = (idx - (int)threadIdx.x) >> 8;
+          if (held && k0 == 0 && j < kHeld) {
+#pragma unroll
+            for (int jj = 0; jj < kHeld; ++jj)
+              if (jj == j) { h0 = hv[jj][0]; h1 = hv[jj][1]; g = gv[jj]; }
+          } else {
+            const float *h = p.h_src + (int64_t)b * p.h_stride + col;
+            h0 = *reinterpret_cast<const float4 *>(h);
+            h1 = *reinterpret_cast<const float4 *>(h + 4);
+            g = *reinterpret_cast<const uint4 *>(p.gain + col);
+          }
           float ssb = 0.f;
 #pragma unroll
           for (int bb = 0; bb < M; ++bb) ssb = bb == b ? sums[bb] : ssb;
@@ -418,7 +500,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
   // lane-local epilogue state kept across tasks
   float ed = 0.f, ea = 0.f, eb = 0.f;
   uint64_t best = 0;
-  const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && ctl->force_E < 0;
+  const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && force0 < 0;
 
   auto finish_task = [&](int first) {
 #pragma unroll
@@ -516,7 +598,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p, int kslab, int 
     zero_acc();
     for (int k0 = 0; k0 < K; k0 += kslab) {
       const int ks = min(kslab, K - k0);
-      if (!single) {
+      if (M > 2 && !single) {
         __syncthreads();
         stage(k0, ks);
       }
@@ -714,7 +796,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   __shared__ float wm[4][GQ];
   __shared__ float wl[4][PPW][GQ];
   __shared__ __align__(16) float wo[4][PPW][GQ][DH];
-  __shared__ float sm[kMaxAttnSplits][GQ][2];
   __shared__ int last_flag;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -849,43 +930,39 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   }
   if (direct) return;
   if (arrive_last(&p.counters[b * p.Hkv + kvh], gridDim.x, &last_flag)) {
-    // merge the splits that hold positions: scale factors first, then the
-    // weighted sum with every load of a thread issued together
+    // merge the splits that hold positions, 16 splits per round of loads,
+    // with the same running-max rescaling as inside a split
     const int nval = (n + p.chunk - 1) / p.chunk;
-    for (int idx = threadIdx.x; idx < nval * GQ; idx += 256) {
-      const int sp = idx / GQ, h = idx % GQ;
-      const float *pp = part_base + ((int64_t)h * p.splits + sp) * (DH + 2);
-      sm[sp][h][0] = ld_coherent(pp + DH);
-      sm[sp][h][1] = ld_coherent(pp + DH + 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < GQ) {
-      const int h = threadIdx.x;
-      float mx = -INFINITY;
-      for (int sp = 0; sp < nval; ++sp) mx = fmaxf(mx, sm[sp][h][0]);
-      float L = 0.f;
-      for (int sp = 0; sp < nval; ++sp) {
-        const float f = sm[sp][h][0] == -INFINITY ? 0.f : expf(sm[sp][h][0] - mx);
-        sm[sp][h][0] = f;
-        L += f * sm[sp][h][1];
-      }
-      wm[0][h] = 1.0f / L;
-    }
-    __syncthreads();
     for (int idx = threadIdx.x; idx < GQ * DH; idx += 256) {
       const int h = idx / DH, e = idx % DH;
-      const float *base = part_base + (int64_t)h * p.splits * (DH + 2) + e;
-      float o = 0.f;
-      int sp = 0;
-      for (; sp + 8 <= nval; sp += 8) {
-        float v[8];
+      const float *base = part_base + (int64_t)h * p.splits * (DH + 2);
+      float M = -INFINITY, L = 0.f, O = 0.f;
+      for (int s0 = 0; s0 < nval; s0 += 16) {
+        float ms[16], ls[16], os[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = ld_coherent(base + (sp + u) * (DH + 2));
+        for (int u = 0; u < 16; ++u) {
+          const bool ok = s0 + u < nval;
+          const float *pp = base + (int64_t)(s0 + u) * (DH + 2);
+          ms[u] = ok ? ld_coherent(pp + DH) : -INFINITY;
+          ls[u] = ok ? ld_coherent(pp + DH + 1) : 0.f;
+          os[u] = ok ? ld_coherent(pp + e) : 0.f;
+        }
+        float mx = M;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o = fmaf(sm[sp + u][h][0], v[u], o);
+        for (int u = 0; u < 16; ++u) mx = fmaxf(mx, ms[u]);
+        if (mx == -INFINITY) continue;
+        const float corr = expf(M - mx);
+        L *= corr;
+        O *= corr;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float f = expf(ms[u] - mx);
+          L = fmaf(f, ls[u], L);
+          O = fmaf(f, os[u], O);
+        }
+        M = mx;
       }
-      for (; sp < nval; ++sp) o = fmaf(sm[sp][h][0], ld_coherent(base + sp * (DH + 2)), o);
-      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(o * wm[0][h]);
+      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(O / L);
     }
   }
 }
