@@ -144,6 +144,7 @@ template <> struct GemvTile<kEpResid> { static constexpr int R = 4, UQ = 2, UB =
 template <> struct GemvTile<kEpSwiGLU> { static constexpr int R = 8, UQ = 2, UB = 2; };
 template <> struct GemvTile<kEpResidExit> { static constexpr int R = 2, UQ = 8, UB = 8; };
 template <> struct GemvTile<kEpLogits> { static constexpr int R = 2, UQ = 8, UB = 8; };
+template <> struct GemvTile<kEpPlain> { static constexpr int R = 4, UQ = 2, UB = 2; };
 
 template <int M, int XS, int EP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M == 1 ? 4 : 1, 8)))
@@ -176,9 +177,10 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   // choice, because every workgroup also takes the pending decision itself.)
   const int flag0 = ctl->flag;
   const int force0 = ctl->force_E;
-  const bool pending = EP == kEpQKV && p.test_prev && force0 < 0 && flag0 == 0;
+  const bool pending = EP == kEpQKV && p.path == kPathDevice && p.test_prev && force0 < 0 && flag0 == 0;
   bool ex = flag0 != 0 || (p.layer >= 0 && force0 >= 0 && p.layer >= force0);
   if (p.layer < 0) ex = false;
+  if (p.path != kPathDevice) ex = p.path == kPathExit;
   bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
 
   // Rows of the current task: row indices plus at most two segment bases (the
@@ -571,6 +573,12 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
           }
         }
       }
+    } else if constexpr (EP == kEpPlain) {
+      if (lane < R * M) {
+        const int r = lane / M, b = lane % M;
+        const int n = first + r;
+        if (b < p.B && n < p.N) p.y_out[(int64_t)b * p.y_stride + n] = pick(r, b);
+      }
     } else if constexpr (EP == kEpLogits) {
       if (lane < R * M) {
         const int r = lane / M, b = lane % M;
@@ -734,6 +742,7 @@ static GemvPlan plan_for(Epilogue ep, const GemvParams &p) {
     case kEpSwiGLU: return gemv_plan_m<kXNorm, kEpSwiGLU>(p);
     case kEpResid: return gemv_plan_m<kXBf16, kEpResid>(p);
     case kEpResidExit: return gemv_plan_m<kXBf16, kEpResidExit>(p);
+    case kEpPlain: return gemv_plan_m<kXBf16, kEpPlain>(p);
     default: return gemv_plan_m<kXNorm, kEpLogits>(p);
   }
 }
@@ -742,7 +751,7 @@ int gemv_grid(Epilogue ep, const GemvParams &p) { return plan_for(ep, p).grid; }
 
 hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s) {
   (void)xs;
-  if (p.B < 1 || p.B > 8 || ep > kEpLogits) return hipErrorInvalidValue;
+  if (p.B < 1 || p.B > 8 || ep > kEpPlain) return hipErrorInvalidValue;
   const GemvPlan g = plan_for(ep, p);
   int kslab = g.kslab, ntask = g.ntask;
   GemvParams pc = p;

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   __shared__ uint32_t szs[BN];
   __shared__ float xsg[BM];
 
-  const bool ex = layer_uses_exit(p.ctrl, p.layer);
+  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -324,6 +324,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       const float gt = Cs[r][jj], up = Cs[r][hw + jj];
       p.u_out[m * p.w.seg_rows[0] + n] = f2bf(gt / (1.0f + expf(-gt)) * up);
     }
+  } else if constexpr (EP == kEpPlain) {
+    for (int idx = tid; idx < BM * BN; idx += 256) {
+      const int r = idx / BN, j = idx % BN;
+      const int64_t m = m0 + r;
+      const int n = blockIdx.y * BN + j;
+      if (m < p.M && n < p.N) p.y_out[m * p.y_stride + n] = Cs[r][j];
+    }
   } else {  // residual
     for (int idx = tid; idx < BM * BN; idx += 256) {
       const int r = idx / BN, j = idx % BN;
@@ -352,6 +359,7 @@ hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
     case kEpQKV: return gemm_launch_ep<kEpQKV>(p, s);
     case kEpSwiGLU: return gemm_launch_ep<kEpSwiGLU>(p, s);
     case kEpResid: return gemm_launch_ep<kEpResid>(p, s);
+    case kEpPlain: return gemm_launch_ep<kEpPlain>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -86,6 +86,26 @@ Workspace workspace_layout(const river_config &c) {
   return w;
 }
 
+// Offsets of the activation record of one pass with `rows` rows.
+struct RecordLayout {
+  size_t h_in, q, attn, h_mid, u, per_layer, h_out, total;
+};
+RecordLayout record_layout(const river_config &c, int64_t rows) {
+  RecordLayout r{};
+  const int64_t qd = (int64_t)c.n_q_heads * c.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  r.h_in = take(rows * c.d_model * 4);
+  r.q = take(rows * qd * 2);
+  r.attn = take(rows * qd * 2);
+  r.h_mid = take(rows * c.d_model * 4);
+  r.u = take(rows * c.ffn_dim * 2);
+  r.per_layer = off;
+  r.h_out = r.per_layer * c.n_layers;
+  r.total = r.h_out + align256(rows * c.d_model * 4);
+  return r;
+}
+
 }  // namespace river
 
 using namespace river;
@@ -126,6 +146,9 @@ struct river_ctx {
   };
   std::vector<Timed> timed;
   std::vector<hipEvent_t> event_pool;
+  // activation record (off when rec == nullptr)
+  char *rec = nullptr;
+  size_t rec_bytes = 0;
 };
 
 namespace {
@@ -235,12 +258,26 @@ struct TimedLaunch {
 #define TIMED(kind, expr) RV_TRY(TimedLaunch(ctx, kind).done(expr))
 
 // Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
+// Copy one produced array into the activation record (no-op when off).
+struct Recorder {
+  river_ctx *ctx;
+  RecordLayout lay;
+  int64_t rows;
+  hipError_t put(int layer, size_t field, const void *src, size_t bytes) const {
+    if (!ctx->rec) return hipSuccess;
+    const size_t off = layer < 0 ? lay.h_out : layer * lay.per_layer + field;
+    return hipMemcpyAsync(ctx->rec + off, src, bytes, hipMemcpyDeviceToDevice, ctx->stream);
+  }
+};
+
 int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next) {
   const river_config &c = ctx->cfg;
   const int B = ctx->batch;
   hipStream_t s = ctx->stream;
   float *hA = at<float>(ctx->ws, ctx->wl.hA), *hB = at<float>(ctx->ws, ctx->wl.hB);
   const int qd = c.n_q_heads * c.head_dim;
+  const Recorder rec{ctx, record_layout(c, B), B};
+  const size_t hbytes = (size_t)B * c.d_model * 4, qbytes = (size_t)B * qd * 2;
 
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
@@ -268,7 +305,9 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
     // the exit test after layer l-1 is decided at the start of this kernel
     q.test_prev = l > 0; q.part = at<float>(ctx->ws, ctx->wl.part); q.part_wgs = down_wgs;
+    RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
     TIMED(RIVER_K_QKV, launch_gemv(kXNorm, kEpQKV, q, s));
+    RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
 
     AttnParams a{};
     a.q = q.q_out; a.k_cache = q.k_cache; a.v_cache = q.v_cache;
@@ -279,12 +318,14 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
     TIMED(RIVER_K_ATTN, launch_attn_decode(a, s));
+    RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
     GemvParams o = g;
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x_src = a.out; o.x_stride = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
     TIMED(RIVER_K_O, launch_gemv(kXBf16, kEpResid, o, s));
+    RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
     GemvParams gu = g;
     fill_weights(ctx, l, 4, 2, gu.w);
@@ -292,6 +333,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     gu.h_src = hB; gu.h_stride = c.d_model; gu.gain = static_cast<const uint16_t *>(L.mlp_norm);
     gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u); gu.u_stride = c.ffn_dim;
     TIMED(RIVER_K_GATEUP, launch_gemv(kXNorm, kEpSwiGLU, gu, s));
+    RV_TRY(rec.put(l, rec.lay.u, gu.u_out, (size_t)B * c.ffn_dim * 2));
 
     GemvParams dn = g;
     fill_weights(ctx, l, 6, 1, dn.w);
@@ -303,6 +345,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     TIMED(RIVER_K_DOWN, launch_gemv(kXBf16, kEpResidExit, dn, s));
     std::swap(hA, hB);
   }
+  RV_TRY(rec.put(-1, 0, hA, hbytes));
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
@@ -322,6 +365,8 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
   float *hA = at<float>(ctx->ws, ctx->wl.hA), *hB = at<float>(ctx->ws, ctx->wl.hB);
   uint16_t *x = at<uint16_t>(ctx->ws, ctx->wl.x);
   const int qd = c.n_q_heads * c.head_dim;
+  const Recorder rec{ctx, record_layout(c, R), R};
+  const size_t hbytes = (size_t)R * c.d_model * 4, qbytes = (size_t)R * qd * 2;
 
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = R; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
@@ -337,6 +382,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     g.max_batch = c.max_batch; g.T = T; g.rope_theta = c.rope_theta;
     g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
 
+    RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
     RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), R, c.d_model, c.rms_eps};
     TIMED(RIVER_K_P_NORM, launch_rows_norm(rn, s));
 
@@ -346,6 +392,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
     q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
     TIMED(RIVER_K_P_GEMM, launch_gemm(kEpQKV, q, s));
+    RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
 
     AttnPrefillParams ap{};
     ap.q = q.q_out; ap.k_cache = q.k_cache; ap.v_cache = q.v_cache;
@@ -353,12 +400,14 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     ap.Hkv = c.n_kv_heads; ap.Dh = c.head_dim; ap.S = c.max_seq;
     ap.scale = 1.0f / std::sqrt((float)c.head_dim);
     TIMED(RIVER_K_P_ATTN, launch_attn_prefill(ap, s));
+    RV_TRY(rec.put(l, rec.lay.attn, ap.out, qbytes));
 
     GemmParams o = g;
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x = ap.out; o.ldx = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
     TIMED(RIVER_K_P_GEMM, launch_gemm(kEpResid, o, s));
+    RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
     RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), R, c.d_model, c.rms_eps};
     TIMED(RIVER_K_P_NORM, launch_rows_norm(rn2, s));
@@ -368,6 +417,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     gu.N = 2 * c.ffn_dim; gu.K = c.d_model; gu.x = x; gu.ldx = c.d_model;
     gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u);
     TIMED(RIVER_K_P_GEMM, launch_gemm(kEpSwiGLU, gu, s));
+    RV_TRY(rec.put(l, rec.lay.u, gu.u_out, (size_t)R * c.ffn_dim * 2));
 
     GemmParams dn = g;
     fill_weights(ctx, l, 6, 1, dn.w);
@@ -382,6 +432,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     }
     std::swap(hA, hB);
   }
+  RV_TRY(rec.put(-1, 0, hA, hbytes));
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
@@ -534,6 +585,8 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
   if (!ctx->built) return RIVER_E_STATE;
   if (B < 1 || T < 1 || B > ctx->cfg.max_batch || T > ctx->cfg.max_seq) return RIVER_E_RANGE;
   if (B > 8) return RIVER_E_UNIMPLEMENTED;
+  if (ctx->rec && record_layout(ctx->cfg, (int64_t)B * T).total > ctx->rec_bytes)
+    return RIVER_E_BAD_SIZE;
   const int st = enqueue_prefill(ctx, d_tokens, B, T, tau, d_logits, d_next);
   if (st != RIVER_OK) return st;
   ctx->pos = T;
@@ -547,7 +600,9 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
   if (!std::isfinite(tau)) return RIVER_E_INVALID_ARG;
   if (!ctx->built || ctx->batch == 0) return RIVER_E_STATE;
   if (ctx->pos + 1 > ctx->cfg.max_seq) return RIVER_E_RANGE;
-  if (ctx->use_graph && !ctx->profiling && ctx->stream != nullptr) {
+  if (ctx->rec && record_layout(ctx->cfg, ctx->batch).total > ctx->rec_bytes)
+    return RIVER_E_BAD_SIZE;
+  if (ctx->use_graph && !ctx->profiling && !ctx->rec && ctx->stream != nullptr) {
     river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E, 0};
     std::memcpy(&key.tau_bits, &tau, 4);
     auto it = ctx->graphs.find(key);
@@ -617,6 +672,20 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
   return RIVER_E_INVALID_ARG;
 }
 
+int river_record_bytes(const river_config *cfg, int32_t rows, size_t *bytes) {
+  if (!cfg || !bytes || !valid_config(cfg) || rows < 1) return RIVER_E_INVALID_ARG;
+  *bytes = record_layout(*cfg, rows).total;
+  return RIVER_OK;
+}
+
+int river_set_record(river_ctx *ctx, void *d_buf, size_t bytes) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  if (d_buf && bytes < record_layout(ctx->cfg, 1).total) return RIVER_E_BAD_SIZE;
+  ctx->rec = static_cast<char *>(d_buf);
+  ctx->rec_bytes = d_buf ? bytes : 0;
+  return RIVER_OK;
+}
+
 int river_reset(river_ctx *ctx) {
   if (!ctx) return RIVER_E_INVALID_ARG;
   ctx->pos = 0;
@@ -639,6 +708,38 @@ int river_profile_read(river_ctx *ctx, river_kernel_time_t *out) {
     ctx->event_pool.push_back(t.b);
   }
   ctx->timed.clear();
+  return RIVER_OK;
+}
+
+int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit,
+                       const void *d_x, int32_t M, float *d_y) {
+  if (!ctx || !d_x || !d_y) return RIVER_E_INVALID_ARG;
+  if (!ctx->built) return RIVER_E_STATE;
+  const river_config &c = ctx->cfg;
+  if (layer < 0 || layer >= c.n_layers || linear < 0 || linear >= 7 || M < 1 ||
+      (use_exit != 0 && use_exit != 1))
+    return RIVER_E_RANGE;
+  LinearShape sh[7];
+  linear_shapes(c, sh);
+  const int path = use_exit ? kPathExit : kPathBackbone;
+  if (M <= 8) {
+    GemvParams g{};
+    fill_weights(ctx, layer, linear, 1, g.w);
+    g.N = sh[linear].N; g.K = sh[linear].K; g.G = c.group_size;
+    g.gshift = __builtin_ctz((unsigned)c.group_size);
+    g.layer = layer; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl; g.B = M;
+    g.x_src = static_cast<const uint16_t *>(d_x); g.x_stride = sh[linear].K;
+    g.path = path; g.y_out = d_y; g.y_stride = sh[linear].N;
+    RV_TRY(launch_gemv(kXBf16, kEpPlain, g, ctx->stream));
+  } else {
+    GemmParams g{};
+    fill_weights(ctx, layer, linear, 1, g.w);
+    g.M = M; g.N = sh[linear].N; g.K = sh[linear].K; g.G = c.group_size;
+    g.layer = layer; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl;
+    g.x = static_cast<const uint16_t *>(d_x); g.ldx = sh[linear].K;
+    g.path = path; g.y_out = d_y; g.y_stride = sh[linear].N;
+    RV_TRY(launch_gemm(kEpPlain, g, ctx->stream));
+  }
   return RIVER_OK;
 }
 

@@ -101,7 +101,9 @@ constexpr int kPartFloatsPerWG = 3 * 64;  // B <= 64 rows x (dot, |a|^2, |b|^2)
 // Kernel launch parameters
 // ---------------------------------------------------------------------------
 enum XSource { kXNorm = 0, kXBf16 = 1 };
-enum Epilogue { kEpQKV = 0, kEpResid = 1, kEpResidExit = 2, kEpSwiGLU = 3, kEpLogits = 4 };
+enum Epilogue { kEpQKV = 0, kEpResid = 1, kEpResidExit = 2, kEpSwiGLU = 3, kEpLogits = 4, kEpPlain = 5 };
+// weight path of a launch: decided on the device, or fixed (debug entry point)
+enum PathChoice { kPathDevice = 0, kPathBackbone = 1, kPathExit = 2 };
 
 struct LinearWeights {
   const uint16_t *bf[3];   // backbone bf16 segments (or exit bf16 copies)
@@ -136,6 +138,8 @@ struct GemvParams {
   int test_exit; int n_layers;                            // down: write the partials
   int test_prev; int part_wgs;    // QKV: decide the previous layer's test first
   int gshift;                     // log2(group size)
+  int path;                       // PathChoice
+  float *y_out; int64_t y_stride; // kEpPlain: fp32 [B][N]
   float *logits; int32_t *next; int is_prefill; int vocab;// LM head
 };
 
@@ -197,6 +201,8 @@ struct GemmParams {
   int Hq, Hkv, Dh, max_seq, max_batch, T; float rope_theta;
   const float2 *rope;
   uint16_t *u_out;
+  int path;                        // PathChoice
+  float *y_out; int64_t y_stride;  // kEpPlain
 };
 hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 

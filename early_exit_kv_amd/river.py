@@ -27,6 +27,7 @@ EXPORTS = (
     "river_query_sizes", "river_exit_bank_offsets", "river_init", "river_build_exit_layers",
     "river_prefill", "river_decode_step", "river_exit_stats", "river_set_option",
     "river_reset", "river_destroy", "river_strerror", "river_profile_read",
+    "river_debug_linear", "river_record_bytes", "river_set_record",
 )
 
 
@@ -106,6 +107,9 @@ def load_library(path=LIB_PATH):
         "river_destroy": (None, [P]),
         "river_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "river_profile_read": (ctypes.c_int, [P, ctypes.POINTER(RiverKernelTime)]),
+        "river_debug_linear": (ctypes.c_int, [P, i32, i32, i32, P, i32, P]),
+        "river_record_bytes": (ctypes.c_int, [ctypes.POINTER(RiverConfig), i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "river_set_record": (ctypes.c_int, [P, P, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -148,6 +152,17 @@ def exit_bank_offsets(cfg, layer, linear, copy_layout=False):
                                                   ctypes.byref(co), ctypes.byref(so)),
            "river_exit_bank_offsets")
     return co.value, so.value
+
+
+def record_bytes(cfg, rows):
+    out = ctypes.c_size_t(0)
+    _check(load_library().river_record_bytes(ctypes.byref(cfg), int(rows), ctypes.byref(out)),
+           "river_record_bytes")
+    return out.value
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
 
 
 def _ptr(t):
@@ -279,6 +294,51 @@ class River:
         arr = (RiverKernelTime * len(KERNEL_KINDS))()
         self._call(self.lib.river_profile_read, "river_profile_read", arr)
         return {k: (arr[i].launches, arr[i].total_ms) for i, k in enumerate(KERNEL_KINDS)}
+
+    def debug_linear(self, layer, linear, use_exit, x):
+        """y = x W^T (fp32 [M][N]) for one linear through the production cores."""
+        N, K = self.linear_shape(linear)
+        x = x.to(torch.bfloat16).contiguous()
+        assert x.shape[1] == K
+        y = torch.empty((x.shape[0], N), dtype=torch.float32, device=x.device)
+        self._call(self.lib.river_debug_linear, "river_debug_linear", layer, linear, int(use_exit),
+                   _ptr(x), x.shape[0], _ptr(y))
+        return y
+
+    def record(self, max_rows):
+        """Switch the activation record on for passes of up to max_rows rows
+        (max_rows=0 switches it off)."""
+        if max_rows <= 0:
+            _check(self.lib.river_set_record(self.ctx, None, 0), "river_set_record")
+            self.rec = None
+            return
+        n = record_bytes(self.cfg, max_rows)
+        self.rec = torch.zeros(n, dtype=torch.uint8, device=self.ws.device)
+        _check(self.lib.river_set_record(self.ctx, _ptr(self.rec), n), "river_set_record")
+
+    def read_record(self, rows):
+        """Arrays of the last pass with `rows` rows: a list of per-layer dicts
+        (h_in, q, attn, h_mid, u) and the final residual, as float64 numpy."""
+        torch.cuda.synchronize()
+        c = self.cfg
+        qd = c.n_q_heads * c.head_dim
+        fields = (("h_in", c.d_model, 4), ("q", qd, 2), ("attn", qd, 2), ("h_mid", c.d_model, 4),
+                  ("u", c.ffn_dim, 2))
+        buf = self.rec
+
+        def arr(off, width, nbytes):
+            v = buf[off:off + rows * width * nbytes]
+            t = v.view(torch.float32) if nbytes == 4 else v.view(torch.bfloat16).float()
+            return t.reshape(rows, width).cpu().double().numpy()
+
+        layers, off = [], 0
+        for _ in range(c.n_layers):
+            d = {}
+            for name, width, nb in fields:
+                d[name] = arr(off, width, nb)
+                off += _align256(rows * width * nb)
+            layers.append(d)
+        return layers, arr(off, c.d_model, 4)
 
     def reset(self):
         _check(self.lib.river_reset(self.ctx), "river_reset")

@@ -213,6 +213,35 @@ typedef struct {
  * the stream.  RIVER_E_STATE when profiling is off. */
 int river_profile_read(river_ctx *ctx, river_kernel_time_t *out);
 
+/* Debug / test entry point: y = x W^T for one linear of one layer, through
+ * the same weight-streaming cores the passes use (GEMV for M <= 8 rows, the
+ * MFMA GEMM above), with a plain fp32 output instead of a fused epilogue.
+ *   linear: as in river_exit_bank_offsets; use_exit: 0 backbone bf16 weights,
+ *   1 the exit copy (int4 or bf16 copy, per the built mode);
+ *   d_x: device bf16 [M][K]; d_y: device fp32 [M][N].
+ * Enqueues one kernel; RIVER_E_STATE before river_build_exit_layers. */
+int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit,
+                       const void *d_x, int32_t M, float *d_y);
+
+/* Activation record, for checking a pass stage by stage (each layer of a
+ * reference can then be fed the states this library stored).  When a record
+ * buffer is set, every prefill and decode pass copies, after the kernels that
+ * produce them, for each layer l in order:
+ *   h_in   fp32 [R][d_model]   residual stream entering layer l
+ *   q      bf16 [R][Hq*Dh]     queries after RoPE
+ *   attn   bf16 [R][Hq*Dh]     attention output
+ *   h_mid  fp32 [R][d_model]   residual after the attention block
+ *   u      bf16 [R][ffn_dim]   SwiGLU product
+ * and finally h_out fp32 [R][d_model], the residual leaving the last layer.
+ * R is the number of rows of the pass (B*T for a prefill, B for a decode
+ * step); each array starts on a 256-byte boundary.  K/V are in the cache.
+ * river_record_bytes gives the size needed for `rows` rows.  Passing a NULL
+ * buffer switches recording off.  While it is on, decode steps run eagerly
+ * (no graph); a pass with more rows than the buffer holds fails with
+ * RIVER_E_BAD_SIZE before launching anything. */
+int river_record_bytes(const river_config *cfg, int32_t rows, size_t *bytes);
+int river_set_record(river_ctx *ctx, void *d_buf, size_t bytes);
+
 /* Start a new sequence: position back to 0 (statistics are kept). */
 int river_reset(river_ctx *ctx);
 

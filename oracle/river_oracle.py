@@ -197,12 +197,14 @@ def attention(q, kc, vc, start, n):
     return out
 
 
-def decoder_layer(shape, lw, h, start, kc, vc):
+def decoder_layer(shape, lw, h, start, kc, vc, rec=None):
     """One decoder layer on h [B, n, d] at positions start..start+n-1.
 
     ``lw`` holds float32 copies of the layer weights (backbone or exit copy).
     Writes the new K/V into kc/vc [B, Hkv, S, D] (this layer's slots of the
     shared cache) and returns the residual stream after the layer (float64).
+    If ``rec`` is a dict, the stored activations are put in it (q after RoPE,
+    attention output, residual after the attention block, SwiGLU product).
     """
     B, n, d = h.shape
     Hq, Hkv, D = shape.Hq, shape.Hkv, shape.Dh
@@ -220,6 +222,8 @@ def decoder_layer(shape, lw, h, start, kc, vc):
     h1 = h + linear(o, lw["wo"])
     x2 = bf16_from_f64(rmsnorm(h1, lw["mlp_norm"], shape.eps))
     u = bf16_from_f64(silu(linear(x2, lw["w_gate"])) * linear(x2, lw["w_up"]))
+    if rec is not None:
+        rec.update(h_in=h.copy(), q=q.reshape(B, n, Hq * D), attn=o.copy(), h_mid=h1.copy(), u=u.copy())
     return h1 + linear(u, lw["w_down"])
 
 
@@ -299,9 +303,10 @@ class RiverOracle:
             else:
                 use_exit = exited
             lw = self.exit_layers[l] if use_exit else self.w["layers"][l]
+            rec = {} if record else None
+            h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B], rec)
             if record:
-                inputs.append(h.copy())
-            h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B])
+                inputs.append(rec)
             if force_E is None:
                 if not exited and l < s.L - 1:
                     # batch minimum of the per-token state-transition similarity
@@ -318,7 +323,7 @@ class RiverOracle:
         logits = lm_head(s, h[:, -1], self.w["final_norm"], w_lm)
         res = {"logits": logits, "next": greedy(logits), "E": E, "trace": trace, "h_final": h}
         if record:
-            res["layer_inputs"] = inputs
+            res["layers"] = inputs
         return res
 
     def prefill(self, tokens, tau, force_E=None, record=False):

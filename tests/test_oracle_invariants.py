@@ -129,13 +129,13 @@ def test_trace_is_batch_min_and_no_recheck(tiny_np):
     o = make(tiny_np)
     r0 = o.prefill(prompt(), 2.0, record=True)
     # prefill: the minimum over all B*T prompt rows, one entry per tested layer
-    ins = r0["layer_inputs"] + [r0["h_final"]]
+    ins = [d["h_in"] for d in r0["layers"]] + [r0["h_final"]]
     assert len(r0["trace"]) == o.s.L - 1
     for l, m in enumerate(r0["trace"]):
         c = ro.cosine_rows(ins[l].reshape(-1, o.s.d), ins[l + 1].reshape(-1, o.s.d))
         assert m == c.min() and c.size == B * T
     r = o.decode_step(r0["next"], 2.0, record=True)
-    ins = r["layer_inputs"] + [r["h_final"]]
+    ins = [d["h_in"] for d in r["layers"]] + [r["h_final"]]
     for l, m in enumerate(r["trace"]):
         c = ro.cosine_rows(ins[l].reshape(-1, o.s.d), ins[l + 1].reshape(-1, o.s.d))
         assert c.size == B and m == c.min()
@@ -176,7 +176,7 @@ def test_exit_kv_lands_in_the_backbone_slot(tiny_np):
     # the slots hold the K/V the used path produces from the recorded layer inputs
     for l in range(o.s.L):
         lw = tiny_np["layers"][l] if l < r["E"] else o.exit_layers[l]
-        x = ro.bf16_from_f64(ro.rmsnorm(r["layer_inputs"][l][:, 0], lw["attn_norm"], o.s.eps))
+        x = ro.bf16_from_f64(ro.rmsnorm(r["layers"][l]["h_in"][:, 0], lw["attn_norm"], o.s.eps))
         k = ro.linear(x, lw["wk"]).reshape(B, 1, o.s.Hkv, o.s.Dh)
         v = ro.linear(x, lw["wv"]).reshape(B, o.s.Hkv, o.s.Dh)
         c, s_ = ro.rope_tables([pos], o.s.Dh, o.s.theta)
