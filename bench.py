@@ -29,12 +29,16 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="8b")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch decode steps without HIP graphs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB three times (a plain "
+                         "copy kernel of known size, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -157,7 +161,7 @@ def main():
     if args.workload == "8b":
         tau = 0.5 if args.tau is None else args.tau
     K, W = args.steps, args.warmup
-    max_seq = T + W + K
+    max_seq = T + W + K + 2   # + the profiled step and the slot kernel timing writes
     print(f"[bench] workload {wl.name} B={B} T={T} steps={K} warmup={W} tau={tau}", file=sys.stderr,
           flush=True)
 
@@ -179,6 +183,16 @@ def main():
     prefill_s = time.perf_counter() - t0
     st0 = r.exit_stats()
     prefill_E = st0["last_E"]
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    r.use_graph(not args.eager)
 
     bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
     bufs[0].copy_(nxt)
@@ -209,32 +223,42 @@ def main():
     roofline = None
     kinds = {}
     if not args.no_profile:
-        # same workload again, eager launches with HIP events around every kernel
-        r.reset()
-        _, nxt = r.prefill(tokens, tau, want_logits=False)
-        bufs[0].copy_(nxt)
-        run(W, 0)
+        # Layer kernels: each class launched back to back for all layers from a
+        # replayed graph, with the exit mix of the timed steps (force_E = the
+        # E they took), timed by events around the replays on the library's
+        # stream.  LM head and begin: one eager step with events around each
+        # kernel (a single launch per step, so the gap in front is included).
+        E_mix = max(range(len(hist)), key=lambda e: hist[e])
+        mix = [0] * len(hist)
+        mix[E_mix] = 1
+        r.force_exit_layer(E_mix)
+        for kind in ("qkv", "attn", "o", "gateup", "down"):
+            avg_us = r.time_kernel(kind, reps=20)
+            mb = mean_kind_bytes(shape, B, kind, mix, [T + W + K + 1])
+            kinds[kind] = {"launches_per_step": shape.n_layers, "avg_us": round(avg_us, 3),
+                           "avg_bytes": int(mb), "gbs": round(mb / (avg_us * 1e-6) / 1e9, 1),
+                           "timing": "graph replay, back to back"}
+        r.force_exit_layer(-1)
         r.profile(True)
-        h0 = r.exit_stats()["decode_hist"]
         r.profile_read()
-        run(K, W)
+        run(1, W + K)
         times = r.profile_read()
-        h1 = r.exit_stats()["decode_hist"]
         r.profile(False)
-        phist = [a - b for a, b in zip(h1, h0)]
-        for kind, (n, ms) in times.items():
-            if n == 0 or kind.startswith("p_"):
-                continue
-            mb = mean_kind_bytes(shape, B, kind, phist, positions)
-            avg_us = ms / n * 1e3
-            kinds[kind] = {"launches": n, "avg_us": round(avg_us, 3), "total_ms": round(ms, 3),
-                           "avg_bytes": int(mb), "gbs": round(mb / (avg_us * 1e-6) / 1e9, 1)}
-        dom = max(kinds, key=lambda k: kinds[k]["total_ms"])
+        for kind in ("begin", "lm_head"):
+            n, ms = times[kind]
+            mb = mean_kind_bytes(shape, B, kind, hist, positions)
+            avg_us = ms / max(n, 1) * 1e3
+            kinds[kind] = {"launches_per_step": 1, "avg_us": round(avg_us, 3), "avg_bytes": int(mb),
+                           "gbs": round(mb / (avg_us * 1e-6) / 1e9, 1), "timing": "eager, events around"}
+        dom = max(kinds, key=lambda k: kinds[k]["avg_us"] * kinds[k]["launches_per_step"])
         dk = kinds[dom]
         achieved = dk["avg_bytes"] / (dk["avg_us"] * 1e-6) / 1e9
+        from early_exit_kv_amd.profiling import load_traffic
+        traffic = load_traffic(os.path.join(ROOT, "profiles", f"{dom}_{wl.name}_traffic.json"))
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": dom}
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None if traffic is None else int(traffic),
+                    "kernel": dom, "algorithmic_bytes": dk["avg_bytes"], "avg_us": dk["avg_us"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -244,8 +268,11 @@ def main():
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, uniform tokens)",
-        "config": {"workload": wl.name, "shape": shape.name, "batch": B, "prompt": T, "tau": tau,
-                   "exit_layers": "int4 g%d" % shape.group_size},
+        "config": {"workload": f"{wl.name}: decoder L={shape.n_layers} d={shape.d_model} "
+                               f"{shape.n_q_heads}q/{shape.n_kv_heads}kv heads x {shape.head_dim} "
+                               f"FFN {shape.ffn_dim} vocab {shape.vocab}",
+                   "batch": B, "prompt": T, "tau": tau, "exit_layers": "int4 g%d" % shape.group_size,
+                   "graphs": not args.eager},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_hbm_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

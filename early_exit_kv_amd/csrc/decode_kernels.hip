@@ -53,14 +53,18 @@ hipError_t launch_begin(const BeginParams &p, hipStream_t s) {
   int64_t blocks = (work + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(begin_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_1(begin_kernel, dim3((unsigned)blocks), dim3(256), p, s);
 }
 
 __global__ void clear_kernel(uint32_t *p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
+}
+
+hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds,
+                         hipStream_t s) {
+  return hipLaunchKernel(fn, grid, block, args, lds, s);
 }
 
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
@@ -756,7 +760,7 @@ hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t
   int kslab = g.kslab, ntask = g.ntask;
   GemvParams pc = p;
   void *args[] = {&pc, &kslab, &ntask};
-  return hipLaunchKernel(g.fn, dim3(g.grid), dim3(256), args, g.lds, s);
+  return launch_kernel(g.fn, dim3(g.grid), dim3(256), args, g.lds, s);
 }
 
 // ===========================================================================
@@ -981,12 +985,11 @@ static hipError_t attn_launch_dh(const AttnParams &p, hipStream_t s) {
   dim3 grid(p.splits, p.Hkv, p.B);
   const int gq = p.Hq / p.Hkv;
   switch (gq) {
-    case 1: hipLaunchKernelGGL((attn_decode_kernel<DH, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((attn_decode_kernel<DH, 2>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<DH, 4>), grid, dim3(256), 0, s, p); break;
+    case 1: return launch_1(attn_decode_kernel<DH, 1>, grid, dim3(256), p, s);
+    case 2: return launch_1(attn_decode_kernel<DH, 2>, grid, dim3(256), p, s);
+    case 4: return launch_1(attn_decode_kernel<DH, 4>, grid, dim3(256), p, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {

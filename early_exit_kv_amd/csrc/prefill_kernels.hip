@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) void rows_norm_kernel(RowsNormParams p) {
 
 hipError_t launch_rows_norm(const RowsNormParams &p, hipStream_t s) {
   const int64_t blocks = (p.rows + 3) / 4;
-  hipLaunchKernelGGL(rows_norm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_1(rows_norm_kernel, dim3((unsigned)blocks), dim3(256), p, s);
 }
 
 // ===========================================================================
@@ -94,8 +93,7 @@ __global__ __launch_bounds__(256) void rows_cos_kernel(RowsCosParams p) {
 
 hipError_t launch_rows_cos_exit(const RowsCosParams &p, hipStream_t s) {
   const int64_t blocks = (p.rows + 3) / 4;
-  hipLaunchKernelGGL(rows_cos_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_1(rows_cos_kernel, dim3((unsigned)blocks), dim3(256), p, s);
 }
 
 // ===========================================================================
@@ -349,8 +347,7 @@ static hipError_t gemm_launch_ep(const GemmParams &p, hipStream_t s) {
   int ncols = p.N;
   if (EP == kEpSwiGLU) ncols = 2 * p.w.seg_rows[0];
   dim3 grid((p.M + BM - 1) / BM, (ncols + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EP>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_1(gemm_kernel<BM, BN, EP>, grid, dim3(256), p, s);
 }
 
 hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
@@ -451,11 +448,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
 hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
   dim3 grid((p.T + 63) / 64, p.Hq, p.B);
   switch (p.Dh) {
-    case 64: hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, s, p); break;
+    case 64: return launch_1(attn_prefill_kernel<64>, grid, dim3(256), p, s);
+    case 128: return launch_1(attn_prefill_kernel<128>, grid, dim3(256), p, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace river

@@ -234,7 +234,8 @@ hipEvent_t take_event(river_ctx *ctx) {
   return e;
 }
 
-// Records an event before the launch and one after it when profiling.
+// When profiling, records an event before the launch and one after it (the
+// interval holds the kernel and the dispatch gap in front of it).
 struct TimedLaunch {
   river_ctx *ctx;
   int kind;
@@ -256,8 +257,10 @@ struct TimedLaunch {
   }
 };
 #define TIMED(kind, expr) RV_TRY(TimedLaunch(ctx, kind).done(expr))
+// Launch of one decode kernel class; with only >= 0 the others are skipped.
+#define TIMED_ONLY(kind, expr) \
+  if (only < 0 || only == (kind)) TIMED(kind, expr)
 
-// Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
 // Copy one produced array into the activation record (no-op when off).
 struct Recorder {
   river_ctx *ctx;
@@ -270,7 +273,12 @@ struct Recorder {
   }
 };
 
-int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next) {
+// Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
+//
+// only >= 0 (a RIVER_K_* layer kernel class) enqueues nothing but that class's
+// launch for every layer, with the same parameters (kernel timing).
+int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next,
+                   int only = -1) {
   const river_config &c = ctx->cfg;
   const int B = ctx->batch;
   hipStream_t s = ctx->stream;
@@ -283,7 +291,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
   bp.tau = tau; bp.is_prefill = 0; bp.set_pos = -1;
-  TIMED(RIVER_K_BEGIN, launch_begin(bp, s));
+  TIMED_ONLY(RIVER_K_BEGIN, launch_begin(bp, s));
 
   int down_wgs = 0;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -306,7 +314,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     // the exit test after layer l-1 is decided at the start of this kernel
     q.test_prev = l > 0; q.part = at<float>(ctx->ws, ctx->wl.part); q.part_wgs = down_wgs;
     RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
-    TIMED(RIVER_K_QKV, launch_gemv(kXNorm, kEpQKV, q, s));
+    TIMED_ONLY(RIVER_K_QKV, launch_gemv(kXNorm, kEpQKV, q, s));
     RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
 
     AttnParams a{};
@@ -317,14 +325,14 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     a.chunk = attn_chunk(c.max_seq, B, c.n_kv_heads);
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
-    TIMED(RIVER_K_ATTN, launch_attn_decode(a, s));
+    TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
     GemvParams o = g;
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x_src = a.out; o.x_stride = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
-    TIMED(RIVER_K_O, launch_gemv(kXBf16, kEpResid, o, s));
+    TIMED_ONLY(RIVER_K_O, launch_gemv(kXBf16, kEpResid, o, s));
     RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
     GemvParams gu = g;
@@ -332,7 +340,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     gu.N = 2 * c.ffn_dim; gu.K = c.d_model;
     gu.h_src = hB; gu.h_stride = c.d_model; gu.gain = static_cast<const uint16_t *>(L.mlp_norm);
     gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u); gu.u_stride = c.ffn_dim;
-    TIMED(RIVER_K_GATEUP, launch_gemv(kXNorm, kEpSwiGLU, gu, s));
+    TIMED_ONLY(RIVER_K_GATEUP, launch_gemv(kXNorm, kEpSwiGLU, gu, s));
     RV_TRY(rec.put(l, rec.lay.u, gu.u_out, (size_t)B * c.ffn_dim * 2));
 
     GemvParams dn = g;
@@ -342,7 +350,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     dn.part = at<float>(ctx->ws, ctx->wl.part);
     dn.test_exit = l < c.n_layers - 1;
     down_wgs = gemv_grid(kEpResidExit, dn);
-    TIMED(RIVER_K_DOWN, launch_gemv(kXBf16, kEpResidExit, dn, s));
+    TIMED_ONLY(RIVER_K_DOWN, launch_gemv(kXBf16, kEpResidExit, dn, s));
     std::swap(hA, hB);
   }
   RV_TRY(rec.put(-1, 0, hA, hbytes));
@@ -353,7 +361,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
   lm.h_src = hA; lm.h_stride = c.d_model; lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
   lm.logits = logits; lm.next = next; lm.is_prefill = 0; lm.vocab = c.vocab;
-  TIMED(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
+  TIMED_ONLY(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
   return RIVER_OK;
 }
 
@@ -670,6 +678,46 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
       return RIVER_OK;
   }
   return RIVER_E_INVALID_ARG;
+}
+
+int river_time_kernel(river_ctx *ctx, int32_t kind, int32_t reps, double *avg_us) {
+  if (!ctx || !avg_us || reps < 1) return RIVER_E_INVALID_ARG;
+  if (kind < RIVER_K_QKV || kind > RIVER_K_DOWN) return RIVER_E_INVALID_ARG;
+  if (!ctx->built || ctx->batch == 0) return RIVER_E_STATE;
+  if (ctx->stream == nullptr) return RIVER_E_STATE;
+  char *rec = ctx->rec;
+  const bool prof = ctx->profiling;
+  ctx->rec = nullptr;
+  ctx->profiling = false;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  int st = RIVER_OK;
+  hipError_t e = hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    st = enqueue_decode(ctx, nullptr, 0.f, nullptr, nullptr, kind);
+    e = hipStreamEndCapture(ctx->stream, &graph);
+  }
+  ctx->rec = rec;
+  ctx->profiling = prof;
+  if (st != RIVER_OK) return st;
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (e == hipSuccess) e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = hipGraphLaunch(exec, ctx->stream);   // warm-up replay
+  if (e == hipSuccess) e = hipEventRecord(a, ctx->stream);
+  for (int i = 0; i < reps && e == hipSuccess; ++i) e = hipGraphLaunch(exec, ctx->stream);
+  if (e == hipSuccess) e = hipEventRecord(b, ctx->stream);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (e != hipSuccess) return RIVER_E_HIP;
+  *avg_us = (double)ms * 1e3 / ((double)reps * ctx->cfg.n_layers);
+  return RIVER_OK;
 }
 
 int river_record_bytes(const river_config *cfg, int32_t rows, size_t *bytes) {

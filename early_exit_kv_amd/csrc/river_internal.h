@@ -171,6 +171,16 @@ struct BeginParams {
 };
 
 // ---- launchers (each returns hipGetLastError() after the launch) ----------
+// Launch with an argument array (one place for every pass kernel).
+hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds,
+                         hipStream_t s);
+template <typename P>
+hipError_t launch_1(void (*kernel)(P), dim3 grid, dim3 block, const P &p, hipStream_t s) {
+  P copy = p;
+  void *args[] = {&copy};
+  return launch_kernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, s);
+}
+
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
                            hipStream_t s);

@@ -27,7 +27,7 @@ EXPORTS = (
     "river_query_sizes", "river_exit_bank_offsets", "river_init", "river_build_exit_layers",
     "river_prefill", "river_decode_step", "river_exit_stats", "river_set_option",
     "river_reset", "river_destroy", "river_strerror", "river_profile_read",
-    "river_debug_linear", "river_record_bytes", "river_set_record",
+    "river_debug_linear", "river_record_bytes", "river_set_record", "river_time_kernel",
 )
 
 
@@ -110,6 +110,7 @@ def load_library(path=LIB_PATH):
         "river_debug_linear": (ctypes.c_int, [P, i32, i32, i32, P, i32, P]),
         "river_record_bytes": (ctypes.c_int, [ctypes.POINTER(RiverConfig), i32, ctypes.POINTER(ctypes.c_size_t)]),
         "river_set_record": (ctypes.c_int, [P, P, ctypes.c_size_t]),
+        "river_time_kernel": (ctypes.c_int, [P, i32, i32, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -304,6 +305,14 @@ class River:
         self._call(self.lib.river_debug_linear, "river_debug_linear", layer, linear, int(use_exit),
                    _ptr(x), x.shape[0], _ptr(y))
         return y
+
+    def time_kernel(self, kind, reps=20):
+        """Mean execution time (us) of one decode kernel class, launched back to
+        back for every layer from a replayed graph (see river_time_kernel)."""
+        k = KERNEL_KINDS.index(kind) if isinstance(kind, str) else int(kind)
+        out = ctypes.c_double(0.0)
+        self._call(self.lib.river_time_kernel, "river_time_kernel", k, int(reps), ctypes.byref(out))
+        return out.value
 
     def record(self, max_rows):
         """Switch the activation record on for passes of up to max_rows rows

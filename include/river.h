@@ -213,6 +213,20 @@ typedef struct {
  * the stream.  RIVER_E_STATE when profiling is off. */
 int river_profile_read(river_ctx *ctx, river_kernel_time_t *out);
 
+/* Kernel timing: the mean execution time of one decode kernel class
+ * (RIVER_K_QKV .. RIVER_K_DOWN) in the launch configuration of the current
+ * batch.  A HIP graph holding that class's launch for every layer, with the
+ * parameters a decode step uses, is replayed `reps` times back to back
+ * between two events on the context's stream; avg_us = elapsed / (reps *
+ * n_layers).  Which layers take the exit copy follows RIVER_OPT_FORCE_E (set
+ * it to the mix to be timed; with -1 the exit flag left by the last step
+ * decides).  The kernels overwrite the workspace, and the q|k|v kernel the
+ * cache slot of the next position, so call it between steps, not inside a
+ * sequence whose next step must see the previous step's state unchanged.
+ * Needs a context built on a non-default stream and a prefill before it;
+ * synchronises the stream. */
+int river_time_kernel(river_ctx *ctx, int32_t kind, int32_t reps, double *avg_us);
+
 /* Debug / test entry point: y = x W^T for one linear of one layer, through
  * the same weight-streaming cores the passes use (GEMV for M <= 8 rows, the
  * MFMA GEMM above), with a plain fp32 output instead of a fused epilogue.

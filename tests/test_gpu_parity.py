@@ -288,3 +288,37 @@ def test_gpu_error_paths(tiny):
     r.decode_step(bad, 0.5)
     assert r.exit_stats()["token_errors"] == 1
     r.close()
+
+
+def test_record_and_kernel_timing_entry_points(tiny):
+    """Activation record: too small a buffer is refused before any launch, and
+    recording does not change what a step computes; kernel timing returns a
+    positive time and refuses classes it cannot time alone."""
+    rv = _river()
+    s = synth.TINY
+    toks = synth.make_tokens(s, 2, 8, seed=0).cuda()
+    outs = []
+    for rec in (False, True):
+        r = rv.River(s, tiny["cuda"], 2, 12)
+        r.build_exit_layers("int4")
+        if rec:
+            r.record(2)                                       # room for 2 rows only
+            with pytest.raises(rv.RiverError) as e:
+                r.prefill(toks, 0.5)                          # 16 rows
+            assert e.value.code == rv.RIVER_E_BAD_SIZE
+            r.record(16)
+        gl, nx = r.prefill(toks, 0.5)
+        g2, _ = r.decode_step(nx.clone(), 0.5)
+        outs.append((gl.cpu(), g2.cpu()))
+        if rec:
+            layers, h_out = r.read_record(2)
+            assert len(layers) == s.n_layers and h_out.shape == (2, s.d_model)
+            assert np.all(np.isfinite(h_out))
+            for kind in ("qkv", "attn", "o", "gateup", "down"):
+                t = r.time_kernel(kind, reps=3)
+                assert 0.0 < t < 1e5, (kind, t)
+            with pytest.raises(rv.RiverError) as e:
+                r.time_kernel("lm_head")
+            assert e.value.code == rv.RIVER_E_INVALID_ARG
+        r.close()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
