@@ -128,16 +128,6 @@ __device__ __forceinline__ RowRef map_row(const GemvParams &p, int L, int wave_f
   return r;
 }
 
-// int4 codes of one 32-bit word (column 8w+j in bits 4j..4j+3) as the four
-// bf16 pairs (128+q_a, 128+q_b) for the column pairs (0,2) (4,6) (1,3) (5,7)
-__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&pr)[4]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  pr[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x05010400u);
-  pr[1] = __builtin_amdgcn_perm(0x43434343u, lo, 0x05030402u);
-  pr[2] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05010400u);
-  pr[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05030402u);
-}
-
 // Row groups, chunks per lane and activation layout of one GEMV launch.
 //   R rows per wavefront task; UQ int4 chunks or UB bf16 chunks per lane are
 //   loaded together (16 loads of 16 bytes in flight per lane in the common

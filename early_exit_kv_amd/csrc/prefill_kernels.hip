@@ -6,6 +6,8 @@
 // Method: "River-LLM: Large Language Model Seamless Exit Based on KV Share",
 // section 5: prefill exits at the sequence level so that every prompt token
 // leaves at the same layer and the prompt stays one parallel pass.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace river {
@@ -21,7 +23,7 @@ __global__ __launch_bounds__(256) void rows_norm_kernel(RowsNormParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= p.rows) return;
-  const float *h = p.h + r * p.d;
+  const float *h = p.h + r * (p.h_stride ? p.h_stride : (int64_t)p.d);
   float ss = 0.f;
   for (int k = lane * 4; k < p.d; k += 256) {
     const float4 v = *reinterpret_cast<const float4 *>(h + k);
@@ -132,6 +134,74 @@ __device__ __forceinline__ void map_col(const GemmParams &p, int col_blk, int BN
     seg = 0;
     row = col_blk * BN + j;
     valid = row < p.N;
+  }
+}
+
+// Epilogue of one finished tile: Cs holds rows x BN results (row stride cs)
+// for rows m0.. and column block colblk (columns mapped as map_col<EP> says).
+template <int EP, int BN>
+__device__ void tile_epilogue(const GemmParams &p, const float *Cs, int cs, int BM, int64_t m0,
+                              int colblk) {
+  const int tid = threadIdx.x;
+  if constexpr (EP == kEpQKV) {
+    const int half = p.Dh >> 1;
+    for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
+      const int r = idx / (BN / 2), pp = idx % (BN / 2);
+      const int64_t m = m0 + r;
+      const int L0 = colblk * BN + 2 * pp;
+      if (m >= p.M || L0 >= p.N) continue;
+      int b, t;
+      if (p.T > 0) { b = (int)(m / p.T); t = (int)(m % p.T); }
+      else { b = (int)m; t = p.ctrl->pos; }
+      const int P = L0 >> 1;
+      const int hh = P / half, i = P % half;
+      float y0 = Cs[r * cs + (2 * pp)], y1 = Cs[r * cs + (2 * pp + 1)];
+      if (hh < p.Hq + p.Hkv) {
+        const float2 rc = p.rope[(int64_t)t * half + i];  // (cos, sin) of t * theta^(-2i/Dh)
+        const float a0 = y0 * rc.x - y1 * rc.y;
+        const float a1 = y1 * rc.x + y0 * rc.y;
+        y0 = a0;
+        y1 = a1;
+      }
+      if (hh < p.Hq) {
+        uint16_t *q = p.q_out + m * (int64_t)(p.Hq * p.Dh) + hh * p.Dh;
+        q[i] = f2bf(y0);
+        q[i + half] = f2bf(y1);
+      } else {
+        const bool isk = hh < p.Hq + p.Hkv;
+        const int kvh = isk ? hh - p.Hq : hh - p.Hq - p.Hkv;
+        uint16_t *dst = (isk ? p.k_cache : p.v_cache) +
+                        (((int64_t)b * p.Hkv + kvh) * p.max_seq + t) * p.Dh;
+        dst[i] = f2bf(y0);
+        dst[i + half] = f2bf(y1);
+      }
+    }
+  } else if constexpr (EP == kEpSwiGLU) {
+    const int hw = BN / 2;
+    for (int idx = tid; idx < BM * hw; idx += 256) {
+      const int r = idx / hw, jj = idx % hw;
+      const int64_t m = m0 + r;
+      const int n = colblk * hw + jj;
+      if (m >= p.M || n >= p.w.seg_rows[0]) continue;
+      const float gt = Cs[r * cs + (jj)], up = Cs[r * cs + (hw + jj)];
+      p.u_out[m * p.w.seg_rows[0] + n] = f2bf(gt / (1.0f + expf(-gt)) * up);
+    }
+  } else if constexpr (EP == kEpPlain) {
+    for (int idx = tid; idx < BM * BN; idx += 256) {
+      const int r = idx / BN, j = idx % BN;
+      const int64_t m = m0 + r;
+      const int n = colblk * BN + j;
+      if (m < p.M && n < p.N) p.y_out[m * p.y_stride + n] = Cs[r * cs + (j)];
+    }
+  } else {  // residual
+    for (int idx = tid; idx < BM * BN; idx += 256) {
+      const int r = idx / BN, j = idx % BN;
+      const int64_t m = m0 + r;
+      const int n = colblk * BN + j;
+      if (m >= p.M || n >= p.N) continue;
+      const int64_t o = m * p.h_io_stride + n;
+      p.h_out[o] = p.h_in[o] + Cs[r * cs + (j)];
+    }
   }
 }
 
@@ -275,70 +345,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     }
   __syncthreads();
 
-  // ---- epilogues
-  if constexpr (EP == kEpQKV) {
-    const int half = p.Dh >> 1;
-    for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
-      const int r = idx / (BN / 2), pp = idx % (BN / 2);
-      const int64_t m = m0 + r;
-      const int L0 = blockIdx.y * BN + 2 * pp;
-      if (m >= p.M || L0 >= p.N) continue;
-      int b, t;
-      if (p.T > 0) { b = (int)(m / p.T); t = (int)(m % p.T); }
-      else { b = (int)m; t = p.ctrl->pos; }
-      const int P = L0 >> 1;
-      const int hh = P / half, i = P % half;
-      float y0 = Cs[r][2 * pp], y1 = Cs[r][2 * pp + 1];
-      if (hh < p.Hq + p.Hkv) {
-        const double ang = (double)t * pow((double)p.rope_theta, -2.0 * i / (double)p.Dh);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        const float c = (float)cs, s = (float)sn;
-        const float a0 = y0 * c - y1 * s;
-        const float a1 = y1 * c + y0 * s;
-        y0 = a0;
-        y1 = a1;
-      }
-      if (hh < p.Hq) {
-        uint16_t *q = p.q_out + m * (int64_t)(p.Hq * p.Dh) + hh * p.Dh;
-        q[i] = f2bf(y0);
-        q[i + half] = f2bf(y1);
-      } else {
-        const bool isk = hh < p.Hq + p.Hkv;
-        const int kvh = isk ? hh - p.Hq : hh - p.Hq - p.Hkv;
-        uint16_t *dst = (isk ? p.k_cache : p.v_cache) +
-                        (((int64_t)b * p.Hkv + kvh) * p.max_seq + t) * p.Dh;
-        dst[i] = f2bf(y0);
-        dst[i + half] = f2bf(y1);
-      }
-    }
-  } else if constexpr (EP == kEpSwiGLU) {
-    const int hw = BN / 2;
-    for (int idx = tid; idx < BM * hw; idx += 256) {
-      const int r = idx / hw, jj = idx % hw;
-      const int64_t m = m0 + r;
-      const int n = blockIdx.y * hw + jj;
-      if (m >= p.M || n >= p.w.seg_rows[0]) continue;
-      const float gt = Cs[r][jj], up = Cs[r][hw + jj];
-      p.u_out[m * p.w.seg_rows[0] + n] = f2bf(gt / (1.0f + expf(-gt)) * up);
-    }
-  } else if constexpr (EP == kEpPlain) {
-    for (int idx = tid; idx < BM * BN; idx += 256) {
-      const int r = idx / BN, j = idx % BN;
-      const int64_t m = m0 + r;
-      const int n = blockIdx.y * BN + j;
-      if (m < p.M && n < p.N) p.y_out[m * p.y_stride + n] = Cs[r][j];
-    }
-  } else {  // residual
-    for (int idx = tid; idx < BM * BN; idx += 256) {
-      const int r = idx / BN, j = idx % BN;
-      const int64_t m = m0 + r;
-      const int n = blockIdx.y * BN + j;
-      if (m >= p.M || n >= p.N) continue;
-      const int64_t o = m * p.h_io_stride + n;
-      p.h_out[o] = p.h_in[o] + Cs[r][j];
-    }
-  }
+  tile_epilogue<EP, BN>(p, &Cs[0][0], BN + 1, BM, m0, blockIdx.y);
 }
 
 template <int EP>
@@ -451,6 +458,328 @@ hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
     case 64: return launch_1(attn_prefill_kernel<64>, grid, dim3(256), p, s);
     case 128: return launch_1(attn_prefill_kernel<128>, grid, dim3(256), p, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+
+// ===========================================================================
+// Batched-row GEMM for 9..64 rows: Y[m][n] = sum_k X[m][k] W[n][k].
+//   A workgroup (4 wavefronts x 2 column tiles of 16 = 128 columns) takes one
+//   split of K.  Every lane loads the weights of its own output column straight
+//   from HBM into MFMA B operands, two quantisation groups ahead of use; the
+//   rows X sit in LDS, one K slab at a time.  K is walked one group (G columns)
+//   at a time.  int4: lane quarter qq holds the G/4 codes k0 + qq*G/4 ..; the
+//   rows are staged in the same order (within 8 columns: 0 2 4 6 1 3 5 7, the
+//   order the byte permute unpacks codes in), so every MFMA sums inside one
+//   group, which is then folded as  tot += s * (acc - (128 + z) * sum_k x).
+//   bf16 weights use the plain order (quarter qq holds k0 + 32j + 8qq .. +8).
+//   With several K splits each workgroup stores its partial tile; the last of
+//   a column block (arrival counter) adds the splits in order and runs the
+//   epilogue.
+// ===========================================================================
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+template <int N_> struct WordsT;
+template <> struct WordsT<1> { typedef uint32_t T; };
+template <> struct WordsT<2> { typedef v2u T; };
+template <> struct WordsT<4> { typedef v4u T; };
+
+template <int MB, int G, int EP>
+__global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
+  constexpr int NT = 2;                     // column tiles per wavefront
+  constexpr int BN = kMgemmBN;              // 4 x NT x 16
+  constexpr int ROWS = MB * 16;
+  constexpr int KS = MB <= 2 ? 512 : 256;   // K columns per LDS slab
+  constexpr int XS = KS + 8;                // padded LDS row (bf16)
+  constexpr int STEPS = G / 32;             // MFMA k-steps per group
+  constexpr int GW = G / 32;                // code words per lane per group
+  constexpr int XBYTES = ROWS * XS * 2;
+  constexpr int CBYTES = ROWS * (BN + 1) * 4;
+  static_assert(KS % G == 0, "slab holds whole groups");
+  typedef typename WordsT<GW>::T WT;
+  __shared__ __align__(16) char smem[XBYTES > CBYTES ? XBYTES : CBYTES];
+  __shared__ float xsg[ROWS][KS / G];
+  __shared__ uint64_t rowkey[ROWS];
+  __shared__ int last_flag;
+  uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+  float *Cs = reinterpret_cast<float *>(smem);
+
+  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
+  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, cl = lane & 15;
+  const int split = blockIdx.x % p.nsplit, colblk = blockIdx.x / p.nsplit;
+  const int kbeg = split * p.ks;
+  const int kend = min(p.K, kbeg + p.ks);
+  const int nchunk = (kend - kbeg) / G;
+  const int KG = p.K / G;
+
+  const uint16_t *brow[NT];
+  const uint32_t *qrow[NT], *zrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int seg, row;
+    bool valid;
+    map_col<EP>(p, colblk, BN, wid * (NT * 16) + t * 16 + cl, seg, row, valid);
+    if (!valid) { seg = 0; row = 0; }      // a valid row; its results are dropped
+    if (q4) {
+      qrow[t] = p.w.q4[seg] + (int64_t)row * (p.K / 8);
+      zrow[t] = p.w.sz[seg] + (int64_t)row * KG;
+      brow[t] = nullptr;
+    } else {
+      brow[t] = (ex ? p.w.ex_bf[seg] : p.w.bf[seg]) + (int64_t)row * p.K;
+      qrow[t] = zrow[t] = nullptr;
+    }
+  }
+
+  // weight ring: two groups in flight per lane
+  WT wq[2][NT];
+  uint32_t wz[2][NT];
+  v4u wb[2][NT][STEPS];
+  auto load = [&](int c, int sl) {
+    const int k0 = kbeg + c * G;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (q4) {
+        wq[sl][t] = __builtin_nontemporal_load(
+            reinterpret_cast<const WT *>(qrow[t] + (k0 >> 3) + qq * GW));
+        wz[sl][t] = zrow[t][k0 / G];
+      } else {
+#pragma unroll
+        for (int j = 0; j < STEPS; ++j)
+          wb[sl][t][j] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4u *>(brow[t] + k0 + 32 * j + 8 * qq));
+      }
+    }
+  };
+
+  f32x4_t tot[MB][NT];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int slab0 = kbeg;
+  auto stage = [&](int base) {
+    const int sl = min(KS, kend - base);
+    const int n8 = sl >> 3;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * n8; idx += 256) {
+      const int m = idx / n8, g8 = idx - m * n8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m < p.M) v = *reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.ldx + base + 8 * g8);
+      if (q4) v = int4_order(v.x, v.y, v.z, v.w);
+      *reinterpret_cast<uint4 *>(xs + m * XS + 8 * g8) = v;
+    }
+    __syncthreads();
+    if (q4) {
+      const int ng = sl / G;
+      for (int idx = threadIdx.x; idx < ROWS * ng; idx += 256) {
+        const int m = idx / ng, g = idx - m * ng;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(xs + m * XS + g * G);
+        float sacc = 0.f;
+        for (int i = 0; i < G / 2; ++i) sacc += bf_lo(src[i]) + bf_hi(src[i]);
+        xsg[m][g] = sacc;
+      }
+      __syncthreads();
+    }
+  };
+
+  auto compute = [&](int c, int sl) {
+    const int k0 = kbeg + c * G;
+    const int kl = k0 - slab0;
+    if (q4) {
+      f32x4_t ag[MB][NT];
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        bf16x8_t af[MB], bfr[NT];
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+          af[a] = *reinterpret_cast<const bf16x8_t *>(xs + (a * 16 + cl) * XS + kl + qq * (G / 4) + 8 * j);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          uint32_t w;
+          if constexpr (GW == 1) w = wq[sl][t];
+          else w = wq[sl][t][j];
+          uint32_t pr[4];
+          unpack_word(w, pr);
+          bfr[t] = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+        }
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[t], ag[a][t], 0, 0, 0);
+      }
+      const int g = kl / G;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float sc = bf_lo(wz[sl][t]), zo = 128.0f + bf_hi(wz[sl][t]);
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * xsg[a * 16 + 4 * qq + v][g], tot[a][t][v]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        bf16x8_t af[MB];
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+          af[a] = *reinterpret_cast<const bf16x8_t *>(xs + (a * 16 + cl) * XS + kl + 32 * j + 8 * qq);
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                af[a], __builtin_bit_cast(bf16x8_t, wb[sl][t][j]), tot[a][t], 0, 0, 0);
+      }
+    }
+  };
+
+  constexpr int CPS = KS / G;   // groups per slab
+  if (nchunk > 0) load(0, 0);
+  if (nchunk > 1) load(1, 1);
+  for (int c = 0; c < nchunk; c += 2) {
+    if (c % CPS == 0) { slab0 = kbeg + c * G; stage(slab0); }
+    compute(c, 0);
+    if (c + 2 < nchunk) load(c + 2, 0);
+    if (c + 1 < nchunk) {
+      if ((c + 1) % CPS == 0) { slab0 = kbeg + (c + 1) * G; stage(slab0); }
+      compute(c + 1, 1);
+      if (c + 3 < nchunk) load(c + 3, 1);
+    }
+  }
+
+  // ---- results to LDS (the slab buffer is reused)
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        Cs[(a * 16 + 4 * qq + v) * (BN + 1) + wid * (NT * 16) + t * 16 + cl] = tot[a][t][v];
+  __syncthreads();
+
+  if (p.nsplit > 1) {
+    float *mine = p.part + ((int64_t)colblk * p.nsplit + split) * (ROWS * BN);
+    for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256)
+      st_coherent(mine + idx, Cs[(idx / BN) * (BN + 1) + idx % BN]);
+    if (!arrive_last(&p.counters[colblk], p.nsplit, &last_flag)) return;
+    const float *all = p.part + (int64_t)colblk * p.nsplit * (ROWS * BN);
+    for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
+      float v = 0.f;
+      for (int sp = 0; sp < p.nsplit; ++sp) v += ld_coherent(all + (int64_t)sp * (ROWS * BN) + idx);
+      Cs[(idx / BN) * (BN + 1) + idx % BN] = v;
+    }
+    __syncthreads();
+  }
+
+  if constexpr (EP == kEpLogits) {
+    Control *ctl = p.ctrl;
+    if (threadIdx.x < ROWS) rowkey[threadIdx.x] = 0;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
+      const int r = idx / BN, j = idx % BN;
+      const int n = colblk * BN + j;
+      if (r >= p.M || n >= p.N) continue;
+      const float v = Cs[r * (BN + 1) + j];
+      if (p.logits) p.logits[(int64_t)r * p.vocab + n] = v;
+      const uint64_t key = ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+      __hip_atomic_fetch_max(&rowkey[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (threadIdx.x < p.M)
+      __hip_atomic_fetch_max(control_keys(ctl) + threadIdx.x, rowkey[threadIdx.x], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t arrivals = p.nsplit > 1 ? (uint32_t)(gridDim.x / p.nsplit) : gridDim.x;
+    if (arrive_last(&ctl->counters[kCtrLogits], arrivals, &last_flag)) {
+      if (threadIdx.x < p.M && p.next) {
+        const uint64_t key = __hip_atomic_load(control_keys(ctl) + threadIdx.x, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        p.next[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+      }
+      if (threadIdx.x == 0) {
+        const int E = ctl->E;
+        ctl->last_E = E;
+        if (p.is_prefill) {
+          ctl->prefill_hist[E] += 1;
+          ctl->n_prefill += 1;
+        } else {
+          ctl->decode_hist[E] += 1;
+          ctl->n_decode += 1;
+          ctl->pos += 1;
+        }
+      }
+    }
+  } else {
+    tile_epilogue<EP, BN>(p, Cs, BN + 1, ROWS, 0, colblk);
+  }
+}
+
+MgemmPlan mgemm_plan(int M, int ncols, int K, bool allow_split) {
+  MgemmPlan pl{};
+  pl.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  pl.ncolblk = (ncols + kMgemmBN - 1) / kMgemmBN;
+  const int KS = pl.mb <= 2 ? 512 : 256;
+  int ns = 1;
+  if (allow_split && K >= 2 * KS) {
+    ns = std::max(1, 512 / pl.ncolblk);
+    ns = std::min(ns, K / (2 * KS));
+  }
+  int ks = (K + ns - 1) / ns;
+  ks = K >= KS ? (ks + KS - 1) / KS * KS : K;
+  pl.ks = ks;
+  pl.nsplit = (K + ks - 1) / ks;
+  return pl;
+}
+MgemmPlan mgemm_plan(int M, int ncols, int K) { return mgemm_plan(M, ncols, K, true); }
+
+int64_t mgemm_part_floats(const MgemmPlan &pl) {
+  return pl.nsplit > 1 ? (int64_t)pl.ncolblk * pl.nsplit * (pl.mb * 16) * kMgemmBN : 0;
+}
+
+template <int MB, int G>
+static hipError_t mgemm_launch_g(Epilogue ep, const GemmParams &p, int grid, hipStream_t s) {
+  switch (ep) {
+    case kEpQKV: return launch_1(mgemm_kernel<MB, G, kEpQKV>, dim3(grid), dim3(256), p, s);
+    case kEpResid: return launch_1(mgemm_kernel<MB, G, kEpResid>, dim3(grid), dim3(256), p, s);
+    case kEpSwiGLU: return launch_1(mgemm_kernel<MB, G, kEpSwiGLU>, dim3(grid), dim3(256), p, s);
+    case kEpLogits: return launch_1(mgemm_kernel<MB, G, kEpLogits>, dim3(grid), dim3(256), p, s);
+    case kEpPlain: return launch_1(mgemm_kernel<MB, G, kEpPlain>, dim3(grid), dim3(256), p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int MB>
+static hipError_t mgemm_launch_mb(Epilogue ep, const GemmParams &p, int grid, hipStream_t s) {
+  switch (p.G) {
+    case 64: return mgemm_launch_g<MB, 64>(ep, p, grid, s);
+    case 128: return mgemm_launch_g<MB, 128>(ep, p, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
+  if (p.M < 1 || p.M > 64 || p.K % p.G || (p.G != 64 && p.G != 128)) return hipErrorInvalidValue;
+  const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
+  const MgemmPlan pl = mgemm_plan(p.M, ncols, p.K, ep != kEpLogits);
+  if (pl.nsplit > 1 && (!p.part || !p.counters || pl.ncolblk > kMgemmMaxCounters ||
+                        mgemm_part_floats(pl) > p.part_cap))
+    return hipErrorInvalidValue;
+  GemmParams q = p;
+  q.nsplit = pl.nsplit;
+  q.ks = pl.ks;
+  const int grid = pl.ncolblk * pl.nsplit;
+  switch (pl.mb) {
+    case 1: return mgemm_launch_mb<1>(ep, q, grid, s);
+    case 2: return mgemm_launch_mb<2>(ep, q, grid, s);
+    default: return mgemm_launch_mb<4>(ep, q, grid, s);
   }
 }
 

@@ -82,6 +82,20 @@ Workspace workspace_layout(const river_config &c) {
   w.attn_splits = (c.max_seq + kAttnSub - 1) / kAttnSub;  // the most any batch size uses
   w.attn_part = take((size_t)c.max_batch * c.n_q_heads * w.attn_splits * (c.head_dim + 2) * 4);
   w.rope = take((size_t)c.max_seq * (c.head_dim / 2) * 8);
+  // split-K partials of the batched-row GEMM (decode steps of more than 8 rows)
+  int64_t mg = 0;
+  if (c.max_batch > 8) {
+    const int kd = c.n_kv_heads * c.head_dim;
+    const int shapes[4][2] = {{qd + 2 * kd, c.d_model}, {c.d_model, qd}, {2 * c.ffn_dim, c.d_model},
+                              {c.d_model, c.ffn_dim}};
+    const int rows[3] = {std::min(c.max_batch, 16), std::min(c.max_batch, 32), c.max_batch};
+    for (int M : rows)
+      for (auto &sh : shapes)
+        mg = std::max<int64_t>(mg, mgemm_part_floats(mgemm_plan(M, sh[0], sh[1])));
+  }
+  w.mg_part_floats = std::max<int64_t>(mg, 1);
+  w.mg_part = take((size_t)w.mg_part_floats * 4);
+  w.mg_counters = take((size_t)kMgemmMaxCounters * 4);
   w.total = off;
   return w;
 }
@@ -177,6 +191,8 @@ int supported(const river_config *c) {
   const int gq = c->n_q_heads / c->n_kv_heads;
   if (gq != 1 && gq != 2 && gq != 4) return RIVER_E_UNIMPLEMENTED;
   if (c->max_batch > 64) return RIVER_E_UNIMPLEMENTED;
+  // more than 8 rows per decode step run on the batched-row MFMA GEMM
+  if (c->max_batch > 8 && G != 64 && G != 128) return RIVER_E_UNIMPLEMENTED;
   if (c->ffn_dim % 32) return RIVER_E_UNIMPLEMENTED;
   return RIVER_OK;
 }
@@ -273,12 +289,122 @@ struct Recorder {
   }
 };
 
+// Common parameters of the batched-row GEMM launches of layer l.
+GemmParams mgemm_base(river_ctx *ctx, int l, int M) {
+  const river_config &c = ctx->cfg;
+  GemmParams g{};
+  g.M = M; g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl;
+  g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim; g.max_seq = c.max_seq;
+  g.max_batch = c.max_batch; g.T = 0; g.rope_theta = c.rope_theta;
+  g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
+  g.part = at<float>(ctx->ws, ctx->wl.mg_part);
+  g.part_cap = ctx->wl.mg_part_floats;
+  g.counters = at<uint32_t>(ctx->ws, ctx->wl.mg_counters);
+  return g;
+}
+
+// Final RMSNorm of B rows (row stride `stride` floats) + LM head + argmax on
+// the batched-row GEMM.
+int enqueue_lm_head_rows(river_ctx *ctx, const float *h, int64_t stride, int B, float *logits,
+                         int32_t *next, int is_prefill) {
+  const river_config &c = ctx->cfg;
+  uint16_t *x = at<uint16_t>(ctx->ws, ctx->wl.x);
+  RowsNormParams rn{h, x, ctx->final_norm, B, c.d_model, c.rms_eps, stride};
+  TIMED(RIVER_K_P_NORM, launch_rows_norm(rn, ctx->stream));
+  GemmParams lm = mgemm_base(ctx, -1, B);
+  lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
+  lm.N = c.vocab; lm.K = c.d_model; lm.x = x; lm.ldx = c.d_model;
+  lm.logits = logits; lm.next = next; lm.vocab = c.vocab; lm.is_prefill = is_prefill;
+  TIMED(RIVER_K_LMHEAD, launch_mgemm(kEpLogits, lm, ctx->stream));
+  return RIVER_OK;
+}
+
+// Decode step of more than 8 rows: every linear on the batched-row MFMA GEMM,
+// RMSNorm and the exit test as row kernels (the test is the same batch-min
+// rule; its flag is read by the next layer's GEMMs).
+int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next,
+                        int only) {
+  const river_config &c = ctx->cfg;
+  const int B = ctx->batch;
+  hipStream_t s = ctx->stream;
+  float *hA = at<float>(ctx->ws, ctx->wl.hA), *hB = at<float>(ctx->ws, ctx->wl.hB);
+  uint16_t *x = at<uint16_t>(ctx->ws, ctx->wl.x);
+  const int qd = c.n_q_heads * c.head_dim;
+  const Recorder rec{ctx, record_layout(c, B), B};
+  const size_t hbytes = (size_t)B * c.d_model * 4, qbytes = (size_t)B * qd * 2;
+
+  BeginParams bp{};
+  bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
+  bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
+  bp.tau = tau; bp.is_prefill = 0; bp.set_pos = -1;
+  TIMED_ONLY(RIVER_K_BEGIN, launch_begin(bp, s));
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const river_layer_w &L = ctx->layers[l];
+    RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
+    RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), B, c.d_model, c.rms_eps, 0};
+    TIMED_ONLY(RIVER_K_P_NORM, launch_rows_norm(rn, s));
+
+    GemmParams q = mgemm_base(ctx, l, B);
+    fill_weights(ctx, l, 0, 3, q.w);
+    q.N = qd + 2 * c.n_kv_heads * c.head_dim; q.K = c.d_model; q.x = x; q.ldx = c.d_model;
+    q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
+    q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
+    TIMED_ONLY(RIVER_K_QKV, launch_mgemm(kEpQKV, q, s));
+    RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
+
+    AttnParams a{};
+    a.q = q.q_out; a.k_cache = q.k_cache; a.v_cache = q.v_cache;
+    a.out = at<uint16_t>(ctx->ws, ctx->wl.attn); a.part = at<float>(ctx->ws, ctx->wl.attn_part);
+    a.counters = control_attn_counters(ctx->ctrl, c.max_batch); a.ctrl = ctx->ctrl;
+    a.B = B; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.Dh = c.head_dim; a.S = c.max_seq;
+    a.chunk = attn_chunk(c.max_seq, B, c.n_kv_heads);
+    a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
+    RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
+
+    GemmParams o = mgemm_base(ctx, l, B);
+    fill_weights(ctx, l, 3, 1, o.w);
+    o.N = c.d_model; o.K = qd; o.x = a.out; o.ldx = qd;
+    o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
+    TIMED_ONLY(RIVER_K_O, launch_mgemm(kEpResid, o, s));
+    RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
+
+    RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), B, c.d_model, c.rms_eps, 0};
+    TIMED_ONLY(RIVER_K_P_NORM, launch_rows_norm(rn2, s));
+    GemmParams gu = mgemm_base(ctx, l, B);
+    fill_weights(ctx, l, 4, 2, gu.w);
+    gu.N = 2 * c.ffn_dim; gu.K = c.d_model; gu.x = x; gu.ldx = c.d_model;
+    gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u);
+    TIMED_ONLY(RIVER_K_GATEUP, launch_mgemm(kEpSwiGLU, gu, s));
+    RV_TRY(rec.put(l, rec.lay.u, gu.u_out, (size_t)B * c.ffn_dim * 2));
+
+    GemmParams dn = mgemm_base(ctx, l, B);
+    fill_weights(ctx, l, 6, 1, dn.w);
+    dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
+    dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
+    TIMED_ONLY(RIVER_K_DOWN, launch_mgemm(kEpResid, dn, s));
+
+    if (l < c.n_layers - 1 && ctx->force_E < 0) {
+      RowsCosParams rc{hA, hB, B, c.d_model, at<float>(ctx->ws, ctx->wl.part), ctx->ctrl, l,
+                       c.n_layers};
+      TIMED_ONLY(RIVER_K_P_COS, launch_rows_cos_exit(rc, s));
+    }
+    std::swap(hA, hB);
+  }
+  RV_TRY(rec.put(-1, 0, hA, hbytes));
+  if (only < 0) return enqueue_lm_head_rows(ctx, hA, c.d_model, B, logits, next, 0);
+  return RIVER_OK;
+}
+
 // Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
 //
 // only >= 0 (a RIVER_K_* layer kernel class) enqueues nothing but that class's
 // launch for every layer, with the same parameters (kernel timing).
 int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next,
                    int only = -1) {
+  if (ctx->batch > 8) return enqueue_decode_rows(ctx, tok, tau, logits, next, only);
   const river_config &c = ctx->cfg;
   const int B = ctx->batch;
   hipStream_t s = ctx->stream;
@@ -441,6 +567,9 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     std::swap(hA, hB);
   }
   RV_TRY(rec.put(-1, 0, hA, hbytes));
+  if (B > 8)
+    return enqueue_lm_head_rows(ctx, hA + (int64_t)(T - 1) * c.d_model, (int64_t)T * c.d_model, B,
+                                logits, next, 1);
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
@@ -559,6 +688,8 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
   drop_graphs(ctx);
   ctx->built = false;
   RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads), ctx->stream));
+  RV_TRY(launch_clear(at<uint32_t>(ctx->ws, ctx->wl.mg_counters), (size_t)kMgemmMaxCounters * 4,
+                      ctx->stream));
   RV_TRY(launch_rope_table(at<float2>(ctx->ws, ctx->wl.rope), c.max_seq, c.head_dim, c.rope_theta,
                            ctx->stream));
   LinearShape sh[7];
@@ -592,7 +723,6 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
   if (!std::isfinite(tau)) return RIVER_E_INVALID_ARG;
   if (!ctx->built) return RIVER_E_STATE;
   if (B < 1 || T < 1 || B > ctx->cfg.max_batch || T > ctx->cfg.max_seq) return RIVER_E_RANGE;
-  if (B > 8) return RIVER_E_UNIMPLEMENTED;
   if (ctx->rec && record_layout(ctx->cfg, (int64_t)B * T).total > ctx->rec_bytes)
     return RIVER_E_BAD_SIZE;
   const int st = enqueue_prefill(ctx, d_tokens, B, T, tau, d_logits, d_next);
@@ -780,13 +910,15 @@ int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t us
     g.path = path; g.y_out = d_y; g.y_stride = sh[linear].N;
     RV_TRY(launch_gemv(kXBf16, kEpPlain, g, ctx->stream));
   } else {
-    GemmParams g{};
+    GemmParams g = mgemm_base(ctx, layer, M);
     fill_weights(ctx, layer, linear, 1, g.w);
-    g.M = M; g.N = sh[linear].N; g.K = sh[linear].K; g.G = c.group_size;
-    g.layer = layer; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl;
+    g.M = M; g.N = sh[linear].N; g.K = sh[linear].K;
     g.x = static_cast<const uint16_t *>(d_x); g.ldx = sh[linear].K;
     g.path = path; g.y_out = d_y; g.y_stride = sh[linear].N;
-    RV_TRY(launch_gemm(kEpPlain, g, ctx->stream));
+    if (M <= 64 && ctx->cfg.max_batch > 8)
+      RV_TRY(launch_mgemm(kEpPlain, g, ctx->stream));    // the decode core of 9..64 rows
+    else
+      RV_TRY(launch_gemm(kEpPlain, g, ctx->stream));     // the prefill core
   }
   return RIVER_OK;
 }

@@ -86,10 +86,13 @@ struct Workspace {
   size_t part;         // fp32 per-workgroup partial sums for the exit test
   size_t attn_part;    // fp32 split-K attention partials
   size_t rope;         // fp32 (cos, sin) of pos * theta^(-2i/Dh), [max_seq][Dh/2]
+  size_t mg_part;      // fp32 split-K partials of the batched-row GEMM
+  size_t mg_counters;  // uint32 per column block: split-K arrivals
   size_t total;
   int64_t rows;        // R: rows the buffers hold
   int part_floats;
   int attn_splits;     // split count the decode attention is sized for
+  int64_t mg_part_floats;
 };
 Workspace workspace_layout(const river_config &c);
 
@@ -196,6 +199,7 @@ hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 // prefill
 struct RowsNormParams {
   const float *h; uint16_t *x; const uint16_t *gain; int64_t rows; int d; float eps;
+  int64_t h_stride;   // floats between input rows (0: d)
 };
 hipError_t launch_rows_norm(const RowsNormParams &p, hipStream_t s);
 
@@ -213,7 +217,23 @@ struct GemmParams {
   uint16_t *u_out;
   int path;                        // PathChoice
   float *y_out; int64_t y_stride;  // kEpPlain
+  // batched-row GEMM (mgemm) only
+  float *logits; int32_t *next; int vocab; int is_prefill;   // kEpLogits
+  float *part; uint32_t *counters;                           // split-K partials
+  int64_t part_cap;                                          // floats at part
+  int nsplit, ks;                                            // K splits, K per split
 };
+
+// Batched-row GEMM for 9..64 rows (decode of larger batches, LM head of
+// prefill): weights stream from HBM straight into MFMA operands, the rows sit
+// in LDS.  Plan: 16-row blocks, 128-column workgroups, K split over nsplit
+// workgroups (last one reduces).
+constexpr int kMgemmBN = 128;
+constexpr int kMgemmMaxCounters = 4096;
+struct MgemmPlan { int mb, ncolblk, nsplit, ks; };
+MgemmPlan mgemm_plan(int M, int ncols, int K);
+int64_t mgemm_part_floats(const MgemmPlan &pl);
+hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 
 struct AttnPrefillParams {

@@ -228,8 +228,11 @@ int river_profile_read(river_ctx *ctx, river_kernel_time_t *out);
 int river_time_kernel(river_ctx *ctx, int32_t kind, int32_t reps, double *avg_us);
 
 /* Debug / test entry point: y = x W^T for one linear of one layer, through
- * the same weight-streaming cores the passes use (GEMV for M <= 8 rows, the
- * MFMA GEMM above), with a plain fp32 output instead of a fused epilogue.
+ * the same weight-streaming cores the passes use, with a plain fp32 output
+ * instead of a fused epilogue: the GEMV for M <= 8 rows; for 9 <= M <= 64 the
+ * batched-row MFMA GEMM of decode steps when the context was made for more
+ * than 8 rows (max_batch > 8), else the prefill MFMA GEMM, which also takes
+ * every M > 64.
  *   linear: as in river_exit_bank_offsets; use_exit: 0 backbone bf16 weights,
  *   1 the exit copy (int4 or bf16 copy, per the built mode);
  *   d_x: device bf16 [M][K]; d_y: device fp32 [M][N].

@@ -42,10 +42,34 @@ def ctx8b():
     r.close()
 
 
+@pytest.fixture(scope="module")
+def ctx8b_rows():
+    """Context made for up to 64 rows per step: 9..64 rows run on the
+    batched-row MFMA GEMM of decode steps."""
+    from early_exit_kv_amd import river as rv
+    sh = synth.shrink(synth.LLAMA_8B, n_layers=1)
+    w = synth.make_weights(synth.LLAMA_8B, seed=0, device="cuda", n_layers=1)
+    r = rv.River(sh, w, 64, 8)
+    r.build_exit_layers("int4")
+    torch.cuda.synchronize()
+    yield sh, w, r
+    r.close()
+
+
 @pytest.mark.parametrize("M", [1, 8, 40])
 @pytest.mark.parametrize("use_exit", [0, 1])
 def test_linear_cores_8b(ctx8b, M, use_exit):
-    sh, w, r = ctx8b
+    check_linears(ctx8b, M, use_exit)
+
+
+@pytest.mark.parametrize("M", [9, 32, 33, 64])
+@pytest.mark.parametrize("use_exit", [0, 1])
+def test_linear_batched_rows_8b(ctx8b_rows, M, use_exit):
+    check_linears(ctx8b_rows, M, use_exit)
+
+
+def check_linears(ctx, M, use_exit):
+    sh, w, r = ctx
     g = torch.Generator(device="cpu").manual_seed(1234 + M)
     worst = []
     for i, name in enumerate(LINEARS):

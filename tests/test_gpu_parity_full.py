@@ -157,6 +157,23 @@ def test_decode_parity_8b_layer_shapes_batch8(w8b):
     parity_run(synth.LLAMA_8B, w, B=8, T=6, steps=2, tau=0.3)
 
 
+def test_decode_parity_8b_layer_shapes_batch32(w8b):
+    """32 rows per step: every linear on the batched-row MFMA GEMM (split K,
+    last-workgroup reduction), RMSNorm and the exit test as row kernels."""
+    w = dict(w8b)
+    w["layers"] = w8b["layers"][:2]
+    parity_run(synth.LLAMA_8B, w, B=32, T=4, steps=2, tau=0.3)
+
+
+@pytest.mark.parametrize("tau", [0.5, -1.5])
+def test_decode_parity_tiny_batch16(tau):
+    """16 rows per step on the tiny decoder (group size 64)."""
+    w = synth.make_weights(synth.TINY, seed=0, device="cuda")
+    Es = parity_run(synth.TINY, w, B=16, T=8, steps=3, tau=tau)
+    if tau < -1:
+        assert all(e == 1 for e in Es)
+
+
 def test_split_attention_long_context_tiny():
     """A context of several hundred positions splits the decode attention over
     workgroups and merges the splits in the last one; B=8 fills the GEMV's
