@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s, 8B-shape KV-shared exit, τ=0.5; HBM GB/s as % of peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -260,6 +261,31 @@ def main():
                     "traffic": None if traffic is None else int(traffic),
                     "kernel": dom, "algorithmic_bytes": dk["avg_bytes"], "avg_us": dk["avg_us"]}
 
+    prefill_gemm = None
+    if not args.no_profile:
+        # prefill GEMMs with every layer on its exit copy (forced E = 0): the
+        # int4-dequant MFMA GEMMs at M = B*T rows, timed with events
+        r.reset()
+        r.force_exit_layer(0)
+        r.profile(True)
+        r.profile_read()
+        r.prefill(tokens, tau, want_logits=False)
+        times = r.profile_read()
+        r.profile(False)
+        r.force_exit_layer(-1)
+        n, ms = times["p_gemm"]
+        s_ = shape
+        qd, kd = s_.n_q_heads * s_.head_dim, s_.n_kv_heads * s_.head_dim
+        nk = ((qd + 2 * kd) * s_.d_model + s_.d_model * qd + 2 * s_.ffn_dim * s_.d_model
+              + s_.d_model * s_.ffn_dim)
+        flop = 2.0 * B * T * nk * s_.n_layers
+        tflops = flop / (ms * 1e-3) / 1e12
+        prefill_gemm = {"rows": B * T, "launches": n, "total_ms": round(ms, 3),
+                        "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "what": "all q|k|v, o, gate|up, down GEMMs of a prefill with every layer on "
+                                "its int4 exit copy (forced E=0), 2*M*N*K flop over their event time"}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, weights, B, T, mean_E)
@@ -278,7 +304,7 @@ def main():
         "step_hbm_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "mean_exit_layer": round(mean_E, 3), "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
         "prefill_tok_s": round(B * T / prefill_s, 1), "prefill_E": prefill_E,
-        "build_exit_layers_s": round(build_s, 4), "kernels": kinds,
+        "build_exit_layers_s": round(build_s, 4), "kernels": kinds, "prefill_exit_gemm": prefill_gemm,
     }
     r.close()
     print(json.dumps(out))

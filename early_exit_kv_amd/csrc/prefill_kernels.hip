@@ -16,35 +16,45 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ===========================================================================
-// RMSNorm rows: x[r] = bf16(h[r] / sqrt(mean(h[r]^2) + eps) * gain); one
-// wavefront per row.
+// RMSNorm rows: x[r] = bf16(h[r] / sqrt(mean(h[r]^2) + eps) * gain).
+// One workgroup per row; every thread loads its (up to 8) groups of 4 values
+// before reducing, so a row costs one round trip to memory.
 // ===========================================================================
+constexpr int kNormHeld = 8;   // float4 per thread held in registers (d <= 8192)
+
 __global__ __launch_bounds__(256) void rows_norm_kernel(RowsNormParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= p.rows) return;
+  __shared__ float red[4];
+  const int64_t r = blockIdx.x;
   const float *h = p.h + r * (p.h_stride ? p.h_stride : (int64_t)p.d);
+  float4 v[kNormHeld];
   float ss = 0.f;
-  for (int k = lane * 4; k < p.d; k += 256) {
-    const float4 v = *reinterpret_cast<const float4 *>(h + k);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int i = 0; i < kNormHeld; ++i) {
+    const int k = 4 * (threadIdx.x + 256 * i);
+    v[i] = k < p.d ? *reinterpret_cast<const float4 *>(h + k) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  ss = wave_sum(ss);
+#pragma unroll
+  for (int i = 0; i < kNormHeld; ++i)
+    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)p.d + p.eps);
   uint16_t *x = p.x + r * p.d;
-  for (int k = lane * 4; k < p.d; k += 256) {
-    const float4 v = *reinterpret_cast<const float4 *>(h + k);
-    const uint2 g = *reinterpret_cast<const uint2 *>(p.gain + k);
-    uint2 o;
-    o.x = pack_bf2(v.x * rs * bf_lo(g.x), v.y * rs * bf_hi(g.x));
-    o.y = pack_bf2(v.z * rs * bf_lo(g.y), v.w * rs * bf_hi(g.y));
-    *reinterpret_cast<uint2 *>(x + k) = o;
+#pragma unroll
+  for (int i = 0; i < kNormHeld; ++i) {
+    const int k = 4 * (threadIdx.x + 256 * i);
+    if (k < p.d) {
+      const uint2 g = *reinterpret_cast<const uint2 *>(p.gain + k);
+      uint2 o;
+      o.x = pack_bf2(v[i].x * rs * bf_lo(g.x), v[i].y * rs * bf_hi(g.x));
+      o.y = pack_bf2(v[i].z * rs * bf_lo(g.y), v[i].w * rs * bf_hi(g.y));
+      *reinterpret_cast<uint2 *>(x + k) = o;
+    }
   }
 }
 
 hipError_t launch_rows_norm(const RowsNormParams &p, hipStream_t s) {
-  const int64_t blocks = (p.rows + 3) / 4;
-  return launch_1(rows_norm_kernel, dim3((unsigned)blocks), dim3(256), p, s);
+  if (p.d % 4 || p.d > 4 * 256 * kNormHeld) return hipErrorInvalidValue;
+  return launch_1(rows_norm_kernel, dim3((unsigned)p.rows), dim3(256), p, s);
 }
 
 // ===========================================================================
@@ -473,9 +483,9 @@ hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
 //   order the byte permute unpacks codes in), so every MFMA sums inside one
 //   group, which is then folded as  tot += s * (acc - (128 + z) * sum_k x).
 //   bf16 weights use the plain order (quarter qq holds k0 + 32j + 8qq .. +8).
-//   With several K splits each workgroup stores its partial tile; the last of
-//   a column block (arrival counter) adds the splits in order and runs the
-//   epilogue.
+//   With several K splits each workgroup stores its partial tile and a second
+//   kernel (one workgroup per column block) adds the splits in order and runs
+//   the epilogue.
 // ===========================================================================
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 template <int N_> struct WordsT;
@@ -483,33 +493,84 @@ template <> struct WordsT<1> { typedef uint32_t T; };
 template <> struct WordsT<2> { typedef v2u T; };
 template <> struct WordsT<4> { typedef v4u T; };
 
-template <int MB, int G, int EP>
-__global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
-  constexpr int NT = 2;                     // column tiles per wavefront
-  constexpr int BN = kMgemmBN;              // 4 x NT x 16
-  constexpr int ROWS = MB * 16;
-  constexpr int KS = MB <= 2 ? 512 : 256;   // K columns per LDS slab
-  constexpr int XS = KS + 8;                // padded LDS row (bf16)
-  constexpr int STEPS = G / 32;             // MFMA k-steps per group
-  constexpr int GW = G / 32;                // code words per lane per group
-  constexpr int XBYTES = ROWS * XS * 2;
-  constexpr int CBYTES = ROWS * (BN + 1) * 4;
-  static_assert(KS % G == 0, "slab holds whole groups");
-  typedef typename WordsT<GW>::T WT;
-  __shared__ __align__(16) char smem[XBYTES > CBYTES ? XBYTES : CBYTES];
-  __shared__ float xsg[ROWS][KS / G];
-  __shared__ uint64_t rowkey[ROWS];
-  __shared__ int last_flag;
-  uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-  float *Cs = reinterpret_cast<float *>(smem);
+// LM head epilogue of one column block: logits out, per-row argmax keys
+// (value order, then lowest index), and in the last workgroup of the launch
+// the next tokens and the pass bookkeeping (E histogram, position).
+template <int ROWS, int BN>
+__device__ void logits_epilogue(const GemmParams &p, const float *Cs, int m0, int colblk,
+                                uint64_t *rowkey, int *last_flag) {
+  Control *ctl = p.ctrl;
+  if (threadIdx.x < ROWS) rowkey[threadIdx.x] = 0;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
+    const int r = idx / BN, j = idx % BN;
+    const int n = colblk * BN + j;
+    if (m0 + r >= p.M || n >= p.N) continue;
+    const float v = Cs[r * (BN + 1) + j];
+    if (p.logits) p.logits[(int64_t)(m0 + r) * p.vocab + n] = v;
+    const uint64_t key = ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+    __hip_atomic_fetch_max(&rowkey[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  if (threadIdx.x < ROWS && m0 + (int)threadIdx.x < p.M)
+    __hip_atomic_fetch_max(control_keys(ctl) + m0 + threadIdx.x, rowkey[threadIdx.x], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  if (arrive_last(&ctl->counters[kCtrLogits], gridDim.x, last_flag)) {
+    if (threadIdx.x < p.M && p.next) {
+      const uint64_t key = __hip_atomic_load(control_keys(ctl) + threadIdx.x, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      p.next[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+    }
+    if (threadIdx.x == 0) {
+      const int E = ctl->E;
+      ctl->last_E = E;
+      if (p.is_prefill) {
+        ctl->prefill_hist[E] += 1;
+        ctl->n_prefill += 1;
+      } else {
+        ctl->decode_hist[E] += 1;
+        ctl->n_decode += 1;
+        ctl->pos += 1;
+      }
+    }
+  }
+}
 
-  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
-  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+template <int MB, int G> struct MgemmShape {
+  static constexpr int NT = 2;                    // column tiles per wavefront
+  static constexpr int BN = kMgemmBN;             // 4 x NT x 16
+  static constexpr int ROWS = MB * 16;
+  // K columns of the rows held in LDS: the whole K split of a workgroup is
+  // staged once, before any weight load is issued, so the weight stream never
+  // waits behind activation loads (about 66 KB: two workgroups per CU)
+  static constexpr int KS = MB == 1 ? 2048 : MB == 2 ? 1024 : 512;
+  static constexpr int XS = KS + 8;               // padded LDS row (bf16)
+  static constexpr int STEPS = G / 32;            // MFMA k-steps per group
+  static constexpr int GW = G / 32;               // code words per lane per group
+  static constexpr int XBYTES = ROWS * XS * 2;
+  static constexpr int CBYTES = ROWS * (BN + 1) * 4;
+  static constexpr int SMEM = XBYTES > CBYTES ? XBYTES : CBYTES;
+  static_assert(KS % G == 0, "slab holds whole groups");
+};
+
+struct MgemmLds {
+  uint16_t *xs;        // staged rows [ROWS][XS]
+  float *xsg;          // [ROWS][KS/G] group sums of the staged rows (int4)
+};
+
+// Main loop of the batched-row GEMM over this workgroup's K split, for one
+// weight form (Q4: int4 exit copy; else bf16).  Weights run D groups ahead.
+template <int MB, int G, int EP, bool Q4>
+__device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &L, bool ex, int colblk,
+                                           int kbeg, int kend,
+                                           f32x4_t (&tot)[MB][MgemmShape<MB, G>::NT]) {
+  typedef MgemmShape<MB, G> S;
+  constexpr int NT = S::NT, BN = S::BN, ROWS = S::ROWS, KS = S::KS, XS = S::XS;
+  constexpr int STEPS = S::STEPS, GW = S::GW;
+  constexpr int D = Q4 ? 8 : 4;                   // groups in flight per lane
+  typedef typename WordsT<GW>::T WT;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
-  const int split = blockIdx.x % p.nsplit, colblk = blockIdx.x / p.nsplit;
-  const int kbeg = split * p.ks;
-  const int kend = min(p.K, kbeg + p.ks);
   const int nchunk = (kend - kbeg) / G;
   const int KG = p.K / G;
 
@@ -521,73 +582,78 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
     bool valid;
     map_col<EP>(p, colblk, BN, wid * (NT * 16) + t * 16 + cl, seg, row, valid);
     if (!valid) { seg = 0; row = 0; }      // a valid row; its results are dropped
-    if (q4) {
+    if constexpr (Q4) {
       qrow[t] = p.w.q4[seg] + (int64_t)row * (p.K / 8);
       zrow[t] = p.w.sz[seg] + (int64_t)row * KG;
-      brow[t] = nullptr;
     } else {
       brow[t] = (ex ? p.w.ex_bf[seg] : p.w.bf[seg]) + (int64_t)row * p.K;
-      qrow[t] = zrow[t] = nullptr;
     }
   }
 
-  // weight ring: two groups in flight per lane
-  WT wq[2][NT];
-  uint32_t wz[2][NT];
-  v4u wb[2][NT][STEPS];
-  auto load = [&](int c, int sl) {
+  WT wq[D][NT];
+  uint32_t wz[D][NT];
+  v4u wb[D][NT][STEPS];
+  auto load = [&](int c, int u) {
     const int k0 = kbeg + c * G;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (q4) {
-        wq[sl][t] = __builtin_nontemporal_load(
+      if constexpr (Q4) {
+        wq[u][t] = __builtin_nontemporal_load(
             reinterpret_cast<const WT *>(qrow[t] + (k0 >> 3) + qq * GW));
-        wz[sl][t] = zrow[t][k0 / G];
+        wz[u][t] = zrow[t][k0 / G];
       } else {
 #pragma unroll
         for (int j = 0; j < STEPS; ++j)
-          wb[sl][t][j] = __builtin_nontemporal_load(
+          wb[u][t][j] = __builtin_nontemporal_load(
               reinterpret_cast<const v4u *>(brow[t] + k0 + 32 * j + 8 * qq));
       }
     }
   };
 
-  f32x4_t tot[MB][NT];
-#pragma unroll
-  for (int a = 0; a < MB; ++a)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  int slab0 = kbeg;
+  const int slab0 = kbeg;
   auto stage = [&](int base) {
-    const int sl = min(KS, kend - base);
-    const int n8 = sl >> 3;
+    // all loads of a batch are issued before any is used (the rows come from
+    // L2; one round trip per batch instead of one per item)
+    constexpr int PER = ROWS * (KS / 8) / 256;    // items per thread at most
+    const int n8 = (kend - base) >> 3;
+    const int total = ROWS * n8;
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * n8; idx += 256) {
-      const int m = idx / n8, g8 = idx - m * n8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < p.M) v = *reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.ldx + base + 8 * g8);
-      if (q4) v = int4_order(v.x, v.y, v.z, v.w);
-      *reinterpret_cast<uint4 *>(xs + m * XS + 8 * g8) = v;
-    }
-    __syncthreads();
-    if (q4) {
-      const int ng = sl / G;
-      for (int idx = threadIdx.x; idx < ROWS * ng; idx += 256) {
-        const int m = idx / ng, g = idx - m * ng;
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(xs + m * XS + g * G);
-        float sacc = 0.f;
-        for (int i = 0; i < G / 2; ++i) sacc += bf_lo(src[i]) + bf_hi(src[i]);
-        xsg[m][g] = sacc;
+#pragma unroll
+    for (int h = 0; h < PER; h += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = threadIdx.x + 256 * (h + i);
+        const int m = idx / n8, g8 = idx - m * n8;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (idx < total && m < p.M)
+          v[i] = *reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.ldx + base + 8 * g8);
       }
-      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = threadIdx.x + 256 * (h + i);
+        if (idx < total) {
+          const int m = idx / n8, g8 = idx - m * n8;
+          uint4 w = v[i];
+          if constexpr (Q4) {
+            // group sum: the G/8 items of a group sit in G/8 adjacent lanes
+            // (n8 and the 256-thread stride are multiples of G/8)
+            float gs = ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
+                       ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
+            gs = G == 128 ? sum16(gs) : sum8(gs);
+            if (g8 % (G / 8) == 0) L.xsg[m * (KS / G) + g8 / (G / 8)] = gs;
+            w = int4_order(w.x, w.y, w.z, w.w);
+          }
+          *reinterpret_cast<uint4 *>(L.xs + m * XS + 8 * g8) = w;
+        }
+      }
     }
+    __syncthreads();
   };
 
-  auto compute = [&](int c, int sl) {
-    const int k0 = kbeg + c * G;
-    const int kl = k0 - slab0;
-    if (q4) {
+  auto compute = [&](int c, int u) {
+    const int kl = kbeg + c * G - slab0;
+    if constexpr (Q4) {
       f32x4_t ag[MB][NT];
 #pragma unroll
       for (int a = 0; a < MB; ++a)
@@ -598,12 +664,12 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
         bf16x8_t af[MB], bfr[NT];
 #pragma unroll
         for (int a = 0; a < MB; ++a)
-          af[a] = *reinterpret_cast<const bf16x8_t *>(xs + (a * 16 + cl) * XS + kl + qq * (G / 4) + 8 * j);
+          af[a] = *reinterpret_cast<const bf16x8_t *>(L.xs + (a * 16 + cl) * XS + kl + qq * (G / 4) + 8 * j);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           uint32_t w;
-          if constexpr (GW == 1) w = wq[sl][t];
-          else w = wq[sl][t][j];
+          if constexpr (GW == 1) w = wq[u][t];
+          else w = wq[u][t][j];
           uint32_t pr[4];
           unpack_word(w, pr);
           bfr[t] = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
@@ -617,12 +683,13 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
       const int g = kl / G;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float sc = bf_lo(wz[sl][t]), zo = 128.0f + bf_hi(wz[sl][t]);
+        const float sc = bf_lo(wz[u][t]), zo = 128.0f + bf_hi(wz[u][t]);
 #pragma unroll
         for (int a = 0; a < MB; ++a)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * xsg[a * 16 + 4 * qq + v][g], tot[a][t][v]);
+            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * L.xsg[(a * 16 + 4 * qq + v) * (KS / G) + g],
+                                tot[a][t][v]);
       }
     } else {
 #pragma unroll
@@ -630,29 +697,74 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
         bf16x8_t af[MB];
 #pragma unroll
         for (int a = 0; a < MB; ++a)
-          af[a] = *reinterpret_cast<const bf16x8_t *>(xs + (a * 16 + cl) * XS + kl + 32 * j + 8 * qq);
+          af[a] = *reinterpret_cast<const bf16x8_t *>(L.xs + (a * 16 + cl) * XS + kl + 32 * j + 8 * qq);
 #pragma unroll
         for (int a = 0; a < MB; ++a)
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                af[a], __builtin_bit_cast(bf16x8_t, wb[sl][t][j]), tot[a][t], 0, 0, 0);
+                af[a], __builtin_bit_cast(bf16x8_t, wb[u][t][j]), tot[a][t], 0, 0, 0);
       }
     }
   };
 
-  constexpr int CPS = KS / G;   // groups per slab
-  if (nchunk > 0) load(0, 0);
-  if (nchunk > 1) load(1, 1);
-  for (int c = 0; c < nchunk; c += 2) {
-    if (c % CPS == 0) { slab0 = kbeg + c * G; stage(slab0); }
-    compute(c, 0);
-    if (c + 2 < nchunk) load(c + 2, 0);
-    if (c + 1 < nchunk) {
-      if ((c + 1) % CPS == 0) { slab0 = kbeg + (c + 1) * G; stage(slab0); }
-      compute(c + 1, 1);
-      if (c + 3 < nchunk) load(c + 3, 1);
+  // the first D groups of weights are requested before the rows of the whole
+  // split (the plan keeps it within KS) are staged, so both latencies overlap;
+  // after that the loop only ever waits for the oldest weight group
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < nchunk) load(u, u);
+  stage(kbeg);
+  for (int c0 = 0; c0 < nchunk; c0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int c = c0 + u;
+      if (c < nchunk) {
+        compute(c, u);
+        if (c + D < nchunk) load(c + D, u);
+      }
     }
+  }
+}
+
+template <int MB, int G, int EP>
+__global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
+  typedef MgemmShape<MB, G> S;
+  constexpr int NT = S::NT, BN = S::BN, ROWS = S::ROWS, KS = S::KS;
+  __shared__ __align__(16) char smem[S::SMEM];
+  __shared__ float xsg[ROWS * (KS / G)];
+  __shared__ uint64_t rowkey[ROWS];
+  __shared__ int last_flag;
+  const MgemmLds L{reinterpret_cast<uint16_t *>(smem), xsg};
+  float *Cs = reinterpret_cast<float *>(smem);
+
+  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
+  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, cl = lane & 15;
+  const int split = blockIdx.x % p.nsplit, colblk = blockIdx.x / p.nsplit;
+  const int kbeg = split * p.ks;
+  const int kend = min(p.K, kbeg + p.ks);
+
+  f32x4_t tot[MB][NT];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (q4) mgemm_body<MB, G, EP, true>(p, L, ex, colblk, kbeg, kend, tot);
+  else mgemm_body<MB, G, EP, false>(p, L, ex, colblk, kbeg, kend, tot);
+
+  if (p.nsplit > 1) {
+    // partial tile straight from the accumulators, [ROWS][BN] row-major
+    float *mine = p.part + ((int64_t)colblk * p.nsplit + split) * (ROWS * BN);
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          mine[(a * 16 + 4 * qq + v) * BN + wid * (NT * 16) + t * 16 + cl] = tot[a][t][v];
+    return;
   }
 
   // ---- results to LDS (the slab buffer is reused)
@@ -666,59 +778,39 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
         Cs[(a * 16 + 4 * qq + v) * (BN + 1) + wid * (NT * 16) + t * 16 + cl] = tot[a][t][v];
   __syncthreads();
 
-  if (p.nsplit > 1) {
-    float *mine = p.part + ((int64_t)colblk * p.nsplit + split) * (ROWS * BN);
-    for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256)
-      st_coherent(mine + idx, Cs[(idx / BN) * (BN + 1) + idx % BN]);
-    if (!arrive_last(&p.counters[colblk], p.nsplit, &last_flag)) return;
-    const float *all = p.part + (int64_t)colblk * p.nsplit * (ROWS * BN);
-    for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
-      float v = 0.f;
-      for (int sp = 0; sp < p.nsplit; ++sp) v += ld_coherent(all + (int64_t)sp * (ROWS * BN) + idx);
-      Cs[(idx / BN) * (BN + 1) + idx % BN] = v;
-    }
-    __syncthreads();
-  }
-
   if constexpr (EP == kEpLogits) {
-    Control *ctl = p.ctrl;
-    if (threadIdx.x < ROWS) rowkey[threadIdx.x] = 0;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
-      const int r = idx / BN, j = idx % BN;
-      const int n = colblk * BN + j;
-      if (r >= p.M || n >= p.N) continue;
-      const float v = Cs[r * (BN + 1) + j];
-      if (p.logits) p.logits[(int64_t)r * p.vocab + n] = v;
-      const uint64_t key = ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
-      __hip_atomic_fetch_max(&rowkey[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __syncthreads();
-    if (threadIdx.x < p.M)
-      __hip_atomic_fetch_max(control_keys(ctl) + threadIdx.x, rowkey[threadIdx.x], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t arrivals = p.nsplit > 1 ? (uint32_t)(gridDim.x / p.nsplit) : gridDim.x;
-    if (arrive_last(&ctl->counters[kCtrLogits], arrivals, &last_flag)) {
-      if (threadIdx.x < p.M && p.next) {
-        const uint64_t key = __hip_atomic_load(control_keys(ctl) + threadIdx.x, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        p.next[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
-      }
-      if (threadIdx.x == 0) {
-        const int E = ctl->E;
-        ctl->last_E = E;
-        if (p.is_prefill) {
-          ctl->prefill_hist[E] += 1;
-          ctl->n_prefill += 1;
-        } else {
-          ctl->decode_hist[E] += 1;
-          ctl->n_decode += 1;
-          ctl->pos += 1;
-        }
-      }
-    }
+    logits_epilogue<ROWS, BN>(p, Cs, 0, colblk, rowkey, &last_flag);
   } else {
     tile_epilogue<EP, BN>(p, Cs, BN + 1, ROWS, 0, colblk);
+  }
+}
+
+// Split-K sum of the batched-row GEMM and its epilogue: workgroup (column
+// block, group of 8 rows) adds the partial tiles of the splits in order.
+constexpr int kReduceRows = 8;
+template <int MB, int EP>
+__global__ __launch_bounds__(256) void mgemm_reduce_kernel(GemmParams p) {
+  constexpr int BN = kMgemmBN, ROWS = MB * 16, RG = kReduceRows;
+  __shared__ float Cs[RG * (BN + 1)];
+  const int colblk = blockIdx.x / (ROWS / RG), rg = blockIdx.x % (ROWS / RG);
+  const int i4 = threadIdx.x;                       // RG * BN / 4 == 256 float4
+  const int r = (4 * i4) / BN, j = (4 * i4) % BN;
+  const float *src = p.part + (int64_t)colblk * p.nsplit * (ROWS * BN) + (rg * RG + r) * BN + j;
+  float4 v = *reinterpret_cast<const float4 *>(src);
+#pragma unroll 4
+  for (int sp = 1; sp < p.nsplit; ++sp) {
+    const float4 t = *reinterpret_cast<const float4 *>(src + (int64_t)sp * (ROWS * BN));
+    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+  }
+  float *c = Cs + r * (BN + 1) + j;
+  c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+  __syncthreads();
+  if constexpr (EP == kEpLogits) {
+    __shared__ uint64_t rowkey[RG];
+    __shared__ int last_flag;
+    logits_epilogue<RG, BN>(p, Cs, rg * RG, colblk, rowkey, &last_flag);
+  } else {
+    tile_epilogue<EP, BN>(p, Cs, BN + 1, RG, rg * RG, colblk);
   }
 }
 
@@ -726,22 +818,35 @@ MgemmPlan mgemm_plan(int M, int ncols, int K, bool allow_split) {
   MgemmPlan pl{};
   pl.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   pl.ncolblk = (ncols + kMgemmBN - 1) / kMgemmBN;
-  const int KS = pl.mb <= 2 ? 512 : 256;
-  int ns = 1;
-  if (allow_split && K >= 2 * KS) {
-    ns = std::max(1, 512 / pl.ncolblk);
-    ns = std::min(ns, K / (2 * KS));
-  }
+  const int KS = pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512;
+  // fewest splits the LDS allows (each split adds a partial tile of
+  // rows x 128 fp32 per column block); more only if the grid would leave
+  // most CUs idle
+  int ns = (K + KS - 1) / KS;
+  if (allow_split)
+    while (pl.ncolblk * ns < 128 && K / (ns * 2) >= 256 && (K / (ns * 2)) % 128 == 0) ns *= 2;
   int ks = (K + ns - 1) / ns;
-  ks = K >= KS ? (ks + KS - 1) / KS * KS : K;
-  pl.ks = ks;
-  pl.nsplit = (K + ks - 1) / ks;
+  ks = (ks + 127) / 128 * 128;
+  pl.ks = std::min(ks, K);
+  pl.nsplit = (K + pl.ks - 1) / pl.ks;
   return pl;
 }
 MgemmPlan mgemm_plan(int M, int ncols, int K) { return mgemm_plan(M, ncols, K, true); }
 
 int64_t mgemm_part_floats(const MgemmPlan &pl) {
   return pl.nsplit > 1 ? (int64_t)pl.ncolblk * pl.nsplit * (pl.mb * 16) * kMgemmBN : 0;
+}
+
+template <int MB>
+static hipError_t mgemm_reduce(Epilogue ep, const GemmParams &p, int grid, hipStream_t s) {
+  switch (ep) {
+    case kEpQKV: return launch_1(mgemm_reduce_kernel<MB, kEpQKV>, dim3(grid), dim3(256), p, s);
+    case kEpResid: return launch_1(mgemm_reduce_kernel<MB, kEpResid>, dim3(grid), dim3(256), p, s);
+    case kEpSwiGLU: return launch_1(mgemm_reduce_kernel<MB, kEpSwiGLU>, dim3(grid), dim3(256), p, s);
+    case kEpPlain: return launch_1(mgemm_reduce_kernel<MB, kEpPlain>, dim3(grid), dim3(256), p, s);
+    case kEpLogits: return launch_1(mgemm_reduce_kernel<MB, kEpLogits>, dim3(grid), dim3(256), p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int MB, int G>
@@ -757,29 +862,31 @@ static hipError_t mgemm_launch_g(Epilogue ep, const GemmParams &p, int grid, hip
 }
 
 template <int MB>
-static hipError_t mgemm_launch_mb(Epilogue ep, const GemmParams &p, int grid, hipStream_t s) {
+static hipError_t mgemm_launch_mb(Epilogue ep, const GemmParams &p, int ncolblk, hipStream_t s) {
+  hipError_t e;
   switch (p.G) {
-    case 64: return mgemm_launch_g<MB, 64>(ep, p, grid, s);
-    case 128: return mgemm_launch_g<MB, 128>(ep, p, grid, s);
+    case 64: e = mgemm_launch_g<MB, 64>(ep, p, ncolblk * p.nsplit, s); break;
+    case 128: e = mgemm_launch_g<MB, 128>(ep, p, ncolblk * p.nsplit, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  static_assert(kReduceRows * kMgemmBN / 4 == 256, "one float4 per thread");
+  return mgemm_reduce<MB>(ep, p, ncolblk * (MB * 16 / kReduceRows), s);
 }
 
 hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
   if (p.M < 1 || p.M > 64 || p.K % p.G || (p.G != 64 && p.G != 128)) return hipErrorInvalidValue;
   const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
   const MgemmPlan pl = mgemm_plan(p.M, ncols, p.K, ep != kEpLogits);
-  if (pl.nsplit > 1 && (!p.part || !p.counters || pl.ncolblk > kMgemmMaxCounters ||
-                        mgemm_part_floats(pl) > p.part_cap))
-    return hipErrorInvalidValue;
+  if (pl.nsplit > 1 && (!p.part || mgemm_part_floats(pl) > p.part_cap)) return hipErrorInvalidValue;
+  if (pl.ks > (pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512)) return hipErrorInvalidValue;
   GemmParams q = p;
   q.nsplit = pl.nsplit;
   q.ks = pl.ks;
-  const int grid = pl.ncolblk * pl.nsplit;
   switch (pl.mb) {
-    case 1: return mgemm_launch_mb<1>(ep, q, grid, s);
-    case 2: return mgemm_launch_mb<2>(ep, q, grid, s);
-    default: return mgemm_launch_mb<4>(ep, q, grid, s);
+    case 1: return mgemm_launch_mb<1>(ep, q, pl.ncolblk, s);
+    case 2: return mgemm_launch_mb<2>(ep, q, pl.ncolblk, s);
+    default: return mgemm_launch_mb<4>(ep, q, pl.ncolblk, s);
   }
 }
 

@@ -86,8 +86,8 @@ Workspace workspace_layout(const river_config &c) {
   int64_t mg = 0;
   if (c.max_batch > 8) {
     const int kd = c.n_kv_heads * c.head_dim;
-    const int shapes[4][2] = {{qd + 2 * kd, c.d_model}, {c.d_model, qd}, {2 * c.ffn_dim, c.d_model},
-                              {c.d_model, c.ffn_dim}};
+    const int shapes[5][2] = {{qd + 2 * kd, c.d_model}, {c.d_model, qd}, {2 * c.ffn_dim, c.d_model},
+                              {c.d_model, c.ffn_dim}, {c.vocab, c.d_model}};
     const int rows[3] = {std::min(c.max_batch, 16), std::min(c.max_batch, 32), c.max_batch};
     for (int M : rows)
       for (auto &sh : shapes)
@@ -95,7 +95,6 @@ Workspace workspace_layout(const river_config &c) {
   }
   w.mg_part_floats = std::max<int64_t>(mg, 1);
   w.mg_part = take((size_t)w.mg_part_floats * 4);
-  w.mg_counters = take((size_t)kMgemmMaxCounters * 4);
   w.total = off;
   return w;
 }
@@ -187,6 +186,7 @@ int supported(const river_config *c) {
   if (G < 32 || G > 512 || (G & (G - 1))) return RIVER_E_UNIMPLEMENTED;
   if (c->d_model % G || c->ffn_dim % G || qd % G) return RIVER_E_UNIMPLEMENTED;
   if (c->d_model % 256 || c->ffn_dim % 256 || qd % 256) return RIVER_E_UNIMPLEMENTED;
+  if (c->d_model > 8192) return RIVER_E_UNIMPLEMENTED;   // RMSNorm rows held in registers
   if (c->head_dim != 64 && c->head_dim != 128) return RIVER_E_UNIMPLEMENTED;
   const int gq = c->n_q_heads / c->n_kv_heads;
   if (gq != 1 && gq != 2 && gq != 4) return RIVER_E_UNIMPLEMENTED;
@@ -299,7 +299,6 @@ GemmParams mgemm_base(river_ctx *ctx, int l, int M) {
   g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
   g.part = at<float>(ctx->ws, ctx->wl.mg_part);
   g.part_cap = ctx->wl.mg_part_floats;
-  g.counters = at<uint32_t>(ctx->ws, ctx->wl.mg_counters);
   return g;
 }
 
@@ -688,8 +687,6 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
   drop_graphs(ctx);
   ctx->built = false;
   RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads), ctx->stream));
-  RV_TRY(launch_clear(at<uint32_t>(ctx->ws, ctx->wl.mg_counters), (size_t)kMgemmMaxCounters * 4,
-                      ctx->stream));
   RV_TRY(launch_rope_table(at<float2>(ctx->ws, ctx->wl.rope), c.max_seq, c.head_dim, c.rope_theta,
                            ctx->stream));
   LinearShape sh[7];

@@ -87,7 +87,6 @@ struct Workspace {
   size_t attn_part;    // fp32 split-K attention partials
   size_t rope;         // fp32 (cos, sin) of pos * theta^(-2i/Dh), [max_seq][Dh/2]
   size_t mg_part;      // fp32 split-K partials of the batched-row GEMM
-  size_t mg_counters;  // uint32 per column block: split-K arrivals
   size_t total;
   int64_t rows;        // R: rows the buffers hold
   int part_floats;
@@ -219,7 +218,7 @@ struct GemmParams {
   float *y_out; int64_t y_stride;  // kEpPlain
   // batched-row GEMM (mgemm) only
   float *logits; int32_t *next; int vocab; int is_prefill;   // kEpLogits
-  float *part; uint32_t *counters;                           // split-K partials
+  float *part;                                               // split-K partial tiles
   int64_t part_cap;                                          // floats at part
   int nsplit, ks;                                            // K splits, K per split
 };
@@ -227,9 +226,8 @@ struct GemmParams {
 // Batched-row GEMM for 9..64 rows (decode of larger batches, LM head of
 // prefill): weights stream from HBM straight into MFMA operands, the rows sit
 // in LDS.  Plan: 16-row blocks, 128-column workgroups, K split over nsplit
-// workgroups (last one reduces).
+// workgroups whose partial tiles a second kernel adds up.
 constexpr int kMgemmBN = 128;
-constexpr int kMgemmMaxCounters = 4096;
 struct MgemmPlan { int mb, ncolblk, nsplit, ks; };
 MgemmPlan mgemm_plan(int M, int ncols, int K);
 int64_t mgemm_part_floats(const MgemmPlan &pl);
