@@ -6,6 +6,8 @@
 // Method: "River-LLM: Large Language Model Seamless Exit Based on KV Share",
 // section 3 (exit layers share the backbone's KV slots), section 4 (batch-min
 // state-transition similarity against tau, no re-check after the exit).
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace river {
@@ -784,7 +786,9 @@ hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float thet
 // ===========================================================================
 int attn_chunk(int max_seq, int batch, int n_kv_heads) {
   const int pairs = batch * n_kv_heads;
-  const int target = (2048 + pairs - 1) / pairs;           // splits per (b, kv head)
+  // about 2048 workgroups, but at most 16 splits per (b, kv head): merging
+  // more costs more than the extra parallelism brings
+  const int target = std::min(16, (2048 + pairs - 1) / pairs);   // splits per (b, kv head)
   int chunk = (max_seq + target - 1) / target;
   chunk = (chunk + kAttnSub - 1) / kAttnSub * kAttnSub;
   return chunk < kAttnSub ? kAttnSub : chunk;
@@ -804,8 +808,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int slot = lane / LPP, ln = lane % LPP;
-  const int n = p.ctrl->pos + 1;
+  // the first sub-chunk's K/V loads do not wait for the position: their
+  // addresses stay inside the cache whatever it is, and positions past it are
+  // masked once it has arrived
   const int t0 = split * p.chunk;
+  const int n = p.ctrl->pos + 1;
   const int t1 = min(n, t0 + p.chunk);
   const int64_t kvbase = (((int64_t)b * p.Hkv + kvh) * p.S) * DH + ln * 8;
   const uint16_t *K = p.k_cache + kvbase;
@@ -828,15 +835,23 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
-  for (int sb = t0; sb < t1; sb += kAttnSub) {
+  const int tend = min(t0 + p.chunk, p.S);
+  for (int sb = t0; sb < tend; sb += kAttnSub) {
+    if (sb > t0 && sb >= t1) break;
     uint4 kr[NP], vr[NP];
     bool ok[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int t = sb + i * PPP + wid * PPW + slot;
+      const int tc = min(t, p.S - 1);
+      kr[i] = *reinterpret_cast<const uint4 *>(K + (int64_t)tc * DH);
+      vr[i] = *reinterpret_cast<const uint4 *>(V + (int64_t)tc * DH);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = sb + i * PPP + wid * PPW + slot;
       ok[i] = t < t1;
-      kr[i] = ok[i] ? *reinterpret_cast<const uint4 *>(K + (int64_t)t * DH) : make_uint4(0, 0, 0, 0);
-      vr[i] = ok[i] ? *reinterpret_cast<const uint4 *>(V + (int64_t)t * DH) : make_uint4(0, 0, 0, 0);
+      if (!ok[i]) { kr[i] = make_uint4(0, 0, 0, 0); vr[i] = make_uint4(0, 0, 0, 0); }
     }
     float s[NP][GQ];
 #pragma unroll

@@ -149,13 +149,13 @@ __device__ __forceinline__ void map_col(const GemmParams &p, int col_blk, int BN
 
 // Epilogue of one finished tile: Cs holds rows x BN results (row stride cs)
 // for rows m0.. and column block colblk (columns mapped as map_col<EP> says).
-template <int EP, int BN>
+template <int EP, int BN, int NTHR = 256>
 __device__ void tile_epilogue(const GemmParams &p, const float *Cs, int cs, int BM, int64_t m0,
                               int colblk) {
   const int tid = threadIdx.x;
   if constexpr (EP == kEpQKV) {
     const int half = p.Dh >> 1;
-    for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
+    for (int idx = tid; idx < BM * (BN / 2); idx += NTHR) {
       const int r = idx / (BN / 2), pp = idx % (BN / 2);
       const int64_t m = m0 + r;
       const int L0 = colblk * BN + 2 * pp;
@@ -188,7 +188,7 @@ __device__ void tile_epilogue(const GemmParams &p, const float *Cs, int cs, int 
     }
   } else if constexpr (EP == kEpSwiGLU) {
     const int hw = BN / 2;
-    for (int idx = tid; idx < BM * hw; idx += 256) {
+    for (int idx = tid; idx < BM * hw; idx += NTHR) {
       const int r = idx / hw, jj = idx % hw;
       const int64_t m = m0 + r;
       const int n = colblk * hw + jj;
@@ -197,14 +197,14 @@ __device__ void tile_epilogue(const GemmParams &p, const float *Cs, int cs, int 
       p.u_out[m * p.w.seg_rows[0] + n] = f2bf(gt / (1.0f + expf(-gt)) * up);
     }
   } else if constexpr (EP == kEpPlain) {
-    for (int idx = tid; idx < BM * BN; idx += 256) {
+    for (int idx = tid; idx < BM * BN; idx += NTHR) {
       const int r = idx / BN, j = idx % BN;
       const int64_t m = m0 + r;
       const int n = colblk * BN + j;
       if (m < p.M && n < p.N) p.y_out[m * p.y_stride + n] = Cs[r * cs + (j)];
     }
   } else {  // residual
-    for (int idx = tid; idx < BM * BN; idx += 256) {
+    for (int idx = tid; idx < BM * BN; idx += NTHR) {
       const int r = idx / BN, j = idx % BN;
       const int64_t m = m0 + r;
       const int n = colblk * BN + j;
@@ -888,6 +888,260 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
     case 2: return mgemm_launch_mb<2>(ep, q, pl.ncolblk, s);
     default: return mgemm_launch_mb<4>(ep, q, pl.ncolblk, s);
   }
+}
+
+
+// ===========================================================================
+// Prefill GEMM for many rows: Y[m][n] = sum_k X[m][k] W[n][k] on
+// v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 x 128, eight wavefronts in a
+// 4 x 2 arrangement, each 32 x 64 (2 x 4 MFMA tiles: every row fragment read
+// from LDS feeds four MFMAs, which keeps LDS at half its bandwidth); two
+// wavefronts per SIMD so that one's waits overlap the other's MFMAs.  The rows X go through LDS in
+// k-tiles of 128 columns, double buffered (the next tile is loaded into
+// registers while the current one feeds the MFMAs); the weights go from memory
+// straight into B operands, every lane loading its own column, with the same
+// int4 conventions as the batched-row GEMM (per-group accumulation, lane
+// quarters over G/4 codes, rows staged in the matching column order, group
+// fold tot += s * (acc - (128 + z) * sum_k x)).  Workgroups are ordered in
+// groups of 8 row blocks so that the rows and weights they share stay in L2.
+// ===========================================================================
+constexpr int kPBM = 128, kPBN = 128, kPKT = 128, kPXS = kPKT + 8, kPGroupRows = 8;
+constexpr int kPThreads = 512;
+
+template <int G, int EP, bool Q4>
+__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, float *xsg, bool ex,
+                                           int rowblk, int colblk, f32x4_t (&tot)[2][4]) {
+  constexpr int STEPS = G / 32, GW = G / 32;
+  constexpr int GPT = kPKT / G;                 // groups per k-tile
+  typedef typename WordsT<GW>::T WT;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, cl = lane & 15;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int64_t m0 = (int64_t)rowblk * kPBM;
+  const int KG = p.K / G;
+  const int ntile = p.K / kPKT;
+
+  // segment bases are uniform over a 16-column tile (scalar registers); only
+  // the 32-bit row offsets live in vector registers
+  const uint16_t *bbase[4];
+  const uint32_t *qbase[4], *zbase[4];
+  int roff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    int seg, row;
+    bool valid;
+    map_col<EP>(p, colblk, kPBN, wn * 64 + t * 16 + cl, seg, row, valid);
+    if (!valid) row = 0;
+    seg = __builtin_amdgcn_readfirstlane(seg);
+    roff[t] = row;
+    if constexpr (Q4) {
+      qbase[t] = p.w.q4[seg];
+      zbase[t] = p.w.sz[seg];
+    } else {
+      bbase[t] = ex ? p.w.ex_bf[seg] : p.w.bf[seg];
+    }
+  }
+
+  // ---- rows: 128 x 128 bf16 per k-tile, 4 items of 16 B per thread
+  constexpr int AI = kPBM * kPKT / 8 / kPThreads;
+  uint4 av[AI];
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int idx = threadIdx.x + kPThreads * i;
+      const int r = idx >> 4, c8 = idx & 15;
+      av[i] = make_uint4(0, 0, 0, 0);
+      if (m0 + r < p.M)
+        av[i] = *reinterpret_cast<const uint4 *>(p.x + (m0 + r) * p.ldx + (int64_t)kt * kPKT + 8 * c8);
+    }
+  };
+  auto store_a = [&](int buf) {
+    uint16_t *dst = xs + buf * (kPBM * kPXS);
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int idx = threadIdx.x + kPThreads * i;
+      const int r = idx >> 4, c8 = idx & 15;
+      uint4 w = av[i];
+      if constexpr (Q4) {
+        float gs = ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
+                   ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
+        gs = G == 128 ? sum16(gs) : sum8(gs);    // the 16 items of a row are 16 adjacent lanes
+        if (c8 % (G / 8) == 0) xsg[(buf * kPBM + r) * GPT + c8 / (G / 8)] = gs;
+        w = int4_order(w.x, w.y, w.z, w.w);
+      }
+      *reinterpret_cast<uint4 *>(dst + r * kPXS + 8 * c8) = w;
+    }
+  };
+
+  // ---- weights: int4 one group per chunk, bf16 one k-step of 32 per chunk
+  constexpr int D = Q4 ? 2 : 4;
+  constexpr int CK = Q4 ? G : 32;              // k columns per chunk
+  WT wq[D][4];
+  uint32_t wz[D][4];
+  v4u wb[D][4];
+  auto load_w = [&](int c, int u) {
+    const int k0 = c * CK;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (Q4) {
+        wq[u][t] = __builtin_nontemporal_load(reinterpret_cast<const WT *>(
+            qbase[t] + (uint32_t)(roff[t] * (p.K / 8) + (k0 >> 3) + qq * GW)));
+        wz[u][t] = zbase[t][(uint32_t)(roff[t] * KG + k0 / G)];
+      } else {
+        wb[u][t] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u *>(bbase[t] + (uint32_t)(roff[t] * p.K + k0 + 8 * qq)));
+      }
+    }
+  };
+
+  const int nchunk = p.K / CK;
+  load_a(0);
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_w(min(u, nchunk - 1), u);
+  store_a(0);
+  __syncthreads();
+
+  auto compute = [&](int c, int u) {
+    const int k0 = c * CK;
+    const int buf = (k0 / kPKT) & 1;
+    const int kl = k0 % kPKT;
+    const uint16_t *xb = xs + buf * (kPBM * kPXS) + (wm * 32 + cl) * kPXS;
+    if constexpr (Q4) {
+      f32x4_t ag[2][4];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        bf16x8_t af[2], bfr[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          af[a] = *reinterpret_cast<const bf16x8_t *>(xb + a * 16 * kPXS + kl + qq * (G / 4) + 8 * j);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t w;
+          if constexpr (GW == 1) w = wq[u][t];
+          else w = wq[u][t][j];
+          uint32_t pr[4];
+          unpack_word(w, pr);
+          bfr[t] = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[t], ag[a][t], 0, 0, 0);
+      }
+      const int g = kl / G;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float sc = bf_lo(wz[u][t]), zo = 128.0f + bf_hi(wz[u][t]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * xsg[(buf * kPBM + wm * 32 + a * 16 + 4 * qq + v) * GPT + g],
+                                tot[a][t][v]);
+      }
+    } else {
+      bf16x8_t af[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const bf16x8_t *>(xb + a * 16 * kPXS + kl + 8 * qq);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], __builtin_bit_cast(bf16x8_t, wb[u][t]),
+                                                              tot[a][t], 0, 0, 0);
+    }
+  };
+
+  constexpr int CPT = kPKT / CK;                // chunks per k-tile
+  static_assert(CPT % D == 0 || D % CPT == 0, "ring and tile line up");
+  for (int kt = 0; kt < ntile; ++kt) {
+    if (kt + 1 < ntile) load_a(kt + 1);
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = kt * CPT + cc;
+      // the refill is unconditional (the last chunk again near the end) so that
+      // every path issues the same loads and the wait for the rows in store_a
+      // counts only the weight loads issued after them
+      const int nc = min(c + D, nchunk - 1);
+      if constexpr (CPT % D == 0) {
+        compute(c, cc % D);
+        load_w(nc, cc % D);
+      } else {
+        if ((c & 1) == 0) { compute(c, 0); load_w(nc, 0); }
+        else { compute(c, 1); load_w(nc, 1); }
+      }
+    }
+    if (kt + 1 < ntile) store_a((kt + 1) & 1);
+    __syncthreads();
+  }
+}
+
+template <int G, int EP>
+__global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
+  __shared__ __align__(16) uint16_t xs[2 * kPBM * kPXS];   // 69.6 KB; reused for the results
+  __shared__ float xsg[2 * kPBM * (kPKT / G)];
+  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
+  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+  // grouped order: kPGroupRows row blocks share the weights of each column block
+  const int per_group = kPGroupRows * ncolblk;
+  const int grp = blockIdx.x / per_group;
+  const int first = grp * kPGroupRows;
+  const int gm = min(nrowblk - first, kPGroupRows);
+  const int in_grp = blockIdx.x - grp * per_group;
+  const int rowblk = first + in_grp % gm, colblk = in_grp / gm;
+
+  f32x4_t tot[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (q4) pgemm_body<G, EP, true>(p, xs, xsg, ex, rowblk, colblk, tot);
+  else pgemm_body<G, EP, false>(p, xs, xsg, ex, rowblk, colblk, tot);
+
+  // results through LDS (the body ends with a barrier, so the row buffers,
+  // 128 x 129 floats of them, are free)
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, cl = lane & 15, wm = wid >> 1, wn = wid & 1;
+  float *Cs = reinterpret_cast<float *>(xs);
+  static_assert(kPBM * (kPBN + 1) * 4 <= 2 * kPBM * kPXS * 2, "the results fit the row buffers");
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        Cs[(wm * 32 + a * 16 + 4 * qq + v) * (kPBN + 1) + wn * 64 + t * 16 + cl] = tot[a][t][v];
+  __syncthreads();
+  tile_epilogue<EP, kPBN, kPThreads>(p, Cs, kPBN + 1, kPBM, (int64_t)rowblk * kPBM, colblk);
+}
+
+template <int G>
+static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s) {
+  const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
+  int nrowblk = (p.M + kPBM - 1) / kPBM, ncolblk = (ncols + kPBN - 1) / kPBN;
+  GemmParams q = p;
+  void *args[] = {&q, &nrowblk, &ncolblk};
+  const dim3 grid((unsigned)(nrowblk * ncolblk));
+  const void *fn;
+  switch (ep) {
+    case kEpQKV: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpQKV>); break;
+    case kEpSwiGLU: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpSwiGLU>); break;
+    case kEpResid: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpResid>); break;
+    case kEpPlain: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpPlain>); break;
+    default: return hipErrorInvalidValue;
+  }
+  return launch_kernel(fn, grid, dim3(kPThreads), args, 0, s);
+}
+
+hipError_t launch_pgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
+  if (p.K % kPKT || (p.G != 64 && p.G != 128)) return hipErrorInvalidValue;
+  return p.G == 64 ? pgemm_launch_g<64>(ep, p, s) : pgemm_launch_g<128>(ep, p, s);
 }
 
 }  // namespace river

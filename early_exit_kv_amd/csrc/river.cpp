@@ -162,6 +162,7 @@ struct river_ctx {
   // activation record (off when rec == nullptr)
   char *rec = nullptr;
   size_t rec_bytes = 0;
+  int attn_chunk = 0;   // positions per decode-attention workgroup (0: chosen per shape)
 };
 
 namespace {
@@ -289,6 +290,13 @@ struct Recorder {
   }
 };
 
+// Prefill GEMMs: the 128 x 128 tile kernel where its shape rules hold, the
+// 64 x 64 one otherwise.
+hipError_t launch_prefill_gemm(Epilogue ep, const GemmParams &g, hipStream_t s) {
+  if (g.K % 128 == 0 && (g.G == 64 || g.G == 128)) return launch_pgemm(ep, g, s);
+  return launch_gemm(ep, g, s);
+}
+
 // Common parameters of the batched-row GEMM launches of layer l.
 GemmParams mgemm_base(river_ctx *ctx, int l, int M) {
   const river_config &c = ctx->cfg;
@@ -299,6 +307,7 @@ GemmParams mgemm_base(river_ctx *ctx, int l, int M) {
   g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
   g.part = at<float>(ctx->ws, ctx->wl.mg_part);
   g.part_cap = ctx->wl.mg_part_floats;
+  if (ctx->force_E >= 0 && l >= 0) g.path = l >= ctx->force_E ? kPathExit : kPathBackbone;
   return g;
 }
 
@@ -357,7 +366,7 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     a.out = at<uint16_t>(ctx->ws, ctx->wl.attn); a.part = at<float>(ctx->ws, ctx->wl.attn_part);
     a.counters = control_attn_counters(ctx->ctrl, c.max_batch); a.ctrl = ctx->ctrl;
     a.B = B; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.Dh = c.head_dim; a.S = c.max_seq;
-    a.chunk = attn_chunk(c.max_seq, B, c.n_kv_heads);
+    a.chunk = ctx->attn_chunk > 0 ? ctx->attn_chunk : attn_chunk(c.max_seq, B, c.n_kv_heads);
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
@@ -428,6 +437,9 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     g.max_seq = c.max_seq; g.max_batch = c.max_batch; g.rope_theta = c.rope_theta;
     g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
     g.n_layers = c.n_layers;
+    // a forced exit layer fixes every weight choice on the host: no kernel
+    // then waits for the device flag before streaming its weights
+    if (ctx->force_E >= 0) g.path = l >= ctx->force_E ? kPathExit : kPathBackbone;
 
     // attention RMSNorm + fused q|k|v + RoPE + write into the shared slot
     GemvParams q = g;
@@ -447,7 +459,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     a.out = at<uint16_t>(ctx->ws, ctx->wl.attn); a.part = at<float>(ctx->ws, ctx->wl.attn_part);
     a.counters = control_attn_counters(ctx->ctrl, c.max_batch); a.ctrl = ctx->ctrl;
     a.B = B; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.Dh = c.head_dim; a.S = c.max_seq;
-    a.chunk = attn_chunk(c.max_seq, B, c.n_kv_heads);
+    a.chunk = ctx->attn_chunk > 0 ? ctx->attn_chunk : attn_chunk(c.max_seq, B, c.n_kv_heads);
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
@@ -514,6 +526,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim; g.max_seq = c.max_seq;
     g.max_batch = c.max_batch; g.T = T; g.rope_theta = c.rope_theta;
     g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
+    if (ctx->force_E >= 0) g.path = l >= ctx->force_E ? kPathExit : kPathBackbone;
 
     RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
     RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), R, c.d_model, c.rms_eps};
@@ -524,7 +537,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     q.N = qd + 2 * c.n_kv_heads * c.head_dim; q.K = c.d_model; q.x = x; q.ldx = c.d_model;
     q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q);
     q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
-    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpQKV, q, s));
+    TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpQKV, q, s));
     RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
 
     AttnPrefillParams ap{};
@@ -539,7 +552,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x = ap.out; o.ldx = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
-    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpResid, o, s));
+    TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, o, s));
     RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
     RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), R, c.d_model, c.rms_eps};
@@ -549,14 +562,14 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     fill_weights(ctx, l, 4, 2, gu.w);
     gu.N = 2 * c.ffn_dim; gu.K = c.d_model; gu.x = x; gu.ldx = c.d_model;
     gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u);
-    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpSwiGLU, gu, s));
+    TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpSwiGLU, gu, s));
     RV_TRY(rec.put(l, rec.lay.u, gu.u_out, (size_t)R * c.ffn_dim * 2));
 
     GemmParams dn = g;
     fill_weights(ctx, l, 6, 1, dn.w);
     dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
     dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
-    TIMED(RIVER_K_P_GEMM, launch_gemm(kEpResid, dn, s));
+    TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, dn, s));
 
     if (l < c.n_layers - 1 && ctx->force_E < 0) {
       RowsCosParams rc{hA, hB, R, c.d_model, at<float>(ctx->ws, ctx->wl.part), ctx->ctrl, l,
@@ -798,6 +811,13 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
       if (value < -1 || value > ctx->cfg.n_layers) return RIVER_E_RANGE;
       ctx->force_E = (int)value;
       return RIVER_OK;
+    case RIVER_OPT_ATTN_CHUNK:
+      if (value != 0 && (value < kAttnSub || value % kAttnSub ||
+                         (ctx->cfg.max_seq + value - 1) / value > kMaxAttnSplits))
+        return RIVER_E_INVALID_ARG;
+      ctx->attn_chunk = (int)value;
+      drop_graphs(ctx);
+      return RIVER_OK;
     case RIVER_OPT_PROFILE:
       if (value != 0 && value != 1) return RIVER_E_INVALID_ARG;
       if (!value) drop_events(ctx);
@@ -915,7 +935,7 @@ int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t us
     if (M <= 64 && ctx->cfg.max_batch > 8)
       RV_TRY(launch_mgemm(kEpPlain, g, ctx->stream));    // the decode core of 9..64 rows
     else
-      RV_TRY(launch_gemm(kEpPlain, g, ctx->stream));     // the prefill core
+      RV_TRY(launch_prefill_gemm(kEpPlain, g, ctx->stream));   // the prefill core
   }
   return RIVER_OK;
 }

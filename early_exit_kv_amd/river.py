@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libriver.so")
 RIVER_OK, RIVER_E_INVALID_ARG, RIVER_E_BAD_SIZE, RIVER_E_STATE = 0, 1, 2, 3
 RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
 RIVER_EXIT_INT4, RIVER_EXIT_COPY = 1, 2
-RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE = 1, 2, 3
+RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK = 1, 2, 3, 4
 KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
                 "p_norm", "p_gemm", "p_attn", "p_cos")
 RIVER_MAX_LAYERS = 256

@@ -182,8 +182,11 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *   RIVER_OPT_FORCE_E -1 (default) to decide with tau, or e in 0..n_layers to
  *                     run layers < e on the backbone and the rest as exit
  *                     layers without testing (e = n_layers: original model,
- *                     e = 0: every layer quantised). */
-enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3 };
+ *                     e = 0: every layer quantised);
+ *   RIVER_OPT_ATTN_CHUNK positions per decode-attention workgroup: 0 (default)
+ *                     lets the library choose per shape, else a multiple of
+ *                     64 giving at most 512 splits of max_seq. */
+enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
 
 /* Kernel classes timed when RIVER_OPT_PROFILE is 1 (decode steps then launch

@@ -56,7 +56,7 @@ def ctx8b_rows():
     r.close()
 
 
-@pytest.mark.parametrize("M", [1, 8, 40])
+@pytest.mark.parametrize("M", [1, 8, 40, 300])
 @pytest.mark.parametrize("use_exit", [0, 1])
 def test_linear_cores_8b(ctx8b, M, use_exit):
     check_linears(ctx8b, M, use_exit)
