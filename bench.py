@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch decode steps without HIP graphs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB three times (a plain "
@@ -221,6 +222,31 @@ def main():
     avg_step_bytes = sum(n * step_bytes(shape, B, e, sum(positions) / K) for e, n in enumerate(hist)) / K
     step_gbs = avg_step_bytes / (elapsed / K) / 1e9
 
+    # the same decode steps with the decision fixed: E = L is the original
+    # model (every layer on its backbone), E = 0 the statically quantised one
+    # (every layer on its int4 copy); the pages report River against both
+    baselines = None
+    if not args.no_baselines:
+        baselines = {}
+        for name, e in (("original", shape.n_layers), ("full_int4", 0)):
+            r.force_exit_layer(e)
+            r.reset()
+            _, nxt_b = r.prefill(tokens, tau, want_logits=False)
+            bufs[0].copy_(nxt_b)
+            run(W, 0)                      # same positions as the timed River steps
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run(K, W)
+            torch.cuda.synchronize()
+            baselines[name] = round(B * K / (time.perf_counter() - t0), 2)
+        r.force_exit_layer(-1)
+        r.reset()
+        _, nxt_b = r.prefill(tokens, tau, want_logits=False)
+        bufs[0].copy_(nxt_b)
+        run(W + K, 0)                      # back to the state the profiling below expects
+        baselines["river_vs_original"] = round(tok_s / baselines["original"], 3)
+        baselines["river_vs_full_int4"] = round(tok_s / baselines["full_int4"], 3)
+
     roofline = None
     kinds = {}
     if not args.no_profile:
@@ -305,6 +331,7 @@ def main():
         "mean_exit_layer": round(mean_E, 3), "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
         "prefill_tok_s": round(B * T / prefill_s, 1), "prefill_E": prefill_E,
         "build_exit_layers_s": round(build_s, 4), "kernels": kinds, "prefill_exit_gemm": prefill_gemm,
+        "baselines_tok_s": baselines,
     }
     r.close()
     print(json.dumps(out))

@@ -477,18 +477,12 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
         csum = (bf_lo(a0) + bf_hi(a0)) + (bf_lo(a1) + bf_hi(a1)) + (bf_lo(a2) + bf_hi(a2)) +
                (bf_lo(a3) + bf_hi(a3));
       }
-      uint4 o;
-      if (q4) {  // column pairs (0,2) (4,6) (1,3) (5,7), as unpack_word makes them
-        o.x = (a0 & 0xFFFFu) | (a1 << 16);
-        o.y = (a2 & 0xFFFFu) | (a3 << 16);
-        o.z = (a0 >> 16) | (a1 & 0xFFFF0000u);
-        o.w = (a2 >> 16) | (a3 & 0xFFFF0000u);
+      const uint4 o = make_uint4(a0, a1, a2, a3);
+      if (q4) {
         // the four items of a 32-column chunk sit in four adjacent lanes
         csum += dpp<kDppXor1>(csum);
         csum += dpp<kDppXor2>(csum);
         if ((g8 & 3) == 0) xs[b * (kslab >> 5) + (g8 >> 2)] = csum;
-      } else {
-        o = make_uint4(a0, a1, a2, a3);
       }
       *reinterpret_cast<uint4 *>(xl + b * half + 4 * g8) = o;
     }

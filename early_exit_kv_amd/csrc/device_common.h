@@ -150,21 +150,16 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t total, i
   return *smem_flag != 0;
 }
 
-// int4 codes of one 32-bit word (column 8w+j in bits 4j..4j+3) as the four
-// bf16 pairs (128+q_a, 128+q_b) for the column pairs (0,2) (4,6) (1,3) (5,7)
+// int4 codes of one 32-bit word (byte i: column i in the low nibble, column
+// i+4 in the high nibble) as the four bf16 pairs (128+q_a, 128+q_b) of the
+// columns (0,1) (2,3) (4,5) (6,7): the byte permute places each code under a
+// 0x43 byte, and 0x43nn is the bf16 value 128 + nn for nn < 16
 __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&pr)[4]) {
   const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
   pr[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x05010400u);
   pr[1] = __builtin_amdgcn_perm(0x43434343u, lo, 0x05030402u);
   pr[2] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05010400u);
   pr[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05030402u);
-}
-
-// x[8g..8g+7] as bf16 pairs in the same column order: (0,2) (4,6) (1,3) (5,7)
-// (a0..a3 hold the natural pairs (0,1) (2,3) (4,5) (6,7)).
-__device__ __forceinline__ uint4 int4_order(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
-  return make_uint4((a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16),
-                    (a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u));
 }
 
 // Exit choice of a layer, read at the start of every kernel of that layer.

@@ -276,16 +276,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         uint4 cw = bvalid ? *reinterpret_cast<const uint4 *>(qrow + (k0 >> 3))
                           : make_uint4(0, 0, 0, 0);
         const uint32_t wd[4] = {cw.x, cw.y, cw.z, cw.w};
-        // word i covers columns 8i..8i+7; column 8i+j sits in bits 4j..4j+3
+        // word i covers columns 8i..8i+7 (bf16 128+q in column order)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t o[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t c0 = (wd[i] >> (8 * jj)) & 0xF;
-            const uint32_t c1 = (wd[i] >> (8 * jj + 4)) & 0xF;
-            o[jj] = (0x4300u | c0) | ((0x4300u | c1) << 16);
-          }
+          unpack_word(wd[i], o);
           *reinterpret_cast<uint4 *>(&Bs[tid][i * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
         if (st % steps_per_group == 0) szs[tid] = bvalid ? zrow[k0 / p.G] : 0u;
@@ -476,12 +471,12 @@ hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
 // Batched-row GEMM for 9..64 rows: Y[m][n] = sum_k X[m][k] W[n][k].
 //   A workgroup (4 wavefronts x 2 column tiles of 16 = 128 columns) takes one
 //   split of K.  Every lane loads the weights of its own output column straight
-//   from HBM into MFMA B operands, two quantisation groups ahead of use; the
-//   rows X sit in LDS, one K slab at a time.  K is walked one group (G columns)
-//   at a time.  int4: lane quarter qq holds the G/4 codes k0 + qq*G/4 ..; the
-//   rows are staged in the same order (within 8 columns: 0 2 4 6 1 3 5 7, the
-//   order the byte permute unpacks codes in), so every MFMA sums inside one
-//   group, which is then folded as  tot += s * (acc - (128 + z) * sum_k x).
+//   from HBM into MFMA B operands, several quantisation groups ahead of use;
+//   the rows X of the whole split sit in LDS.  K is walked one group (G
+//   columns) at a time.  int4: lane quarter qq holds the G/4 codes
+//   k0 + qq*G/4 .. (unpacked in column order by the byte permute), so every
+//   MFMA sums inside one group, which is then folded as
+//   tot += s * (acc - (128 + z) * sum_k x).
 //   bf16 weights use the plain order (quarter qq holds k0 + 32j + 8qq .. +8).
 //   With several K splits each workgroup stores its partial tile and a second
 //   kernel (one workgroup per column block) adds the splits in order and runs
@@ -642,7 +637,6 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
                        ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
             gs = G == 128 ? sum16(gs) : sum8(gs);
             if (g8 % (G / 8) == 0) L.xsg[m * (KS / G) + g8 / (G / 8)] = gs;
-            w = int4_order(w.x, w.y, w.z, w.w);
           }
           *reinterpret_cast<uint4 *>(L.xs + m * XS + 8 * g8) = w;
         }
@@ -901,7 +895,7 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 // registers while the current one feeds the MFMAs); the weights go from memory
 // straight into B operands, every lane loading its own column, with the same
 // int4 conventions as the batched-row GEMM (per-group accumulation, lane
-// quarters over G/4 codes, rows staged in the matching column order, group
+// quarters over G/4 codes, group
 // fold tot += s * (acc - (128 + z) * sum_k x)).  Workgroups are ordered in
 // groups of 8 row blocks so that the rows and weights they share stay in L2.
 // ===========================================================================
@@ -967,7 +961,6 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, fl
                    ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
         gs = G == 128 ? sum16(gs) : sum8(gs);    // the 16 items of a row are 16 adjacent lanes
         if (c8 % (G / 8) == 0) xsg[(buf * kPBM + r) * GPT + c8 / (G / 8)] = gs;
-        w = int4_order(w.x, w.y, w.z, w.w);
       }
       *reinterpret_cast<uint4 *>(dst + r * kPXS + 8 * c8) = w;
     }

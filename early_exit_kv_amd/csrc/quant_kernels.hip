@@ -8,7 +8,10 @@
 // bit for bit:
 //   s = bf16((hi - lo) / 15), s = 1 if that is 0;  z = bf16(-lo / s);
 //   code = clamp(round_half_even(w / s + z), 0, 15).
-// One thread packs one 32-bit word (8 columns); the G/8 threads of a group sit
+// One thread packs one 32-bit word (8 columns: byte i holds column i in its
+// low nibble and column i+4 in its high nibble, so that a byte permute turns
+// the word into the bf16 pairs of columns (0,1) (2,3) (4,5) (6,7) in order);
+// the G/8 threads of a group sit
 // in adjacent lanes and find the group's min and max with lane shuffles.
 #include "device_common.h"
 
@@ -46,7 +49,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
   for (int j = 0; j < 8; ++j) {
     float q = rintf(__fadd_rn(__fdiv_rn(v[j], s), z));
     q = fminf(fmaxf(q, 0.0f), 15.0f);
-    word |= (uint32_t)q << (4 * j);   // column 8w+j in bits 4j..4j+3
+    // byte i of the word: column 8w+i in the low nibble, column 8w+i+4 in the high one
+    word |= (uint32_t)q << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
   }
   codes[i] = word;
   const int64_t row = i / KW;

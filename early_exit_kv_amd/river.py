@@ -392,8 +392,9 @@ def unpack_int4(words, sz, group):
     w = np.asarray(words, dtype=np.int64) & 0xFFFFFFFF
     N, KW = w.shape
     codes = np.empty((N, KW * 8), dtype=np.uint8)
-    for j in range(8):
-        codes[:, j::8] = ((w >> (4 * j)) & 0xF).astype(np.uint8)
+    for j in range(8):   # byte i: column i low nibble, column i + 4 high nibble
+        shift = 8 * j if j < 4 else 8 * (j - 4) + 4
+        codes[:, j::8] = ((w >> shift) & 0xF).astype(np.uint8)
     z32 = np.asarray(sz, dtype=np.int64) & 0xFFFFFFFF
     s = ((z32 & 0xFFFF).astype(np.uint32) << 16).view(np.float32)
     z = ((z32 >> 16).astype(np.uint32) << 16).view(np.float32)

@@ -126,7 +126,8 @@ int river_query_sizes(const river_config *cfg, river_sizes *out);
  * linear: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down.
  * Packed int4 layout of a linear with N rows and K columns:
  *   codes: uint32 [N][K/8]; word w of row n holds the codes of columns
- *          8w..8w+7, column 8w+j in bits 4j..4j+3;
+ *          8w..8w+7: byte i holds column 8w+i in its low nibble and column
+ *          8w+i+4 in its high nibble;
  *   sz:    uint32 [N][K/G]; bf16 scale in bits 0..15, bf16 zero in 16..31;
  *   w_hat = (code - zero) * scale.
  * In RIVER_EXIT_COPY mode the bank holds bf16 [N][K] copies instead, each

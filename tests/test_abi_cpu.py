@@ -183,12 +183,12 @@ def test_product_path_has_no_cpu_fallback(monkeypatch):
 
 def test_unpack_int4_layout():
     import numpy as np
-    # column 8w+j sits in bits 4j..4j+3 of word w
+    # byte i of word w: column 8w+i in the low nibble, column 8w+i+4 in the high one
     codes = (np.arange(16, dtype=np.uint8).reshape(1, 16) * 7) % 16
     words = np.zeros((1, 2), dtype=np.int64)
     for c in range(16):
         w, j = divmod(c, 8)
-        words[0, w] |= int(codes[0, c]) << (4 * j)
+        words[0, w] |= int(codes[0, c]) << (8 * (j % 4) + 4 * (j // 4))
     sz = np.array([[(0x3F80 | (0x40A0 << 16))]], dtype=np.int64)  # s = 1.0, z = 5.0
     got, s, z = rv.unpack_int4(words, sz, 16)
     assert np.array_equal(got, codes) and s[0, 0] == 1.0 and z[0, 0] == 5.0
