@@ -890,21 +890,30 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 // v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 x 128, eight wavefronts in a
 // 4 x 2 arrangement, each 32 x 64 (2 x 4 MFMA tiles: every row fragment read
 // from LDS feeds four MFMAs, which keeps LDS at half its bandwidth); two
-// wavefronts per SIMD so that one's waits overlap the other's MFMAs.  The rows X go through LDS in
-// k-tiles of 128 columns, double buffered (the next tile is loaded into
-// registers while the current one feeds the MFMAs); the weights go from memory
-// straight into B operands, every lane loading its own column, with the same
-// int4 conventions as the batched-row GEMM (per-group accumulation, lane
-// quarters over G/4 codes, group
-// fold tot += s * (acc - (128 + z) * sum_k x)).  Workgroups are ordered in
-// groups of 8 row blocks so that the rows and weights they share stay in L2.
+// wavefronts per SIMD so that one's waits overlap the other's MFMAs.
+//   Rows X: k-tiles of 128 columns copied straight from memory into LDS
+//   (global_load_lds, no registers), four buffers, so three tiles are in
+//   flight while one feeds the MFMAs; 16-byte chunks are XOR-swizzled within a
+//   row (chunk c of row r at slot c ^ (r mod 16)) so that the 16 rows one
+//   fragment read touches fall in distinct banks.
+//   Weights: from memory straight into B operands, every lane loading its own
+//   column several groups ahead, with the same int4 conventions as the
+//   batched-row GEMM (per-group accumulation, lane quarters over G/4 codes,
+//   group fold tot += s * (acc - (128 + z) * sum_k x), the row sums of each
+//   group taken from the LDS tile).
+//   Workgroups are ordered in groups of 8 row blocks so that the rows and
+//   weights they share stay in L2.
 // ===========================================================================
-constexpr int kPBM = 128, kPBN = 128, kPKT = 128, kPXS = kPKT + 8, kPGroupRows = 8;
-constexpr int kPThreads = 512;
+constexpr int kPBM = 128, kPBN = 128, kPKT = 128, kPGroupRows = 8;
+constexpr int kPThreads = 512, kPBufs = 3;
+constexpr int kPTileSlots = kPBM * kPKT / 8;      // 16-byte slots of rows per k-tile (2048)
+constexpr int kPCodeSlots = kPBN * kPKT / 32;     // 16-byte slots of int4 codes per k-tile (512)
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 template <int G, int EP, bool Q4>
-__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, float *xsg, bool ex,
-                                           int rowblk, int colblk, f32x4_t (&tot)[2][4]) {
+__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs, float *xsg,
+                                           bool ex, int rowblk, int colblk, f32x4_t (&tot)[2][4]) {
   constexpr int STEPS = G / 32, GW = G / 32;
   constexpr int GPT = kPKT / G;                 // groups per k-tile
   typedef typename WordsT<GW>::T WT;
@@ -936,49 +945,75 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, fl
     }
   }
 
-  // ---- rows: 128 x 128 bf16 per k-tile, 4 items of 16 B per thread
-  constexpr int AI = kPBM * kPKT / 8 / kPThreads;
-  uint4 av[AI];
-  auto load_a = [&](int kt) {
+  // ---- int4 codes of a k-tile: 128 columns x 64 bytes, one 16-byte slot
+  //      per lane of every wavefront; column c's chunk q sits at slot
+  //      4c + (q ^ ((c >> 2) & 3)), so the 16 columns one B-fragment read
+  //      touches fall in distinct banks
+  const uint32_t *crow = nullptr;
+  if constexpr (Q4) {
+    const int slot = wid * 64 + lane;
+    const int c = slot >> 2, q = (slot & 3) ^ ((c >> 2) & 3);
+    int seg, row;
+    bool valid;
+    map_col<EP>(p, colblk, kPBN, c, seg, row, valid);
+    if (!valid) { seg = 0; row = 0; }
+    crow = p.w.q4[seg] + (int64_t)row * (p.K / 8) + 4 * q;
+  }
+
+  // ---- rows: each wavefront copies 4 x 64 slots of a k-tile into LDS
+  const uint16_t *arow[4];
+  int acol[4];
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int idx = threadIdx.x + kPThreads * i;
-      const int r = idx >> 4, c8 = idx & 15;
-      av[i] = make_uint4(0, 0, 0, 0);
-      if (m0 + r < p.M)
-        av[i] = *reinterpret_cast<const uint4 *>(p.x + (m0 + r) * p.ldx + (int64_t)kt * kPKT + 8 * c8);
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (wid * 4 + i) * 64 + lane;
+    const int r = slot >> 4, sc = slot & 15;
+    const int64_t m = min(m0 + r, (int64_t)p.M - 1);      // rows past M: any valid row
+    arow[i] = p.x + m * p.ldx;
+    acol[i] = 8 * (sc ^ (r & 15));
+  }
+  // The copies are issued from inline assembly: the compiler then does not
+  // treat every later LDS read as possibly overlapping them (it would wait for
+  // all memory operations before each one); the loop waits for exactly the
+  // copies it needs with an explicit s_waitcnt.  m0 holds the LDS destination
+  // of a copy (each lane writes 16 bytes at m0 + 16 * lane).
+  const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_ptr_t)xs;
+  const int uwid = __builtin_amdgcn_readfirstlane(wid);
+  const uint32_t cs_base = (uint32_t)(uintptr_t)(lds_ptr_t)cs;
+  auto load_a = [&](int kt) {
+    const int ktc = min(kt, ntile - 1);                    // unconditional: fixed load count
+    const uint32_t buf = xs_base + (uint32_t)((kt % kPBufs) * kPTileSlots * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(buf + (uint32_t)((uwid * 4 + i) * 64 * 16));
+      const uint16_t *src = arow[i] + ktc * kPKT + acol[i];
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                   : "memory", "m0");
+    }
+    if constexpr (Q4) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          cs_base + (uint32_t)(((kt % kPBufs) * kPCodeSlots + uwid * 64) * 16));
+      const uint32_t *src = crow + ktc * (kPKT / 8);
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                   : "memory", "m0");
     }
   };
-  auto store_a = [&](int buf) {
-    uint16_t *dst = xs + buf * (kPBM * kPXS);
-#pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int idx = threadIdx.x + kPThreads * i;
-      const int r = idx >> 4, c8 = idx & 15;
-      uint4 w = av[i];
-      if constexpr (Q4) {
-        float gs = ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
-                   ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
-        gs = G == 128 ? sum16(gs) : sum8(gs);    // the 16 items of a row are 16 adjacent lanes
-        if (c8 % (G / 8) == 0) xsg[(buf * kPBM + r) * GPT + c8 / (G / 8)] = gs;
-      }
-      *reinterpret_cast<uint4 *>(dst + r * kPXS + 8 * c8) = w;
-    }
+  auto a_frag = [&](const uint4 *buf, int r, int k) -> bf16x8_t {
+    const int c = k >> 3;
+    return __builtin_bit_cast(bf16x8_t, buf[r * 16 + (c ^ (r & 15))]);
   };
 
-  // ---- weights: int4 one group per chunk, bf16 one k-step of 32 per chunk
-  constexpr int D = Q4 ? 2 : 4;
+  // ---- weights: int4 codes come through LDS with the rows (only scale/zero
+  //      words per group here); bf16 one k-step of 32 per chunk
+  constexpr int D = Q4 ? 2 : 8;
   constexpr int CK = Q4 ? G : 32;              // k columns per chunk
-  WT wq[D][4];
   uint32_t wz[D][4];
   v4u wb[D][4];
+  const int nchunk = p.K / CK;
   auto load_w = [&](int c, int u) {
-    const int k0 = c * CK;
+    const int k0 = min(c, nchunk - 1) * CK;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (Q4) {
-        wq[u][t] = __builtin_nontemporal_load(reinterpret_cast<const WT *>(
-            qbase[t] + (uint32_t)(roff[t] * (p.K / 8) + (k0 >> 3) + qq * GW)));
         wz[u][t] = zbase[t][(uint32_t)(roff[t] * KG + k0 / G)];
       } else {
         wb[u][t] = __builtin_nontemporal_load(
@@ -987,19 +1022,22 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, fl
     }
   };
 
-  const int nchunk = p.K / CK;
-  load_a(0);
-#pragma unroll
-  for (int u = 0; u < D; ++u) load_w(min(u, nchunk - 1), u);
-  store_a(0);
-  __syncthreads();
-
   auto compute = [&](int c, int u) {
     const int k0 = c * CK;
-    const int buf = (k0 / kPKT) & 1;
+    const uint4 *buf = xs + ((k0 / kPKT) % kPBufs) * kPTileSlots;
     const int kl = k0 % kPKT;
-    const uint16_t *xb = xs + buf * (kPBM * kPXS) + (wm * 32 + cl) * kPXS;
+    const int r0 = wm * 32 + cl;
     if constexpr (Q4) {
+      // this lane's GW code words of the group, for each of its 4 column tiles
+      const uint32_t *cb = reinterpret_cast<const uint32_t *>(cs + ((k0 / kPKT) % kPBufs) * kPCodeSlots);
+      const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
+      WT wq[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int col = wn * 64 + t * 16 + cl;
+        const int slot = col * 4 + ((wo >> 2) ^ ((col >> 2) & 3));
+        wq[t] = *reinterpret_cast<const WT *>(cb + slot * 4 + (wo & 3));
+      }
       f32x4_t ag[2][4];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -1009,13 +1047,12 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, fl
       for (int j = 0; j < STEPS; ++j) {
         bf16x8_t af[2], bfr[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          af[a] = *reinterpret_cast<const bf16x8_t *>(xb + a * 16 * kPXS + kl + qq * (G / 4) + 8 * j);
+        for (int a = 0; a < 2; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + qq * (G / 4) + 8 * j);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           uint32_t w;
-          if constexpr (GW == 1) w = wq[u][t];
-          else w = wq[u][t][j];
+          if constexpr (GW == 1) w = wq[t];
+          else w = wq[t][j];
           uint32_t pr[4];
           unpack_word(w, pr);
           bfr[t] = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
@@ -1034,14 +1071,13 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, fl
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * xsg[(buf * kPBM + wm * 32 + a * 16 + 4 * qq + v) * GPT + g],
+            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * xsg[(wm * 32 + a * 16 + 4 * qq + v) * GPT + g],
                                 tot[a][t][v]);
       }
     } else {
       bf16x8_t af[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = *reinterpret_cast<const bf16x8_t *>(xb + a * 16 * kPXS + kl + 8 * qq);
+      for (int a = 0; a < 2; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + 8 * qq);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -1051,34 +1087,74 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint16_t *xs, fl
     }
   };
 
-  constexpr int CPT = kPKT / CK;                // chunks per k-tile
-  static_assert(CPT % D == 0 || D % CPT == 0, "ring and tile line up");
-  for (int kt = 0; kt < ntile; ++kt) {
-    if (kt + 1 < ntile) load_a(kt + 1);
+  // group sums of the rows of one landed k-tile (int4 fold): 4 threads per
+  // row, 32 columns each, reduced over the 4 (G=128) or 2 (G=64) lanes
+  auto row_sums = [&](int kt) {
+    const uint4 *buf = xs + (kt % kPBufs) * kPTileSlots;
+    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+    float sacc = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int c = kt * CPT + cc;
-      // the refill is unconditional (the last chunk again near the end) so that
-      // every path issues the same loads and the wait for the rows in store_a
-      // counts only the weight loads issued after them
-      const int nc = min(c + D, nchunk - 1);
-      if constexpr (CPT % D == 0) {
-        compute(c, cc % D);
-        load_w(nc, cc % D);
-      } else {
-        if ((c & 1) == 0) { compute(c, 0); load_w(nc, 0); }
-        else { compute(c, 1); load_w(nc, 1); }
+    for (int i = 0; i < 4; ++i) {
+      const int c = part * 4 + i;
+      const uint4 w = buf[r * 16 + (c ^ (r & 15))];
+      sacc += ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
+              ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
+    }
+    sacc += dpp<kDppXor1>(sacc);
+    if (G == 128) sacc += dpp<kDppXor2>(sacc);
+    if (G == 128 ? part == 0 : (part & 1) == 0) xsg[r * GPT + (G == 128 ? 0 : part >> 1)] = sacc;
+  };
+
+  constexpr int CPT = kPKT / CK;                // chunks per k-tile
+  static_assert(D % CPT == 0, "the ring holds whole k-tiles");
+  constexpr int UT = D / CPT;                   // k-tiles per pass of the ring
+#pragma unroll
+  for (int t = 0; t < kPBufs - 1; ++t) load_a(t);
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_w(u, u);
+  for (int kt0 = 0; kt0 < ntile; kt0 += UT) {
+#pragma unroll
+    for (int ti = 0; ti < UT; ++ti) {
+      const int kt = kt0 + ti;              // ntile is a multiple of UT (checked at launch)
+      {
+        // tile kt has landed once no more than `later` vector-memory operations
+        // are outstanding: after its 4 copies came those of the next 2 k-tiles
+        // and at least min(the first D refills, 3 k-tiles of refills) weight
+        // loads (every load is unconditional, so the count holds throughout)
+        // (a k-tile is 4 copies of rows, plus 1 of codes for int4; a weight
+        // refill is 4 loads per chunk)
+        constexpr int per_tile = Q4 ? 5 : 4;
+        constexpr int ring = (kPBufs - 1) * CPT;
+        constexpr int later = (kPBufs - 2) * per_tile + (D < ring ? D : ring) * 4;
+        static_assert(later < 64, "vmcnt field");
+        // s_waitcnt: vmcnt = later, expcnt and lgkmcnt not waited for
+        __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
+        __syncthreads();                        // tile kt visible; tile kt-1 done everywhere
+        load_a(kt + kPBufs - 1);                // into the buffer tile kt-1 used
+        if constexpr (Q4) {
+          row_sums(kt);
+          __syncthreads();
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          const int c = kt * CPT + cc;
+          compute(c, ti * CPT + cc);            // ring slot known at compile time
+          load_w(c + D, ti * CPT + cc);
+        }
       }
     }
-    if (kt + 1 < ntile) store_a((kt + 1) & 1);
-    __syncthreads();
   }
+  // the last k-tiles' spare copies may still be landing in LDS, which the
+  // results reuse: wait for every memory operation, then for every wavefront
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 template <int G, int EP>
 __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
-  __shared__ __align__(16) uint16_t xs[2 * kPBM * kPXS];   // 69.6 KB; reused for the results
-  __shared__ float xsg[2 * kPBM * (kPKT / G)];
+  __shared__ __align__(16) uint4 xs[kPBufs * kPTileSlots];   // 96 KB; reused for the results
+  __shared__ __align__(16) uint4 cs[kPBufs * kPCodeSlots];   // 24 KB of int4 codes
+  __shared__ float xsg[kPBM * (kPKT / G)];
   const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
   // grouped order: kPGroupRows row blocks share the weights of each column block
@@ -1094,15 +1170,14 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true>(p, xs, xsg, ex, rowblk, colblk, tot);
-  else pgemm_body<G, EP, false>(p, xs, xsg, ex, rowblk, colblk, tot);
+  if (q4) pgemm_body<G, EP, true>(p, xs, cs, xsg, ex, rowblk, colblk, tot);
+  else pgemm_body<G, EP, false>(p, xs, cs, xsg, ex, rowblk, colblk, tot);
 
-  // results through LDS (the body ends with a barrier, so the row buffers,
-  // 128 x 129 floats of them, are free)
+  // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15, wm = wid >> 1, wn = wid & 1;
   float *Cs = reinterpret_cast<float *>(xs);
-  static_assert(kPBM * (kPBN + 1) * 4 <= 2 * kPBM * kPXS * 2, "the results fit the row buffers");
+  static_assert(kPBM * (kPBN + 1) * 4 <= kPBufs * kPTileSlots * 16, "the results fit the row buffers");
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -1132,8 +1207,13 @@ static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s
   return launch_kernel(fn, grid, dim3(kPThreads), args, 0, s);
 }
 
+bool pgemm_fits(int K, int G) {
+  // K in whole passes of the weight ring (2 k-tiles)
+  return (G == 64 || G == 128) && K % (2 * kPKT) == 0;
+}
+
 hipError_t launch_pgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
-  if (p.K % kPKT || (p.G != 64 && p.G != 128)) return hipErrorInvalidValue;
+  if (!pgemm_fits(p.K, p.G)) return hipErrorInvalidValue;
   return p.G == 64 ? pgemm_launch_g<64>(ep, p, s) : pgemm_launch_g<128>(ep, p, s);
 }
 

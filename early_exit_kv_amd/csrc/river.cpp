@@ -293,7 +293,7 @@ struct Recorder {
 // Prefill GEMMs: the 128 x 128 tile kernel where its shape rules hold, the
 // 64 x 64 one otherwise.
 hipError_t launch_prefill_gemm(Epilogue ep, const GemmParams &g, hipStream_t s) {
-  if (g.K % 128 == 0 && (g.G == 64 || g.G == 128)) return launch_pgemm(ep, g, s);
+  if (pgemm_fits(g.K, g.G)) return launch_pgemm(ep, g, s);
   return launch_gemm(ep, g, s);
 }
 

@@ -233,7 +233,8 @@ MgemmPlan mgemm_plan(int M, int ncols, int K);
 int64_t mgemm_part_floats(const MgemmPlan &pl);
 hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s);
-// Prefill GEMM for many rows (128 x 128 tiles, K a multiple of 128, G 64 or 128).
+// Prefill GEMM for many rows (128 x 128 tiles; shapes where pgemm_fits holds).
+bool pgemm_fits(int K, int G);
 hipError_t launch_pgemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 
 struct AttnPrefillParams {
