@@ -99,6 +99,9 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
 // ===========================================================================
 constexpr int kXLdsBytes = 64 * 1024;
 
+// compile-time index of a register buffer, passed to generic lambdas
+template <int N> struct Buf { static constexpr int value = N; };
+
 struct RowRef {
   int seg, row;
   bool valid;
@@ -130,22 +133,26 @@ __device__ __forceinline__ RowRef map_row(const GemvParams &p, int L, int wave_f
   return r;
 }
 
-// Row groups, chunks per lane and activation layout of one GEMV launch.
-//   R rows per wavefront task; UQ int4 chunks or UB bf16 chunks per lane are
-//   loaded together (16 loads of 16 bytes in flight per lane in the common
-//   shapes), so the chip keeps tens of MB of weight reads outstanding.
-template <int EP> struct GemvTile;
-template <> struct GemvTile<kEpQKV> { static constexpr int R = 4, UQ = 2, UB = 2; };
-template <> struct GemvTile<kEpResid> { static constexpr int R = 4, UQ = 2, UB = 2; };
-template <> struct GemvTile<kEpSwiGLU> { static constexpr int R = 8, UQ = 2, UB = 2; };
-template <> struct GemvTile<kEpResidExit> { static constexpr int R = 2, UQ = 8, UB = 8; };
-template <> struct GemvTile<kEpLogits> { static constexpr int R = 2, UQ = 8, UB = 8; };
-template <> struct GemvTile<kEpPlain> { static constexpr int R = 4, UQ = 2, UB = 2; };
+// Rows per task and chunks per batch of one GEMV launch.
+//   R rows per wavefront task (even for the RoPE pairs of QKV and the
+//   gate/up halves of SwiGLU); UQ int4 chunks or UB bf16 chunks per lane make
+//   one batch of loads.  With two batches in registers per wavefront and two
+//   workgroups per CU, a batch of 8-16 KB per wavefront keeps 16-32 MB of
+//   weight reads in flight over the chip.  Larger batches (M) take fewer rows
+//   so that the accumulators and both buffers stay in registers.
+template <int EP, int M> struct GemvTile {
+  static constexpr bool wide = EP == kEpResidExit || EP == kEpLogits;   // long rows / many rows
+  static constexpr int R = wide ? (M >= 8 ? 1 : 2) : EP == kEpSwiGLU ? (M >= 4 ? 2 : M == 2 ? 4 : 8)
+                                                                     : (M >= 8 ? 2 : 4);
+  static constexpr int UQ = wide ? (M >= 4 ? 4 : 8) : (M >= 4 ? 1 : 2);
+  static constexpr int UB = UQ;
+};
+constexpr int kGemvWgsPerCu = 2;
 
 template <int M, int XS, int EP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(M == 1 ? 4 : 1, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void gemv_kernel(GemvParams p, int kslab, int ntask) {
-  constexpr int R = GemvTile<EP>::R, UQ = GemvTile<EP>::UQ, UB = GemvTile<EP>::UB;
+  constexpr int R = GemvTile<EP, M>::R, UQ = GemvTile<EP, M>::UQ, UB = GemvTile<EP, M>::UB;
   constexpr int UMAX = UQ > UB ? UQ : UB;
   extern __shared__ uint4 smem4[];
   uint32_t *xl = reinterpret_cast<uint32_t *>(smem4);            // [M][kslab/2] bf16 pairs
@@ -204,12 +211,15 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
     }
   };
   auto second_half = [&](int r) { return EP == kEpSwiGLU && r >= R / 2; };
-  v4u wv[UMAX][R];
-  uint32_t zv[UQ][R];
-  // Every load is issued unconditionally (straight-line code, one batch in
-  // flight): chunks past the end of a row are clamped to its last chunk and
-  // rows past the end of the matrix read row 0; neither result is used.
-  auto load_batch = [&](int k0, int nch, int c0) {
+  // Two register buffers of weights: while one batch is reduced, the loads of
+  // the next are in flight.  Every load is issued unconditionally (so the wait
+  // before a batch is a fixed count): chunks past the end of a row are clamped
+  // to its last chunk, rows past the end of the matrix read row 0, and past
+  // the last batch a spare batch is fetched; none of these results is used.
+  v4u wv[2][UMAX][R];
+  uint32_t zv[2][UQ][R];
+  auto load_batch = [&](auto bc, int k0, int nch, int c0) {
+    constexpr int bi = decltype(bc)::value;
     if (q4) {
 #pragma unroll
       for (int u = 0; u < UQ; ++u) {
@@ -218,8 +228,8 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
         for (int r = 0; r < R; ++r) {
           const uint32_t *q = (second_half(r) ? qB : qA) + (int64_t)rowi[r] * KW + (k0 >> 3) + 4 * c;
           const uint32_t *z = (second_half(r) ? zB : zA) + (int64_t)rowi[r] * KG + ((k0 + 32 * c) >> p.gshift);
-          wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(q));
-          zv[u][r] = *z;
+          wv[bi][u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(q));
+          zv[bi][u][r] = *z;
         }
       }
     } else {
@@ -229,7 +239,7 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const uint16_t *w = (second_half(r) ? bfB : bfA) + (int64_t)rowi[r] * K + k0 + 8 * c;
-          wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(w));
+          wv[bi][u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(w));
         }
       }
     }
@@ -237,7 +247,8 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   auto nchunks = [&](int ks) { return q4 ? (ks >> 5) : (ks >> 3); };
   auto per_iter = [&]() { return 64 * (q4 ? UQ : UB); };
   float acc[R][M];
-  auto compute_batch = [&](int nch, int c0) {
+  auto compute_batch = [&](auto bc, int nch, int c0) {
+    constexpr int bi = decltype(bc)::value;
     if (q4) {
 #pragma unroll
       for (int u = 0; u < UQ; ++u) {
@@ -252,20 +263,20 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
             for (int r = 0; r < R; ++r) {
               uint32_t pr[4];
               float d = 0.f;
-              unpack_word(wv[u][r][0], pr);
+              unpack_word(wv[bi][u][r][0], pr);
               d = dot2_bf16(pr[0], x0.x, d); d = dot2_bf16(pr[1], x0.y, d);
               d = dot2_bf16(pr[2], x0.z, d); d = dot2_bf16(pr[3], x0.w, d);
-              unpack_word(wv[u][r][1], pr);
+              unpack_word(wv[bi][u][r][1], pr);
               d = dot2_bf16(pr[0], x1.x, d); d = dot2_bf16(pr[1], x1.y, d);
               d = dot2_bf16(pr[2], x1.z, d); d = dot2_bf16(pr[3], x1.w, d);
-              unpack_word(wv[u][r][2], pr);
+              unpack_word(wv[bi][u][r][2], pr);
               d = dot2_bf16(pr[0], x2.x, d); d = dot2_bf16(pr[1], x2.y, d);
               d = dot2_bf16(pr[2], x2.z, d); d = dot2_bf16(pr[3], x2.w, d);
-              unpack_word(wv[u][r][3], pr);
+              unpack_word(wv[bi][u][r][3], pr);
               d = dot2_bf16(pr[0], x3.x, d); d = dot2_bf16(pr[1], x3.y, d);
               d = dot2_bf16(pr[2], x3.z, d); d = dot2_bf16(pr[3], x3.w, d);
-              const float sc = bf_lo(zv[u][r]);
-              const float zo = 128.0f + bf_hi(zv[u][r]);
+              const float sc = bf_lo(zv[bi][u][r]);
+              const float zo = 128.0f + bf_hi(zv[bi][u][r]);
               acc[r][b] = fmaf(sc, d - zo * xsum, acc[r][b]);
             }
           }
@@ -282,10 +293,10 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               float d = acc[r][b];
-              d = dot2_bf16(wv[u][r][0], xv.x, d);
-              d = dot2_bf16(wv[u][r][1], xv.y, d);
-              d = dot2_bf16(wv[u][r][2], xv.z, d);
-              d = dot2_bf16(wv[u][r][3], xv.w, d);
+              d = dot2_bf16(wv[bi][u][r][0], xv.x, d);
+              d = dot2_bf16(wv[bi][u][r][1], xv.y, d);
+              d = dot2_bf16(wv[bi][u][r][2], xv.z, d);
+              d = dot2_bf16(wv[bi][u][r][3], xv.w, d);
               acc[r][b] = d;
             }
           }
@@ -331,7 +342,7 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   }
   int task = blockIdx.x * 4 + wid;
   setup_rows(task);
-  load_batch(0, nchunks(min(kslab, K)), lane);
+  load_batch(Buf<0>{}, 0, nchunks(min(kslab, K)), lane);
 
   if constexpr (XS == kXNorm) {
     if (held) {
@@ -434,7 +445,7 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
       ex = true;
       q4 = p.exit_mode == RIVER_EXIT_INT4;
       setup_rows(task);
-      load_batch(0, nchunks(min(kslab, K)), lane);
+      load_batch(Buf<0>{}, 0, nchunks(min(kslab, K)), lane);
     }
   }
 
@@ -494,7 +505,36 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   uint64_t best = 0;
   const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && force0 < 0;
 
-  auto finish_task = [&](int first) {
+  // Operands the epilogue reads from memory (the residual row entries, the
+  // layer input for the exit sums, the RoPE rotation), fetched with the
+  // weights of a batch so that no load is waited for behind the next batch.
+  // Indices are clamped into range: lanes without an output read a valid
+  // element and ignore it.
+  struct EpiIn {
+    float a, b;
+    float2 cs;
+  };
+  const int pos = ctl->pos;
+  const float *hsrc = exit_sums ? p.h_src : p.h_in;
+  auto epi_load = [&](int first) {
+    EpiIn e;
+    e.a = 0.f;
+    e.b = 0.f;
+    e.cs = make_float2(1.f, 0.f);
+    if constexpr (EP == kEpQKV) {
+      const int hd = p.Dh >> 1;
+      const int i = ((first + 2 * (lane / M)) >> 1) % hd;
+      e.cs = p.rope[(int64_t)pos * hd + i];
+    } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
+      const int n = min(first + lane / M, p.N - 1), b = min(lane % M, p.B - 1);
+      const int64_t o = (int64_t)b * p.h_io_stride + n;
+      e.a = p.h_in[o];
+      if constexpr (EP == kEpResidExit) e.b = hsrc[o];
+    }
+    return e;
+  };
+
+  auto finish_task = [&](int first, const EpiIn &e) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -517,9 +557,8 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
           const int P = L0 >> 1;
           const int hh = P / hd, i = P % hd;
           float y0 = pick(2 * pp, b), y1 = pick(2 * pp + 1, b);
-          const int pos = ctl->pos;
           if (hh < p.Hq + p.Hkv) {
-            const float2 cs = p.rope[(int64_t)pos * hd + i];
+            const float2 cs = e.cs;
             const float a = y0 * cs.x - y1 * cs.y;
             y1 = y1 * cs.x + y0 * cs.y;
             y0 = a;
@@ -553,10 +592,10 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
         const int n = first + r;
         if (b < p.B && n < p.N) {
           const int64_t o = (int64_t)b * p.h_io_stride + n;
-          const float v = p.h_in[o] + pick(r, b);
+          const float v = e.a + pick(r, b);
           p.h_out[o] = v;
           if (exit_sums) {
-            const float a = p.h_src[o];
+            const float a = e.b;
             ed += a * v;
             ea += a * a;
             eb += v * v;
@@ -589,25 +628,58 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
       for (int b = 0; b < M; ++b) acc[r][b] = 0.f;
   };
 
-  bool prefetched = true;
-  if (single) stage(0, K);
-  for (; task < ntask; task += wstride) {
-    if (!prefetched) setup_rows(task);
+  if (single) {
+    // All of K is staged once.  A wavefront walks its batches (one or more
+    // per task) with the next batch's loads issued before the current batch
+    // is reduced, so its weight stream never stops for the arithmetic.
+    stage(0, K);
+    const int nch = nchunks(K), pi = per_iter();
+    int cur = task, c0 = lane;
+    EpiIn epi[2];
+    epi[0] = epi_load(task * R);
     zero_acc();
-    for (int k0 = 0; k0 < K; k0 += kslab) {
-      const int ks = min(kslab, K - k0);
-      if (M > 2 && !single) {
+    auto step = [&](auto bc) -> bool {
+      constexpr int bi = decltype(bc)::value;
+      int nt = cur, nc0 = c0 + pi;
+      const bool task_end = nc0 - lane >= nch;
+      if (task_end) {
+        nt = cur + wstride;
+        nc0 = lane;
+      }
+      setup_rows(nt);                       // rows past the last task read row 0
+      load_batch(Buf<1 - bi>{}, 0, nch, nc0);
+      epi[1 - bi] = epi_load(nt * R);
+      compute_batch(bc, nch, c0);
+      if (task_end) {
+        finish_task(cur * R, epi[bi]);
+        zero_acc();
+      }
+      cur = nt;
+      c0 = nc0;
+      return cur < ntask;
+    };
+    if (task < ntask)
+      while (step(Buf<0>{}) && step(Buf<1>{})) {
+      }
+  } else {
+    // several K slabs: every slab is staged by the whole workgroup in turn
+    bool prefetched = true;
+    for (; task < ntask; task += wstride) {
+      if (!prefetched) setup_rows(task);
+      zero_acc();
+      for (int k0 = 0; k0 < K; k0 += kslab) {
+        const int ks = min(kslab, K - k0);
         __syncthreads();
         stage(k0, ks);
+        const int nch = nchunks(ks);
+        for (int c0 = lane; c0 - lane < nch; c0 += per_iter()) {
+          if (!prefetched) load_batch(Buf<0>{}, k0, nch, c0);
+          prefetched = false;
+          compute_batch(Buf<0>{}, nch, c0);
+        }
       }
-      const int nch = nchunks(ks);
-      for (int c0 = lane; c0 - lane < nch; c0 += per_iter()) {
-        if (!prefetched) load_batch(k0, nch, c0);
-        prefetched = false;
-        compute_batch(nch, c0);
-      }
+      finish_task(task * R, epi_load(task * R));
     }
-    finish_task(task * R);
   }
 
   // ---- per-workgroup tails
@@ -661,6 +733,557 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   }
 }
 
+// ===========================================================================
+// Decode GEMV on the matrix cores: y[m][n] = sum_k x[m][k] W[n][k] for the
+// B <= 8 rows of a decode step (M = B padded to 1, 2, 4 or 8).
+//
+// A tile is 16 logical output rows; the four wavefronts of a workgroup split
+// its K.  One unit of a wavefront is one load per lane shaped as the B
+// operand of MFMA 16x16x32 (tile column n = lane % 16, K quarter lane / 16):
+// int4: G/32 code words, one quantisation group of the row; bf16: 8 columns.
+// The staged activations are the A operand (batch row m = lane % 16; rows
+// past M repeat row M-1 and are never read back).  The MFMA sums over the K
+// quarters itself, so no cross-lane reduction is needed: the four partial
+// tiles meet once in LDS at the end of a tile, where the epilogue runs.
+//   int4: per group, sum_k x (q - z) s = s * (sum_k x (128+q) - (128+z) sum_k x)
+//   with 128+q made by unpack_word and the group sums of x taken at staging.
+// Workgroups are persistent over tiles; each wavefront keeps kMvD units in
+// flight (weights, scale/zero word, and the epilogue operands of the unit's
+// tile), every load issued unconditionally so that each wait is a fixed
+// count.  Everything the prologue reads from memory is requested before the
+// first weights, so waiting for it never waits for the weight stream.
+// ===========================================================================
+constexpr int kMvD = 8;          // units in flight per wavefront
+constexpr int kMvWgsPerCu = 2;
+constexpr int kMvHold = 4;       // staging items per thread held in registers
+constexpr int kMvPartHeld = 2;   // exit partials per thread held in registers
+
+struct MvEpi {
+  float a, b;
+  float2 cs;
+};
+
+// epilogue outputs per batch row of a tile: QKV 8 RoPE pairs, SwiGLU 8 products
+template <int EP> constexpr int mv_outs() { return (EP == kEpQKV || EP == kEpSwiGLU) ? 8 : 16; }
+
+// weight row of logical row L (tile column L % 16 of tile L / 16)
+template <int EP>
+__device__ __forceinline__ RowRef mv_row(const GemvParams &p, int L) {
+  if constexpr (EP == kEpQKV) {
+    return map_row<kEpQKV>(p, L, 0, 0);
+  } else if constexpr (EP == kEpSwiGLU) {
+    // a tile holds 8 gate rows (columns 0..7) and the 8 up rows of the same index
+    RowRef r;
+    const int j = L & 15;
+    r.seg = j < 8 ? 0 : 1;
+    r.row = 8 * (L >> 4) + (j & 7);
+    r.valid = r.row < p.w.seg_rows[0];
+    return r;
+  } else {
+    RowRef r;
+    r.seg = 0;
+    r.row = L;
+    r.valid = L < p.N;
+    return r;
+  }
+}
+
+template <int M, int XS, int EP, int G>
+__global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
+  extern __shared__ uint4 mv_smem[];
+  constexpr int OUTS = mv_outs<EP>();
+  constexpr int ITEMS = OUTS * M;                  // epilogue items per tile (<= 128)
+  constexpr int IM = M < 4 ? M : 4;                // result rows per lane: 4 * (lane / 16) + i
+  constexpr int GW = G / 32;                       // int4 code words per lane per unit
+  typedef typename WordsT<GW>::T WT;
+  const int K = p.K, KG = K / G, xrow = K + 8;
+  uint16_t *xl = reinterpret_cast<uint16_t *>(mv_smem);           // [M][K + 8] bf16
+  float *xsg = reinterpret_cast<float *>(xl + M * xrow);          // [M][K / G] group sums
+  float *red = xsg + M * KG;                                      // [2][4][M][16] partial tiles
+  __shared__ float pred[4][4 * M];
+  __shared__ float tred[ITEMS][3];
+  __shared__ uint64_t tkey[ITEMS];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qq = lane >> 4, cl = lane & 15;
+  const int mrow = cl < M ? cl : M - 1;            // A-operand row of this lane
+  Control *ctl = p.ctrl;
+
+  // ---- exit choice as far as it is known before the pending test (as in the
+  // GEMV above: every workgroup of a QKV launch that has to take the test
+  // takes it itself and reaches the same result)
+  const int flag0 = ctl->flag;
+  const int force0 = ctl->force_E;
+  const bool pending = EP == kEpQKV && p.path == kPathDevice && p.test_prev && force0 < 0 && flag0 == 0;
+  bool ex = flag0 != 0 || (p.layer >= 0 && force0 >= 0 && p.layer >= force0);
+  if (p.layer < 0) ex = false;
+  if (p.path != kPathDevice) ex = p.path == kPathExit;
+  const bool int4_mode = p.exit_mode == RIVER_EXIT_INT4;
+  const int pos = ctl->pos;
+
+  // ---- prologue loads (before any weight load): staging items, exit partials
+  const int n8 = K >> 3, total = M * n8;
+  float4 hv[kMvHold][2];
+  uint4 gv[kMvHold], bv[kMvHold];
+#pragma unroll
+  for (int j = 0; j < kMvHold; ++j) {
+    const int idx = min(tid + 256 * j, total - 1);
+    const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
+    if constexpr (XS == kXNorm) {
+      const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
+      hv[j][0] = *reinterpret_cast<const float4 *>(h);
+      hv[j][1] = *reinterpret_cast<const float4 *>(h + 4);
+      gv[j] = *reinterpret_cast<const uint4 *>(p.gain + 8 * g8);
+    } else {
+      bv[j] = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)m * p.x_stride + 8 * g8);
+    }
+  }
+  float pv[kMvPartHeld][3 * M];
+  if (pending) {
+#pragma unroll
+    for (int j = 0; j < kMvPartHeld; ++j) {
+      const int wg = min(tid + 256 * j, p.part_wgs - 1);
+      const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
+#pragma unroll
+      for (int i = 0; i < 3 * M; ++i) pv[j][i] = pp[i];
+    }
+  }
+
+  // ---- per-thread epilogue state kept across tiles (the down projection has
+  // no pending test, so its weight choice is final here)
+  float ed = 0.f, ea = 0.f, eb = 0.f;
+  uint64_t best = 0;
+  const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && force0 < 0;
+
+  // One pass for one weight form (Q4: int4 codes; else bf16 backbone or bf16
+  // exit copy).  Returns true when the pending test chose the exit layer and
+  // the weights this pass started to stream are the wrong ones.
+  auto run = [&](auto qc, bool restart) -> bool {
+    constexpr bool Q4 = decltype(qc)::value == 1;
+    constexpr int UK = Q4 ? G : 32;                // K columns per unit
+    const int KU = K / UK, U = (KU + 3) >> 2;      // units per tile row, per wavefront
+    const int my_tiles = (ntile - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const float *hsrc = exit_sums ? p.h_src : p.h_in;
+
+    // load side: row pointers of the tile being fetched, and this thread's
+    // epilogue operands in it
+    int ltile = -1;
+    const uint32_t *qb = nullptr, *zb = nullptr;
+    const uint16_t *bb = nullptr;
+    const float2 *ep_cs = p.rope;
+    const float *ep_a = p.h_in, *ep_b = p.h_in;
+    auto set_tile = [&](int t) {
+      {
+        const int m = tid / OUTS, j = tid % OUTS;
+        if constexpr (EP == kEpQKV) {
+          const int hd = p.Dh >> 1;
+          ep_cs = p.rope + (int64_t)pos * hd + (t * 8 + j) % hd;
+        } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
+          const int n = min(t * 16 + j, p.N - 1), b = min(m, p.B - 1);
+          const int64_t o = (int64_t)b * p.h_io_stride + n;
+          ep_a = p.h_in + o;
+          ep_b = hsrc + o;
+        }
+        (void)m;
+      }
+      const RowRef rr = mv_row<EP>(p, t * 16 + cl);
+      const int row = rr.valid ? rr.row : 0;
+      const int sg = rr.seg;
+      if constexpr (Q4) {
+        qb = (sg == 0 ? p.w.q4[0] : sg == 1 ? p.w.q4[1] : p.w.q4[2]) + (int64_t)row * (K >> 3) + qq * GW;
+        zb = (sg == 0 ? p.w.sz[0] : sg == 1 ? p.w.sz[1] : p.w.sz[2]) + (int64_t)row * KG;
+      } else {
+        const uint16_t *b0 = ex ? p.w.ex_bf[0] : p.w.bf[0];
+        const uint16_t *b1 = ex ? p.w.ex_bf[1] : p.w.bf[1];
+        const uint16_t *b2 = ex ? p.w.ex_bf[2] : p.w.bf[2];
+        bb = (sg == 0 ? b0 : sg == 1 ? b1 : b2) + (int64_t)row * K + 8 * qq;
+      }
+    };
+    WT wq[kMvD];
+    uint32_t wz[kMvD];
+    v4u wb[kMvD];
+    MvEpi epi[kMvD];
+    auto epi_load = [&]() {
+      MvEpi e;
+      e.a = 0.f;
+      e.b = 0.f;
+      e.cs = make_float2(1.f, 0.f);
+      if constexpr (EP == kEpQKV) {
+        e.cs = *ep_cs;
+      } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
+        e.a = *ep_a;
+        if constexpr (EP == kEpResidExit) e.b = *ep_b;
+      }
+      return e;
+    };
+    // the next unit to fetch: tile iteration lti, unit ls of the tile (past
+    // the last unit: the last unit again)
+    int lti = 0, ls = 0;
+    auto load = [&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      const bool past = lti >= my_tiles;
+      const int ti = past ? my_tiles - 1 : lti, s = past ? U - 1 : ls;
+      const int t = (int)blockIdx.x + ti * (int)gridDim.x;
+      if (t != ltile) {
+        set_tile(t);
+        ltile = t;
+      }
+      const int k0 = min(wid * U + s, KU - 1) * UK;
+      if constexpr (Q4) {
+        wq[d] = __builtin_nontemporal_load(reinterpret_cast<const WT *>(qb + (k0 >> 3)));
+        wz[d] = zb[k0 / G];
+      } else {
+        wb[d] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(bb + k0));
+      }
+      epi[d] = epi_load();
+      if (++ls == U) {
+        ls = 0;
+        ++lti;
+      }
+    };
+
+    f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](auto dc, int k0) {
+      constexpr int d = decltype(dc)::value;
+      const uint16_t *xa = xl + mrow * xrow + k0;
+      if constexpr (Q4) {
+        f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < GW; ++j) {
+          const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xa + qq * (G / 4) + 8 * j);
+          uint32_t w;
+          if constexpr (GW == 1) w = wq[d];
+          else w = wq[d][j];
+          uint32_t pr[4];
+          unpack_word(w, pr);
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af, __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3])), ag, 0, 0, 0);
+        }
+        const float sc = bf_lo(wz[d]), zo = 128.0f + bf_hi(wz[d]);
+        const int g = k0 / G;
+#pragma unroll
+        for (int i = 0; i < IM; ++i) {
+          const int m = min(4 * qq + i, M - 1);
+          tot[i] = fmaf(sc, ag[i] - zo * xsg[m * KG + g], tot[i]);
+        }
+      } else {
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xa + 8 * qq);
+        tot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, wb[d]), tot, 0, 0, 0);
+      }
+    };
+
+    // ---- the tile epilogue: partial tiles into LDS, then one thread per item
+    auto end_tile = [&](auto dc, int ti) {
+      constexpr int d = decltype(dc)::value;
+      const int par = ti & 1;
+      const int t = (int)blockIdx.x + ti * (int)gridDim.x;
+#pragma unroll
+      for (int i = 0; i < IM; ++i) {
+        const int m = 4 * qq + i;
+        if (m < M) red[((par * 4 + wid) * M + m) * 16 + cl] = tot[i];
+      }
+      tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      if (tid < ITEMS) {
+        const int m = tid / OUTS, j = tid % OUTS;
+        const float *rb = red + (par * 4 * M + m) * 16;
+        auto y = [&](int n) {
+          return (rb[n] + rb[M * 16 + n]) + (rb[2 * M * 16 + n] + rb[3 * M * 16 + n]);
+        };
+        const MvEpi &e = epi[d];
+        if constexpr (EP == kEpQKV) {
+          const int L0 = t * 16 + 2 * j;
+          if (m < p.B && L0 < p.N) {
+            const int hd = p.Dh >> 1;
+            const int P = L0 >> 1;
+            const int hh = P / hd, i = P % hd;
+            float y0 = y(2 * j), y1 = y(2 * j + 1);
+            if (hh < p.Hq + p.Hkv) {
+              const float a = y0 * e.cs.x - y1 * e.cs.y;
+              y1 = y1 * e.cs.x + y0 * e.cs.y;
+              y0 = a;
+            }
+            if (hh < p.Hq) {
+              uint16_t *q = p.q_out + (int64_t)m * p.Hq * p.Dh + hh * p.Dh;
+              q[i] = f2bf(y0);
+              q[i + hd] = f2bf(y1);
+            } else {
+              const bool isk = hh < p.Hq + p.Hkv;
+              const int kvh = isk ? hh - p.Hq : hh - p.Hq - p.Hkv;
+              uint16_t *dst = (isk ? p.k_cache : p.v_cache) +
+                              (((int64_t)m * p.Hkv + kvh) * p.max_seq + pos) * p.Dh;
+              dst[i] = f2bf(y0);
+              dst[i + hd] = f2bf(y1);
+            }
+          }
+        } else if constexpr (EP == kEpSwiGLU) {
+          const int n = t * 8 + j;
+          if (m < p.B && n < p.w.seg_rows[0]) {
+            const float gt = y(j), up = y(j + 8);
+            p.u_out[(int64_t)m * p.u_stride + n] = f2bf(gt / (1.0f + expf(-gt)) * up);
+          }
+        } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
+          const int n = t * 16 + j;
+          if (m < p.B && n < p.N) {
+            const int64_t o = (int64_t)m * p.h_io_stride + n;
+            const float v = e.a + y(j);
+            p.h_out[o] = v;
+            if (exit_sums) {
+              ed += e.b * v;
+              ea += e.b * e.b;
+              eb += v * v;
+            }
+          }
+        } else if constexpr (EP == kEpPlain) {
+          const int n = t * 16 + j;
+          if (m < p.B && n < p.N) p.y_out[(int64_t)m * p.y_stride + n] = y(j);
+        } else if constexpr (EP == kEpLogits) {
+          const int n = t * 16 + j;
+          if (m < p.B && n < p.N) {
+            const float v = y(j);
+            if (p.logits) p.logits[(int64_t)m * p.vocab + n] = v;
+            const uint64_t key = ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+            best = key > best ? key : best;
+          }
+        }
+      }
+    };
+
+    // ---- first weights in flight, then the prologue arithmetic
+    static_assert(kMvD == 8, "the ring is unrolled for 8 slots");
+    load(Buf<0>{});
+    load(Buf<1>{});
+    load(Buf<2>{});
+    load(Buf<3>{});
+    load(Buf<4>{});
+    load(Buf<5>{});
+    load(Buf<6>{});
+    load(Buf<7>{});
+
+    if (!restart) {
+      // RMSNorm sums of squares of the batch rows, and the exit partials of
+      // the previous layer (pending test)
+      float sums[4 * M];
+#pragma unroll
+      for (int i = 0; i < 4 * M; ++i) sums[i] = 0.f;
+      if constexpr (XS == kXNorm) {
+#pragma unroll
+        for (int j = 0; j < kMvHold; ++j) {
+          const int idx = tid + 256 * j;
+          if (idx < total && idx / n8 < p.B) {
+            const float4 a0 = hv[j][0], a1 = hv[j][1];
+            const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
+                             a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+#pragma unroll
+            for (int b = 0; b < M; ++b) sums[b] += b == idx / n8 ? ss : 0.f;
+          }
+        }
+        for (int idx = tid + 256 * kMvHold; idx < total; idx += 256) {
+          const int m = idx / n8, g8 = idx - m * n8;
+          if (m < p.B) {
+            const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
+            const float4 a0 = *reinterpret_cast<const float4 *>(h);
+            const float4 a1 = *reinterpret_cast<const float4 *>(h + 4);
+            const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
+                             a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+#pragma unroll
+            for (int b = 0; b < M; ++b) sums[b] += b == m ? ss : 0.f;
+          }
+        }
+      }
+      if (pending) {
+#pragma unroll
+        for (int j = 0; j < kMvPartHeld; ++j) {
+          if (tid + 256 * j < p.part_wgs) {
+#pragma unroll
+            for (int i = 0; i < 3 * M; ++i)
+              if (i < 3 * p.B) sums[M + i] += pv[j][i];
+          }
+        }
+        for (int wg = tid + 256 * kMvPartHeld; wg < p.part_wgs; wg += 256) {
+          const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
+#pragma unroll
+          for (int i = 0; i < 3 * M; ++i)
+            if (i < 3 * p.B) sums[M + i] += pp[i];
+        }
+      }
+      if (XS == kXNorm || pending) {
+#pragma unroll
+        for (int i = 0; i < 4 * M; ++i) {
+          const float v = wave_sum_uniform(sums[i]);
+          if (lane == 0) pred[wid][i] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4 * M; ++i) sums[i] = (pred[0][i] + pred[1][i]) + (pred[2][i] + pred[3][i]);
+      }
+      bool fired = false;
+      if (pending) {
+        // exit decision of the previous layer (lead page, section 4): the
+        // minimum over the batch of cos(layer input, layer output) must exceed
+        // tau; workgroup 0 records it
+        float mcos = 2.0f;
+#pragma unroll
+        for (int b = 0; b < M; ++b) {
+          if (b < p.B) {
+            const float sd = sums[M + 3 * b], sa = sums[M + 3 * b + 1], sb = sums[M + 3 * b + 2];
+            float cs = sd / fmaxf(sqrtf(sa) * sqrtf(sb), 1e-8f);
+            cs = fminf(fmaxf(cs, -1.0f), 1.0f);
+            mcos = fminf(mcos, cs);
+          }
+        }
+        fired = mcos > ctl->tau;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+          ctl->trace[p.layer - 1] = mcos;
+          if (fired) {
+            ctl->E = p.layer;
+            __hip_atomic_store(&ctl->flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+
+      // stage x as bf16 rows (zeros past B) with the group sums of each row
+      auto put = [&](int idx, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+        const int m = idx / n8, g8 = idx - m * n8;
+        float gs = (bf_lo(a0) + bf_hi(a0)) + (bf_lo(a1) + bf_hi(a1)) + (bf_lo(a2) + bf_hi(a2)) +
+                   (bf_lo(a3) + bf_hi(a3));
+        // the G/8 items of a group sit in G/8 adjacent lanes
+        gs = G == 128 ? sum16(gs) : sum8(gs);
+        if (idx < total) {
+          *reinterpret_cast<uint4 *>(xl + m * xrow + 8 * g8) = make_uint4(a0, a1, a2, a3);
+          if (g8 % (G / 8) == 0) xsg[m * KG + g8 / (G / 8)] = gs;
+        }
+      };
+      auto norm8 = [&](int m, float4 h0, float4 h1, uint4 g, uint32_t &a0, uint32_t &a1, uint32_t &a2,
+                       uint32_t &a3) {
+        float ssb = 0.f;
+#pragma unroll
+        for (int b = 0; b < M; ++b) ssb = b == m ? sums[b] : ssb;
+        const float rs = 1.0f / sqrtf(ssb / (float)K + p.eps);
+        a0 = pack_bf2(h0.x * rs * bf_lo(g.x), h0.y * rs * bf_hi(g.x));
+        a1 = pack_bf2(h0.z * rs * bf_lo(g.y), h0.w * rs * bf_hi(g.y));
+        a2 = pack_bf2(h1.x * rs * bf_lo(g.z), h1.y * rs * bf_hi(g.z));
+        a3 = pack_bf2(h1.z * rs * bf_lo(g.w), h1.w * rs * bf_hi(g.w));
+      };
+#pragma unroll
+      for (int j = 0; j < kMvHold; ++j) {
+        const int idx = tid + 256 * j;
+        const int m = min(idx, total - 1) / n8;
+        uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+        if (idx < total && m < p.B) {
+          if constexpr (XS == kXNorm) norm8(m, hv[j][0], hv[j][1], gv[j], a0, a1, a2, a3);
+          else { a0 = bv[j].x; a1 = bv[j].y; a2 = bv[j].z; a3 = bv[j].w; }
+        }
+        put(idx, a0, a1, a2, a3);
+      }
+      for (int idx0 = 256 * kMvHold; idx0 < total; idx0 += 256) {
+        const int idx = idx0 + tid;
+        const int m = min(idx, total - 1) / n8, g8 = min(idx, total - 1) - m * n8;
+        uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+        if (idx < total && m < p.B) {
+          if constexpr (XS == kXNorm) {
+            const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
+            norm8(m, *reinterpret_cast<const float4 *>(h), *reinterpret_cast<const float4 *>(h + 4),
+                  *reinterpret_cast<const uint4 *>(p.gain + 8 * g8), a0, a1, a2, a3);
+          } else {
+            const uint4 v = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)m * p.x_stride + 8 * g8);
+            a0 = v.x; a1 = v.y; a2 = v.z; a3 = v.w;
+          }
+        }
+        put(idx, a0, a1, a2, a3);
+      }
+      __syncthreads();
+      if (fired && !ex) return true;
+    }
+
+    // ---- main loop: unit n of the sequence sits in ring slot n % kMvD; the
+    // unit being reduced is unit cs of tile iteration cti
+    int cti = 0, cs = 0;
+    auto step = [&](auto dc) {
+      if (cti < my_tiles) {
+        const int ku = wid * U + cs;
+        if (ku < KU) compute(dc, ku * UK);        // units past K (short rows) add nothing
+        if (cs == U - 1) end_tile(dc, cti);
+        if (++cs == U) {
+          cs = 0;
+          ++cti;
+        }
+      }
+      load(dc);
+    };
+    while (cti < my_tiles) {
+      step(Buf<0>{});
+      step(Buf<1>{});
+      step(Buf<2>{});
+      step(Buf<3>{});
+      step(Buf<4>{});
+      step(Buf<5>{});
+      step(Buf<6>{});
+      step(Buf<7>{});
+    }
+    return false;
+  };
+
+  const bool q4 = ex && int4_mode;
+  if (q4) {
+    run(Buf<1>{}, false);
+  } else if (run(Buf<0>{}, false)) {
+    ex = true;   // the pending test fired: the exit weights instead
+    if (int4_mode) run(Buf<1>{}, true);
+    else run(Buf<0>{}, true);
+  }
+
+  // ---- per-workgroup tails
+  if constexpr (EP == kEpResidExit) {
+    if (exit_sums) {
+      // exit-test partial sums of this workgroup's rows in a fixed order; the
+      // next layer's first kernel reads them after the kernel boundary
+      if (tid < ITEMS) {
+        tred[tid][0] = ed;
+        tred[tid][1] = ea;
+        tred[tid][2] = eb;
+      }
+      __syncthreads();
+      if (tid < 3 * M) {
+        const int b = tid / 3, k = tid % 3;
+        float s = 0.f;
+        for (int j = 0; j < OUTS; ++j) s += tred[b * OUTS + j][k];
+        if (b < p.B) p.part[(int64_t)blockIdx.x * kPartFloatsPerWG + 3 * b + k] = s;
+      }
+    }
+  } else if constexpr (EP == kEpLogits) {
+    if (tid < ITEMS) tkey[tid] = best;
+    __syncthreads();
+    if (tid < M && tid < p.B) {
+      uint64_t m = 0;
+      for (int j = 0; j < OUTS; ++j) m = tkey[tid * OUTS + j] > m ? tkey[tid * OUTS + j] : m;
+      __hip_atomic_fetch_max(control_keys(ctl) + tid, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (arrive_last(&ctl->counters[kCtrLogits], gridDim.x, &last_flag)) {
+      if (threadIdx.x < p.B && p.next) {
+        const uint64_t key = __hip_atomic_load(control_keys(ctl) + threadIdx.x, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        p.next[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+      }
+      if (threadIdx.x == 0) {
+        const int E = ctl->E;
+        ctl->last_E = E;
+        if (p.is_prefill) {
+          ctl->prefill_hist[E] += 1;
+          ctl->n_prefill += 1;
+        } else {
+          ctl->decode_hist[E] += 1;
+          ctl->n_decode += 1;
+          ctl->pos += 1;
+        }
+      }
+    }
+  }
+}
+
+
 static int gemv_kslab(int M, int K) {
   int kslab = kXLdsBytes / (M * 2);
   kslab = kslab / 256 * 256;
@@ -680,6 +1303,67 @@ static int num_cus() {
   return n;
 }
 
+// LDS bytes of one mgemv workgroup
+static size_t mgemv_lds(int M, int K, int G) {
+  return (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4 + (size_t)2 * 4 * M * 16 * 4;
+}
+
+static int mgemv_ntile(Epilogue ep, const GemvParams &p) {
+  if (ep == kEpSwiGLU) return (p.w.seg_rows[0] + 7) / 8;
+  return (p.N + 15) / 16;
+}
+
+bool mgemv_fits(Epilogue ep, const GemvParams &p) {
+  const int M = p.B <= 1 ? 1 : p.B <= 2 ? 2 : p.B <= 4 ? 4 : 8;
+  if (p.G != 64 && p.G != 128) return false;
+  if (p.K % 128 != 0 || p.K % p.G != 0) return false;
+  if (ep == kEpQKV && p.Dh % 16 != 0) return false;
+  return mgemv_lds(M, p.K, p.G) <= 80 * 1024;
+}
+
+struct MvPlan {
+  int grid, ntile;
+  size_t lds;
+  const void *fn;
+};
+
+template <int M, int XS, int EP>
+static MvPlan mgemv_plan_t(Epilogue ep, const GemvParams &p) {
+  MvPlan g;
+  g.ntile = mgemv_ntile(ep, p);
+  g.lds = mgemv_lds(M, p.K, p.G);
+  g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64>)
+                   : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128>);
+  // 160 KB of LDS per CU, a few KB of it static per workgroup
+  const int fit = (int)((160 * 1024) / (g.lds + 4 * 1024));
+  const int per_cu = std::max(1, std::min(kMvWgsPerCu, fit));
+  g.grid = std::min(g.ntile, per_cu * num_cus());
+  return g;
+}
+
+template <int XS, int EP>
+static MvPlan mgemv_plan_m(Epilogue ep, const GemvParams &p) {
+  switch (mpad(p.B)) {
+    case 1: return mgemv_plan_t<1, XS, EP>(ep, p);
+    case 2: return mgemv_plan_t<2, XS, EP>(ep, p);
+    case 4: return mgemv_plan_t<4, XS, EP>(ep, p);
+    default: return mgemv_plan_t<8, XS, EP>(ep, p);
+  }
+}
+
+static MvPlan mgemv_plan(Epilogue ep, const GemvParams &p) {
+  switch (ep) {
+    case kEpQKV: return mgemv_plan_m<kXNorm, kEpQKV>(ep, p);
+    case kEpSwiGLU: return mgemv_plan_m<kXNorm, kEpSwiGLU>(ep, p);
+    case kEpResid: return mgemv_plan_m<kXBf16, kEpResid>(ep, p);
+    case kEpResidExit: return mgemv_plan_m<kXBf16, kEpResidExit>(ep, p);
+    case kEpPlain: return mgemv_plan_m<kXBf16, kEpPlain>(ep, p);
+    default: return mgemv_plan_m<kXNorm, kEpLogits>(ep, p);
+  }
+}
+
+static bool use_mgemv(Epilogue ep, const GemvParams &p) { return !p.dot_gemv && mgemv_fits(ep, p); }
+
 struct GemvPlan {
   int grid, ntask, kslab;
   size_t lds;
@@ -691,7 +1375,7 @@ struct GemvPlan {
 // task group of 4 tasks.
 template <int M, int XS, int EP>
 static GemvPlan gemv_plan(const GemvParams &p) {
-  constexpr int R = GemvTile<EP>::R;
+  constexpr int R = GemvTile<EP, M>::R;
   GemvPlan g;
   g.kslab = gemv_kslab(M, p.K);
   g.lds = (size_t)M * g.kslab * 2 + (size_t)M * (g.kslab / 32) * 4;
@@ -709,7 +1393,7 @@ static GemvPlan gemv_plan(const GemvParams &p) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g.fn, 256, g.lds) != hipSuccess ||
         per_cu < 1)
       per_cu = 2;
-    resident = per_cu * num_cus();
+    resident = min(per_cu, kGemvWgsPerCu) * num_cus();
   }
   const int per = (wgs + resident - 1) / resident;   // task groups per workgroup
   g.grid = (wgs + per - 1) / per;
@@ -737,11 +1421,20 @@ static GemvPlan plan_for(Epilogue ep, const GemvParams &p) {
   }
 }
 
-int gemv_grid(Epilogue ep, const GemvParams &p) { return plan_for(ep, p).grid; }
+int gemv_grid(Epilogue ep, const GemvParams &p) {
+  return use_mgemv(ep, p) ? mgemv_plan(ep, p).grid : plan_for(ep, p).grid;
+}
 
 hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s) {
   (void)xs;
   if (p.B < 1 || p.B > 8 || ep > kEpPlain) return hipErrorInvalidValue;
+  if (use_mgemv(ep, p)) {
+    const MvPlan g = mgemv_plan(ep, p);
+    int ntile = g.ntile;
+    GemvParams pc = p;
+    void *args[] = {&pc, &ntile};
+    return launch_kernel(g.fn, dim3(g.grid), dim3(256), args, g.lds, s);
+  }
   const GemvPlan g = plan_for(ep, p);
   int kslab = g.kslab, ntask = g.ntask;
   GemvParams pc = p;

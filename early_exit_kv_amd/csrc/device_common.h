@@ -11,6 +11,14 @@ namespace river {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// N consecutive 32-bit words as one load
+template <int N_> struct WordsT;
+template <> struct WordsT<1> { typedef uint32_t T; };
+template <> struct WordsT<2> { typedef v2u T; };
+template <> struct WordsT<4> { typedef v4u T; };
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -12,8 +12,6 @@
 
 namespace river {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ===========================================================================
 // RMSNorm rows: x[r] = bf16(h[r] / sqrt(mean(h[r]^2) + eps) * gain).
@@ -482,11 +480,6 @@ hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
 //   kernel (one workgroup per column block) adds the splits in order and runs
 //   the epilogue.
 // ===========================================================================
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-template <int N_> struct WordsT;
-template <> struct WordsT<1> { typedef uint32_t T; };
-template <> struct WordsT<2> { typedef v2u T; };
-template <> struct WordsT<4> { typedef v4u T; };
 
 // LM head epilogue of one column block: logits out, per-row argmax keys
 // (value order, then lowest index), and in the last workgroup of the launch

@@ -143,6 +143,7 @@ struct GemvParams {
   int path;                       // PathChoice
   float *y_out; int64_t y_stride; // kEpPlain: fp32 [B][N]
   float *logits; int32_t *next; int is_prefill; int vocab;// LM head
+  int dot_gemv;                   // 1: the dot-product GEMV even where the MFMA one fits
 };
 
 
@@ -193,6 +194,8 @@ hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t
 // workgroups launch_gemv uses for these parameters (the QKV launch reads that
 // many partials left by the previous layer's down projection)
 int gemv_grid(Epilogue ep, const GemvParams &p);
+// the matrix-core GEMV handles these parameters (LDS, group size, K)
+bool mgemv_fits(Epilogue ep, const GemvParams &p);
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 
 // prefill

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libriver.so")
 RIVER_OK, RIVER_E_INVALID_ARG, RIVER_E_BAD_SIZE, RIVER_E_STATE = 0, 1, 2, 3
 RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
 RIVER_EXIT_INT4, RIVER_EXIT_COPY = 1, 2
-RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK = 1, 2, 3, 4
+RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK, RIVER_OPT_GEMV = 1, 2, 3, 4, 5
 KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
                 "p_norm", "p_gemm", "p_attn", "p_cos")
 RIVER_MAX_LAYERS = 256
@@ -285,6 +285,11 @@ class River:
     def force_exit_layer(self, e):
         """-1: decide with tau; e in 0..L: layers < e backbone, the rest exit layers."""
         self.set_option(RIVER_OPT_FORCE_E, e)
+
+    def use_dot_gemv(self, on=True):
+        """Decode linears of <= 8 rows on the dot-product GEMV (else on the
+        matrix cores wherever the shape allows)."""
+        self.set_option(RIVER_OPT_GEMV, 1 if on else 0)
 
     def profile(self, on=True):
         """Time every kernel with HIP events (decode steps then launch eagerly)."""

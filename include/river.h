@@ -186,8 +186,15 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     e = 0: every layer quantised);
  *   RIVER_OPT_ATTN_CHUNK positions per decode-attention workgroup: 0 (default)
  *                     lets the library choose per shape, else a multiple of
- *                     64 giving at most 512 splits of max_seq. */
-enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4 };
+ *                     64 giving at most 512 splits of max_seq;
+ *   RIVER_OPT_GEMV    linears of decode steps of at most 8 rows: 0 on the
+ *                     matrix cores wherever the shape allows (group size 64
+ *                     or 128, K a multiple of 128, the rows of one step
+ *                     within 80 KB of LDS), 1 (default) always on the
+ *                     dot-product GEMV.  Both give the same results up to
+ *                     the fp32 summation order. */
+enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4,
+       RIVER_OPT_GEMV = 5 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
 
 /* Kernel classes timed when RIVER_OPT_PROFILE is 1 (decode steps then launch

@@ -62,6 +62,18 @@ def test_linear_cores_8b(ctx8b, M, use_exit):
     check_linears(ctx8b, M, use_exit)
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("use_exit", [0, 1])
+def test_linear_mfma_gemv_8b(ctx8b, M, use_exit):
+    """The matrix-core GEMV of decode steps (where it fits) on the same shapes."""
+    _, _, r = ctx8b
+    r.use_dot_gemv(False)
+    try:
+        check_linears(ctx8b, M, use_exit)
+    finally:
+        r.use_dot_gemv(True)
+
+
 @pytest.mark.parametrize("M", [9, 32, 33, 64])
 @pytest.mark.parametrize("use_exit", [0, 1])
 def test_linear_batched_rows_8b(ctx8b_rows, M, use_exit):

@@ -39,7 +39,7 @@ def host_weights(w, dtype=np.float64):
             "layers": [{k: cv(v) for k, v in lw.items()} for lw in w["layers"]]}
 
 
-def parity_run(shape, w_dev, B, T, steps, tau, mode="int4"):
+def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", dot_gemv=True):
     """Prefill + decode steps on the GPU with every pass checked stage by stage
     (teacher forcing at each stored activation), and a free-running oracle
     beside it for the exit decisions and the K/V cosine bar."""
@@ -49,6 +49,7 @@ def parity_run(shape, w_dev, B, T, steps, tau, mode="int4"):
     print(f"[parity-full] {shape.name} L={L} B={B} T={T} steps={steps} tau={tau}", flush=True)
     sh = synth.shrink(shape, n_layers=L)
     r = rv.River(sh, w_dev, B, max_seq)
+    r.use_dot_gemv(dot_gemv)
     r.build_exit_layers(mode)
     r.record(B * T)
     hw = host_weights(w_dev)
@@ -147,6 +148,11 @@ def test_decode_parity_8b_layer_shapes(w8b, tau):
         assert all(e == 1 for e in Es)
 
 
+def test_decode_parity_8b_mfma_gemv(w8b):
+    """Every decode linear on the matrix-core GEMV."""
+    parity_run(synth.LLAMA_8B, w8b, B=1, T=12, steps=3, tau=0.5, dot_gemv=False)
+
+
 def test_decode_parity_1b_layer_shapes_tied(w1b):
     parity_run(synth.LLAMA_1B, w1b, B=1, T=12, steps=3, tau=0.5)
 
@@ -186,3 +192,17 @@ def test_prefill_ragged_rows_tiny():
     """B*T rows that end inside a GEMM tile, one row per batch element."""
     w = synth.make_weights(synth.TINY, seed=0, device="cuda")
     parity_run(synth.TINY, w, B=3, T=45, steps=2, tau=0.5)
+
+
+def test_prefill_ragged_rows_tiny_mfma_gemv():
+    """Three rows per decode step (padded to four) on the matrix-core GEMV."""
+    w = synth.make_weights(synth.TINY, seed=0, device="cuda")
+    parity_run(synth.TINY, w, B=3, T=45, steps=2, tau=0.5, dot_gemv=False)
+
+
+def test_decode_parity_8b_batch8_mfma_gemv(w8b):
+    """Eight rows: q|k|v, o and gate|up on the matrix-core GEMV, the down
+    projection (its rows too wide for LDS) on the dot-product GEMV."""
+    w = dict(w8b)
+    w["layers"] = w8b["layers"][:2]
+    parity_run(synth.LLAMA_8B, w, B=8, T=6, steps=2, tau=0.3, dot_gemv=False)
