@@ -738,33 +738,38 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
 // B <= 8 rows of a decode step (M = B padded to 1, 2, 4 or 8).
 //
 // A tile is 16 logical output rows; the four wavefronts of a workgroup split
-// its K.  One unit of a wavefront is one load per lane shaped as the B
-// operand of MFMA 16x16x32 (tile column n = lane % 16, K quarter lane / 16):
-// int4: G/32 code words, one quantisation group of the row; bf16: 8 columns.
-// The staged activations are the A operand (batch row m = lane % 16; rows
-// past M repeat row M-1 and are never read back).  The MFMA sums over the K
+// its K.  A unit of a wavefront is 128 bytes of each of the tile's 16 rows
+// (int4: 256 codes; bf16: 64 columns), fetched by two LDS-DMA loads of 8 rows
+// x 128 bytes: whole cache lines, which stream almost as fast as contiguous
+// reads, where the MFMA operand order itself (16 rows x 64 bytes per load)
+// would not.  Each row's eight 16-byte chunks land XOR-swizzled by the row
+// index so that the operand reads below hit distinct banks.  The unit's
+// scale/zero words and the epilogue operands of its tile come in by DMA too,
+// and every wait is an explicit count of the DMAs issued since.
+//   The MFMA 16x16x32 takes the staged activations as A (batch row m = lane
+// % 16; rows past M repeat row M-1 and are never read back) and the weights
+// as B (tile column n = lane % 16, K quarter lane / 16).  It sums over the K
 // quarters itself, so no cross-lane reduction is needed: the four partial
 // tiles meet once in LDS at the end of a tile, where the epilogue runs.
 //   int4: per group, sum_k x (q - z) s = s * (sum_k x (128+q) - (128+z) sum_k x)
 //   with 128+q made by unpack_word and the group sums of x taken at staging.
 // Workgroups are persistent over tiles; each wavefront keeps kMvD units in
-// flight (weights, scale/zero word, and the epilogue operands of the unit's
-// tile), every load issued unconditionally so that each wait is a fixed
-// count.  Everything the prologue reads from memory is requested before the
-// first weights, so waiting for it never waits for the weight stream.
+// flight in its own LDS ring.
 // ===========================================================================
-constexpr int kMvD = 8;          // units in flight per wavefront
+constexpr int kMvD = 4;                 // units in flight per wavefront
 constexpr int kMvWgsPerCu = 2;
-constexpr int kMvHold = 4;       // staging items per thread held in registers
-constexpr int kMvPartHeld = 2;   // exit partials per thread held in registers
-
-struct MvEpi {
-  float a, b;
-  float2 cs;
-};
+constexpr int kMvHold = 4;              // staging items per thread held in registers
+constexpr int kMvPartHeld = 2;          // exit partials per thread held in registers
+constexpr int kMvSlotW = 2048;          // weight bytes of a unit (16 rows x 128 B)
+constexpr int kMvSlot = kMvSlotW + 3 * 256;   // + scale words + two epilogue operands
 
 // epilogue outputs per batch row of a tile: QKV 8 RoPE pairs, SwiGLU 8 products
 template <int EP> constexpr int mv_outs() { return (EP == kEpQKV || EP == kEpSwiGLU) ? 8 : 16; }
+// epilogue operands per item fetched with every unit (QKV cos/sin, residual
+// h_in, exit test h_in and the layer input)
+template <int EP> constexpr int mv_nepi() {
+  return EP == kEpQKV ? 2 : EP == kEpResid ? 1 : EP == kEpResidExit ? 2 : 0;
+}
 
 // weight row of logical row L (tile column L % 16 of tile L / 16)
 template <int EP>
@@ -788,16 +793,34 @@ __device__ __forceinline__ RowRef mv_row(const GemvParams &p, int L) {
   }
 }
 
+// LDS-DMA: lane L writes its 16 (4) bytes at lds + 16 L (lds + 4 L); `lds` is
+// wave-uniform.  Issued from inline assembly so that the compiler does not
+// wait for every outstanding DMA before each LDS read; the loop waits itself.
+__device__ __forceinline__ void dma16(uint32_t lds, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int M, int XS, int EP, int G>
 __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   extern __shared__ uint4 mv_smem[];
   constexpr int OUTS = mv_outs<EP>();
+  constexpr int NEPI = mv_nepi<EP>();
   constexpr int ITEMS = OUTS * M;                  // epilogue items per tile (<= 128)
   constexpr int IM = M < 4 ? M : 4;                // result rows per lane: 4 * (lane / 16) + i
-  constexpr int GW = G / 32;                       // int4 code words per lane per unit
+  constexpr int GW = G / 32;                       // int4 code words per lane per group
+  constexpr int NGU = 256 / G;                     // int4 groups per unit
   typedef typename WordsT<GW>::T WT;
   const int K = p.K, KG = K / G, xrow = K + 8;
-  uint16_t *xl = reinterpret_cast<uint16_t *>(mv_smem);           // [M][K + 8] bf16
+  char *ring = reinterpret_cast<char *>(mv_smem);                 // [4 waves][kMvD][kMvSlot]
+  uint16_t *xl = reinterpret_cast<uint16_t *>(ring + 4 * kMvD * kMvSlot);   // [M][K + 8] bf16
   float *xsg = reinterpret_cast<float *>(xl + M * xrow);          // [M][K / G] group sums
   float *red = xsg + M * KG;                                      // [2][4][M][16] partial tiles
   __shared__ float pred[4][4 * M];
@@ -810,6 +833,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   const int qq = lane >> 4, cl = lane & 15;
   const int mrow = cl < M ? cl : M - 1;            // A-operand row of this lane
   Control *ctl = p.ctrl;
+  char *wring = ring + wid * kMvD * kMvSlot;       // this wavefront's ring
+  const uint32_t wring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)wring);
 
   // ---- exit choice as far as it is known before the pending test (as in the
   // GEMV above: every workgroup of a QKV launch that has to take the test
@@ -823,154 +848,139 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   const bool int4_mode = p.exit_mode == RIVER_EXIT_INT4;
   const int pos = ctl->pos;
 
-  // ---- prologue loads (before any weight load): staging items, exit partials
-  const int n8 = K >> 3, total = M * n8;
-  float4 hv[kMvHold][2];
-  uint4 gv[kMvHold], bv[kMvHold];
-#pragma unroll
-  for (int j = 0; j < kMvHold; ++j) {
-    const int idx = min(tid + 256 * j, total - 1);
-    const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
-    if constexpr (XS == kXNorm) {
-      const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
-      hv[j][0] = *reinterpret_cast<const float4 *>(h);
-      hv[j][1] = *reinterpret_cast<const float4 *>(h + 4);
-      gv[j] = *reinterpret_cast<const uint4 *>(p.gain + 8 * g8);
-    } else {
-      bv[j] = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)m * p.x_stride + 8 * g8);
-    }
-  }
-  float pv[kMvPartHeld][3 * M];
-  if (pending) {
-#pragma unroll
-    for (int j = 0; j < kMvPartHeld; ++j) {
-      const int wg = min(tid + 256 * j, p.part_wgs - 1);
-      const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
-#pragma unroll
-      for (int i = 0; i < 3 * M; ++i) pv[j][i] = pp[i];
-    }
-  }
-
   // ---- per-thread epilogue state kept across tiles (the down projection has
   // no pending test, so its weight choice is final here)
   float ed = 0.f, ea = 0.f, eb = 0.f;
   uint64_t best = 0;
   const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && force0 < 0;
+  const float *hsrc = exit_sums ? p.h_src : p.h_in;
+  const int n8 = K >> 3, total = M * n8;
 
   // One pass for one weight form (Q4: int4 codes; else bf16 backbone or bf16
   // exit copy).  Returns true when the pending test chose the exit layer and
   // the weights this pass started to stream are the wrong ones.
   auto run = [&](auto qc, bool restart) -> bool {
     constexpr bool Q4 = decltype(qc)::value == 1;
-    constexpr int UK = Q4 ? G : 32;                // K columns per unit
-    const int KU = K / UK, U = (KU + 3) >> 2;      // units per tile row, per wavefront
+    constexpr int NDMA = 2 + (Q4 ? 1 : 0) + NEPI;  // DMAs per unit
+    constexpr int UKB = Q4 ? 256 : 64;             // K columns per unit
+    const int KU = K / UKB, U = (KU + 3) >> 2;     // units per tile row, per wavefront
     const int my_tiles = (ntile - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const float *hsrc = exit_sums ? p.h_src : p.h_in;
 
-    // load side: row pointers of the tile being fetched, and this thread's
-    // epilogue operands in it
+    // ---- fetch side: the tile being fetched (this lane's two weight rows,
+    // its scale row, its epilogue operands) and the next unit (lti, ls)
     int ltile = -1;
-    const uint32_t *qb = nullptr, *zb = nullptr;
-    const uint16_t *bb = nullptr;
-    const float2 *ep_cs = p.rope;
-    const float *ep_a = p.h_in, *ep_b = p.h_in;
-    auto set_tile = [&](int t) {
-      {
-        const int m = tid / OUTS, j = tid % OUTS;
-        if constexpr (EP == kEpQKV) {
-          const int hd = p.Dh >> 1;
-          ep_cs = p.rope + (int64_t)pos * hd + (t * 8 + j) % hd;
-        } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
-          const int n = min(t * 16 + j, p.N - 1), b = min(m, p.B - 1);
-          const int64_t o = (int64_t)b * p.h_io_stride + n;
-          ep_a = p.h_in + o;
-          ep_b = hsrc + o;
-        }
-        (void)m;
-      }
-      const RowRef rr = mv_row<EP>(p, t * 16 + cl);
+    const char *wr0 = nullptr, *wr1 = nullptr;     // weight rows 8h + lane / 8, as bytes
+    const uint32_t *zr = nullptr;                  // scale row lane / 4
+    const float *e0 = p.h_in, *e1 = p.h_in;        // epilogue operands of item 64 wid + lane
+    const int wchunk = 16 * ((lane & 7) ^ (((lane >> 3) >> 1) & 7));   // swizzled chunk, h = 0
+    const int wchunk1 = 16 * ((lane & 7) ^ ((((lane >> 3) + 8) >> 1) & 7));
+    auto weight_row = [&](int t, int r) -> const char * {
+      const RowRef rr = mv_row<EP>(p, t * 16 + r);
       const int row = rr.valid ? rr.row : 0;
       const int sg = rr.seg;
       if constexpr (Q4) {
-        qb = (sg == 0 ? p.w.q4[0] : sg == 1 ? p.w.q4[1] : p.w.q4[2]) + (int64_t)row * (K >> 3) + qq * GW;
-        zb = (sg == 0 ? p.w.sz[0] : sg == 1 ? p.w.sz[1] : p.w.sz[2]) + (int64_t)row * KG;
+        const uint32_t *q = sg == 0 ? p.w.q4[0] : sg == 1 ? p.w.q4[1] : p.w.q4[2];
+        return reinterpret_cast<const char *>(q + (int64_t)row * (K >> 3));
       } else {
         const uint16_t *b0 = ex ? p.w.ex_bf[0] : p.w.bf[0];
         const uint16_t *b1 = ex ? p.w.ex_bf[1] : p.w.bf[1];
         const uint16_t *b2 = ex ? p.w.ex_bf[2] : p.w.bf[2];
-        bb = (sg == 0 ? b0 : sg == 1 ? b1 : b2) + (int64_t)row * K + 8 * qq;
+        return reinterpret_cast<const char *>((sg == 0 ? b0 : sg == 1 ? b1 : b2) + (int64_t)row * K);
       }
     };
-    WT wq[kMvD];
-    uint32_t wz[kMvD];
-    v4u wb[kMvD];
-    MvEpi epi[kMvD];
-    auto epi_load = [&]() {
-      MvEpi e;
-      e.a = 0.f;
-      e.b = 0.f;
-      e.cs = make_float2(1.f, 0.f);
+    auto set_tile = [&](int t) {
+      wr0 = weight_row(t, lane >> 3);
+      wr1 = weight_row(t, 8 + (lane >> 3));
+      if constexpr (Q4) {
+        const RowRef rr = mv_row<EP>(p, t * 16 + (lane >> 2));
+        const int row = rr.valid ? rr.row : 0;
+        const int sg = rr.seg;
+        zr = (sg == 0 ? p.w.sz[0] : sg == 1 ? p.w.sz[1] : p.w.sz[2]) + (int64_t)row * KG;
+      }
+      const int item = 64 * wid + lane;
+      const int m = min(item / OUTS, p.B - 1), j = item % OUTS;
       if constexpr (EP == kEpQKV) {
-        e.cs = *ep_cs;
+        const int hd = p.Dh >> 1;
+        const float *cs = reinterpret_cast<const float *>(p.rope + (int64_t)pos * hd + (t * 8 + j) % hd);
+        e0 = cs;
+        e1 = cs + 1;
       } else if constexpr (EP == kEpResid || EP == kEpResidExit) {
-        e.a = *ep_a;
-        if constexpr (EP == kEpResidExit) e.b = *ep_b;
+        const int n = min(t * 16 + j, p.N - 1);
+        const int64_t o = (int64_t)m * p.h_io_stride + n;
+        e0 = p.h_in + o;
+        e1 = hsrc + o;
       }
-      return e;
     };
-    // the next unit to fetch: tile iteration lti, unit ls of the tile (past
-    // the last unit: the last unit again)
     int lti = 0, ls = 0;
-    auto load = [&](auto dc) {
+    auto fetch = [&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      const bool past = lti >= my_tiles;
+      const bool past = lti >= my_tiles;             // past the last unit: the last unit again
       const int ti = past ? my_tiles - 1 : lti, s = past ? U - 1 : ls;
       const int t = (int)blockIdx.x + ti * (int)gridDim.x;
       if (t != ltile) {
         set_tile(t);
         ltile = t;
       }
-      const int k0 = min(wid * U + s, KU - 1) * UK;
-      if constexpr (Q4) {
-        wq[d] = __builtin_nontemporal_load(reinterpret_cast<const WT *>(qb + (k0 >> 3)));
-        wz[d] = zb[k0 / G];
-      } else {
-        wb[d] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(bb + k0));
-      }
-      epi[d] = epi_load();
+      const int ku = min(wid * U + s, KU - 1);
+      const uint32_t slot = wring_lds + d * kMvSlot;
+      dma16(slot, wr0 + ku * 128 + wchunk);
+      dma16(slot + 1024, wr1 + ku * 128 + wchunk1);
+      if constexpr (Q4) dma4(slot + kMvSlotW, zr + ku * NGU + min(lane & 3, NGU - 1));
+      if constexpr (NEPI >= 1) dma4(slot + kMvSlotW + 256, e0);
+      if constexpr (NEPI >= 2) dma4(slot + kMvSlotW + 512, e1);
       if (++ls == U) {
         ls = 0;
         ++lti;
       }
     };
 
+    // ---- reduce one unit from ring slot d into tot
     f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+    // weight chunk c (16 bytes) of tile row cl inside a slot
+    const int rbase = (cl >> 3) * 1024 + 128 * (cl & 7);
+    const int rswz = (cl >> 1) & 7;
     auto compute = [&](auto dc, int k0) {
       constexpr int d = decltype(dc)::value;
+      const char *slot = wring + d * kMvSlot;
       const uint16_t *xa = xl + mrow * xrow + k0;
       if constexpr (Q4) {
-        f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+        uint32_t zw[NGU];
 #pragma unroll
-        for (int j = 0; j < GW; ++j) {
-          const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xa + qq * (G / 4) + 8 * j);
-          uint32_t w;
-          if constexpr (GW == 1) w = wq[d];
-          else w = wq[d][j];
-          uint32_t pr[4];
-          unpack_word(w, pr);
-          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              af, __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3])), ag, 0, 0, 0);
-        }
-        const float sc = bf_lo(wz[d]), zo = 128.0f + bf_hi(wz[d]);
-        const int g = k0 / G;
+        for (int g = 0; g < NGU; ++g) zw[g] = reinterpret_cast<const uint32_t *>(slot + kMvSlotW)[4 * cl + g];
 #pragma unroll
-        for (int i = 0; i < IM; ++i) {
-          const int m = min(4 * qq + i, M - 1);
-          tot[i] = fmaf(sc, ag[i] - zo * xsg[m * KG + g], tot[i]);
+        for (int g = 0; g < NGU; ++g) {
+          // this lane's G/4 codes of group g: chunk (G/64) g + qq / (64/G... ) of row cl
+          WT w;
+          if constexpr (G == 128) {
+            w = *reinterpret_cast<const WT *>(slot + rbase + 16 * ((4 * g + qq) ^ rswz));
+          } else {
+            w = *reinterpret_cast<const WT *>(slot + rbase + 16 * ((2 * g + (qq >> 1)) ^ rswz) + 8 * (qq & 1));
+          }
+          f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < GW; ++j) {
+            const bf16x8_t af =
+                *reinterpret_cast<const bf16x8_t *>(xa + g * G + qq * (G / 4) + 8 * j);
+            uint32_t pr[4];
+            unpack_word(w[j], pr);
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                af, __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3])), ag, 0, 0, 0);
+          }
+          const float sc = bf_lo(zw[g]), zo = 128.0f + bf_hi(zw[g]);
+          const int gg = k0 / G + g;
+#pragma unroll
+          for (int i = 0; i < IM; ++i) {
+            const int m = min(4 * qq + i, M - 1);
+            tot[i] = fmaf(sc, ag[i] - zo * xsg[m * KG + gg], tot[i]);
+          }
         }
       } else {
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xa + 8 * qq);
-        tot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, wb[d]), tot, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xa + 32 * j + 8 * qq);
+          const bf16x8_t bw = *reinterpret_cast<const bf16x8_t *>(slot + rbase + 16 * ((4 * j + qq) ^ rswz));
+          tot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, tot, 0, 0, 0);
+        }
       }
     };
 
@@ -992,7 +1002,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         auto y = [&](int n) {
           return (rb[n] + rb[M * 16 + n]) + (rb[2 * M * 16 + n] + rb[3 * M * 16 + n]);
         };
-        const MvEpi &e = epi[d];
+        // this thread's epilogue operands, fetched by its own wavefront
+        const float *eo = reinterpret_cast<const float *>(wring + d * kMvSlot + kMvSlotW + 256) + lane;
         if constexpr (EP == kEpQKV) {
           const int L0 = t * 16 + 2 * j;
           if (m < p.B && L0 < p.N) {
@@ -1001,8 +1012,9 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
             const int hh = P / hd, i = P % hd;
             float y0 = y(2 * j), y1 = y(2 * j + 1);
             if (hh < p.Hq + p.Hkv) {
-              const float a = y0 * e.cs.x - y1 * e.cs.y;
-              y1 = y1 * e.cs.x + y0 * e.cs.y;
+              const float c = eo[0], sn = eo[64];
+              const float a = y0 * c - y1 * sn;
+              y1 = y1 * c + y0 * sn;
               y0 = a;
             }
             if (hh < p.Hq) {
@@ -1028,11 +1040,12 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
           const int n = t * 16 + j;
           if (m < p.B && n < p.N) {
             const int64_t o = (int64_t)m * p.h_io_stride + n;
-            const float v = e.a + y(j);
+            const float v = eo[0] + y(j);
             p.h_out[o] = v;
             if (exit_sums) {
-              ed += e.b * v;
-              ea += e.b * e.b;
+              const float a = eo[64];
+              ed += a * v;
+              ea += a * a;
               eb += v * v;
             }
           }
@@ -1048,21 +1061,45 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
             best = key > best ? key : best;
           }
         }
+        (void)eo;
       }
     };
 
-    // ---- first weights in flight, then the prologue arithmetic
-    static_assert(kMvD == 8, "the ring is unrolled for 8 slots");
-    load(Buf<0>{});
-    load(Buf<1>{});
-    load(Buf<2>{});
-    load(Buf<3>{});
-    load(Buf<4>{});
-    load(Buf<5>{});
-    load(Buf<6>{});
-    load(Buf<7>{});
+    // ---- the first units in flight, then the prologue (its loads come after
+    // the weight DMAs: waiting for them waits for those DMAs too, but the
+    // ring is full by then and its first units are needed right after)
+    static_assert(kMvD == 4, "the ring is unrolled for 4 slots");
+    fetch(Buf<0>{});
+    fetch(Buf<1>{});
+    fetch(Buf<2>{});
+    fetch(Buf<3>{});
 
     if (!restart) {
+      float4 hv[kMvHold][2];
+      uint4 gv[kMvHold], bv[kMvHold];
+#pragma unroll
+      for (int j = 0; j < kMvHold; ++j) {
+        const int idx = min(tid + 256 * j, total - 1);
+        const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
+        if constexpr (XS == kXNorm) {
+          const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
+          hv[j][0] = *reinterpret_cast<const float4 *>(h);
+          hv[j][1] = *reinterpret_cast<const float4 *>(h + 4);
+          gv[j] = *reinterpret_cast<const uint4 *>(p.gain + 8 * g8);
+        } else {
+          bv[j] = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)m * p.x_stride + 8 * g8);
+        }
+      }
+      float pv[kMvPartHeld][3 * M];
+      if (pending) {
+#pragma unroll
+        for (int j = 0; j < kMvPartHeld; ++j) {
+          const int wg = min(tid + 256 * j, p.part_wgs - 1);
+          const float *pp = p.part + (int64_t)wg * kPartFloatsPerWG;
+#pragma unroll
+          for (int i = 0; i < 3 * M; ++i) pv[j][i] = pp[i];
+        }
+      }
       // RMSNorm sums of squares of the batch rows, and the exit partials of
       // the previous layer (pending test)
       float sums[4 * M];
@@ -1195,34 +1232,40 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         put(idx, a0, a1, a2, a3);
       }
       __syncthreads();
-      if (fired && !ex) return true;
+      if (fired && !ex) {
+        // the units in flight are the backbone's: let them land before the
+        // exit pass refills the same slots
+        wait_vm<0>();
+        return true;
+      }
     }
 
     // ---- main loop: unit n of the sequence sits in ring slot n % kMvD; the
-    // unit being reduced is unit cs of tile iteration cti
+    // unit being reduced is unit cs of tile iteration cti.  Before a unit is
+    // read, only the DMAs of the kMvD - 1 units fetched after it may still
+    // be in flight.
     int cti = 0, cs = 0;
     auto step = [&](auto dc) {
       if (cti < my_tiles) {
+        wait_vm<(kMvD - 1) * NDMA>();
         const int ku = wid * U + cs;
-        if (ku < KU) compute(dc, ku * UK);        // units past K (short rows) add nothing
+        if (ku < KU) compute(dc, ku * UKB);        // units past K (short rows) add nothing
         if (cs == U - 1) end_tile(dc, cti);
         if (++cs == U) {
           cs = 0;
           ++cti;
         }
       }
-      load(dc);
+      fetch(dc);
     };
     while (cti < my_tiles) {
       step(Buf<0>{});
       step(Buf<1>{});
       step(Buf<2>{});
       step(Buf<3>{});
-      step(Buf<4>{});
-      step(Buf<5>{});
-      step(Buf<6>{});
-      step(Buf<7>{});
     }
+    // the spare fetches past the end land before the workgroup leaves
+    wait_vm<0>();
     return false;
   };
 
@@ -1305,7 +1348,8 @@ static int num_cus() {
 
 // LDS bytes of one mgemv workgroup
 static size_t mgemv_lds(int M, int K, int G) {
-  return (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4 + (size_t)2 * 4 * M * 16 * 4;
+  return (size_t)4 * kMvD * kMvSlot + (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4 +
+         (size_t)2 * 4 * M * 16 * 4;
 }
 
 static int mgemv_ntile(Epilogue ep, const GemvParams &p) {
@@ -1316,9 +1360,9 @@ static int mgemv_ntile(Epilogue ep, const GemvParams &p) {
 bool mgemv_fits(Epilogue ep, const GemvParams &p) {
   const int M = p.B <= 1 ? 1 : p.B <= 2 ? 2 : p.B <= 4 ? 4 : 8;
   if (p.G != 64 && p.G != 128) return false;
-  if (p.K % 128 != 0 || p.K % p.G != 0) return false;
+  if (p.K % 256 != 0 || p.K % p.G != 0) return false;
   if (ep == kEpQKV && p.Dh % 16 != 0) return false;
-  return mgemv_lds(M, p.K, p.G) <= 80 * 1024;
+  return mgemv_lds(M, p.K, p.G) <= 120 * 1024;
 }
 
 struct MvPlan {
@@ -1473,9 +1517,12 @@ hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float thet
 // ===========================================================================
 int attn_chunk(int max_seq, int batch, int n_kv_heads) {
   const int pairs = batch * n_kv_heads;
-  // about 2048 workgroups, but at most 16 splits per (b, kv head): merging
-  // more costs more than the extra parallelism brings
-  const int target = std::min(16, (2048 + pairs - 1) / pairs);   // splits per (b, kv head)
+  // splits per (b, kv head): enough for about 512 workgroups (two per CU),
+  // and at least one per 1024 positions so that long caches stream through
+  // many workgroups at once; at most 16, as merging more costs more than the
+  // extra parallelism brings (measured on 8B shapes: B=1 and B=8 at 1K
+  // positions, B=8 at 16K)
+  const int target = std::min(16, std::max((512 + pairs - 1) / pairs, (max_seq + 1023) / 1024));
   int chunk = (max_seq + target - 1) / target;
   chunk = (chunk + kAttnSub - 1) / kAttnSub * kAttnSub;
   return chunk < kAttnSub ? kAttnSub : chunk;
@@ -1500,6 +1547,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   // masked once it has arrived
   const int t0 = split * p.chunk;
   const int n = p.ctrl->pos + 1;
+  // scores are kept in the base-2 domain: s * log2(e), so that every softmax
+  // exponential is one hardware 2^x (exp(a - b) = 2^(a log2 e - b log2 e))
+  const float scale2 = p.scale * 1.4426950408889634f;
   const int t1 = min(n, t0 + p.chunk);
   const int64_t kvbase = (((int64_t)b * p.Hkv + kvh) * p.S) * DH + ln * 8;
   const uint16_t *K = p.k_cache + kvbase;
@@ -1522,36 +1572,43 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
-  const int tend = min(t0 + p.chunk, p.S);
-  for (int sb = t0; sb < tend; sb += kAttnSub) {
-    if (sb > t0 && sb >= t1) break;
-    uint4 kr[NP], vr[NP];
-    bool ok[NP];
+  const int tend = min(t1, min(t0 + p.chunk, p.S));   // positions this workgroup reads
+  // K/V of one sub-chunk in registers, two sub-chunks in flight: the loads of
+  // the next are issued before the current one is reduced
+  uint4 kr[2][NP], vr[2][NP];
+  auto load = [&](auto bc, int sb) {
+    constexpr int bi = decltype(bc)::value;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int t = sb + i * PPP + wid * PPW + slot;
       const int tc = min(t, p.S - 1);
-      kr[i] = *reinterpret_cast<const uint4 *>(K + (int64_t)tc * DH);
-      vr[i] = *reinterpret_cast<const uint4 *>(V + (int64_t)tc * DH);
+      kr[bi][i] = *reinterpret_cast<const uint4 *>(K + (int64_t)tc * DH);
+      vr[bi][i] = *reinterpret_cast<const uint4 *>(V + (int64_t)tc * DH);
     }
+  };
+  auto reduce = [&](auto bc, int sb) {
+    constexpr int bi = decltype(bc)::value;
+    bool ok[NP];
+    uint4 kv[NP], vv[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int t = sb + i * PPP + wid * PPW + slot;
       ok[i] = t < t1;
-      if (!ok[i]) { kr[i] = make_uint4(0, 0, 0, 0); vr[i] = make_uint4(0, 0, 0, 0); }
+      kv[i] = ok[i] ? kr[bi][i] : make_uint4(0, 0, 0, 0);
+      vv[i] = ok[i] ? vr[bi][i] : make_uint4(0, 0, 0, 0);
     }
     float s[NP][GQ];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const float kf[8] = {bf_lo(kr[i].x), bf_hi(kr[i].x), bf_lo(kr[i].y), bf_hi(kr[i].y),
-                           bf_lo(kr[i].z), bf_hi(kr[i].z), bf_lo(kr[i].w), bf_hi(kr[i].w)};
+      const float kf[8] = {bf_lo(kv[i].x), bf_hi(kv[i].x), bf_lo(kv[i].y), bf_hi(kv[i].y),
+                           bf_lo(kv[i].z), bf_hi(kv[i].z), bf_lo(kv[i].w), bf_hi(kv[i].w)};
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = fmaf(qv[h][e], kf[e], d);
         d = LPP == 16 ? sum16(d) : sum8(d);   // the lanes of one position
-        s[i][h] = ok[i] ? d * p.scale : -INFINITY;
+        s[i][h] = ok[i] ? d * scale2 : -INFINITY;
       }
     }
 #pragma unroll
@@ -1568,21 +1625,40 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       mx = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
       const float mnew = fmaxf(m[h], mx);
       if (mnew == -INFINITY) continue;   // nothing visible yet in this wavefront
-      const float corr = expf(m[h] - mnew);
+      const float corr = exp2_fast(m[h] - mnew);
       l[h] *= corr;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
       m[h] = mnew;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const float pr = ok[i] ? expf(s[i][h] - mnew) : 0.f;
+        const float pr = ok[i] ? exp2_fast(s[i][h] - mnew) : 0.f;
         l[h] += pr;
-        const float vf[8] = {bf_lo(vr[i].x), bf_hi(vr[i].x), bf_lo(vr[i].y), bf_hi(vr[i].y),
-                             bf_lo(vr[i].z), bf_hi(vr[i].z), bf_lo(vr[i].w), bf_hi(vr[i].w)};
+        const float vf[8] = {bf_lo(vv[i].x), bf_hi(vv[i].x), bf_lo(vv[i].y), bf_hi(vv[i].y),
+                             bf_lo(vv[i].z), bf_hi(vv[i].z), bf_lo(vv[i].w), bf_hi(vv[i].w)};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
       }
     }
+  };
+  // the first sub-chunk was requested before the position was known (t0 is
+  // always a valid position); the last one is reduced without a prefetch
+  load(Buf<0>{}, t0);
+  for (int sb = t0; sb < tend;) {
+    if (sb + kAttnSub >= tend) {
+      reduce(Buf<0>{}, sb);
+      break;
+    }
+    load(Buf<1>{}, sb + kAttnSub);
+    reduce(Buf<0>{}, sb);
+    sb += kAttnSub;
+    if (sb + kAttnSub >= tend) {
+      reduce(Buf<1>{}, sb);
+      break;
+    }
+    load(Buf<0>{}, sb + kAttnSub);
+    reduce(Buf<1>{}, sb);
+    sb += kAttnSub;
   }
   // per-slot results to LDS; m is uniform over the wavefront
   if (lane == 0) {
@@ -1611,7 +1687,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     if (M != -INFINITY) {
 #pragma unroll
       for (int wv = 0; wv < 4; ++wv) {
-        const float f = expf(wm[wv][h] - M);
+        const float f = exp2_fast(wm[wv][h] - M);
         float lw = 0.f, ow = 0.f;
 #pragma unroll
         for (int sl = 0; sl < PPW; ++sl) {
@@ -1656,12 +1732,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) mx = fmaxf(mx, ms[u]);
         if (mx == -INFINITY) continue;
-        const float corr = expf(M - mx);
+        const float corr = exp2_fast(M - mx);
         L *= corr;
         O *= corr;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const float f = expf(ms[u] - mx);
+          const float f = exp2_fast(ms[u] - mx);
           L = fmaf(f, ls[u], L);
           O = fmaf(f, os[u], O);
         }

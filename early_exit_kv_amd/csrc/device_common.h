@@ -15,6 +15,8 @@ typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // N consecutive 32-bit words as one load
+// LDS pointer type (for the LDS byte address of a __shared__ object)
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 template <int N_> struct WordsT;
 template <> struct WordsT<1> { typedef uint32_t T; };
 template <> struct WordsT<2> { typedef v2u T; };
@@ -169,6 +171,9 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&pr)[4]) {
   pr[2] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05010400u);
   pr[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x05030402u);
 }
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Exit choice of a layer, read at the start of every kernel of that layer.
 __device__ __forceinline__ bool layer_uses_exit(const Control *c, int layer) {

@@ -902,7 +902,6 @@ constexpr int kPThreads = 512, kPBufs = 3;
 constexpr int kPTileSlots = kPBM * kPKT / 8;      // 16-byte slots of rows per k-tile (2048)
 constexpr int kPCodeSlots = kPBN * kPKT / 32;     // 16-byte slots of int4 codes per k-tile (512)
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 template <int G, int EP, bool Q4>
 __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs, float *xsg,

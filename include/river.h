@@ -189,8 +189,8 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     64 giving at most 512 splits of max_seq;
  *   RIVER_OPT_GEMV    linears of decode steps of at most 8 rows: 0 on the
  *                     matrix cores wherever the shape allows (group size 64
- *                     or 128, K a multiple of 128, the rows of one step
- *                     within 80 KB of LDS), 1 (default) always on the
+ *                     or 128, K a multiple of 256, the rows of one step and
+ *                     the load rings within 120 KB of LDS), 1 (default) on the
  *                     dot-product GEMV.  Both give the same results up to
  *                     the fp32 summation order. */
 enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4,
