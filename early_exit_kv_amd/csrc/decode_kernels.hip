@@ -142,9 +142,10 @@ __device__ __forceinline__ RowRef map_row(const GemvParams &p, int L, int wave_f
 //   so that the accumulators and both buffers stay in registers.
 template <int EP, int M> struct GemvTile {
   static constexpr bool wide = EP == kEpResidExit || EP == kEpLogits;   // long rows / many rows
-  static constexpr int R = wide ? (M >= 8 ? 1 : 2) : EP == kEpSwiGLU ? (M >= 4 ? 2 : M == 2 ? 4 : 8)
-                                                                     : (M >= 8 ? 2 : 4);
-  static constexpr int UQ = wide ? (M >= 4 ? 4 : 8) : (M >= 4 ? 1 : 2);
+  // (the LM head streams best in 4 KB tasks: one row, four chunks per lane)
+  static constexpr int R = wide ? (M >= 8 || EP == kEpLogits ? 1 : 2)
+                                : EP == kEpSwiGLU ? (M >= 4 ? 2 : M == 2 ? 4 : 8) : (M >= 8 ? 2 : 4);
+  static constexpr int UQ = wide ? (M >= 4 || EP == kEpLogits ? 4 : 8) : (M >= 4 ? 1 : 2);
   static constexpr int UB = UQ;
 };
 constexpr int kGemvWgsPerCu = 2;
@@ -761,7 +762,6 @@ constexpr int kMvWgsPerCu = 2;
 constexpr int kMvHold = 4;              // staging items per thread held in registers
 constexpr int kMvPartHeld = 2;          // exit partials per thread held in registers
 constexpr int kMvSlotW = 2048;          // weight bytes of a unit (16 rows x 128 B)
-constexpr int kMvSlot = kMvSlotW + 3 * 256;   // + scale words + two epilogue operands
 
 // epilogue outputs per batch row of a tile: QKV 8 RoPE pairs, SwiGLU 8 products
 template <int EP> constexpr int mv_outs() { return (EP == kEpQKV || EP == kEpSwiGLU) ? 8 : 16; }
@@ -769,6 +769,20 @@ template <int EP> constexpr int mv_outs() { return (EP == kEpQKV || EP == kEpSwi
 // h_in, exit test h_in and the layer input)
 template <int EP> constexpr int mv_nepi() {
   return EP == kEpQKV ? 2 : EP == kEpResid ? 1 : EP == kEpResidExit ? 2 : 0;
+}
+// bytes of a ring slot: weights, scale/zero words, epilogue operands
+template <int EP> constexpr int mv_slot() { return kMvSlotW + 256 + 256 * mv_nepi<EP>(); }
+static int mv_slot_bytes(Epilogue ep) {
+  return kMvSlotW + 256 + 256 * (ep == kEpQKV ? 2 : ep == kEpResid ? 1 : ep == kEpResidExit ? 2 : 0);
+}
+
+// f(Buf<I>{}) for I = I0 .. N-1, unrolled at compile time
+template <int I, int N, class F>
+__device__ __forceinline__ void for_slots(F &f) {
+  if constexpr (I < N) {
+    f(Buf<I>{});
+    for_slots<I + 1, N>(f);
+  }
 }
 
 // weight row of logical row L (tile column L % 16 of tile L / 16)
@@ -813,6 +827,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   extern __shared__ uint4 mv_smem[];
   constexpr int OUTS = mv_outs<EP>();
   constexpr int NEPI = mv_nepi<EP>();
+  constexpr int kMvSlot = mv_slot<EP>();
   constexpr int ITEMS = OUTS * M;                  // epilogue items per tile (<= 128)
   constexpr int IM = M < 4 ? M : 4;                // result rows per lane: 4 * (lane / 16) + i
   constexpr int GW = G / 32;                       // int4 code words per lane per group
@@ -1068,11 +1083,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
     // ---- the first units in flight, then the prologue (its loads come after
     // the weight DMAs: waiting for them waits for those DMAs too, but the
     // ring is full by then and its first units are needed right after)
-    static_assert(kMvD == 4, "the ring is unrolled for 4 slots");
-    fetch(Buf<0>{});
-    fetch(Buf<1>{});
-    fetch(Buf<2>{});
-    fetch(Buf<3>{});
+    for_slots<0, kMvD>(fetch);
 
     if (!restart) {
       float4 hv[kMvHold][2];
@@ -1258,12 +1269,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
       }
       fetch(dc);
     };
-    while (cti < my_tiles) {
-      step(Buf<0>{});
-      step(Buf<1>{});
-      step(Buf<2>{});
-      step(Buf<3>{});
-    }
+    while (cti < my_tiles) for_slots<0, kMvD>(step);
     // the spare fetches past the end land before the workgroup leaves
     wait_vm<0>();
     return false;
@@ -1347,8 +1353,8 @@ static int num_cus() {
 }
 
 // LDS bytes of one mgemv workgroup
-static size_t mgemv_lds(int M, int K, int G) {
-  return (size_t)4 * kMvD * kMvSlot + (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4 +
+static size_t mgemv_lds(Epilogue ep, int M, int K, int G) {
+  return (size_t)4 * kMvD * mv_slot_bytes(ep) + (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4 +
          (size_t)2 * 4 * M * 16 * 4;
 }
 
@@ -1362,7 +1368,7 @@ bool mgemv_fits(Epilogue ep, const GemvParams &p) {
   if (p.G != 64 && p.G != 128) return false;
   if (p.K % 256 != 0 || p.K % p.G != 0) return false;
   if (ep == kEpQKV && p.Dh % 16 != 0) return false;
-  return mgemv_lds(M, p.K, p.G) <= 120 * 1024;
+  return mgemv_lds(ep, M, p.K, p.G) <= 120 * 1024;
 }
 
 struct MvPlan {
@@ -1375,7 +1381,7 @@ template <int M, int XS, int EP>
 static MvPlan mgemv_plan_t(Epilogue ep, const GemvParams &p) {
   MvPlan g;
   g.ntile = mgemv_ntile(ep, p);
-  g.lds = mgemv_lds(M, p.K, p.G);
+  g.lds = mgemv_lds(ep, M, p.K, p.G);
   g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64>)
                    : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128>);
   // 160 KB of LDS per CU, a few KB of it static per workgroup
@@ -1406,7 +1412,14 @@ static MvPlan mgemv_plan(Epilogue ep, const GemvParams &p) {
   }
 }
 
-static bool use_mgemv(Epilogue ep, const GemvParams &p) { return !p.dot_gemv && mgemv_fits(ep, p); }
+// GEMV choice: mode 1 the dot-product kernel everywhere, mode 2 the
+// matrix-core one wherever it fits, mode 0 (default) the one measured faster
+// per linear at one or two rows (matrix cores for gate|up and down)
+static bool use_mgemv(Epilogue ep, const GemvParams &p) {
+  if (p.gemv_mode == 1 || !mgemv_fits(ep, p)) return false;
+  if (p.gemv_mode == 2) return true;
+  return p.B <= 2 && (ep == kEpSwiGLU || ep == kEpResidExit);
+}
 
 struct GemvPlan {
   int grid, ntask, kslab;

@@ -163,7 +163,7 @@ struct river_ctx {
   char *rec = nullptr;
   size_t rec_bytes = 0;
   int attn_chunk = 0;   // positions per decode-attention workgroup (0: chosen per shape)
-  int dot_gemv = 1;     // 1: decode linears on the dot-product GEMV only
+  int gemv_mode = 0;    // RIVER_OPT_GEMV
 };
 
 namespace {
@@ -433,7 +433,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     const river_layer_w &L = ctx->layers[l];
     GemvParams g{};
     g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl; g.B = B;
-    g.dot_gemv = ctx->dot_gemv;
+    g.gemv_mode = ctx->gemv_mode;
     g.gshift = __builtin_ctz((unsigned)c.group_size);
     g.eps = c.rms_eps; g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim;
     g.max_seq = c.max_seq; g.max_batch = c.max_batch; g.rope_theta = c.rope_theta;
@@ -495,7 +495,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   RV_TRY(rec.put(-1, 0, hA, hbytes));
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
-  lm.dot_gemv = ctx->dot_gemv;
+  lm.gemv_mode = ctx->gemv_mode;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
   lm.gshift = __builtin_ctz((unsigned)c.group_size);
   lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
@@ -587,7 +587,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
                                 logits, next, 1);
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
-  lm.dot_gemv = ctx->dot_gemv;
+  lm.gemv_mode = ctx->gemv_mode;
   lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
   lm.gshift = __builtin_ctz((unsigned)c.group_size);
   lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
@@ -823,8 +823,8 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
       drop_graphs(ctx);
       return RIVER_OK;
     case RIVER_OPT_GEMV:
-      if (value != 0 && value != 1) return RIVER_E_INVALID_ARG;
-      ctx->dot_gemv = (int)value;
+      if (value < 0 || value > 2) return RIVER_E_INVALID_ARG;
+      ctx->gemv_mode = (int)value;
       drop_graphs(ctx);
       return RIVER_OK;
     case RIVER_OPT_PROFILE:
@@ -930,7 +930,7 @@ int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t us
     GemvParams g{};
     fill_weights(ctx, layer, linear, 1, g.w);
     g.N = sh[linear].N; g.K = sh[linear].K; g.G = c.group_size;
-    g.dot_gemv = ctx->dot_gemv;
+    g.gemv_mode = ctx->gemv_mode;
     g.gshift = __builtin_ctz((unsigned)c.group_size);
     g.layer = layer; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl; g.B = M;
     g.x_src = static_cast<const uint16_t *>(d_x); g.x_stride = sh[linear].K;

@@ -143,7 +143,7 @@ struct GemvParams {
   int path;                       // PathChoice
   float *y_out; int64_t y_stride; // kEpPlain: fp32 [B][N]
   float *logits; int32_t *next; int is_prefill; int vocab;// LM head
-  int dot_gemv;                   // 1: the dot-product GEMV even where the MFMA one fits
+  int gemv_mode;                  // 0 per-linear choice, 1 dot-product GEMV, 2 MFMA GEMV where it fits
 };
 
 

@@ -286,10 +286,10 @@ class River:
         """-1: decide with tau; e in 0..L: layers < e backbone, the rest exit layers."""
         self.set_option(RIVER_OPT_FORCE_E, e)
 
-    def use_dot_gemv(self, on=True):
-        """Decode linears of <= 8 rows on the dot-product GEMV (else on the
-        matrix cores wherever the shape allows)."""
-        self.set_option(RIVER_OPT_GEMV, 1 if on else 0)
+    def gemv_mode(self, mode):
+        """Kernel of decode linears of <= 8 rows: "auto" (per linear), "dot"
+        (dot-product GEMV) or "mfma" (matrix-core GEMV where it fits)."""
+        self.set_option(RIVER_OPT_GEMV, {"auto": 0, "dot": 1, "mfma": 2}[mode])
 
     def profile(self, on=True):
         """Time every kernel with HIP events (decode steps then launch eagerly)."""

@@ -187,12 +187,14 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *   RIVER_OPT_ATTN_CHUNK positions per decode-attention workgroup: 0 (default)
  *                     lets the library choose per shape, else a multiple of
  *                     64 giving at most 512 splits of max_seq;
- *   RIVER_OPT_GEMV    linears of decode steps of at most 8 rows: 0 on the
- *                     matrix cores wherever the shape allows (group size 64
- *                     or 128, K a multiple of 256, the rows of one step and
- *                     the load rings within 120 KB of LDS), 1 (default) on the
- *                     dot-product GEMV.  Both give the same results up to
- *                     the fp32 summation order. */
+ *   RIVER_OPT_GEMV    kernel of the linears of decode steps of at most 8
+ *                     rows: 1 the dot-product GEMV, 2 the matrix-core GEMV
+ *                     wherever the shape allows (group size 64 or 128, K a
+ *                     multiple of 256, the step's rows and the load rings
+ *                     within 120 KB of LDS), 0 (default) per linear the one
+ *                     that is faster (the matrix-core GEMV for gate|up and
+ *                     down at one or two rows).  All give the same results
+ *                     up to the fp32 summation order. */
 enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4,
        RIVER_OPT_GEMV = 5 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);

@@ -67,11 +67,23 @@ def test_linear_cores_8b(ctx8b, M, use_exit):
 def test_linear_mfma_gemv_8b(ctx8b, M, use_exit):
     """The matrix-core GEMV of decode steps (where it fits) on the same shapes."""
     _, _, r = ctx8b
-    r.use_dot_gemv(False)
+    r.gemv_mode("mfma")
     try:
         check_linears(ctx8b, M, use_exit)
     finally:
-        r.use_dot_gemv(True)
+        r.gemv_mode("auto")
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("use_exit", [0, 1])
+def test_linear_dot_gemv_8b(ctx8b, M, use_exit):
+    """The dot-product GEMV on the same shapes."""
+    _, _, r = ctx8b
+    r.gemv_mode("dot")
+    try:
+        check_linears(ctx8b, M, use_exit)
+    finally:
+        r.gemv_mode("auto")
 
 
 @pytest.mark.parametrize("M", [9, 32, 33, 64])

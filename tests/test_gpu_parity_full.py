@@ -39,7 +39,7 @@ def host_weights(w, dtype=np.float64):
             "layers": [{k: cv(v) for k, v in lw.items()} for lw in w["layers"]]}
 
 
-def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", dot_gemv=True):
+def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto"):
     """Prefill + decode steps on the GPU with every pass checked stage by stage
     (teacher forcing at each stored activation), and a free-running oracle
     beside it for the exit decisions and the K/V cosine bar."""
@@ -49,7 +49,7 @@ def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", dot_gemv=True):
     print(f"[parity-full] {shape.name} L={L} B={B} T={T} steps={steps} tau={tau}", flush=True)
     sh = synth.shrink(shape, n_layers=L)
     r = rv.River(sh, w_dev, B, max_seq)
-    r.use_dot_gemv(dot_gemv)
+    r.gemv_mode(gemv)
     r.build_exit_layers(mode)
     r.record(B * T)
     hw = host_weights(w_dev)
@@ -150,7 +150,7 @@ def test_decode_parity_8b_layer_shapes(w8b, tau):
 
 def test_decode_parity_8b_mfma_gemv(w8b):
     """Every decode linear on the matrix-core GEMV."""
-    parity_run(synth.LLAMA_8B, w8b, B=1, T=12, steps=3, tau=0.5, dot_gemv=False)
+    parity_run(synth.LLAMA_8B, w8b, B=1, T=12, steps=3, tau=0.5, gemv="mfma")
 
 
 def test_decode_parity_1b_layer_shapes_tied(w1b):
@@ -197,7 +197,7 @@ def test_prefill_ragged_rows_tiny():
 def test_prefill_ragged_rows_tiny_mfma_gemv():
     """Three rows per decode step (padded to four) on the matrix-core GEMV."""
     w = synth.make_weights(synth.TINY, seed=0, device="cuda")
-    parity_run(synth.TINY, w, B=3, T=45, steps=2, tau=0.5, dot_gemv=False)
+    parity_run(synth.TINY, w, B=3, T=45, steps=2, tau=0.5, gemv="mfma")
 
 
 def test_decode_parity_8b_batch8_mfma_gemv(w8b):
@@ -205,4 +205,9 @@ def test_decode_parity_8b_batch8_mfma_gemv(w8b):
     projection (its rows too wide for LDS) on the dot-product GEMV."""
     w = dict(w8b)
     w["layers"] = w8b["layers"][:2]
-    parity_run(synth.LLAMA_8B, w, B=8, T=6, steps=2, tau=0.3, dot_gemv=False)
+    parity_run(synth.LLAMA_8B, w, B=8, T=6, steps=2, tau=0.3, gemv="mfma")
+
+
+def test_decode_parity_8b_dot_gemv(w8b):
+    """Every decode linear on the dot-product GEMV."""
+    parity_run(synth.LLAMA_8B, w8b, B=1, T=12, steps=3, tau=0.5, gemv="dot")
