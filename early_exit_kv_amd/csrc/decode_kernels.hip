@@ -770,10 +770,14 @@ template <int EP> constexpr int mv_outs() { return (EP == kEpQKV || EP == kEpSwi
 template <int EP> constexpr int mv_nepi() {
   return EP == kEpQKV ? 2 : EP == kEpResid ? 1 : EP == kEpResidExit ? 2 : 0;
 }
-// bytes of a ring slot: weights, scale/zero words, epilogue operands
-template <int EP> constexpr int mv_slot() { return kMvSlotW + 256 + 256 * mv_nepi<EP>(); }
-static int mv_slot_bytes(Epilogue ep) {
-  return kMvSlotW + 256 + 256 * (ep == kEpQKV ? 2 : ep == kEpResid ? 1 : ep == kEpResidExit ? 2 : 0);
+// bytes of a ring slot: weights, scale/zero words, epilogue operands, and
+// with XR the unit's slice of the M activation rows (256 columns each)
+template <int EP, int M, bool XR> constexpr int mv_slot() {
+  return kMvSlotW + 256 + 256 * mv_nepi<EP>() + (XR ? 512 * M : 0);
+}
+static int mv_slot_bytes(Epilogue ep, int M, bool xr) {
+  return kMvSlotW + 256 + 256 * (ep == kEpQKV ? 2 : ep == kEpResid ? 1 : ep == kEpResidExit ? 2 : 0) +
+         (xr ? 512 * M : 0);
 }
 
 // f(Buf<I>{}) for I = I0 .. N-1, unrolled at compile time
@@ -822,12 +826,17 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int M, int XS, int EP, int G>
+// XR: the activation rows do not fit LDS whole (bf16 input only); each unit
+// then brings its 256-column slice of them through the ring as well, and the
+// group sums of x come from one more MFMA against a B operand of ones.
+template <int M, int XS, int EP, int G, bool XR>
 __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
+  static_assert(!XR || (XS == kXBf16 && M >= 2), "ring-fed rows: bf16 input, two rows or more");
   extern __shared__ uint4 mv_smem[];
   constexpr int OUTS = mv_outs<EP>();
   constexpr int NEPI = mv_nepi<EP>();
-  constexpr int kMvSlot = mv_slot<EP>();
+  constexpr int kMvSlot = mv_slot<EP, M, XR>();
+  constexpr int kOffX = kMvSlotW + 256 + 256 * NEPI;   // activation slice in a slot (XR)
   constexpr int ITEMS = OUTS * M;                  // epilogue items per tile (<= 128)
   constexpr int IM = M < 4 ? M : 4;                // result rows per lane: 4 * (lane / 16) + i
   constexpr int GW = G / 32;                       // int4 code words per lane per group
@@ -836,8 +845,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   const int K = p.K, KG = K / G, xrow = K + 8;
   char *ring = reinterpret_cast<char *>(mv_smem);                 // [4 waves][kMvD][kMvSlot]
   uint16_t *xl = reinterpret_cast<uint16_t *>(ring + 4 * kMvD * kMvSlot);   // [M][K + 8] bf16
-  float *xsg = reinterpret_cast<float *>(xl + M * xrow);          // [M][K / G] group sums
-  float *red = xsg + M * KG;                                      // [2][4][M][16] partial tiles
+  float *xsg = reinterpret_cast<float *>(xl + (XR ? 0 : M * xrow));         // [M][K / G] group sums
+  float *red = xsg + (XR ? 0 : M * KG);                           // [2][4][M][16] partial tiles
   __shared__ float pred[4][4 * M];
   __shared__ float tred[ITEMS][3];
   __shared__ uint64_t tkey[ITEMS];
@@ -876,7 +885,10 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   // the weights this pass started to stream are the wrong ones.
   auto run = [&](auto qc, bool restart) -> bool {
     constexpr bool Q4 = decltype(qc)::value == 1;
-    constexpr int NDMA = 2 + (Q4 ? 1 : 0) + NEPI;  // DMAs per unit
+    // XR: the unit's activation slice, M rows of CR 16-byte chunks, in NX DMAs
+    constexpr int CR = (Q4 ? 256 : 64) / 8;
+    constexpr int NX = XR ? (M * CR * 16 + 1023) / 1024 : 0;
+    constexpr int NDMA = 2 + (Q4 ? 1 : 0) + NEPI + NX;  // DMAs per unit
     constexpr int UKB = Q4 ? 256 : 64;             // K columns per unit
     const int KU = K / UKB, U = (KU + 3) >> 2;     // units per tile row, per wavefront
     const int my_tiles = (ntile - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
@@ -943,6 +955,17 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
       if constexpr (Q4) dma4(slot + kMvSlotW, zr + ku * NGU + min(lane & 3, NGU - 1));
       if constexpr (NEPI >= 1) dma4(slot + kMvSlotW + 256, e0);
       if constexpr (NEPI >= 2) dma4(slot + kMvSlotW + 512, e1);
+      if constexpr (XR) {
+        // 16-byte chunk c of row m lands at chunk CR m + (c ^ m) of the slice,
+        // so that the rows of one operand read sit in distinct banks (chunks
+        // past the M rows, when a DMA is not full, repeat a valid one)
+#pragma unroll
+        for (int h = 0; h < NX; ++h) {
+          const int P = 64 * h + lane, m = P / CR, c = (P % CR) ^ (m & (CR - 1));
+          dma16(slot + kOffX + 1024 * h,
+                p.x_src + (int64_t)min(m, p.B - 1) * p.x_stride + ku * (CR * 8) + 8 * (c & (CR - 1)));
+        }
+      }
       if (++ls == U) {
         ls = 0;
         ++lti;
@@ -954,10 +977,21 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
     // weight chunk c (16 bytes) of tile row cl inside a slot
     const int rbase = (cl >> 3) * 1024 + 128 * (cl & 7);
     const int rswz = (cl >> 1) & 7;
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
     auto compute = [&](auto dc, int k0) {
       constexpr int d = decltype(dc)::value;
       const char *slot = wring + d * kMvSlot;
       const uint16_t *xa = xl + mrow * xrow + k0;
+      // A operand: 8 columns of this lane's row at column kk of the unit
+      auto a_op = [&](int kk) -> bf16x8_t {
+        if constexpr (XR) {
+          constexpr int CRc = (Q4 ? 256 : 64) / 8;
+          const int c = kk >> 3;
+          return *reinterpret_cast<const bf16x8_t *>(slot + kOffX + 16 * (CRc * mrow + (c ^ (mrow & (CRc - 1)))));
+        } else {
+          return *reinterpret_cast<const bf16x8_t *>(xa + kk);
+        }
+      };
       if constexpr (Q4) {
         uint32_t zw[NGU];
 #pragma unroll
@@ -971,28 +1005,29 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
           } else {
             w = *reinterpret_cast<const WT *>(slot + rbase + 16 * ((2 * g + (qq >> 1)) ^ rswz) + 8 * (qq & 1));
           }
-          f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, as = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int j = 0; j < GW; ++j) {
-            const bf16x8_t af =
-                *reinterpret_cast<const bf16x8_t *>(xa + g * G + qq * (G / 4) + 8 * j);
+            const bf16x8_t af = a_op(g * G + qq * (G / 4) + 8 * j);
             uint32_t pr[4];
             unpack_word(w[j], pr);
             ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 af, __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3])), ag, 0, 0, 0);
+            if constexpr (XR) as = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, as, 0, 0, 0);
           }
           const float sc = bf_lo(zw[g]), zo = 128.0f + bf_hi(zw[g]);
           const int gg = k0 / G + g;
 #pragma unroll
           for (int i = 0; i < IM; ++i) {
             const int m = min(4 * qq + i, M - 1);
-            tot[i] = fmaf(sc, ag[i] - zo * xsg[m * KG + gg], tot[i]);
+            const float xs = XR ? as[i] : xsg[m * KG + gg];
+            tot[i] = fmaf(sc, ag[i] - zo * xs, tot[i]);
           }
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xa + 32 * j + 8 * qq);
+          const bf16x8_t af = a_op(32 * j + 8 * qq);
           const bf16x8_t bw = *reinterpret_cast<const bf16x8_t *>(slot + rbase + 16 * ((4 * j + qq) ^ rswz));
           tot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, tot, 0, 0, 0);
         }
@@ -1085,7 +1120,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
     // ring is full by then and its first units are needed right after)
     for_slots<0, kMvD>(fetch);
 
-    if (!restart) {
+    if (!restart && !XR) {
       float4 hv[kMvHold][2];
       uint4 gv[kMvHold], bv[kMvHold];
 #pragma unroll
@@ -1353,8 +1388,9 @@ static int num_cus() {
 }
 
 // LDS bytes of one mgemv workgroup
-static size_t mgemv_lds(Epilogue ep, int M, int K, int G) {
-  return (size_t)4 * kMvD * mv_slot_bytes(ep) + (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4 +
+static size_t mgemv_lds(Epilogue ep, int M, int K, int G, bool xr) {
+  return (size_t)4 * kMvD * mv_slot_bytes(ep, M, xr) +
+         (xr ? 0 : (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4) +
          (size_t)2 * 4 * M * 16 * 4;
 }
 
@@ -1363,12 +1399,22 @@ static int mgemv_ntile(Epilogue ep, const GemvParams &p) {
   return (p.N + 15) / 16;
 }
 
+constexpr size_t kMvMaxLds = 120 * 1024;
+
+// the activation rows come through the ring (they do not fit LDS whole, and
+// the input is bf16 rows of two or more)
+static bool mgemv_xr(Epilogue ep, const GemvParams &p) {
+  const int M = p.B <= 1 ? 1 : p.B <= 2 ? 2 : p.B <= 4 ? 4 : 8;
+  const bool bf16_in = ep == kEpResid || ep == kEpResidExit || ep == kEpPlain;
+  return bf16_in && M >= 2 && mgemv_lds(ep, M, p.K, p.G, false) > kMvMaxLds;
+}
+
 bool mgemv_fits(Epilogue ep, const GemvParams &p) {
   const int M = p.B <= 1 ? 1 : p.B <= 2 ? 2 : p.B <= 4 ? 4 : 8;
   if (p.G != 64 && p.G != 128) return false;
   if (p.K % 256 != 0 || p.K % p.G != 0) return false;
   if (ep == kEpQKV && p.Dh % 16 != 0) return false;
-  return mgemv_lds(ep, M, p.K, p.G) <= 120 * 1024;
+  return mgemv_lds(ep, M, p.K, p.G, mgemv_xr(ep, p)) <= kMvMaxLds;
 }
 
 struct MvPlan {
@@ -1381,9 +1427,20 @@ template <int M, int XS, int EP>
 static MvPlan mgemv_plan_t(Epilogue ep, const GemvParams &p) {
   MvPlan g;
   g.ntile = mgemv_ntile(ep, p);
-  g.lds = mgemv_lds(ep, M, p.K, p.G);
-  g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64>)
-                   : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128>);
+  const bool xr = mgemv_xr(ep, p);
+  g.lds = mgemv_lds(ep, M, p.K, p.G, xr);
+  if constexpr (XS == kXBf16 && M >= 2) {
+    if (xr) {
+      g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64, true>)
+                       : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128, true>);
+    } else {
+      g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64, false>)
+                       : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128, false>);
+    }
+  } else {
+    g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64, false>)
+                     : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128, false>);
+  }
   // 160 KB of LDS per CU, a few KB of it static per workgroup
   const int fit = (int)((160 * 1024) / (g.lds + 4 * 1024));
   const int per_cu = std::max(1, std::min(kMvWgsPerCu, fit));
@@ -1414,11 +1471,16 @@ static MvPlan mgemv_plan(Epilogue ep, const GemvParams &p) {
 
 // GEMV choice: mode 1 the dot-product kernel everywhere, mode 2 the
 // matrix-core one wherever it fits, mode 0 (default) the one measured faster
-// per linear at one or two rows (matrix cores for gate|up and down)
+// per linear on 8B shapes: at one or two rows the matrix cores for gate|up
+// and down only (the dot-product GEMV's arithmetic is still hidden behind
+// its stream there), from three rows on for every linear that fits (the dot
+// products grow with the rows, the MFMA work does not), except the LM head
+// at four rows
 static bool use_mgemv(Epilogue ep, const GemvParams &p) {
   if (p.gemv_mode == 1 || !mgemv_fits(ep, p)) return false;
   if (p.gemv_mode == 2) return true;
-  return p.B <= 2 && (ep == kEpSwiGLU || ep == kEpResidExit);
+  if (p.B <= 2) return ep == kEpSwiGLU || ep == kEpResidExit;
+  return !(ep == kEpLogits && p.B <= 4);
 }
 
 struct GemvPlan {

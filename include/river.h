@@ -192,9 +192,11 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     wherever the shape allows (group size 64 or 128, K a
  *                     multiple of 256, the step's rows and the load rings
  *                     within 120 KB of LDS), 0 (default) per linear the one
- *                     that is faster (the matrix-core GEMV for gate|up and
- *                     down at one or two rows).  All give the same results
- *                     up to the fp32 summation order. */
+ *                     measured faster (at one or two rows the matrix-core
+ *                     GEMV for gate|up and down only, from three rows on for
+ *                     every linear it fits but the LM head at four rows).
+ *                     All give the same results up to the fp32 summation
+ *                     order. */
 enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4,
        RIVER_OPT_GEMV = 5 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
