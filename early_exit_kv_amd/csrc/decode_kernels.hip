@@ -771,13 +771,14 @@ template <int EP> constexpr int mv_nepi() {
   return EP == kEpQKV ? 2 : EP == kEpResid ? 1 : EP == kEpResidExit ? 2 : 0;
 }
 // bytes of a ring slot: weights, scale/zero words, epilogue operands, and
-// with XR the unit's slice of the M activation rows (256 columns each)
+// with XR the unit's slice of the M activation rows (256 columns each; at
+// least the 1 KB one DMA writes)
 template <int EP, int M, bool XR> constexpr int mv_slot() {
-  return kMvSlotW + 256 + 256 * mv_nepi<EP>() + (XR ? 512 * M : 0);
+  return kMvSlotW + 256 + 256 * mv_nepi<EP>() + (XR ? (M >= 2 ? 512 * M : 1024) : 0);
 }
 static int mv_slot_bytes(Epilogue ep, int M, bool xr) {
   return kMvSlotW + 256 + 256 * (ep == kEpQKV ? 2 : ep == kEpResid ? 1 : ep == kEpResidExit ? 2 : 0) +
-         (xr ? 512 * M : 0);
+         (xr ? (M >= 2 ? 512 * M : 1024) : 0);
 }
 
 // f(Buf<I>{}) for I = I0 .. N-1, unrolled at compile time
@@ -831,7 +832,7 @@ __device__ __forceinline__ void wait_vm() {
 // group sums of x come from one more MFMA against a B operand of ones.
 template <int M, int XS, int EP, int G, bool XR>
 __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
-  static_assert(!XR || (XS == kXBf16 && M >= 2), "ring-fed rows: bf16 input, two rows or more");
+  static_assert(!XR || XS == kXBf16, "ring-fed rows: bf16 input");
   extern __shared__ uint4 mv_smem[];
   constexpr int OUTS = mv_outs<EP>();
   constexpr int NEPI = mv_nepi<EP>();
@@ -1401,12 +1402,11 @@ static int mgemv_ntile(Epilogue ep, const GemvParams &p) {
 
 constexpr size_t kMvMaxLds = 120 * 1024;
 
-// the activation rows come through the ring (they do not fit LDS whole, and
-// the input is bf16 rows of two or more)
-static bool mgemv_xr(Epilogue ep, const GemvParams &p) {
-  const int M = p.B <= 1 ? 1 : p.B <= 2 ? 2 : p.B <= 4 ? 4 : 8;
-  const bool bf16_in = ep == kEpResid || ep == kEpResidExit || ep == kEpPlain;
-  return bf16_in && M >= 2 && mgemv_lds(ep, M, p.K, p.G, false) > kMvMaxLds;
+// bf16 input rows come through the ring with the weights (measured faster
+// than staging them whole at every row count, and the only way once they do
+// not fit LDS); RMSNorm inputs are staged normalised
+static bool mgemv_xr(Epilogue ep, const GemvParams &) {
+  return ep == kEpResid || ep == kEpResidExit || ep == kEpPlain;
 }
 
 bool mgemv_fits(Epilogue ep, const GemvParams &p) {
@@ -1429,7 +1429,7 @@ static MvPlan mgemv_plan_t(Epilogue ep, const GemvParams &p) {
   g.ntile = mgemv_ntile(ep, p);
   const bool xr = mgemv_xr(ep, p);
   g.lds = mgemv_lds(ep, M, p.K, p.G, xr);
-  if constexpr (XS == kXBf16 && M >= 2) {
+  if constexpr (XS == kXBf16) {
     if (xr) {
       g.fn = p.G == 64 ? reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 64, true>)
                        : reinterpret_cast<const void *>(mgemv_kernel<M, XS, EP, 128, true>);
@@ -1471,15 +1471,15 @@ static MvPlan mgemv_plan(Epilogue ep, const GemvParams &p) {
 
 // GEMV choice: mode 1 the dot-product kernel everywhere, mode 2 the
 // matrix-core one wherever it fits, mode 0 (default) the one measured faster
-// per linear on 8B shapes: at one or two rows the matrix cores for gate|up
-// and down only (the dot-product GEMV's arithmetic is still hidden behind
-// its stream there), from three rows on for every linear that fits (the dot
-// products grow with the rows, the MFMA work does not), except the LM head
-// at four rows
+// per linear on 8B shapes: at one or two rows the matrix cores for gate|up,
+// o and down (q|k|v and the LM head keep the dot-product GEMV, whose
+// arithmetic still hides behind its stream there), from three rows on for
+// every linear that fits (the dot products grow with the rows, the MFMA work
+// does not), except the LM head at four rows
 static bool use_mgemv(Epilogue ep, const GemvParams &p) {
   if (p.gemv_mode == 1 || !mgemv_fits(ep, p)) return false;
   if (p.gemv_mode == 2) return true;
-  if (p.B <= 2) return ep == kEpSwiGLU || ep == kEpResidExit;
+  if (p.B <= 2) return ep == kEpSwiGLU || ep == kEpResidExit || ep == kEpResid || ep == kEpPlain;
   return !(ep == kEpLogits && p.B <= 4);
 }
 

@@ -193,7 +193,7 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     multiple of 256, the step's rows and the load rings
  *                     within 120 KB of LDS), 0 (default) per linear the one
  *                     measured faster (at one or two rows the matrix-core
- *                     GEMV for gate|up and down only, from three rows on for
+ *                     GEMV for gate|up, o and down, from three rows on for
  *                     every linear it fits but the LM head at four rows).
  *                     All give the same results up to the fp32 summation
  *                     order. */
