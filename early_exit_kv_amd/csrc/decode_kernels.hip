@@ -1823,10 +1823,257 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   }
 }
 
+// ===========================================================================
+// Decode attention with the scores on the matrix cores.  Same work split as
+// attn_decode_kernel (workgroup = split x kv head x row, sub-chunks of 64
+// positions, the last workgroup of a (row, kv head) merges the splits).
+// Inside a sub-chunk each wavefront owns a block of 16 consecutive positions:
+// their K and V rows (16 x Dh bf16, contiguous in the cache) land in LDS by
+// DMA, the next sub-chunk's while this one is reduced, each row's 16-byte
+// chunks XOR-swizzled by the position so that operand reads hit distinct
+// banks.  Scores: one MFMA 16x16x32 per 32 head dims, the GQ query heads as A
+// (rows past GQ zero) and the K block as B, so every (head, position) score
+// is computed once; the online softmax (base-2 domain, scores pre-scaled by
+// log2 e) reduces over the block's 16 positions by DPP.  P then goes through
+// LDS to the lanes that accumulate P V: Dh/8 lanes per position, 8 head dims
+// each.
+// ===========================================================================
+template <int DH>
+__device__ __forceinline__ int attn_swz(int r) {
+  return DH == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int DH, int GQ>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
+  constexpr int CPR = DH * 2 / 16;             // 16-byte chunks per position
+  constexpr int BLK = 16 * DH * 2;             // bytes of a 16-position K (or V) block
+  constexpr int NDK = BLK / 1024;              // DMAs per block
+  constexpr int NDMA = 2 * NDK;                // K and V DMAs per sub-chunk per wavefront
+  constexpr int LPP = DH / 8;                  // P V lanes per position
+  constexpr int PPW = 64 / LPP;                // positions per P V pass
+  constexpr int NPASS = 16 / PPW;              // passes per block
+  constexpr int NJ = DH / 32;                  // score MFMAs per block
+  constexpr int KVB = 2 * BLK;                 // one buffer: K block then V block
+  // per wavefront two buffers; the split's partial results reuse the space
+  __shared__ __align__(16) char kvs[4 * 2 * KVB];
+  __shared__ __align__(16) float pl[4][16][GQ];
+  __shared__ float wm[4][GQ], wl[4][GQ];
+  __shared__ int last_flag;
+  static_assert(4 * PPW * GQ * DH * 4 <= 4 * 2 * KVB, "the partial results fit the K/V buffers");
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qq = lane >> 4, cl = lane & 15;
+  const int slot = lane / LPP, ln = lane % LPP;
+  const int t0 = split * p.chunk;
+  const int64_t kvbase = ((int64_t)b * p.Hkv + kvh) * p.S * DH;
+  const uint16_t *Kc = p.k_cache + kvbase;
+  const uint16_t *Vc = p.v_cache + kvbase;
+  char *kvw = kvs + wid * 2 * KVB;                 // this wavefront's two buffers
+  const uint32_t kvw_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)kvw);
+
+  // DMA of the block of positions base .. base+15 (clamped into the cache;
+  // positions past the visible ones are masked later) into buffer bi
+  auto fetch = [&](int bi, int sb) {
+    const int base = sb + 16 * wid;
+#pragma unroll
+    for (int h = 0; h < NDK; ++h) {
+      const int P = 64 * h + lane, r = P / CPR, c = (P % CPR) ^ attn_swz<DH>(r);
+      const int64_t off = (int64_t)min(base + r, p.S - 1) * DH + 8 * c;
+      const uint32_t dst = kvw_lds + bi * KVB + 1024 * h;
+      dma16(dst, Kc + off);
+      dma16(dst + BLK, Vc + off);
+    }
+  };
+
+  // the first block is requested before the position is known (t0 is always
+  // a valid position), then q
+  fetch(0, t0);
+  bf16x8_t qa[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (cl < GQ)
+      u = *reinterpret_cast<const uint4 *>(p.q + ((int64_t)b * p.Hq + kvh * GQ + cl) * DH + 32 * j + 8 * qq);
+    qa[j] = __builtin_bit_cast(bf16x8_t, u);
+  }
+  const int n = p.ctrl->pos + 1;
+  const int t1 = min(n, t0 + p.chunk);
+  const float scale2 = p.scale * 1.4426950408889634f;
+
+  // softmax state of head i (rows 4 qq + i; heads live in the lanes of qq = 0)
+  float m[4], l[4], acc[GQ][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  auto reduce = [&](int bi, int sb) {
+    const char *kb = kvw + bi * KVB;
+    const char *vb = kb + BLK;
+    const int base = sb + 16 * wid;
+    // scores of the block: D[head][position], position = lane % 16
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    const int rs = attn_swz<DH>(cl);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(kb + 16 * (cl * CPR + ((4 * j + qq) ^ rs)));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kf, sc, 0, 0, 0);
+    }
+    const bool vis = base + cl < t1;
+    float corr[GQ];
+#pragma unroll
+    for (int i = 0; i < GQ; ++i) {
+      const float s2 = vis ? sc[i] * scale2 : -INFINITY;
+      const float mnew = fmaxf(m[i], max16(s2));
+      float c = 1.f, pr = 0.f;
+      if (mnew != -INFINITY) {
+        c = exp2_fast(m[i] - mnew);
+        pr = vis ? exp2_fast(s2 - mnew) : 0.f;
+      }
+      l[i] = l[i] * c + sum16(pr);
+      m[i] = mnew;
+      if (qq == 0) pl[wid][cl][i] = pr;
+      // every lane takes head i's correction from lane 0
+      corr[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 0));
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= corr[h];
+    // P V: this lane's 8 head dims of position pass * PPW + slot
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = ps * PPW + slot;
+      const uint4 v = *reinterpret_cast<const uint4 *>(vb + 16 * (r * CPR + (ln ^ attn_swz<DH>(r))));
+      const float vf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+      float pr[GQ];
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) pr[h] = pl[wid][r][h];
+#pragma unroll
+      for (int h = 0; h < GQ; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+    }
+  };
+
+  int bi = 0;
+  for (int sb = t0; sb < t1; sb += kAttnSub) {
+    if (sb + kAttnSub < t1) {
+      fetch(bi ^ 1, sb + kAttnSub);
+      wait_vm<NDMA>();
+    } else {
+      wait_vm<0>();
+    }
+    reduce(bi, sb);
+    bi ^= 1;
+  }
+  wait_vm<0>();   // the speculative block of an empty split has landed too
+
+  // per-wavefront results: m and l from lane 0, P V partials per slot
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      wm[wid][h] = m[h];
+      wl[wid][h] = l[h];
+    }
+  }
+  __syncthreads();                               // every wavefront is done with its buffers
+  float *wo = reinterpret_cast<float *>(kvs);    // [4][PPW][GQ][DH]
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float4 *dst = reinterpret_cast<float4 *>(wo + ((wid * PPW + slot) * GQ + h) * DH + ln * 8);
+    dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+    dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+  }
+  __syncthreads();
+  const bool direct = p.splits == 1;
+  float *part_base = p.part + ((int64_t)b * p.Hq + kvh * GQ) * p.splits * (DH + 2);
+  for (int idx = tid; idx < GQ * DH; idx += 256) {
+    const int h = idx / DH, e = idx % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, wm[wv][h]);
+    float L = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        const float f = exp2_fast(wm[wv][h] - M);
+        float ow = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < PPW; ++sl) ow += wo[((wv * PPW + sl) * GQ + h) * DH + e];
+        L += f * wl[wv][h];
+        o += f * ow;
+      }
+    }
+    if (direct) {
+      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(o / L);
+    } else {
+      float *pp = part_base + ((int64_t)h * p.splits + split) * (DH + 2);
+      st_coherent(pp + e, o);
+      if (e == 0) {
+        st_coherent(pp + DH, M);
+        st_coherent(pp + DH + 1, L);
+      }
+    }
+  }
+  if (direct) return;
+  if (arrive_last(&p.counters[b * p.Hkv + kvh], gridDim.x, &last_flag)) {
+    // merge the splits that hold positions, 16 splits per round of loads
+    const int nval = (n + p.chunk - 1) / p.chunk;
+    for (int idx = tid; idx < GQ * DH; idx += 256) {
+      const int h = idx / DH, e = idx % DH;
+      const float *base = part_base + (int64_t)h * p.splits * (DH + 2);
+      float M = -INFINITY, L = 0.f, O = 0.f;
+      for (int s0 = 0; s0 < nval; s0 += 16) {
+        float ms[16], ls[16], os[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const bool ok = s0 + u < nval;
+          const float *pp = base + (int64_t)(s0 + u) * (DH + 2);
+          ms[u] = ok ? ld_coherent(pp + DH) : -INFINITY;
+          ls[u] = ok ? ld_coherent(pp + DH + 1) : 0.f;
+          os[u] = ok ? ld_coherent(pp + e) : 0.f;
+        }
+        float mx = M;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) mx = fmaxf(mx, ms[u]);
+        if (mx == -INFINITY) continue;
+        const float corr = exp2_fast(M - mx);
+        L *= corr;
+        O *= corr;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float f = exp2_fast(ms[u] - mx);
+          L = fmaf(f, ls[u], L);
+          O = fmaf(f, os[u], O);
+        }
+        M = mx;
+      }
+      p.out[((int64_t)b * p.Hq + kvh * GQ + h) * DH + e] = f2bf(O / L);
+    }
+  }
+}
+
 template <int DH>
 static hipError_t attn_launch_dh(const AttnParams &p, hipStream_t s) {
   dim3 grid(p.splits, p.Hkv, p.B);
   const int gq = p.Hq / p.Hkv;
+  if (p.mfma) {
+    switch (gq) {
+      case 1: return launch_1(attn_mfma_kernel<DH, 1>, grid, dim3(256), p, s);
+      case 2: return launch_1(attn_mfma_kernel<DH, 2>, grid, dim3(256), p, s);
+      case 4: return launch_1(attn_mfma_kernel<DH, 4>, grid, dim3(256), p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (gq) {
     case 1: return launch_1(attn_decode_kernel<DH, 1>, grid, dim3(256), p, s);
     case 2: return launch_1(attn_decode_kernel<DH, 2>, grid, dim3(256), p, s);

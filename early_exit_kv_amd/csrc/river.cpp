@@ -164,6 +164,7 @@ struct river_ctx {
   size_t rec_bytes = 0;
   int attn_chunk = 0;   // positions per decode-attention workgroup (0: chosen per shape)
   int gemv_mode = 0;    // RIVER_OPT_GEMV
+  int attn_kind = 0;    // RIVER_OPT_ATTN
 };
 
 namespace {
@@ -370,6 +371,7 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     a.chunk = ctx->attn_chunk > 0 ? ctx->attn_chunk : attn_chunk(c.max_seq, B, c.n_kv_heads);
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    a.mfma = ctx->attn_kind == 0;
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
@@ -464,6 +466,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     a.chunk = ctx->attn_chunk > 0 ? ctx->attn_chunk : attn_chunk(c.max_seq, B, c.n_kv_heads);
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    a.mfma = ctx->attn_kind == 0;
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
@@ -820,6 +823,11 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
                          (ctx->cfg.max_seq + value - 1) / value > kMaxAttnSplits))
         return RIVER_E_INVALID_ARG;
       ctx->attn_chunk = (int)value;
+      drop_graphs(ctx);
+      return RIVER_OK;
+    case RIVER_OPT_ATTN:
+      if (value != 0 && value != 1) return RIVER_E_INVALID_ARG;
+      ctx->attn_kind = (int)value;
       drop_graphs(ctx);
       return RIVER_OK;
     case RIVER_OPT_GEMV:

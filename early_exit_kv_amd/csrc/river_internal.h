@@ -156,6 +156,7 @@ struct AttnParams {
   Control *ctrl;
   int B, Hq, Hkv, Dh, S, splits, chunk;
   float scale;
+  int mfma;               // 1: scores on the matrix cores
 };
 // positions per decode-attention workgroup for a cache of max_seq positions
 int attn_chunk(int max_seq, int batch, int n_kv_heads);

@@ -17,6 +17,7 @@ RIVER_OK, RIVER_E_INVALID_ARG, RIVER_E_BAD_SIZE, RIVER_E_STATE = 0, 1, 2, 3
 RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
 RIVER_EXIT_INT4, RIVER_EXIT_COPY = 1, 2
 RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK, RIVER_OPT_GEMV = 1, 2, 3, 4, 5
+RIVER_OPT_ATTN = 6
 KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
                 "p_norm", "p_gemm", "p_attn", "p_cos")
 RIVER_MAX_LAYERS = 256
@@ -290,6 +291,10 @@ class River:
         """Kernel of decode linears of <= 8 rows: "auto" (per linear), "dot"
         (dot-product GEMV) or "mfma" (matrix-core GEMV where it fits)."""
         self.set_option(RIVER_OPT_GEMV, {"auto": 0, "dot": 1, "mfma": 2}[mode])
+
+    def attn_kind(self, kind):
+        """Decode attention: "mfma" (scores on the matrix cores) or "valu"."""
+        self.set_option(RIVER_OPT_ATTN, {"mfma": 0, "valu": 1}[kind])
 
     def profile(self, on=True):
         """Time every kernel with HIP events (decode steps then launch eagerly)."""
