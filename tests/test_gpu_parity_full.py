@@ -39,7 +39,7 @@ def host_weights(w, dtype=np.float64):
             "layers": [{k: cv(v) for k, v in lw.items()} for lw in w["layers"]]}
 
 
-def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto"):
+def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto", attn="mfma"):
     """Prefill + decode steps on the GPU with every pass checked stage by stage
     (teacher forcing at each stored activation), and a free-running oracle
     beside it for the exit decisions and the K/V cosine bar."""
@@ -50,6 +50,7 @@ def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto"):
     sh = synth.shrink(shape, n_layers=L)
     r = rv.River(sh, w_dev, B, max_seq)
     r.gemv_mode(gemv)
+    r.attn_kind(attn)
     r.build_exit_layers(mode)
     r.record(B * T)
     hw = host_weights(w_dev)
@@ -211,3 +212,14 @@ def test_decode_parity_8b_batch8_mfma_gemv(w8b):
 def test_decode_parity_8b_dot_gemv(w8b):
     """Every decode linear on the dot-product GEMV."""
     parity_run(synth.LLAMA_8B, w8b, B=1, T=12, steps=3, tau=0.5, gemv="dot")
+
+
+def test_split_attention_long_context_tiny_valu():
+    """The vector-ALU decode attention on the same long context."""
+    w = synth.make_weights(synth.TINY, seed=0, device="cuda")
+    parity_run(synth.TINY, w, B=8, T=700, steps=3, tau=0.5, attn="valu")
+
+
+def test_decode_parity_8b_valu_attention(w8b):
+    """The vector-ALU decode attention at head dim 128."""
+    parity_run(synth.LLAMA_8B, w8b, B=1, T=12, steps=3, tau=0.5, attn="valu")
