@@ -312,6 +312,36 @@ def main():
                         "what": "all q|k|v, o, gate|up, down GEMMs of a prefill with every layer on "
                                 "its int4 exit copy (forced E=0), 2*M*N*K flop over their event time"}
 
+    exit_gemm_b32 = None
+    if not args.no_profile and shape.d_model >= 2048:
+        # the int4 exit GEMMs at the batch-32 prefill shape (32 x 1024 rows):
+        # each of layer 0's seven linears through the production prefill GEMM
+        # (plain fp32 output), timed with events after one warm-up call
+        M = 32 * 1024
+        g = torch.Generator(device="cpu").manual_seed(7)
+        flop = ms_tot = 0.0
+        for li in range(7):
+            N_, K_ = r.linear_shape(li)
+            x = (torch.randn((M, K_), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+            r.debug_linear(0, li, 1, x)
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            reps = 3
+            ev0.record()
+            for _ in range(reps):
+                y = r.debug_linear(0, li, 1, x)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms_tot += ev0.elapsed_time(ev1) / reps
+            flop += 2.0 * M * N_ * K_
+            del x, y
+        tf = flop / (ms_tot * 1e-3) / 1e12
+        exit_gemm_b32 = {"rows": M, "total_ms": round(ms_tot, 3), "tflops": round(tf, 1),
+                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "what": "the 7 int4 exit-layer linears of one layer at 32 x 1024 rows "
+                                 "(batch-32 prefill shape), prefill GEMM with fp32 output, "
+                                 "2*M*N*K flop over their event time"}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, weights, B, T, mean_E)
@@ -331,6 +361,7 @@ def main():
         "mean_exit_layer": round(mean_E, 3), "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
         "prefill_tok_s": round(B * T / prefill_s, 1), "prefill_E": prefill_E,
         "build_exit_layers_s": round(build_s, 4), "kernels": kinds, "prefill_exit_gemm": prefill_gemm,
+        "exit_gemm_b32": exit_gemm_b32,
         "baselines_tok_s": baselines,
     }
     r.close()

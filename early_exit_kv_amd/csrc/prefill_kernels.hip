@@ -893,7 +893,7 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 //   column several groups ahead, with the same int4 conventions as the
 //   batched-row GEMM (per-group accumulation, lane quarters over G/4 codes,
 //   group fold tot += s * (acc - (128 + z) * sum_k x), the row sums of each
-//   group taken from the LDS tile).
+//   group from one more MFMA per row block against a B operand of ones).
 //   Workgroups are ordered in groups of 8 row blocks so that the rows and
 //   weights they share stay in L2.
 // ===========================================================================
@@ -904,10 +904,9 @@ constexpr int kPCodeSlots = kPBN * kPKT / 32;     // 16-byte slots of int4 codes
 
 
 template <int G, int EP, bool Q4>
-__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs, float *xsg,
+__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs,
                                            bool ex, int rowblk, int colblk, f32x4_t (&tot)[2][4]) {
   constexpr int STEPS = G / 32, GW = G / 32;
-  constexpr int GPT = kPKT / G;                 // groups per k-tile
   typedef typename WordsT<GW>::T WT;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
@@ -1030,11 +1029,17 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
         const int slot = col * 4 + ((wo >> 2) ^ ((col >> 2) & 3));
         wq[t] = *reinterpret_cast<const WT *>(cb + slot * 4 + (wo & 3));
       }
-      f32x4_t ag[2][4];
+      // the group sums of the rows come from one more MFMA per row block
+      // against a B operand of ones (row sums in every column)
+      const bf16x8_t ones =
+          __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+      f32x4_t ag[2][4], as[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a) {
+        as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
         bf16x8_t af[2], bfr[4];
@@ -1050,21 +1055,20 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
           bfr[t] = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
         }
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a) {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[t], ag[a][t], 0, 0, 0);
+          as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, as[a], 0, 0, 0);
+        }
       }
-      const int g = kl / G;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float sc = bf_lo(wz[u][t]), zo = 128.0f + bf_hi(wz[u][t]);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * xsg[(wm * 32 + a * 16 + 4 * qq + v) * GPT + g],
-                                tot[a][t][v]);
+          for (int v = 0; v < 4; ++v) tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * as[a][v], tot[a][t][v]);
       }
     } else {
       bf16x8_t af[2];
@@ -1077,24 +1081,6 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
           tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], __builtin_bit_cast(bf16x8_t, wb[u][t]),
                                                               tot[a][t], 0, 0, 0);
     }
-  };
-
-  // group sums of the rows of one landed k-tile (int4 fold): 4 threads per
-  // row, 32 columns each, reduced over the 4 (G=128) or 2 (G=64) lanes
-  auto row_sums = [&](int kt) {
-    const uint4 *buf = xs + (kt % kPBufs) * kPTileSlots;
-    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
-    float sacc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = part * 4 + i;
-      const uint4 w = buf[r * 16 + (c ^ (r & 15))];
-      sacc += ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
-              ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
-    }
-    sacc += dpp<kDppXor1>(sacc);
-    if (G == 128) sacc += dpp<kDppXor2>(sacc);
-    if (G == 128 ? part == 0 : (part & 1) == 0) xsg[r * GPT + (G == 128 ? 0 : part >> 1)] = sacc;
   };
 
   constexpr int CPT = kPKT / CK;                // chunks per k-tile
@@ -1123,10 +1109,6 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
         __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
         __syncthreads();                        // tile kt visible; tile kt-1 done everywhere
         load_a(kt + kPBufs - 1);                // into the buffer tile kt-1 used
-        if constexpr (Q4) {
-          row_sums(kt);
-          __syncthreads();
-        }
 #pragma unroll
         for (int cc = 0; cc < CPT; ++cc) {
           const int c = kt * CPT + cc;
@@ -1146,7 +1128,6 @@ template <int G, int EP>
 __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
   __shared__ __align__(16) uint4 xs[kPBufs * kPTileSlots];   // 96 KB; reused for the results
   __shared__ __align__(16) uint4 cs[kPBufs * kPCodeSlots];   // 24 KB of int4 codes
-  __shared__ float xsg[kPBM * (kPKT / G)];
   const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
   // grouped order: kPGroupRows row blocks share the weights of each column block
@@ -1162,8 +1143,8 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true>(p, xs, cs, xsg, ex, rowblk, colblk, tot);
-  else pgemm_body<G, EP, false>(p, xs, cs, xsg, ex, rowblk, colblk, tot);
+  if (q4) pgemm_body<G, EP, true>(p, xs, cs, ex, rowblk, colblk, tot);
+  else pgemm_body<G, EP, false>(p, xs, cs, ex, rowblk, colblk, tot);
 
   // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
