@@ -99,8 +99,6 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
 // ===========================================================================
 constexpr int kXLdsBytes = 64 * 1024;
 
-// compile-time index of a register buffer, passed to generic lambdas
-template <int N> struct Buf { static constexpr int value = N; };
 
 struct RowRef {
   int seg, row;

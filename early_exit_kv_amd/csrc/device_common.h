@@ -17,6 +17,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // N consecutive 32-bit words as one load
 // LDS pointer type (for the LDS byte address of a __shared__ object)
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+// compile-time index (of a register buffer, a ring slot, a variant), passed
+// to generic lambdas
+template <int N> struct Buf { static constexpr int value = N; };
 template <int N_> struct WordsT;
 template <> struct WordsT<1> { typedef uint32_t T; };
 template <> struct WordsT<2> { typedef v2u T; };

@@ -880,37 +880,53 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 
 // ===========================================================================
 // Prefill GEMM for many rows: Y[m][n] = sum_k X[m][k] W[n][k] on
-// v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 x 128, eight wavefronts in a
-// 4 x 2 arrangement, each 32 x 64 (2 x 4 MFMA tiles: every row fragment read
-// from LDS feeds four MFMAs, which keeps LDS at half its bandwidth); two
-// wavefronts per SIMD so that one's waits overlap the other's MFMAs.
+// v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 rows x BN columns, eight
+// wavefronts of 64 columns each: BN = 128 as 4 x 2 wavefronts of 32 x 64, BN
+// = 256 (from 4,096 rows) as 2 x 4 of 64 x 64, where every unpacked int4
+// operand feeds four MFMAs instead of two; two wavefronts per SIMD so that
+// one's waits overlap the other's MFMAs.
 //   Rows X: k-tiles of 128 columns copied straight from memory into LDS
-//   (global_load_lds, no registers), four buffers, so three tiles are in
+//   (global_load_lds, no registers), three buffers, so two tiles are in
 //   flight while one feeds the MFMAs; 16-byte chunks are XOR-swizzled within a
 //   row (chunk c of row r at slot c ^ (r mod 16)) so that the 16 rows one
 //   fragment read touches fall in distinct banks.
-//   Weights: from memory straight into B operands, every lane loading its own
-//   column several groups ahead, with the same int4 conventions as the
-//   batched-row GEMM (per-group accumulation, lane quarters over G/4 codes,
-//   group fold tot += s * (acc - (128 + z) * sum_k x), the row sums of each
-//   group from one more MFMA per row block against a B operand of ones).
+//   int4 weights: the k-tile's codes and scale/zero words are copied into LDS
+//   with the rows (same int4 conventions as the batched-row GEMM: per-group
+//   accumulation, lane quarters over G/4 codes, group fold
+//   tot += s * (acc - (128 + z) * sum_k x), the row sums of each group from
+//   one more MFMA per row block against a B operand of ones).  bf16 weights
+//   go from memory straight into B operands, every lane loading its own column
+//   several k-steps ahead.
 //   Workgroups are ordered in groups of 8 row blocks so that the rows and
 //   weights they share stay in L2.
 // ===========================================================================
-constexpr int kPBM = 128, kPBN = 128, kPKT = 128, kPGroupRows = 8;
+constexpr int kPBM = 128, kPKT = 128, kPGroupRows = 8;
 constexpr int kPThreads = 512, kPBufs = 3;
+constexpr int kPWideRows = 4096;                  // rows from which column blocks are 256 wide
 constexpr int kPTileSlots = kPBM * kPKT / 8;      // 16-byte slots of rows per k-tile (2048)
-constexpr int kPCodeSlots = kPBN * kPKT / 32;     // 16-byte slots of int4 codes per k-tile (512)
+// 16-byte slots of int4 codes per k-tile of BN columns
+template <int BN> constexpr int pcode_slots() { return BN * kPKT / 32; }
+// wavefronts along N (each 64 columns wide) and along M, rows per wavefront
+template <int BN> constexpr int pwn() { return BN / 64; }
+template <int BN> constexpr int pwm() { return 8 / pwn<BN>(); }
+template <int BN> constexpr int ptm() { return kPBM / pwm<BN>(); }
+// 16-byte slots of int4 scale/zero words per k-tile: one word for each of
+// the 512 lanes of the workgroup (at most 2 groups x 256 columns are used)
+constexpr int kPSzSlots = 128;
+// LDS of a workgroup: row buffers, code buffers, scale/zero buffers (the
+// results reuse them all)
+template <int BN> constexpr int psmem_slots() { return kPBufs * (kPTileSlots + pcode_slots<BN>() + kPSzSlots); }
 
 
-template <int G, int EP, bool Q4>
-__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs,
-                                           bool ex, int rowblk, int colblk, f32x4_t (&tot)[2][4]) {
+template <int G, int EP, bool Q4, int BN>
+__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs, uint4 *zs, bool ex,
+                                           int rowblk, int colblk, f32x4_t (&tot)[ptm<BN>() / 16][4]) {
   constexpr int STEPS = G / 32, GW = G / 32;
+  constexpr int WN = pwn<BN>(), TM = ptm<BN>(), AF = TM / 16, CSL = pcode_slots<BN>();
   typedef typename WordsT<GW>::T WT;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WN, wn = wid % WN;
   const int64_t m0 = (int64_t)rowblk * kPBM;
   const int KG = p.K / G;
   const int ntile = p.K / kPKT;
@@ -918,37 +934,50 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
   // segment bases are uniform over a 16-column tile (scalar registers); only
   // the 32-bit row offsets live in vector registers
   const uint16_t *bbase[4];
-  const uint32_t *qbase[4], *zbase[4];
   int roff[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     int seg, row;
     bool valid;
-    map_col<EP>(p, colblk, kPBN, wn * 64 + t * 16 + cl, seg, row, valid);
+    map_col<EP>(p, colblk, BN, wn * 64 + t * 16 + cl, seg, row, valid);
     if (!valid) row = 0;
     seg = __builtin_amdgcn_readfirstlane(seg);
     roff[t] = row;
-    if constexpr (Q4) {
-      qbase[t] = p.w.q4[seg];
-      zbase[t] = p.w.sz[seg];
-    } else {
-      bbase[t] = ex ? p.w.ex_bf[seg] : p.w.bf[seg];
-    }
+    if constexpr (!Q4) bbase[t] = ex ? p.w.ex_bf[seg] : p.w.bf[seg];
   }
 
-  // ---- int4 codes of a k-tile: 128 columns x 64 bytes, one 16-byte slot
-  //      per lane of every wavefront; column c's chunk q sits at slot
-  //      4c + (q ^ ((c >> 2) & 3)), so the 16 columns one B-fragment read
+  // ---- int4 codes of a k-tile: BN columns x 64 bytes, one 16-byte slot per
+  //      lane of every wavefront per BN / 128; column c's chunk q sits at
+  //      slot 4c + (q ^ ((c >> 2) & 3)), so the 16 columns one B-fragment read
   //      touches fall in distinct banks
-  const uint32_t *crow = nullptr;
+  constexpr int NCD = BN / 128;                 // code copies per wavefront per k-tile
+  const uint32_t *crow[NCD];
+#pragma unroll
+  for (int i = 0; i < NCD; ++i) {
+    crow[i] = nullptr;
+    if constexpr (Q4) {
+      const int slot = (i * 8 + wid) * 64 + lane;
+      const int c = slot >> 2, q = (slot & 3) ^ ((c >> 2) & 3);
+      int seg, row;
+      bool valid;
+      map_col<EP>(p, colblk, BN, c, seg, row, valid);
+      if (!valid) { seg = 0; row = 0; }
+      crow[i] = p.w.q4[seg] + (int64_t)row * (p.K / 8) + 4 * q;
+    }
+  }
+  // ---- their scale/zero words: entry e = 64 wid + lane of a k-tile is
+  //      group e / BN of the k-tile for column e % BN (entries past the
+  //      tile's groups repeat the last group)
+  constexpr int GPT = kPKT / G;                 // groups per k-tile
+  const uint32_t *zrow = nullptr;
   if constexpr (Q4) {
-    const int slot = wid * 64 + lane;
-    const int c = slot >> 2, q = (slot & 3) ^ ((c >> 2) & 3);
+    const int e = wid * 64 + lane;
+    const int gi = min(e / BN, GPT - 1), c = e % BN;
     int seg, row;
     bool valid;
-    map_col<EP>(p, colblk, kPBN, c, seg, row, valid);
+    map_col<EP>(p, colblk, BN, c, seg, row, valid);
     if (!valid) { seg = 0; row = 0; }
-    crow = p.w.q4[seg] + (int64_t)row * (p.K / 8) + 4 * q;
+    zrow = p.w.sz[seg] + (int64_t)row * KG + gi;
   }
 
   // ---- rows: each wavefront copies 4 x 64 slots of a k-tile into LDS
@@ -970,6 +999,7 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
   const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_ptr_t)xs;
   const int uwid = __builtin_amdgcn_readfirstlane(wid);
   const uint32_t cs_base = (uint32_t)(uintptr_t)(lds_ptr_t)cs;
+  const uint32_t zs_base = (uint32_t)(uintptr_t)(lds_ptr_t)zs;
   auto load_a = [&](int kt) {
     const int ktc = min(kt, ntile - 1);                    // unconditional: fixed load count
     const uint32_t buf = xs_base + (uint32_t)((kt % kPBufs) * kPTileSlots * 16);
@@ -981,10 +1011,19 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
                    : "memory", "m0");
     }
     if constexpr (Q4) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          cs_base + (uint32_t)(((kt % kPBufs) * kPCodeSlots + uwid * 64) * 16));
-      const uint32_t *src = crow + ktc * (kPKT / 8);
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+#pragma unroll
+      for (int i = 0; i < NCD; ++i) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            cs_base + (uint32_t)(((kt % kPBufs) * CSL + (i * 8 + uwid) * 64) * 16));
+        const uint32_t *src = crow[i] + ktc * (kPKT / 8);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                     : "memory", "m0");
+      }
+      // scale/zero words: each lane writes 4 bytes at m0 + 4 * lane
+      const uint32_t zdst = __builtin_amdgcn_readfirstlane(
+          zs_base + (uint32_t)(((kt % kPBufs) * kPSzSlots) * 16 + uwid * 256));
+      const uint32_t *zsrc = zrow + ktc * GPT;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(zdst), "v"(zsrc)
                    : "memory", "m0");
     }
   };
@@ -993,23 +1032,21 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
     return __builtin_bit_cast(bf16x8_t, buf[r * 16 + (c ^ (r & 15))]);
   };
 
-  // ---- weights: int4 codes come through LDS with the rows (only scale/zero
-  //      words per group here); bf16 one k-step of 32 per chunk
-  constexpr int D = Q4 ? 2 : 8;
+  // ---- weights: int4 codes and their scale/zero words come through LDS with
+  //      the rows, so that no load the compiler tracks sits in the int4 loop
+  //      (its wait for such a load would also wait for every copy issued
+  //      after it); bf16 weights one k-step of 32 per chunk into registers
+  constexpr int D = Q4 ? 2 : AF == 4 ? 4 : 8;   // chunks per pass (bf16: 4 loads each in flight)
   constexpr int CK = Q4 ? G : 32;              // k columns per chunk
-  uint32_t wz[D][4];
   v4u wb[D][4];
   const int nchunk = p.K / CK;
   auto load_w = [&](int c, int u) {
-    const int k0 = min(c, nchunk - 1) * CK;
+    if constexpr (!Q4) {
+      const int k0 = min(c, nchunk - 1) * CK;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if constexpr (Q4) {
-        wz[u][t] = zbase[t][(uint32_t)(roff[t] * KG + k0 / G)];
-      } else {
+      for (int t = 0; t < 4; ++t)
         wb[u][t] = __builtin_nontemporal_load(
             reinterpret_cast<const v4u *>(bbase[t] + (uint32_t)(roff[t] * p.K + k0 + 8 * qq)));
-      }
     }
   };
 
@@ -1017,65 +1054,76 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
     const int k0 = c * CK;
     const uint4 *buf = xs + ((k0 / kPKT) % kPBufs) * kPTileSlots;
     const int kl = k0 % kPKT;
-    const int r0 = wm * 32 + cl;
+    const int r0 = wm * TM + cl;
     if constexpr (Q4) {
       // this lane's GW code words of the group, for each of its 4 column tiles
-      const uint32_t *cb = reinterpret_cast<const uint32_t *>(cs + ((k0 / kPKT) % kPBufs) * kPCodeSlots);
+      const uint32_t *cb = reinterpret_cast<const uint32_t *>(cs + ((k0 / kPKT) % kPBufs) * CSL);
       const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
+      // (64-row wavefronts read them one step at a time: fewer live registers)
+      constexpr bool kByStep = false;
       WT wq[4];
+      int wsl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int col = wn * 64 + t * 16 + cl;
         const int slot = col * 4 + ((wo >> 2) ^ ((col >> 2) & 3));
-        wq[t] = *reinterpret_cast<const WT *>(cb + slot * 4 + (wo & 3));
+        wsl[t] = slot * 4 + (wo & 3);
+        if constexpr (!kByStep) wq[t] = *reinterpret_cast<const WT *>(cb + wsl[t]);
       }
       // the group sums of the rows come from one more MFMA per row block
       // against a B operand of ones (row sums in every column)
       const bf16x8_t ones =
           __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-      f32x4_t ag[2][4], as[2];
+      f32x4_t ag[AF][4], as[AF];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < AF; ++a) {
         as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll
+      // (64-row wavefronts: two steps per trip, so that the compiler does not
+      // hoist every step's operand reads at once and run out of registers)
+#pragma unroll(AF == 4 ? 2 : STEPS)
       for (int j = 0; j < STEPS; ++j) {
-        bf16x8_t af[2], bfr[4];
+        bf16x8_t af[AF];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + qq * (G / 4) + 8 * j);
+        for (int a = 0; a < AF; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + qq * (G / 4) + 8 * j);
+        // one column tile at a time: its unpacked operand feeds the AF MFMAs
+        // of the step and is dead after them
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           uint32_t w;
-          if constexpr (GW == 1) w = wq[t];
+          if constexpr (kByStep) w = cb[wsl[t] + j];
+          else if constexpr (GW == 1) w = wq[t];
           else w = wq[t][j];
           uint32_t pr[4];
           unpack_word(w, pr);
-          bfr[t] = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+          const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+#pragma unroll
+          for (int a = 0; a < AF; ++a)
+            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, ag[a][t], 0, 0, 0);
         }
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[t], ag[a][t], 0, 0, 0);
-          as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, as[a], 0, 0, 0);
-        }
+        for (int a = 0; a < AF; ++a) as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, as[a], 0, 0, 0);
       }
+      // the group's fold: tot += s * (acc - (128 + z) * sum_k x)
+      const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs + ((k0 / kPKT) % kPBufs) * kPSzSlots) +
+                           (kl / G) * BN + wn * 64 + cl;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float sc = bf_lo(wz[u][t]), zo = 128.0f + bf_hi(wz[u][t]);
+        const uint32_t wzt = zb[t * 16];
+        const float sc = bf_lo(wzt), zo = 128.0f + bf_hi(wzt);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < AF; ++a)
 #pragma unroll
           for (int v = 0; v < 4; ++v) tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * as[a][v], tot[a][t][v]);
       }
     } else {
-      bf16x8_t af[2];
+      bf16x8_t af[AF];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + 8 * qq);
+      for (int a = 0; a < AF; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + 8 * qq);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < AF; ++a)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], __builtin_bit_cast(bf16x8_t, wb[u][t]),
@@ -1099,11 +1147,12 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
         // are outstanding: after its 4 copies came those of the next 2 k-tiles
         // and at least min(the first D refills, 3 k-tiles of refills) weight
         // loads (every load is unconditional, so the count holds throughout)
-        // (a k-tile is 4 copies of rows, plus 1 of codes for int4; a weight
-        // refill is 4 loads per chunk)
-        constexpr int per_tile = Q4 ? 5 : 4;
+        // (a k-tile is 4 copies of rows, plus for int4 BN / 128 of codes and
+        // 1 of scale/zero words; a bf16 weight refill is 4 loads per chunk,
+        // int4 has none)
+        constexpr int per_tile = Q4 ? 4 + NCD + 1 : 4;
         constexpr int ring = (kPBufs - 1) * CPT;
-        constexpr int later = (kPBufs - 2) * per_tile + (D < ring ? D : ring) * 4;
+        constexpr int later = (kPBufs - 2) * per_tile + (Q4 ? 0 : (D < ring ? D : ring) * 4);
         static_assert(later < 64, "vmcnt field");
         // s_waitcnt: vmcnt = later, expcnt and lgkmcnt not waited for
         __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
@@ -1124,10 +1173,13 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
   __syncthreads();
 }
 
-template <int G, int EP>
+template <int G, int EP, int BN>
 __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
-  __shared__ __align__(16) uint4 xs[kPBufs * kPTileSlots];   // 96 KB; reused for the results
-  __shared__ __align__(16) uint4 cs[kPBufs * kPCodeSlots];   // 24 KB of int4 codes
+  // 96 KB of row buffers, then 24 (BN 128) or 48 KB (BN 256) of int4 codes;
+  // the results reuse both
+  __shared__ __align__(16) uint4 smem[psmem_slots<BN>()];
+  uint4 *xs = smem, *cs = smem + kPBufs * kPTileSlots, *zs = cs + kPBufs * pcode_slots<BN>();
+  constexpr int AF = ptm<BN>() / 16;
   const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
   // grouped order: kPGroupRows row blocks share the weights of each column block
@@ -1138,46 +1190,56 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   const int in_grp = blockIdx.x - grp * per_group;
   const int rowblk = first + in_grp % gm, colblk = in_grp / gm;
 
-  f32x4_t tot[2][4];
+  f32x4_t tot[AF][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true>(p, xs, cs, ex, rowblk, colblk, tot);
-  else pgemm_body<G, EP, false>(p, xs, cs, ex, rowblk, colblk, tot);
+  if (q4) pgemm_body<G, EP, true, BN>(p, xs, cs, zs, ex, rowblk, colblk, tot);
+  else pgemm_body<G, EP, false, BN>(p, xs, cs, zs, ex, rowblk, colblk, tot);
 
   // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int qq = lane >> 4, cl = lane & 15, wm = wid >> 1, wn = wid & 1;
-  float *Cs = reinterpret_cast<float *>(xs);
-  static_assert(kPBM * (kPBN + 1) * 4 <= kPBufs * kPTileSlots * 16, "the results fit the row buffers");
+  const int qq = lane >> 4, cl = lane & 15;
+  const int wm = wid / pwn<BN>(), wn = wid % pwn<BN>();
+  float *Cs = reinterpret_cast<float *>(smem);
+  static_assert(kPBM * (BN + 1) * 4 <= psmem_slots<BN>() * 16, "the results fit the buffers");
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        Cs[(wm * 32 + a * 16 + 4 * qq + v) * (kPBN + 1) + wn * 64 + t * 16 + cl] = tot[a][t][v];
+        Cs[(wm * ptm<BN>() + a * 16 + 4 * qq + v) * (BN + 1) + wn * 64 + t * 16 + cl] = tot[a][t][v];
   __syncthreads();
-  tile_epilogue<EP, kPBN, kPThreads>(p, Cs, kPBN + 1, kPBM, (int64_t)rowblk * kPBM, colblk);
+  tile_epilogue<EP, BN, kPThreads>(p, Cs, BN + 1, kPBM, (int64_t)rowblk * kPBM, colblk);
 }
 
-template <int G>
-static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s) {
+template <int G, int BN>
+static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t s) {
   const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
-  int nrowblk = (p.M + kPBM - 1) / kPBM, ncolblk = (ncols + kPBN - 1) / kPBN;
+  int nrowblk = (p.M + kPBM - 1) / kPBM, ncolblk = (ncols + BN - 1) / BN;
   GemmParams q = p;
   void *args[] = {&q, &nrowblk, &ncolblk};
   const dim3 grid((unsigned)(nrowblk * ncolblk));
   const void *fn;
   switch (ep) {
-    case kEpQKV: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpQKV>); break;
-    case kEpSwiGLU: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpSwiGLU>); break;
-    case kEpResid: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpResid>); break;
-    case kEpPlain: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpPlain>); break;
+    case kEpQKV: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpQKV, BN>); break;
+    case kEpSwiGLU: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpSwiGLU, BN>); break;
+    case kEpResid: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpResid, BN>); break;
+    case kEpPlain: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpPlain, BN>); break;
     default: return hipErrorInvalidValue;
   }
   return launch_kernel(fn, grid, dim3(kPThreads), args, 0, s);
+}
+
+// 256-column blocks (64 x 64 per wavefront: half the int4 unpacking per
+// MFMA of 128-column blocks) once there are enough rows to fill the chip
+// with them; 128-column blocks for short prompts
+template <int G>
+static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s) {
+  if (p.M >= kPWideRows) return pgemm_launch_gb<G, 256>(ep, p, s);
+  return pgemm_launch_gb<G, 128>(ep, p, s);
 }
 
 bool pgemm_fits(int K, int G) {

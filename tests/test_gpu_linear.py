@@ -92,7 +92,19 @@ def test_linear_batched_rows_8b(ctx8b_rows, M, use_exit):
     check_linears(ctx8b_rows, M, use_exit)
 
 
-def check_linears(ctx, M, use_exit):
+@pytest.mark.parametrize("use_exit", [0, 1])
+def test_linear_wide_prefill_8b(ctx8b, use_exit):
+    """4,100 rows: the prefill GEMM with 256-column blocks (from 4,096 rows),
+    32 full row blocks and a ragged one of 4 rows; the oracle product is taken
+    on 96 sampled rows, every row of the ragged block among them."""
+    M = 4100
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([np.arange(M - 4, M), np.arange(0, 8), [127, 128, 2047, 4095],
+                                     rng.choice(M, 80, replace=False)]))
+    check_linears(ctx8b, M, use_exit, rows=rows)
+
+
+def check_linears(ctx, M, use_exit, rows=None):
     sh, w, r = ctx
     g = torch.Generator(device="cpu").manual_seed(1234 + M)
     worst = []
@@ -106,11 +118,15 @@ def check_linears(ctx, M, use_exit):
         else:
             wh = wb.astype(np.float64)
         x64 = x.float().numpy().astype(np.float64)
+        if rows is not None:
+            x64 = x64[rows]
         y_ref, bound = _ref(x64, wh)
         print(f"[linear] 8b {name} M={M} exit={use_exit}", flush=True)
         y = r.debug_linear(0, i, use_exit, x.cuda())
         torch.cuda.synchronize()
         y = y.cpu().numpy().astype(np.float64)
+        if rows is not None:
+            y = y[rows]
         d = np.abs(y - y_ref)
         rel = np.sqrt(np.mean(d ** 2)) / np.sqrt(np.mean(y_ref ** 2))
         worst.append((name, float(rel), float(np.max(d / (bound + 1e-30)))))
