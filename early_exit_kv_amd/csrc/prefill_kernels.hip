@@ -1050,6 +1050,36 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
     }
   };
 
+  // int4: raw sums of a group (against the codes as 128+q per column tile,
+  // and the row sums against ones) and its scale/zero words, kept across
+  // k-tiles.  The two wavefronts of a SIMD (waves w and w + 4 of the
+  // workgroup) fold a group at different times: the first right after its
+  // MFMAs, the second after the next k-tile's barrier, before its next MFMAs.
+  // Each fold (VALU only) then runs beside the other wavefront's MFMAs
+  // instead of both folding at once while the matrix core idles.
+  f32x4_t ag[AF][4], as[AF];
+  uint32_t pz[4];
+#pragma unroll
+  for (int a = 0; a < AF; ++a) {
+    as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pz[t] = 0u;        // scale 0: a fold before any group adds nothing
+  const bool defer = Q4 && wid >= 4;             // the second wavefront of each SIMD
+  // the group's fold: tot += s * (acc - (128 + z) * sum_k x)
+  auto fold = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float sc = bf_lo(pz[t]), zo = 128.0f + bf_hi(pz[t]);
+#pragma unroll
+      for (int a = 0; a < AF; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * as[a][v], tot[a][t][v]);
+    }
+  };
+
   auto compute = [&](int c, int u) {
     const int k0 = c * CK;
     const uint4 *buf = xs + ((k0 / kPKT) % kPBufs) * kPTileSlots;
@@ -1074,7 +1104,7 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
       // against a B operand of ones (row sums in every column)
       const bf16x8_t ones =
           __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-      f32x4_t ag[AF][4], as[AF];
+      if (defer) fold();                           // the previous group's
 #pragma unroll
       for (int a = 0; a < AF; ++a) {
         as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1106,18 +1136,13 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
 #pragma unroll
         for (int a = 0; a < AF; ++a) as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, as[a], 0, 0, 0);
       }
-      // the group's fold: tot += s * (acc - (128 + z) * sum_k x)
+      // this group's scale/zero words (read now: the buffer is refilled
+      // after the next barrier)
       const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs + ((k0 / kPKT) % kPBufs) * kPSzSlots) +
                            (kl / G) * BN + wn * 64 + cl;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t wzt = zb[t * 16];
-        const float sc = bf_lo(wzt), zo = 128.0f + bf_hi(wzt);
-#pragma unroll
-        for (int a = 0; a < AF; ++a)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * as[a][v], tot[a][t][v]);
-      }
+      for (int t = 0; t < 4; ++t) pz[t] = zb[t * 16];
+      if (!defer) fold();
     } else {
       bf16x8_t af[AF];
 #pragma unroll
@@ -1167,6 +1192,7 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
       }
     }
   }
+  if (defer) fold();                             // the last group's
   // the last k-tiles' spare copies may still be landing in LDS, which the
   // results reuse: wait for every memory operation, then for every wavefront
   __builtin_amdgcn_s_waitcnt(0);
