@@ -181,6 +181,14 @@ def test_decode_parity_tiny_batch16(tau):
         assert all(e == 1 for e in Es)
 
 
+def test_decode_parity_tiny_batch64_max_rows():
+    """64 rows per step, the most the batched-row GEMM takes (four 16-row
+    blocks per workgroup), and 37 rows: a ragged last block."""
+    w = synth.make_weights(synth.TINY, seed=0, device="cuda")
+    parity_run(synth.TINY, w, B=64, T=6, steps=2, tau=0.5)
+    parity_run(synth.TINY, w, B=37, T=5, steps=2, tau=0.5)
+
+
 def test_split_attention_long_context_tiny():
     """A context of several hundred positions splits the decode attention over
     workgroups and merges the splits in the last one; B=8 fills the GEMV's
