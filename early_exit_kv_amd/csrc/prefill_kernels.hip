@@ -555,7 +555,10 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
   typedef MgemmShape<MB, G> S;
   constexpr int NT = S::NT, BN = S::BN, ROWS = S::ROWS, KS = S::KS, XS = S::XS;
   constexpr int STEPS = S::STEPS, GW = S::GW;
-  constexpr int D = Q4 ? 8 : 4;                   // groups in flight per lane
+  // groups in flight per lane: two (measured at 16 and 32 rows: deeper
+  // look-ahead makes the row staging, which waits for every load issued
+  // before it, start later, and saves no latency once the loop runs)
+  constexpr int D = 2;
   typedef typename WordsT<GW>::T WT;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
