@@ -810,11 +810,11 @@ MgemmPlan mgemm_plan(int M, int ncols, int K, bool allow_split) {
   pl.ncolblk = (ncols + kMgemmBN - 1) / kMgemmBN;
   const int KS = pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512;
   // fewest splits the LDS allows (each split adds a partial tile of
-  // rows x 128 fp32 per column block); more only if the grid would leave
-  // most CUs idle
+  // rows x 128 fp32 per column block); more while the grid is short of one
+  // workgroup per CU (256 on this chip)
   int ns = (K + KS - 1) / KS;
   if (allow_split)
-    while (pl.ncolblk * ns < 128 && K / (ns * 2) >= 256 && (K / (ns * 2)) % 128 == 0) ns *= 2;
+    while (pl.ncolblk * ns < 256 && K / (ns * 2) >= 256 && (K / (ns * 2)) % 128 == 0) ns *= 2;
   int ks = (K + ns - 1) / ns;
   ks = (ks + 127) / 128 * 128;
   pl.ks = std::min(ks, K);
