@@ -602,40 +602,42 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
   };
 
   const int slab0 = kbeg;
-  auto stage = [&](int base) {
-    // all loads of a batch are issued before any is used (the rows come from
-    // L2; one round trip per batch instead of one per item)
-    constexpr int PER = ROWS * (KS / 8) / 256;    // items per thread at most
+  // the rows of the split: all their loads are issued first, before any
+  // weight load, so that waiting for them does not wait for the weights (a
+  // wait counts loads in issue order); they land in LDS with their group sums
+  // once the first weight groups are in flight too
+  constexpr int PER = ROWS * (KS / 8) / 256;      // items per thread at most
+  uint4 xv[PER];
+  auto stage_load = [&](int base) {
     const int n8 = (kend - base) >> 3;
     const int total = ROWS * n8;
-    __syncthreads();
 #pragma unroll
-    for (int h = 0; h < PER; h += 8) {
-      uint4 v[8];
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      const int m = idx / n8, g8 = idx - m * n8;
+      xv[i] = make_uint4(0, 0, 0, 0);
+      if (idx < total && m < p.M)
+        xv[i] = *reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.ldx + base + 8 * g8);
+    }
+  };
+  auto stage_store = [&](int base) {
+    const int n8 = (kend - base) >> 3;
+    const int total = ROWS * n8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = threadIdx.x + 256 * (h + i);
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      if (idx < total) {
         const int m = idx / n8, g8 = idx - m * n8;
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (idx < total && m < p.M)
-          v[i] = *reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.ldx + base + 8 * g8);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = threadIdx.x + 256 * (h + i);
-        if (idx < total) {
-          const int m = idx / n8, g8 = idx - m * n8;
-          uint4 w = v[i];
-          if constexpr (Q4) {
-            // group sum: the G/8 items of a group sit in G/8 adjacent lanes
-            // (n8 and the 256-thread stride are multiples of G/8)
-            float gs = ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
-                       ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
-            gs = G == 128 ? sum16(gs) : sum8(gs);
-            if (g8 % (G / 8) == 0) L.xsg[m * (KS / G) + g8 / (G / 8)] = gs;
-          }
-          *reinterpret_cast<uint4 *>(L.xs + m * XS + 8 * g8) = w;
+        const uint4 w = xv[i];
+        if constexpr (Q4) {
+          // group sum: the G/8 items of a group sit in G/8 adjacent lanes
+          // (n8 and the 256-thread stride are multiples of G/8)
+          float gs = ((bf_lo(w.x) + bf_hi(w.x)) + (bf_lo(w.y) + bf_hi(w.y))) +
+                     ((bf_lo(w.z) + bf_hi(w.z)) + (bf_lo(w.w) + bf_hi(w.w)));
+          gs = G == 128 ? sum16(gs) : sum8(gs);
+          if (g8 % (G / 8) == 0) L.xsg[m * (KS / G) + g8 / (G / 8)] = gs;
         }
+        *reinterpret_cast<uint4 *>(L.xs + m * XS + 8 * g8) = w;
       }
     }
     __syncthreads();
@@ -698,13 +700,14 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
     }
   };
 
-  // the first D groups of weights are requested before the rows of the whole
-  // split (the plan keeps it within KS) are staged, so both latencies overlap;
-  // after that the loop only ever waits for the oldest weight group
+  // the rows of the whole split (the plan keeps it within KS), then the first
+  // D groups of weights, so both latencies overlap; after that the loop only
+  // ever waits for the oldest weight group
+  stage_load(kbeg);
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (u < nchunk) load(u, u);
-  stage(kbeg);
+  stage_store(kbeg);
   for (int c0 = 0; c0 < nchunk; c0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
