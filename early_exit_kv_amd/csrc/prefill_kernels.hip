@@ -1095,16 +1095,12 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
       // this lane's GW code words of the group, for each of its 4 column tiles
       const uint32_t *cb = reinterpret_cast<const uint32_t *>(cs + ((k0 / kPKT) % kPBufs) * CSL);
       const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
-      // (64-row wavefronts read them one step at a time: fewer live registers)
-      constexpr bool kByStep = false;
       WT wq[4];
-      int wsl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int col = wn * 64 + t * 16 + cl;
         const int slot = col * 4 + ((wo >> 2) ^ ((col >> 2) & 3));
-        wsl[t] = slot * 4 + (wo & 3);
-        if constexpr (!kByStep) wq[t] = *reinterpret_cast<const WT *>(cb + wsl[t]);
+        wq[t] = *reinterpret_cast<const WT *>(cb + slot * 4 + (wo & 3));
       }
       // the group sums of the rows come from one more MFMA per row block
       // against a B operand of ones (row sums in every column)
@@ -1129,8 +1125,7 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           uint32_t w;
-          if constexpr (kByStep) w = cb[wsl[t] + j];
-          else if constexpr (GW == 1) w = wq[t];
+          if constexpr (GW == 1) w = wq[t];
           else w = wq[t][j];
           uint32_t pr[4];
           unpack_word(w, pr);
