@@ -1162,16 +1162,28 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
             for (int b = 0; b < M; ++b) sums[b] += b == idx / n8 ? ss : 0.f;
           }
         }
-        for (int idx = tid + 256 * kMvHold; idx < total; idx += 256) {
-          const int m = idx / n8, g8 = idx - m * n8;
-          if (m < p.B) {
-            const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
-            const float4 a0 = *reinterpret_cast<const float4 *>(h);
-            const float4 a1 = *reinterpret_cast<const float4 *>(h + 4);
-            const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
-                             a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+        // items past the held ones, kMvHold at a time with all their loads
+        // issued before any is used (addresses clamped into the rows)
+        for (int idx0 = 256 * kMvHold; idx0 < total; idx0 += 256 * kMvHold) {
+          float4 ha[kMvHold], hb[kMvHold];
 #pragma unroll
-            for (int b = 0; b < M; ++b) sums[b] += b == m ? ss : 0.f;
+          for (int j = 0; j < kMvHold; ++j) {
+            const int idx = min(idx0 + 256 * j + tid, total - 1);
+            const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
+            const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
+            ha[j] = *reinterpret_cast<const float4 *>(h);
+            hb[j] = *reinterpret_cast<const float4 *>(h + 4);
+          }
+#pragma unroll
+          for (int j = 0; j < kMvHold; ++j) {
+            const int idx = idx0 + 256 * j + tid;
+            if (idx < total && idx / n8 < p.B) {
+              const float4 a0 = ha[j], a1 = hb[j];
+              const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
+                               a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
+#pragma unroll
+              for (int b = 0; b < M; ++b) sums[b] += b == idx / n8 ? ss : 0.f;
+            }
           }
         }
       }
@@ -1260,21 +1272,41 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         }
         put(idx, a0, a1, a2, a3);
       }
-      for (int idx0 = 256 * kMvHold; idx0 < total; idx0 += 256) {
-        const int idx = idx0 + tid;
-        const int m = min(idx, total - 1) / n8, g8 = min(idx, total - 1) - m * n8;
-        uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-        if (idx < total && m < p.B) {
+      // the items past the held ones, kMvHold at a time with all their loads
+      // issued before any is used (addresses clamped into the rows; the
+      // batch bound is uniform, so every lane of a wave takes part in put)
+      for (int idx0 = 256 * kMvHold; idx0 < total; idx0 += 256 * kMvHold) {
+        float4 ha[kMvHold], hb[kMvHold];
+        uint4 gb[kMvHold];
+#pragma unroll
+        for (int j = 0; j < kMvHold; ++j) {
+          const int idx = min(idx0 + 256 * j + tid, total - 1);
+          const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
           if constexpr (XS == kXNorm) {
             const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
-            norm8(m, *reinterpret_cast<const float4 *>(h), *reinterpret_cast<const float4 *>(h + 4),
-                  *reinterpret_cast<const uint4 *>(p.gain + 8 * g8), a0, a1, a2, a3);
+            ha[j] = *reinterpret_cast<const float4 *>(h);
+            hb[j] = *reinterpret_cast<const float4 *>(h + 4);
+            gb[j] = *reinterpret_cast<const uint4 *>(p.gain + 8 * g8);
           } else {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)m * p.x_stride + 8 * g8);
-            a0 = v.x; a1 = v.y; a2 = v.z; a3 = v.w;
+            gb[j] = *reinterpret_cast<const uint4 *>(p.x_src + (int64_t)m * p.x_stride + 8 * g8);
           }
         }
-        put(idx, a0, a1, a2, a3);
+#pragma unroll
+        for (int j = 0; j < kMvHold; ++j) {
+          if (idx0 + 256 * j < total) {
+            const int idx = idx0 + 256 * j + tid;
+            const int m = min(idx, total - 1) / n8;
+            uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+            if (idx < total && m < p.B) {
+              if constexpr (XS == kXNorm) {
+                norm8(m, ha[j], hb[j], gb[j], a0, a1, a2, a3);
+              } else {
+                a0 = gb[j].x; a1 = gb[j].y; a2 = gb[j].z; a3 = gb[j].w;
+              }
+            }
+            put(idx, a0, a1, a2, a3);
+          }
+        }
       }
       __syncthreads();
       if (fired && !ex) {
