@@ -107,6 +107,80 @@ hipError_t launch_rows_cos_exit(const RowsCosParams &p, hipStream_t s) {
 }
 
 // ===========================================================================
+// End of a decode layer of many rows in one launch: the exit test of the
+// layer (c_r = cos(a_r, b_r), m = min_r c_r against tau in the last
+// workgroup, as rows_cos_kernel) and the RMSNorm of its output rows b for the
+// next layer (as rows_norm_kernel, |b_r|^2 serving both).  One workgroup per
+// row; `test` false (forced decisions) leaves the test out.
+// ===========================================================================
+__global__ __launch_bounds__(256) void rows_cos_norm_kernel(RowsCosParams c, RowsNormParams n, int test) {
+  __shared__ float red[4], bred[4];
+  __shared__ int last_flag;
+  const int64_t r = blockIdx.x;
+  const float *a = c.a + r * c.d, *b = c.b + r * c.d;
+  float4 va[kNormHeld], vb[kNormHeld];
+  float sd = 0.f, sa = 0.f, sb = 0.f;
+  // the flag is read once by every workgroup before any can change it (only
+  // the last one to arrive sets it), so all of them agree on skipping
+  const bool do_test = test && c.ctrl->flag == 0 && c.ctrl->force_E < 0;
+#pragma unroll
+  for (int i = 0; i < kNormHeld; ++i) {
+    const int k = 4 * (threadIdx.x + 256 * i);
+    vb[i] = k < c.d ? *reinterpret_cast<const float4 *>(b + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    va[i] = do_test && k < c.d ? *reinterpret_cast<const float4 *>(a + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < kNormHeld; ++i) {
+    sb += vb[i].x * vb[i].x + vb[i].y * vb[i].y + vb[i].z * vb[i].z + vb[i].w * vb[i].w;
+    sa += va[i].x * va[i].x + va[i].y * va[i].y + va[i].z * va[i].z + va[i].w * va[i].w;
+    sd += va[i].x * vb[i].x + va[i].y * vb[i].y + va[i].z * vb[i].z + va[i].w * vb[i].w;
+  }
+  sb = block_sum(sb, red);
+  // RMSNorm of row b
+  const float rs = 1.0f / sqrtf(sb / (float)n.d + n.eps);
+  uint16_t *x = n.x + r * n.d;
+#pragma unroll
+  for (int i = 0; i < kNormHeld; ++i) {
+    const int k = 4 * (threadIdx.x + 256 * i);
+    if (k < n.d) {
+      const uint2 g = *reinterpret_cast<const uint2 *>(n.gain + k);
+      uint2 o;
+      o.x = pack_bf2(vb[i].x * rs * bf_lo(g.x), vb[i].y * rs * bf_hi(g.x));
+      o.y = pack_bf2(vb[i].z * rs * bf_lo(g.y), vb[i].w * rs * bf_hi(g.y));
+      *reinterpret_cast<uint2 *>(x + k) = o;
+    }
+  }
+  if (!do_test) return;
+  sa = block_sum(sa, red);
+  sd = block_sum(sd, red);
+  float cs = sd / fmaxf(sqrtf(sa) * sqrtf(sb), 1e-8f);
+  cs = fminf(fmaxf(cs, -1.0f), 1.0f);
+  if (threadIdx.x == 0) st_coherent(&c.part[blockIdx.x], cs);
+  if (arrive_last(&c.ctrl->counters[kCtrRowsCos], gridDim.x, &last_flag)) {
+    float mm = 2.0f;
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += 256) mm = fminf(mm, ld_coherent(&c.part[i]));
+    mm = block_min(mm, bred);
+    if (threadIdx.x == 0) {
+      Control *ct = c.ctrl;
+      ct->trace[c.layer] = mm;
+      if (mm > ct->tau) {
+        ct->flag = 1;
+        ct->E = c.layer + 1;
+      }
+    }
+  }
+}
+
+hipError_t launch_rows_cos_norm(const RowsCosParams &c, const RowsNormParams &n, bool test, hipStream_t s) {
+  if (n.d % 4 || n.d > 4 * 256 * kNormHeld || n.d != c.d || n.rows != c.rows) return hipErrorInvalidValue;
+  if (n.h_stride != 0 && n.h_stride != n.d) return hipErrorInvalidValue;
+  const int t = test ? 1 : 0;
+  void *args[] = {const_cast<RowsCosParams *>(&c), const_cast<RowsNormParams *>(&n), const_cast<int *>(&t)};
+  return launch_kernel(reinterpret_cast<const void *>(rows_cos_norm_kernel), dim3((unsigned)c.rows), dim3(256),
+                       args, 0, s);
+}
+
+// ===========================================================================
 // MFMA GEMM: Y[m][n] = sum_k X[m][k] W[n][k] with v_mfma_f32_16x16x32_bf16.
 //   Workgroup tile BM x BN, 4 wavefronts in a 2 x 2 arrangement, k-step 32.
 //   bf16 weights feed the MFMA directly.  int4 weights enter as the exact bf16

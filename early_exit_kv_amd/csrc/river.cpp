@@ -352,8 +352,12 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
   for (int l = 0; l < c.n_layers; ++l) {
     const river_layer_w &L = ctx->layers[l];
     RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
-    RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), B, c.d_model, c.rms_eps, 0};
-    TIMED_ONLY(RIVER_K_P_NORM, launch_rows_norm(rn, s));
+    if (l == 0) {
+      // (deeper layers get their normalised rows from the previous layer's
+      // last launch, together with its exit test)
+      RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), B, c.d_model, c.rms_eps, 0};
+      TIMED_ONLY(RIVER_K_P_NORM, launch_rows_norm(rn, s));
+    }
 
     GemmParams q = mgemm_base(ctx, l, B);
     fill_weights(ctx, l, 0, 3, q.w);
@@ -397,10 +401,13 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
     TIMED_ONLY(RIVER_K_DOWN, launch_mgemm(kEpResid, dn, s));
 
-    if (l < c.n_layers - 1 && ctx->force_E < 0) {
+    if (l < c.n_layers - 1) {
+      // the exit test after this layer and the next layer's input RMSNorm
       RowsCosParams rc{hA, hB, B, c.d_model, at<float>(ctx->ws, ctx->wl.part), ctx->ctrl, l,
                        c.n_layers};
-      TIMED_ONLY(RIVER_K_P_COS, launch_rows_cos_exit(rc, s));
+      RowsNormParams rn{hB, x, static_cast<const uint16_t *>(ctx->layers[l + 1].attn_norm), B, c.d_model,
+                        c.rms_eps, 0};
+      TIMED_ONLY(RIVER_K_P_COS, launch_rows_cos_norm(rc, rn, ctx->force_E < 0, s));
     }
     std::swap(hA, hB);
   }

@@ -255,5 +255,8 @@ struct RowsCosParams {
   float *part; Control *ctrl; int layer; int n_layers;
 };
 hipError_t launch_rows_cos_exit(const RowsCosParams &p, hipStream_t s);
+// Exit test of a layer of many rows and the RMSNorm of its output rows for the
+// next layer, one launch (n.h must be c.b, unit row stride).
+hipError_t launch_rows_cos_norm(const RowsCosParams &c, const RowsNormParams &n, bool test, hipStream_t s);
 
 }  // namespace river
