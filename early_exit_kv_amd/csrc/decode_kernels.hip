@@ -878,6 +878,14 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   const bool exit_sums = (EP == kEpResidExit) && p.test_exit && !ex && force0 < 0;
   const float *hsrc = exit_sums ? p.h_src : p.h_in;
   const int n8 = K >> 3, total = M * n8;
+  // batch row of staging item idx < total (M - 1 comparisons instead of an
+  // integer division by the run-time row length)
+  auto rowof = [&](int idx) {
+    int m = 0;
+#pragma unroll
+    for (int b = 1; b < M; ++b) m += idx >= b * n8 ? 1 : 0;
+    return m;
+  };
 
   // One pass for one weight form (Q4: int4 codes; else bf16 backbone or bf16
   // exit copy).  Returns true when the pending test chose the exit layer and
@@ -1125,7 +1133,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 #pragma unroll
       for (int j = 0; j < kMvHold; ++j) {
         const int idx = min(tid + 256 * j, total - 1);
-        const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
+        const int mr = rowof(idx);
+        const int m = min(mr, p.B - 1), g8 = idx - mr * n8;
         if constexpr (XS == kXNorm) {
           const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
           hv[j][0] = *reinterpret_cast<const float4 *>(h);
@@ -1154,12 +1163,13 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 #pragma unroll
         for (int j = 0; j < kMvHold; ++j) {
           const int idx = tid + 256 * j;
-          if (idx < total && idx / n8 < p.B) {
+          const int mi = rowof(idx);
+          if (idx < total && mi < p.B) {
             const float4 a0 = hv[j][0], a1 = hv[j][1];
             const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
                              a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
 #pragma unroll
-            for (int b = 0; b < M; ++b) sums[b] += b == idx / n8 ? ss : 0.f;
+            for (int b = 0; b < M; ++b) sums[b] += b == mi ? ss : 0.f;
           }
         }
         // items past the held ones, kMvHold at a time with all their loads
@@ -1169,7 +1179,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 #pragma unroll
           for (int j = 0; j < kMvHold; ++j) {
             const int idx = min(idx0 + 256 * j + tid, total - 1);
-            const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
+            const int mr = rowof(idx);
+            const int m = min(mr, p.B - 1), g8 = idx - mr * n8;
             const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
             ha[j] = *reinterpret_cast<const float4 *>(h);
             hb[j] = *reinterpret_cast<const float4 *>(h + 4);
@@ -1177,12 +1188,13 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 #pragma unroll
           for (int j = 0; j < kMvHold; ++j) {
             const int idx = idx0 + 256 * j + tid;
-            if (idx < total && idx / n8 < p.B) {
+            const int mi = rowof(min(idx, total - 1));
+            if (idx < total && mi < p.B) {
               const float4 a0 = ha[j], a1 = hb[j];
               const float ss = a0.x * a0.x + a0.y * a0.y + a0.z * a0.z + a0.w * a0.w + a1.x * a1.x +
                                a1.y * a1.y + a1.z * a1.z + a1.w * a1.w;
 #pragma unroll
-              for (int b = 0; b < M; ++b) sums[b] += b == idx / n8 ? ss : 0.f;
+              for (int b = 0; b < M; ++b) sums[b] += b == mi ? ss : 0.f;
             }
           }
         }
@@ -1240,7 +1252,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 
       // stage x as bf16 rows (zeros past B) with the group sums of each row
       auto put = [&](int idx, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
-        const int m = idx / n8, g8 = idx - m * n8;
+        const int m = rowof(min(idx, total - 1)), g8 = idx - m * n8;
         float gs = (bf_lo(a0) + bf_hi(a0)) + (bf_lo(a1) + bf_hi(a1)) + (bf_lo(a2) + bf_hi(a2)) +
                    (bf_lo(a3) + bf_hi(a3));
         // the G/8 items of a group sit in G/8 adjacent lanes
@@ -1264,7 +1276,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 #pragma unroll
       for (int j = 0; j < kMvHold; ++j) {
         const int idx = tid + 256 * j;
-        const int m = min(idx, total - 1) / n8;
+        const int m = rowof(min(idx, total - 1));
         uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
         if (idx < total && m < p.B) {
           if constexpr (XS == kXNorm) norm8(m, hv[j][0], hv[j][1], gv[j], a0, a1, a2, a3);
@@ -1281,7 +1293,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
 #pragma unroll
         for (int j = 0; j < kMvHold; ++j) {
           const int idx = min(idx0 + 256 * j + tid, total - 1);
-          const int m = min(idx / n8, p.B - 1), g8 = idx % n8;
+          const int mr = rowof(idx);
+          const int m = min(mr, p.B - 1), g8 = idx - mr * n8;
           if constexpr (XS == kXNorm) {
             const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
             ha[j] = *reinterpret_cast<const float4 *>(h);
@@ -1295,7 +1308,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         for (int j = 0; j < kMvHold; ++j) {
           if (idx0 + 256 * j < total) {
             const int idx = idx0 + 256 * j + tid;
-            const int m = min(idx, total - 1) / n8;
+            const int m = rowof(min(idx, total - 1));
             uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
             if (idx < total && m < p.B) {
               if constexpr (XS == kXNorm) {
