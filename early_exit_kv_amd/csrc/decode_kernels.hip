@@ -816,6 +816,11 @@ __device__ __forceinline__ RowRef mv_row(const GemvParams &p, int L) {
 __device__ __forceinline__ void dma16(uint32_t lds, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
+// the same for data read once (weights): non-temporal, so that the stream
+// does not push out of L2 what the workgroups of the launch share (the rows)
+__device__ __forceinline__ void dma16_nt(uint32_t lds, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(g) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(uint32_t lds, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
@@ -957,8 +962,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
       }
       const int ku = min(wid * U + s, KU - 1);
       const uint32_t slot = wring_lds + d * kMvSlot;
-      dma16(slot, wr0 + ku * 128 + wchunk);
-      dma16(slot + 1024, wr1 + ku * 128 + wchunk1);
+      dma16_nt(slot, wr0 + ku * 128 + wchunk);
+      dma16_nt(slot + 1024, wr1 + ku * 128 + wchunk1);
       if constexpr (Q4) dma4(slot + kMvSlotW, zr + ku * NGU + min(lane & 3, NGU - 1));
       if constexpr (NEPI >= 1) dma4(slot + kMvSlotW + 256, e0);
       if constexpr (NEPI >= 2) dma4(slot + kMvSlotW + 512, e1);
