@@ -1930,8 +1930,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       const int P = 64 * h + lane, r = P / CPR, c = (P % CPR) ^ attn_swz<DH>(r);
       const int64_t off = (int64_t)min(base + r, p.S - 1) * DH + 8 * c;
       const uint32_t dst = kvw_lds + bi * KVB + 1024 * h;
-      dma16(dst, Kc + off);
-      dma16(dst + BLK, Vc + off);
+      dma16_nt(dst, Kc + off);
+      dma16_nt(dst + BLK, Vc + off);
     }
   };
 
