@@ -1519,15 +1519,15 @@ static MvPlan mgemv_plan(Epilogue ep, const GemvParams &p) {
 
 // GEMV choice: mode 1 the dot-product kernel everywhere, mode 2 the
 // matrix-core one wherever it fits, mode 0 (default) the one measured faster
-// per linear on 8B shapes: at one or two rows the matrix cores for gate|up,
-// o and down (q|k|v and the LM head keep the dot-product GEMV, whose
-// arithmetic still hides behind its stream there), from three rows on for
-// every linear that fits (the dot products grow with the rows, the MFMA work
-// does not), except the LM head at four rows
+// per linear on 8B shapes: at one row the matrix cores for gate|up, o and
+// down (q|k|v and the LM head keep the dot-product GEMV, whose arithmetic
+// still hides behind its stream there), at two rows for q|k|v too, from three
+// rows on for every linear that fits (the dot products grow with the rows,
+// the MFMA work does not), except the LM head up to four rows
 static bool use_mgemv(Epilogue ep, const GemvParams &p) {
   if (p.gemv_mode == 1 || !mgemv_fits(ep, p)) return false;
   if (p.gemv_mode == 2) return true;
-  if (p.B <= 2) return ep == kEpSwiGLU || ep == kEpResidExit || ep == kEpResid || ep == kEpPlain;
+  if (p.B == 1) return ep != kEpQKV && ep != kEpLogits;
   return !(ep == kEpLogits && p.B <= 4);
 }
 

@@ -62,7 +62,7 @@ def test_linear_cores_8b(ctx8b, M, use_exit):
     check_linears(ctx8b, M, use_exit)
 
 
-@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("use_exit", [0, 1])
 def test_linear_mfma_gemv_8b(ctx8b, M, use_exit):
     """The matrix-core GEMV of decode steps (where it fits) on the same shapes."""
@@ -74,7 +74,7 @@ def test_linear_mfma_gemv_8b(ctx8b, M, use_exit):
         r.gemv_mode("auto")
 
 
-@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("use_exit", [0, 1])
 def test_linear_dot_gemv_8b(ctx8b, M, use_exit):
     """The dot-product GEMV on the same shapes."""
