@@ -13,7 +13,8 @@
 namespace river {
 
 // ===========================================================================
-// Pass begin: reset the per-pass control fields, write tau, gather embeddings.
+// Pass begin: reset the per-pass control fields (and write tau for a
+// prefill), gather embeddings.
 // ===========================================================================
 __global__ __launch_bounds__(256) void begin_kernel(BeginParams p) {
   Control *c = p.ctrl;
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(256) void begin_kernel(BeginParams p) {
       c->flag = 0;
       c->force_E = p.force_E;
       c->E = p.force_E >= 0 ? p.force_E : p.n_layers;
-      c->tau = p.tau;
+      if (p.write_tau) c->tau = p.tau;
       if (p.set_pos >= 0) c->pos = p.set_pos;
     }
     for (int l = threadIdx.x; l < kMaxLayers; l += blockDim.x) c->trace[l] = __builtin_nanf("");
@@ -56,6 +57,13 @@ hipError_t launch_begin(const BeginParams &p, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   if (blocks > 65536) blocks = 65536;
   return launch_1(begin_kernel, dim3((unsigned)blocks), dim3(256), p, s);
+}
+
+__global__ void set_tau_kernel(Control *c, float tau) { c->tau = tau; }
+
+hipError_t launch_set_tau(Control *c, float tau, hipStream_t s) {
+  hipLaunchKernelGGL(set_tau_kernel, dim3(1), dim3(1), 0, s, c, tau);
+  return hipGetLastError();
 }
 
 __global__ void clear_kernel(uint32_t *p, size_t n) {
@@ -1995,11 +2003,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     for (int h = 0; h < GQ; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] *= corr[h];
-    // P V: this lane's 8 head dims of position pass * PPW + slot
+    // P V: this lane's 8 head dims of position pass * PPW + slot.  Rows past
+    // the visible positions have p = 0 but may hold any bits (a cache slot
+    // never written, NaN included), so they are zeroed rather than weighted.
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = ps * PPW + slot;
-      const uint4 v = *reinterpret_cast<const uint4 *>(vb + 16 * (r * CPR + (ln ^ attn_swz<DH>(r))));
+      uint4 v = *reinterpret_cast<const uint4 *>(vb + 16 * (r * CPR + (ln ^ attn_swz<DH>(r))));
+      if (base + r >= t1) v = make_uint4(0, 0, 0, 0);
       const float vf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
                            bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
       float pr[GQ];

@@ -130,16 +130,19 @@ __device__ __forceinline__ float block_min(float v, float *red) {
 }
 
 // Last-workgroup hand-off: every workgroup publishes its results, then thread
-// 0 counts itself in; the workgroup that brings the count to `total` sees all
-// published data (release/acquire at agent scope) and resets the counter.
+// 0 counts itself in; the workgroup that brings the count to `total` resets
+// the counter and may read what the others published.
 //
-// Data handed across workgroups inside one kernel travels only through
-// relaxed agent-scope atomics (coherent at device scope on their own: they are
-// not kept dirty in one XCD's L2), so no release/acquire fence is needed --
-// on gfx950 those fences write back / invalidate the whole L2.  Ordering:
-// each thread waits for its own coherent stores to complete (s_waitcnt, also
-// a compiler barrier) before the workgroup barrier, and only then does thread
-// 0 count the workgroup in.
+// Contract: every value handed from one workgroup to another inside a kernel
+// is written with st_coherent and read with ld_coherent (relaxed agent-scope
+// atomics, which are coherent across the XCDs on their own: they are not kept
+// dirty in one XCD's L2).  The counter itself is a relaxed atomic too; there
+// is no release/acquire fence (on gfx950 such fences write back or invalidate
+// the whole L2), so a plain store or load of handed-over data would NOT be
+// ordered by this hand-off.  Ordering comes from each thread waiting for its
+// own coherent stores to complete (s_waitcnt vmcnt(0), also a compiler
+// barrier) before the workgroup barrier, after which thread 0 counts the
+// workgroup in.
 __device__ __forceinline__ void st_coherent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

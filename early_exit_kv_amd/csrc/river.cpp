@@ -141,16 +141,19 @@ struct river_ctx {
   int batch = 0;
   bool use_graph = true;
   int force_E = -1;
+  // One recorded decode step per (buffers, batch, forced E); tau is not part
+  // of the key: a step reads it from the control block.
   struct GraphKey {
     const void *tok, *logits, *next;
     int B, force_E;
-    uint32_t tau_bits;
     bool operator<(const GraphKey &o) const {
-      return std::tie(tok, logits, next, B, force_E, tau_bits) <
-             std::tie(o.tok, o.logits, o.next, o.B, o.force_E, o.tau_bits);
+      return std::tie(tok, logits, next, B, force_E) < std::tie(o.tok, o.logits, o.next, o.B, o.force_E);
     }
   };
   std::map<GraphKey, hipGraphExec_t> graphs;
+  // tau the control block holds (after a build it holds 0, a prefill writes
+  // its own); a decode step with another tau first enqueues launch_set_tau
+  uint32_t ctrl_tau_bits = 0;
   // profiling: events around every launch, folded into per-class totals on read
   bool profiling = false;
   struct Timed {
@@ -168,6 +171,9 @@ struct river_ctx {
 };
 
 namespace {
+
+// recorded decode steps kept per context before the cache is emptied
+constexpr size_t kMaxGraphs = 32;
 
 bool valid_config(const river_config *c) {
   if (!c) return false;
@@ -346,7 +352,7 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
-  bp.tau = tau; bp.is_prefill = 0; bp.set_pos = -1;
+  bp.tau = tau; bp.write_tau = 0; bp.is_prefill = 0; bp.set_pos = -1;
   TIMED_ONLY(RIVER_K_BEGIN, launch_begin(bp, s));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -434,7 +440,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
-  bp.tau = tau; bp.is_prefill = 0; bp.set_pos = -1;
+  bp.tau = tau; bp.write_tau = 0; bp.is_prefill = 0; bp.set_pos = -1;
   TIMED_ONLY(RIVER_K_BEGIN, launch_begin(bp, s));
 
   int down_wgs = 0;
@@ -529,7 +535,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = R; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
-  bp.tau = tau; bp.is_prefill = 1; bp.set_pos = T;
+  bp.tau = tau; bp.write_tau = 1; bp.is_prefill = 1; bp.set_pos = T;
   TIMED(RIVER_K_BEGIN, launch_begin(bp, s));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -714,6 +720,7 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
   drop_graphs(ctx);
   ctx->built = false;
   RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads), ctx->stream));
+  ctx->ctrl_tau_bits = 0;   // the cleared block holds tau = +0.0
   RV_TRY(launch_rope_table(at<float2>(ctx->ws, ctx->wl.rope), c.max_seq, c.head_dim, c.rope_theta,
                            ctx->stream));
   LinearShape sh[7];
@@ -750,6 +757,12 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
   if (ctx->rec && record_layout(ctx->cfg, (int64_t)B * T).total > ctx->rec_bytes)
     return RIVER_E_BAD_SIZE;
   const int st = enqueue_prefill(ctx, d_tokens, B, T, tau, d_logits, d_next);
+  // its begin kernel wrote tau (after a failure the value is unknown: a bit
+  // pattern no finite tau has makes the next decode step write it again)
+  if (st == RIVER_OK)
+    std::memcpy(&ctx->ctrl_tau_bits, &tau, 4);
+  else
+    ctx->ctrl_tau_bits = 0x7FC00001u;
   if (st != RIVER_OK) return st;
   ctx->pos = T;
   ctx->batch = B;
@@ -764,20 +777,28 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
   if (ctx->pos + 1 > ctx->cfg.max_seq) return RIVER_E_RANGE;
   if (ctx->rec && record_layout(ctx->cfg, ctx->batch).total > ctx->rec_bytes)
     return RIVER_E_BAD_SIZE;
+  // the step reads tau from the control block: write it when it changes
+  uint32_t tau_bits;
+  std::memcpy(&tau_bits, &tau, 4);
+  if (tau_bits != ctx->ctrl_tau_bits) {
+    RV_TRY(launch_set_tau(ctx->ctrl, tau, ctx->stream));
+    ctx->ctrl_tau_bits = tau_bits;
+  }
   if (ctx->use_graph && !ctx->profiling && !ctx->rec && ctx->stream != nullptr) {
-    river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E, 0};
-    std::memcpy(&key.tau_bits, &tau, 4);
+    const river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E};
     auto it = ctx->graphs.find(key);
     if (it == ctx->graphs.end()) {
-      hipGraph_t graph;
+      // every new (tokens, logits, next) triple records a graph; callers that
+      // reuse their buffers hit the cache, the others are bounded here
+      if (ctx->graphs.size() >= kMaxGraphs) drop_graphs(ctx);
+      hipGraph_t graph = nullptr;
       RV_TRY(hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
       const int st = enqueue_decode(ctx, d_tokens, tau, d_logits, d_next);
       hipError_t e = hipStreamEndCapture(ctx->stream, &graph);
+      hipGraphExec_t exec = nullptr;
+      if (st == RIVER_OK && e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      if (graph) (void)hipGraphDestroy(graph);
       if (st != RIVER_OK) return st;
-      if (e != hipSuccess) return RIVER_E_HIP;
-      hipGraphExec_t exec;
-      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-      (void)hipGraphDestroy(graph);
       if (e != hipSuccess) return RIVER_E_HIP;
       it = ctx->graphs.emplace(key, exec).first;
     }

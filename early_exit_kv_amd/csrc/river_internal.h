@@ -170,6 +170,9 @@ struct BeginParams {
   float *h;
   int d, vocab, n_layers, force_E;
   float tau;
+  int write_tau;      // 1: write tau into the control block (prefill); decode
+                      // steps read the tau launch_set_tau left there, so one
+                      // recorded step serves every tau
   int is_prefill;
   int set_pos;        // >= 0: write this position into the control block
 };
@@ -189,6 +192,8 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
                            hipStream_t s);
 hipError_t launch_begin(const BeginParams &p, hipStream_t s);
+// one thread writes tau into the control block
+hipError_t launch_set_tau(Control *c, float tau, hipStream_t s);
 // RoPE table: rope[t][i] = (cos, sin)(t * theta^(-2i/Dh)), angles in float64
 hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float theta, hipStream_t s);
 hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s);

@@ -255,6 +255,16 @@ class River:
         return logits, next_tok
 
     def decode_step(self, tokens, tau, want_logits=True, logits=None, next_tok=None):
+        # the C ABI reads int32 ids in place; a converted copy would be a new
+        # pointer, and so a new recorded graph, on every step
+        if (not isinstance(tokens, torch.Tensor) or tokens.dtype != torch.int32 or not tokens.is_cuda
+                or tokens.dim() != 1 or not tokens.is_contiguous()):
+            raise ValueError("decode_step: tokens must be a contiguous int32 CUDA tensor of shape [B]")
+        if self.batch is not None and tokens.shape[0] != self.batch:
+            raise ValueError(f"decode_step: {tokens.shape[0]} tokens for a batch of {self.batch}")
+        for name, t, dt in (("logits", logits, torch.float32), ("next_tok", next_tok, torch.int32)):
+            if t is not None and (t.dtype != dt or not t.is_cuda or not t.is_contiguous()):
+                raise ValueError(f"decode_step: {name} must be a contiguous {dt} CUDA tensor")
         B = tokens.shape[0]
         if logits is None and want_logits:
             logits = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)

@@ -23,9 +23,11 @@
  *     synchronises except river_exit_stats().  A kernel fault surfaces at the
  *     next synchronisation, as usual for HIP.
  *   - Every call returns a river status code.  Arguments and state are checked
- *     on the host before anything is enqueued; a call that fails enqueues
- *     nothing and leaves the context unchanged.  No C++ exception crosses the
- *     ABI.
+ *     on the host before anything is enqueued: a call rejected by those checks
+ *     enqueues nothing and leaves the context unchanged.  A HIP error met
+ *     while enqueueing (RIVER_E_HIP) can leave the launches made before it on
+ *     the stream; the pass is then incomplete and should be repeated from a
+ *     prefill.  No C++ exception crosses the ABI.
  *   - bf16 means bfloat16 stored as 16-bit words; matrices are row-major
  *     [rows][cols], a linear layer's weight is [out N][in K] (y = x W^T).
  *   - The context is not thread-safe: calls on one context must not overlap.
@@ -119,7 +121,12 @@ typedef struct {
 /* Sizes of the four device buffers the caller must allocate for cfg.
  * Shared KV cache layout (bf16): K then V, each [L][max_batch][Hkv][max_seq][Dh],
  * i.e. L*2*Hkv*Dh*2 bytes per token and row; exit layers add no KV bytes.
- * Returns RIVER_E_INVALID_ARG / RIVER_E_UNIMPLEMENTED for unusable shapes. */
+ * That is the single shared cache of the lead page's section 3 (an exit layer
+ * writes the slot of the layer it copies); section 6's peak-memory figures at
+ * 16K and 64K tokens grow by exactly this per-token amount for the original
+ * model and for the exit scheme alike (131,072 B per token at the Llama-3.1-8B
+ * shape).  Returns RIVER_E_INVALID_ARG / RIVER_E_UNIMPLEMENTED for unusable
+ * shapes. */
 int river_query_sizes(const river_config *cfg, river_sizes *out);
 
 /* Byte offsets, inside the exit bank, of one exit linear of one layer.
@@ -136,7 +143,9 @@ int river_query_sizes(const river_config *cfg, river_sizes *out);
 int river_exit_bank_offsets(const river_config *cfg, int32_t layer, int32_t linear,
                             int32_t copy_layout, size_t *codes_off, size_t *sz_off);
 
-/* Create a context.  exit_bank, kv_cache, workspace, control: device buffers
+/* Create a context for the decoder of the lead page's section 3 (backbone
+ * layers, one exit layer beside each, one shared KV cache).  exit_bank,
+ * kv_cache, workspace, control: device buffers
  * of at least the sizes in `given`, which must be no smaller than what
  * river_query_sizes(cfg) reports (else RIVER_E_BAD_SIZE).  w: backbone weights,
  * borrowed.  hip_stream: a hipStream_t (NULL = the null stream).  Touches no
@@ -170,11 +179,24 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
  * (B from the last prefill) are written at the next position; after each
  * backbone layer l < L-1 the batch-minimum cosine is compared with tau on the
  * device and, once it exceeds tau, layers l+1.. run as exit layers.  Outputs
- * as in river_prefill.  RIVER_E_RANGE when the cache is full. */
+ * as in river_prefill.  RIVER_E_RANGE when the cache is full.
+ * With RIVER_OPT_GRAPH on (and a non-default stream) each step is recorded
+ * once as a HIP graph per (d_tokens, d_logits, d_next, batch, forced E) and
+ * replayed: reuse the same buffers from step to step.  tau is not part of
+ * the recording (a step reads it from the control block, written by one
+ * small kernel when it differs from the previous pass's), so a tau sweep
+ * replays the same graph.  At most 32 recordings are kept; the 33rd
+ * distinct buffer triple drops them all. */
 int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float *d_logits,
                       int32_t *d_next);
 
-/* Copy the statistics to host memory; synchronises the stream. */
+/* Copy the statistics to host memory; synchronises the stream.  The
+ * histograms of E per prefill and per decode step, and their mean, are the
+ * "mean exit layer" statistic the lead page's section 4 reports per tau (E
+ * counts backbone layers run, 1..n_layers).  This is the only call that
+ * synchronises with the device; the per-layer activations and the cache
+ * slots of a pass are read through river_set_record and the caller-owned
+ * kv_cache buffer instead of a separate read-back call. */
 int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
 
 /* Options.

@@ -322,3 +322,38 @@ def test_record_and_kernel_timing_entry_points(tiny):
             assert e.value.code == rv.RIVER_E_INVALID_ARG
         r.close()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_tau_sweep_replays_one_graph(tiny):
+    """tau lives in the control block: decode steps with different tau replay
+    the same recorded step and take each tau's decision (tau > 1 never exits,
+    tau < -1 exits after the first layer), bit for bit as eager launches do."""
+    rv = _river()
+    s = synth.TINY
+    L = s.n_layers
+    toks = synth.make_tokens(s, 2, 16, seed=0).cuda()
+    taus = [2.0, -1.5, 0.5, 2.0, -1.5]
+    runs = []
+    for graph in (True, False):
+        r = rv.River(s, tiny["cuda"], 2, 16 + len(taus))
+        r.use_graph(graph)
+        r.build_exit_layers("int4")
+        _, nx = r.prefill(toks, 0.5)
+        tok = torch.empty(2, dtype=torch.int32, device="cuda")
+        lg = torch.empty((2, s.vocab), dtype=torch.float32, device="cuda")
+        nxt = torch.empty(2, dtype=torch.int32, device="cuda")
+        tok.copy_(nx)
+        out = []
+        for tau in taus:
+            r.decode_step(tok, tau, logits=lg, next_tok=nxt)
+            out.append((r.exit_stats()["last_E"], lg.cpu().clone()))
+            tok.copy_(nxt)
+        r.close()
+        runs.append(out)
+    for (eg, lg_g), (ee, lg_e), tau in zip(runs[0], runs[1], taus):
+        assert eg == ee, (tau, eg, ee)
+        assert torch.equal(lg_g, lg_e), tau
+        if tau > 1:
+            assert eg == L
+        if tau < -1:
+            assert eg == 1

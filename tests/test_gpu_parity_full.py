@@ -39,20 +39,32 @@ def host_weights(w, dtype=np.float64):
             "layers": [{k: cv(v) for k, v in lw.items()} for lw in w["layers"]]}
 
 
-def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto", attn="mfma"):
+def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto", attn="mfma", chunk=0,
+               check_prefill=True, free_running=True):
     """Prefill + decode steps on the GPU with every pass checked stage by stage
     (teacher forcing at each stored activation), and a free-running oracle
-    beside it for the exit decisions and the K/V cosine bar."""
+    beside it for the exit decisions and the K/V cosine bar.
+
+    chunk: positions per decode-attention workgroup (0: the library's choice).
+    check_prefill=False: the prefill pass is not checked stage by stage (the
+    decode steps still are, against the cache the GPU's prefill left: the
+    attention of each step over every stored position included).
+    free_running=False: no free-running oracle (for prompts too long for the
+    float64 oracle to prefill in seconds).
+    """
     rv = _river()
     max_seq = T + steps
     L = len(w_dev["layers"])
-    print(f"[parity-full] {shape.name} L={L} B={B} T={T} steps={steps} tau={tau}", flush=True)
+    print(f"[parity-full] {shape.name} L={L} B={B} T={T} steps={steps} tau={tau} attn={attn} "
+          f"chunk={chunk} gemv={gemv}", flush=True)
     sh = synth.shrink(shape, n_layers=L)
     r = rv.River(sh, w_dev, B, max_seq)
     r.gemv_mode(gemv)
     r.attn_kind(attn)
+    if chunk:
+        r.set_option(rv.RIVER_OPT_ATTN_CHUNK, chunk)
     r.build_exit_layers(mode)
-    r.record(B * T)
+    r.record(B * T if check_prefill else 0)
     hw = host_weights(w_dev)
     orc = ro.RiverOracle(sh.as_dict(), hw, B, max_seq)
     orc.build_exit_layers(mode)
@@ -72,11 +84,19 @@ def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto", attn="m
     toks = synth.make_tokens(sh, B, T, seed=0)
     gl, gn = r.prefill(toks.cuda(), tau)
     st = r.exit_stats()
-    kc, vc = check(gl, gn, st, T, 0)
-    o = orc.prefill(toks.numpy(), tau)
-    if check_decision(st["last_E"], st["last_trace"], o, tau, L):
-        o = orc.prefill(toks.numpy(), tau, force_E=st["last_E"])
-    kv_cos(kc, vc, orc, L, B, 0, T)
+    if check_prefill:
+        kc, vc = check(gl, gn, st, T, 0)
+    else:
+        r.record(B)
+    if free_running:
+        if not check_prefill:
+            k, v = r.kv_views()
+            kc = k[:L, :B, :, :T].double().cpu().numpy()
+            vc = v[:L, :B, :, :T].double().cpu().numpy()
+        o = orc.prefill(toks.numpy(), tau)
+        if check_decision(st["last_E"], st["last_trace"], o, tau, L):
+            o = orc.prefill(toks.numpy(), tau, force_E=st["last_E"])
+        kv_cos(kc, vc, orc, L, B, 0, T)
     Es = [st["last_E"]]
     tok = torch.empty(B, dtype=torch.int32, device="cuda")
     nxt = gn.cpu().numpy().astype(np.int64)
@@ -85,11 +105,12 @@ def parity_run(shape, w_dev, B, T, steps, tau, mode="int4", gemv="auto", attn="m
         gl, gn = r.decode_step(tok, tau)
         st = r.exit_stats()
         kc, vc = check(gl, gn, st, 1, T + step)
-        o = orc.decode_step(nxt, tau)
-        if check_decision(st["last_E"], st["last_trace"], o, tau, L):
-            orc.pos -= 1
-            o = orc.decode_step(nxt, tau, force_E=st["last_E"])
-        kv_cos(kc, vc, orc, L, B, T + step, T + step + 1)
+        if free_running:
+            o = orc.decode_step(nxt, tau)
+            if check_decision(st["last_E"], st["last_trace"], o, tau, L):
+                orc.pos -= 1
+                o = orc.decode_step(nxt, tau, force_E=st["last_E"])
+            kv_cos(kc, vc, orc, L, B, T + step, T + step + 1)
         Es.append(st["last_E"])
         nxt = gn.cpu().numpy().astype(np.int64)
     print(f"[parity-full] worst: {rep.worst}", flush=True)
