@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <tuple>
 #include <vector>
@@ -631,6 +632,52 @@ void drop_events(river_ctx *ctx) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch of river_debug_linear_noalloc: the batched-row GEMM's split-K partial
+// tiles live in this file-scope device array instead of the context's
+// workspace, so that entry point allocates nothing and needs no workspace
+// room.  Every GPU the library runs on holds its own copy (32 MiB) until the
+// process ends; host code uses only the device address hipGetSymbolAddress
+// returns for it on that device (the array's name is a host-side stand-in).
+// Every call on one GPU shares that GPU's copy: calls that overlap on one GPU
+// race.  Each call writes every partial tile it later reads, so nothing needs
+// clearing between calls.
+// ---------------------------------------------------------------------------
+static constexpr int64_t kScratchFloats = int64_t(8) << 20;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of stream s (the current device
+// for the null stream), resolved once per device with that device current.
+int scratch_for_stream(hipStream_t s, float **out) {
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return RIVER_E_HIP;
+  dev = cur;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) return RIVER_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RIVER_E_UNIMPLEMENTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return RIVER_E_HIP;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return RIVER_E_HIP;
+    g_scratch_ptr[dev] = static_cast<float *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return RIVER_OK;
+}
+
+int debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit, const void *d_x,
+                 int32_t M, float *d_y, float *part, int64_t part_cap);
+
+}  // namespace
+
 // ===========================================================================
 // C ABI
 // ===========================================================================
@@ -953,6 +1000,28 @@ int river_profile_read(river_ctx *ctx, river_kernel_time_t *out) {
 
 int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit,
                        const void *d_x, int32_t M, float *d_y) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  return debug_linear(ctx, layer, linear, use_exit, d_x, M, d_y, at<float>(ctx->ws, ctx->wl.mg_part),
+                      ctx->wl.mg_part_floats);
+}
+
+int river_debug_linear_noalloc(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit,
+                               const void *d_x, int32_t M, float *d_y) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  float *part = nullptr;
+  const int st = scratch_for_stream(ctx->stream, &part);
+  if (st != RIVER_OK) return st;
+  return debug_linear(ctx, layer, linear, use_exit, d_x, M, d_y, part, kScratchFloats);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One linear through the production cores; the batched-row GEMM's split-K
+// partial tiles go to `part` (capacity part_cap floats).
+int debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit, const void *d_x,
+                 int32_t M, float *d_y, float *part, int64_t part_cap) {
   if (!ctx || !d_x || !d_y) return RIVER_E_INVALID_ARG;
   if (!ctx->built) return RIVER_E_STATE;
   const river_config &c = ctx->cfg;
@@ -978,13 +1047,23 @@ int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t us
     g.M = M; g.N = sh[linear].N; g.K = sh[linear].K;
     g.x = static_cast<const uint16_t *>(d_x); g.ldx = sh[linear].K;
     g.path = path; g.y_out = d_y; g.y_stride = sh[linear].N;
-    if (M <= 64 && ctx->cfg.max_batch > 8)
-      RV_TRY(launch_mgemm(kEpPlain, g, ctx->stream));    // the decode core of 9..64 rows
-    else
+    if (M <= 64 && ctx->cfg.max_batch > 8) {
+      // the decode core of 9..64 rows
+      g.part = part;
+      g.part_cap = part_cap;
+      const MgemmPlan pl = mgemm_plan(M, sh[linear].N, sh[linear].K);
+      if (pl.nsplit > 1 && mgemm_part_floats(pl) > part_cap) return RIVER_E_BAD_SIZE;
+      RV_TRY(launch_mgemm(kEpPlain, g, ctx->stream));
+    } else {
       RV_TRY(launch_prefill_gemm(kEpPlain, g, ctx->stream));   // the prefill core
+    }
   }
   return RIVER_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 void river_destroy(river_ctx *ctx) {
   if (!ctx) return;

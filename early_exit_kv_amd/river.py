@@ -29,6 +29,7 @@ EXPORTS = (
     "river_prefill", "river_decode_step", "river_exit_stats", "river_set_option",
     "river_reset", "river_destroy", "river_strerror", "river_profile_read",
     "river_debug_linear", "river_record_bytes", "river_set_record", "river_time_kernel",
+    "river_debug_linear_noalloc",
 )
 
 
@@ -109,6 +110,7 @@ def load_library(path=LIB_PATH):
         "river_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "river_profile_read": (ctypes.c_int, [P, ctypes.POINTER(RiverKernelTime)]),
         "river_debug_linear": (ctypes.c_int, [P, i32, i32, i32, P, i32, P]),
+        "river_debug_linear_noalloc": (ctypes.c_int, [P, i32, i32, i32, P, i32, P]),
         "river_record_bytes": (ctypes.c_int, [ctypes.POINTER(RiverConfig), i32, ctypes.POINTER(ctypes.c_size_t)]),
         "river_set_record": (ctypes.c_int, [P, P, ctypes.c_size_t]),
         "river_time_kernel": (ctypes.c_int, [P, i32, i32, ctypes.POINTER(ctypes.c_double)]),
@@ -316,14 +318,19 @@ class River:
         self._call(self.lib.river_profile_read, "river_profile_read", arr)
         return {k: (arr[i].launches, arr[i].total_ms) for i, k in enumerate(KERNEL_KINDS)}
 
-    def debug_linear(self, layer, linear, use_exit, x):
-        """y = x W^T (fp32 [M][N]) for one linear through the production cores."""
+    def debug_linear(self, layer, linear, use_exit, x, y=None, noalloc=False):
+        """y = x W^T (fp32 [M][N]) for one linear through the production cores.
+        noalloc=True calls river_debug_linear_noalloc (partial tiles in the
+        library's static scratch); pass y to reuse an output buffer."""
         N, K = self.linear_shape(linear)
         x = x.to(torch.bfloat16).contiguous()
         assert x.shape[1] == K
-        y = torch.empty((x.shape[0], N), dtype=torch.float32, device=x.device)
-        self._call(self.lib.river_debug_linear, "river_debug_linear", layer, linear, int(use_exit),
-                   _ptr(x), x.shape[0], _ptr(y))
+        if y is None:
+            y = torch.empty((x.shape[0], N), dtype=torch.float32, device=x.device)
+        assert y.dtype == torch.float32 and y.is_contiguous() and y.shape == (x.shape[0], N)
+        fn, name = ((self.lib.river_debug_linear_noalloc, "river_debug_linear_noalloc") if noalloc
+                    else (self.lib.river_debug_linear, "river_debug_linear"))
+        self._call(fn, name, layer, linear, int(use_exit), _ptr(x), x.shape[0], _ptr(y))
         return y
 
     def time_kernel(self, kind, reps=20):

@@ -280,6 +280,20 @@ int river_time_kernel(river_ctx *ctx, int32_t kind, int32_t reps, double *avg_us
 int river_debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit,
                        const void *d_x, int32_t M, float *d_y);
 
+/* river_debug_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): same arguments, same kernels and the same results, but the
+ * batched-row GEMM's split-K partial tiles (9..64 rows on a context made for
+ * more than 8 rows) go to a static device array of the library (32 MiB per
+ * GPU, held until the process ends) instead of the context's workspace; it
+ * calls no allocating routine.  RIVER_E_BAD_SIZE when the partial tiles of
+ * the call would exceed that array (not at the Llama-3.1-8B shapes).  Every
+ * call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (on different streams or from different threads) race; each call writes
+ * every partial tile it reads, so no clearing is needed between calls. */
+int river_debug_linear_noalloc(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit,
+                               const void *d_x, int32_t M, float *d_y);
+
 /* Activation record, for checking a pass stage by stage (each layer of a
  * reference can then be fed the states this library stored).  When a record
  * buffer is set, every prefill and decode pass copies, after the kernels that
