@@ -38,6 +38,11 @@ def parse():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch decode steps without HIP graphs")
+    ap.add_argument("--tau-sweep", action="store_true",
+                    help="instead of the benchmark line: for each tau of the workload (or --taus) "
+                         "the exit histogram, decode tokens/s, the exit-decision share of the step, "
+                         "exit/backbone layer time and exit/backbone K/V cosine, as one JSON line")
+    ap.add_argument("--taus", type=str, default=None, help="comma-separated taus for --tau-sweep")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -146,8 +151,162 @@ def cpu_baseline(shape, weights, B, T, mean_E):
     }
 
 
+def timed_steps(r, bufs, logits, tau, W, K):
+    """W warm-up and K timed decode steps (graph replays): seconds for the K
+    and the histogram of E over the K."""
+    import torch
+
+    def run(n, start):
+        for i in range(n):
+            j = start + i
+            r.decode_step(bufs[j % 2], tau, logits=logits, next_tok=bufs[(j + 1) % 2])
+    run(W, 0)
+    h0 = r.exit_stats()["decode_hist"]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(K, W)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    h1 = r.exit_stats()["decode_hist"]
+    return el, [a - b for a, b in zip(h1, h0)]
+
+
+def kv_cosines(r, tokens, shape, n_rows):
+    """Exit-layer K/V against backbone K/V for the same layer input: for each
+    layer l a prefill with layers < l on the backbone and l.. on their exit
+    copies (forced E = l) writes the exit layer's K/V for the input the
+    backbone layers produced, compared with the all-backbone prefill's K/V of
+    that layer.  Cosine per (layer, row, position) over all kv heads."""
+    import torch
+    L = shape.n_layers
+    B, T = tokens.shape
+    k, v = r.kv_views()
+
+    def prefill_kv(e):
+        r.force_exit_layer(e)
+        r.reset()
+        r.prefill(tokens, 0.5, want_logits=False)
+        torch.cuda.synchronize()
+        return k[:, :B, :, :T].float().clone(), v[:, :B, :, :T].float().clone()
+
+    kb, vb = prefill_kv(L)
+    per_layer = []
+    for l in range(L):
+        ke, ve = prefill_kv(l)
+        cs = []
+        for a, b in ((ke[l], kb[l]), (ve[l], vb[l])):
+            a = a.permute(0, 2, 1, 3).reshape(B * T, -1)
+            b = b.permute(0, 2, 1, 3).reshape(B * T, -1)
+            cs.append(torch.nn.functional.cosine_similarity(a, b, dim=1))
+        per_layer.append((float(cs[0].mean()), float(cs[0].min()), float(cs[1].mean()), float(cs[1].min())))
+        del ke, ve
+    r.force_exit_layer(-1)
+    return {
+        "k_mean": round(sum(x[0] for x in per_layer) / L, 5), "k_min": round(min(x[1] for x in per_layer), 5),
+        "v_mean": round(sum(x[2] for x in per_layer) / L, 5), "v_min": round(min(x[3] for x in per_layer), 5),
+        "per_layer_k_mean": [round(x[0], 5) for x in per_layer],
+        "per_layer_v_mean": [round(x[2], 5) for x in per_layer],
+        "rows_positions": f"{B} x {T}",
+    }
+
+
+def tau_sweep(args):
+    """Per tau: exit histogram, decode tokens/s; then the exit-decision share
+    of the step, exit/backbone layer time and exit/backbone K/V cosine."""
+    import torch
+    import synth
+    from early_exit_kv_amd import river as rv
+
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    B, T = wl.batch, wl.prompt
+    taus = [float(t) for t in args.taus.split(",")] if args.taus else list(wl.taus)
+    K, W = args.steps, args.warmup
+    L = shape.n_layers
+    print(f"[sweep] workload {wl.name} B={B} T={T} steps={K} warmup={W} taus={taus}", file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = synth.make_weights(shape, seed=0, device=dev)
+    tokens = synth.make_tokens(shape, B, T, seed=0).to(dev)
+    r = rv.River(shape, weights, B, T + W + K + 2)
+    r.build_exit_layers("int4")
+    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    rows = []
+    for tau in taus:
+        r.reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, nxt = r.prefill(tokens, tau, want_logits=False)
+        torch.cuda.synchronize()
+        prefill_s = time.perf_counter() - t0
+        pE = r.exit_stats()["last_E"]
+        bufs[0].copy_(nxt)
+        el, hist_all = timed_steps(r, bufs, logits, tau, W, K)
+        mean_E = sum(e * n for e, n in enumerate(hist_all)) / max(1, sum(hist_all))
+        pos = T + W + K / 2
+        byts = sum(n * step_bytes(shape, B, e, pos) for e, n in enumerate(hist_all)) / max(1, sum(hist_all))
+        rows.append({"tau": tau, "prefill_E": pE, "prefill_tok_s": round(B * T / prefill_s, 1),
+                     "decode_tok_s": round(B * K / el, 2), "ms_per_step": round(el / K * 1e3, 4),
+                     "exit_hist": {str(e): n for e, n in enumerate(hist_all) if n},
+                     "mean_exit_layer": round(mean_E, 3),
+                     "step_hbm_frac": round(byts / (el / K) / 1e9 / HBM_PEAK_GBS, 4)})
+        print(f"[sweep] tau={tau}: {rows[-1]}", file=sys.stderr, flush=True)
+
+    # X6: the exit decision's share of a step: the same steps with the
+    # decision fixed on the host at the E the device took (no test, no flag
+    # reads) against the steps that decide on the device
+    ref = rows[len(rows) // 2]
+    E_ref = max(ref["exit_hist"], key=lambda e: ref["exit_hist"][e])
+    tau_ref = ref["tau"]
+    x6 = {}
+    for name, fe in (("device_decision", -1), ("forced_same_E", int(E_ref))):
+        r.force_exit_layer(fe)
+        r.reset()
+        _, nxt = r.prefill(tokens, tau_ref, want_logits=False)
+        bufs[0].copy_(nxt)
+        x6[name + "_ms"] = round(timed_steps(r, bufs, logits, tau_ref, W, K)[0] / K * 1e3, 4)
+    r.force_exit_layer(-1)
+    x6["tau"] = tau_ref
+    x6["E"] = int(E_ref)
+    x6["share"] = round((x6["device_decision_ms"] - x6["forced_same_E_ms"]) / x6["device_decision_ms"], 5)
+
+    # X7: per-layer time of the backbone layer against the exit layer, from
+    # the per-class kernel times with every layer forced to one form
+    x7 = {}
+    r.reset()
+    r.prefill(tokens, 0.5, want_logits=False)
+    for name, fe in (("backbone_layer_us", L), ("exit_layer_us", 0)):
+        r.force_exit_layer(fe)
+        x7[name] = round(sum(r.time_kernel(k, reps=10) for k in ("qkv", "attn", "o", "gateup", "down")), 3)
+    r.force_exit_layer(-1)
+    x7["ratio"] = round(x7["backbone_layer_us"] / x7["exit_layer_us"], 3)
+    d, F, G = shape.d_model, shape.ffn_dim, shape.group_size
+    qd, kd = shape.n_q_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+    nk = [(qd + 2 * kd, d), (d, qd), (2 * F, d), (d, F)]
+    x7["byte_ratio"] = round(sum(linear_bytes(n, k, G, False) for n, k in nk) /
+                             sum(linear_bytes(n, k, G, True) for n, k in nk), 3)
+
+    # X8: exit-layer K/V against backbone K/V for the same layer input
+    Tk = min(T, 128)
+    x8 = kv_cosines(r, tokens[:, :Tk].contiguous(), shape, B)
+    r.close()
+    out = {"what": "tau sweep", "workload": wl.name, "batch": B, "prompt": T, "steps": K, "warmup": W,
+           "config": f"decoder L={L} d={d} {shape.n_q_heads}q/{shape.n_kv_heads}kv heads x {shape.head_dim} "
+                     f"FFN {F} vocab {shape.vocab}, int4 g{G} exit layers",
+           "sweep": rows, "x6_exit_decision": x6, "x7_layer_time": x7, "x8_kv_cosine": x8}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.tau_sweep:
+        if args.gpus != 1:
+            print("the tau sweep runs on one GPU", file=sys.stderr)
+            sys.exit(2)
+        tau_sweep(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the decode path is single-GPU; see the sharding design note).", file=sys.stderr)
