@@ -43,6 +43,9 @@ def parse():
                          "the exit histogram, decode tokens/s, the exit-decision share of the step, "
                          "exit/backbone layer time and exit/backbone K/V cosine, as one JSON line")
     ap.add_argument("--taus", type=str, default=None, help="comma-separated taus for --tau-sweep")
+    ap.add_argument("--exit-gemm-only", action="store_true",
+                    help="run only the int4 exit-layer GEMMs at the batch-32 prefill shape (for "
+                         "hardware-counter runs) and print their rate")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -210,6 +213,36 @@ def kv_cosines(r, tokens, shape, n_rows):
     }
 
 
+def exit_gemm_rate(r, dev, reps=3):
+    """The int4 exit GEMMs at the batch-32 prefill shape (32 x 1024 rows):
+    each of layer 0's seven linears through the production prefill GEMM (plain
+    fp32 output), timed with events after one warm-up call."""
+    import torch
+    M = 32 * 1024
+    g = torch.Generator(device="cpu").manual_seed(7)
+    flop = ms_tot = 0.0
+    for li in range(7):
+        N_, K_ = r.linear_shape(li)
+        x = (torch.randn((M, K_), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+        r.debug_linear(0, li, 1, x)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            y = r.debug_linear(0, li, 1, x)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_tot += ev0.elapsed_time(ev1) / reps
+        flop += 2.0 * M * N_ * K_
+        del x, y
+    tf = flop / (ms_tot * 1e-3) / 1e12
+    return {"rows": M, "total_ms": round(ms_tot, 3), "tflops": round(tf, 1),
+            "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "what": "the 7 int4 exit-layer linears of one layer at 32 x 1024 rows "
+                    "(batch-32 prefill shape), prefill GEMM with fp32 output, "
+                    "2*M*N*K flop over their event time"}
+
+
 def tau_sweep(args):
     """Per tau: exit histogram, decode tokens/s; then the exit-decision share
     of the step, exit/backbone layer time and exit/backbone K/V cosine."""
@@ -306,6 +339,18 @@ def main():
             print("the tau sweep runs on one GPU", file=sys.stderr)
             sys.exit(2)
         tau_sweep(args)
+        return
+    if args.exit_gemm_only:
+        import torch
+        import synth
+        from early_exit_kv_amd import river as rv
+        dev = torch.device("cuda:0")
+        shape = synth.LLAMA_8B
+        w1 = synth.make_weights(shape, seed=0, device=dev, n_layers=1)
+        r = rv.River(synth.shrink(shape, n_layers=1), w1, 1, 8)
+        r.build_exit_layers("int4")
+        print(json.dumps({"exit_gemm_b32": exit_gemm_rate(r, dev)}))
+        r.close()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -473,33 +518,7 @@ def main():
 
     exit_gemm_b32 = None
     if not args.no_profile and shape.d_model >= 2048:
-        # the int4 exit GEMMs at the batch-32 prefill shape (32 x 1024 rows):
-        # each of layer 0's seven linears through the production prefill GEMM
-        # (plain fp32 output), timed with events after one warm-up call
-        M = 32 * 1024
-        g = torch.Generator(device="cpu").manual_seed(7)
-        flop = ms_tot = 0.0
-        for li in range(7):
-            N_, K_ = r.linear_shape(li)
-            x = (torch.randn((M, K_), generator=g) * 0.5).to(torch.bfloat16).to(dev)
-            r.debug_linear(0, li, 1, x)
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            reps = 3
-            ev0.record()
-            for _ in range(reps):
-                y = r.debug_linear(0, li, 1, x)
-            ev1.record()
-            torch.cuda.synchronize()
-            ms_tot += ev0.elapsed_time(ev1) / reps
-            flop += 2.0 * M * N_ * K_
-            del x, y
-        tf = flop / (ms_tot * 1e-3) / 1e12
-        exit_gemm_b32 = {"rows": M, "total_ms": round(ms_tot, 3), "tflops": round(tf, 1),
-                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "what": "the 7 int4 exit-layer linears of one layer at 32 x 1024 rows "
-                                 "(batch-32 prefill shape), prefill GEMM with fp32 output, "
-                                 "2*M*N*K flop over their event time"}
+        exit_gemm_b32 = exit_gemm_rate(r, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -859,6 +859,12 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   uint16_t *xl = reinterpret_cast<uint16_t *>(ring + 4 * kMvD * kMvSlot);   // [M][K + 8] bf16
   float *xsg = reinterpret_cast<float *>(xl + (XR ? 0 : M * xrow));         // [M][K / G] group sums
   float *red = xsg + (XR ? 0 : M * KG);                           // [2][4][M][16] partial tiles
+  // one-row RMSNorm input: the fp32 row and the bf16 gains land here by DMA
+  // ahead of the weight units (see the prologue)
+  constexpr bool kDmaRow = M == 1 && XS == kXNorm && !XR;
+  float *hrow = red + 2 * 4 * M * 16;                             // [K] fp32
+  uint16_t *grow = reinterpret_cast<uint16_t *>(hrow + (kDmaRow ? K : 0));   // [K] bf16, padded
+                                                                            // to whole 1 KB DMAs
   __shared__ float pred[4][4 * M];
   __shared__ float tred[ITEMS][3];
   __shared__ uint64_t tkey[ITEMS];
@@ -1135,12 +1141,32 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
       }
     };
 
-    // ---- the first units in flight, then the prologue (its loads come after
-    // the weight DMAs: waiting for them waits for those DMAs too, but the
-    // ring is full by then and its first units are needed right after)
+    // ---- one-row RMSNorm input (kDmaRow): the fp32 row and the gains go to
+    // LDS by DMA ahead of the weight units, so that the prologue waits for
+    // them alone (s_waitcnt counts the units issued after them) and reduces
+    // while the units stream.  Otherwise the prologue's own loads come after
+    // the weight DMAs (the compiler's wait for them waits for those DMAs too).
+    if constexpr (kDmaRow) {
+      if (!restart) {
+        const uint32_t hl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)hrow);
+        const uint32_t gl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)grow);
+        for (int c = wid; c < K / 256; c += 4)       // 1 KB of the row per DMA
+          dma16(hl + 1024 * c, p.h_src + 256 * c + 4 * lane);
+        for (int c = wid; c < (K + 511) / 512; c += 4) {   // 1 KB of the gains per DMA
+          // (a last, partial chunk: lanes past K read the first gains again,
+          // into the LDS padding past the row's K entries)
+          const int e = 512 * c + 8 * lane;
+          dma16(gl + 1024 * c, p.gain + (e < K ? e : 0));
+        }
+      }
+    }
     for_slots<0, kMvD>(fetch);
 
     if (!restart && !XR) {
+      if constexpr (kDmaRow) {
+        wait_vm<kMvD * NDMA>();   // this wavefront's row DMAs have landed
+        __syncthreads();          // and every other wavefront's
+      }
       float4 hv[kMvHold][2];
       uint4 gv[kMvHold], bv[kMvHold];
 #pragma unroll
@@ -1148,7 +1174,12 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         const int idx = min(tid + 256 * j, total - 1);
         const int mr = rowof(idx);
         const int m = min(mr, p.B - 1), g8 = idx - mr * n8;
-        if constexpr (XS == kXNorm) {
+        if constexpr (kDmaRow) {
+          const float *h = hrow + 8 * g8;
+          hv[j][0] = *reinterpret_cast<const float4 *>(h);
+          hv[j][1] = *reinterpret_cast<const float4 *>(h + 4);
+          gv[j] = *reinterpret_cast<const uint4 *>(grow + 8 * g8);
+        } else if constexpr (XS == kXNorm) {
           const float *h = p.h_src + (int64_t)m * p.h_stride + 8 * g8;
           hv[j][0] = *reinterpret_cast<const float4 *>(h);
           hv[j][1] = *reinterpret_cast<const float4 *>(h + 4);
@@ -1446,9 +1477,11 @@ static int num_cus() {
 
 // LDS bytes of one mgemv workgroup
 static size_t mgemv_lds(Epilogue ep, int M, int K, int G, bool xr) {
+  // one-row RMSNorm inputs staged by DMA: fp32 row + bf16 gains
+  const bool dma_row = M == 1 && !xr && (ep == kEpQKV || ep == kEpSwiGLU || ep == kEpLogits);
   return (size_t)4 * kMvD * mv_slot_bytes(ep, M, xr) +
          (xr ? 0 : (size_t)M * (K + 8) * 2 + (size_t)M * (K / G) * 4) +
-         (size_t)2 * 4 * M * 16 * 4;
+         (size_t)2 * 4 * M * 16 * 4 + (dma_row ? (size_t)K * 4 + (size_t)(K + 511) / 512 * 1024 : 0);
 }
 
 static int mgemv_ntile(Epilogue ep, const GemvParams &p) {

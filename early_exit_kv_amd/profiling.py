@@ -5,6 +5,9 @@
         <write_counter_collection.csv> <kernel-name-substring> <out.json> "<fetch command>"
         "<write command>" <copy bytes>
 
+    python -m early_exit_kv_amd.profiling counters <out.md> <counter_collection.csv> [...]
+        -- "<command>" [...]
+
 ``trace`` tabulates a ``--kernel-trace --stats`` run (calls, mean and total
 duration per kernel).  ``traffic`` takes two ``--pmc`` runs of the same
 program, one with FETCH_SIZE and one with WRITE_SIZE (KiB per dispatch), and
@@ -13,6 +16,8 @@ run (the runtime's buffer-copy kernel of a known size, which must fetch and
 write exactly its size), giving HBM-side bytes per launch of one kernel.  The
 result carries a digest of the kernel sources so that a later reader can tell
 whether the kernels have changed since the counters were taken.
+``counters`` tabulates the mean per dispatch of every counter of one or more
+``--pmc`` runs (instruction mix, matrix-core busy cycles, wait cycles).
 """
 import csv
 import hashlib
@@ -107,6 +112,38 @@ def load_traffic(path):
     return t.get("bytes_per_launch")
 
 
+def summarize_counters(csv_paths, out_md, commands, top=12):
+    """Mean value per dispatch of every counter in one or more ``--pmc`` runs,
+    per kernel (the kernels with the most dispatches first)."""
+    per = {}
+    for path in csv_paths:
+        for r in _rows(path):
+            name = r.get("Counter_Name") or r.get("counter_name")
+            kname = r.get("Kernel_Name") or r.get("kernel_name") or ""
+            val = float(r.get("Counter_Value") or r.get("counter_value"))
+            disp = r.get("Dispatch_Id") or r.get("dispatch_id") or ""
+            k = per.setdefault(kname, {})
+            k.setdefault(name, {}).setdefault(disp, 0.0)
+            k[name][disp] += val       # (a counter reported per XCD or per SE is summed)
+    counters = sorted({c for k in per.values() for c in k})
+    kernels = sorted(per, key=lambda k: -max(len(v) for v in per[k].values()))[:top]
+    lines = ["# rocprofv3 hardware counters, mean per dispatch", "", "Commands:", "", "```"] + list(commands) + \
+            ["```", "", "| kernel | dispatches | " + " | ".join(counters) + " |",
+             "|---|---:|" + "---:|" * len(counters)]
+    for k in kernels:
+        n = max(len(v) for v in per[k].values())
+        vals = []
+        for c in counters:
+            d = per[k].get(c)
+            vals.append(f"{sum(d.values()) / len(d):.4g}" if d else "")
+        name = k.replace("|", "/")
+        if len(name) > 70:
+            name = name[:67] + "..."
+        lines.append(f"| `{name}` | {n} | " + " | ".join(vals) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "trace":
         summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -114,6 +151,10 @@ if __name__ == "__main__":
         r = summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
                               int(sys.argv[8]))
         print(json.dumps(r, indent=1))
+    elif len(sys.argv) >= 5 and sys.argv[1] == "counters":
+        # counters <out.md> <csv> [<csv> ...] -- "<command>" ["<command>" ...]
+        i = sys.argv.index("--")
+        summarize_counters(sys.argv[3:i], sys.argv[2], sys.argv[i + 1:])
     else:
         print(__doc__)
         sys.exit(2)
