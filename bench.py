@@ -43,6 +43,10 @@ def parse():
                          "the exit histogram, decode tokens/s, the exit-decision share of the step, "
                          "exit/backbone layer time and exit/backbone K/V cosine, as one JSON line")
     ap.add_argument("--taus", type=str, default=None, help="comma-separated taus for --tau-sweep")
+    ap.add_argument("--offload-from", type=int, default=None,
+                    help="backbone offloading: the linears of layers >= this one in pinned host "
+                         "memory; prints decode tokens/s at --tau and with every layer on its "
+                         "backbone, and the device bytes, as one JSON line")
     ap.add_argument("--exit-gemm-only", action="store_true",
                     help="run only the int4 exit-layer GEMMs at the batch-32 prefill shape (for "
                          "hardware-counter runs) and print their rate")
@@ -243,6 +247,52 @@ def exit_gemm_rate(r, dev, reps=3):
                     "2*M*N*K flop over their event time"}
 
 
+def offload_measure(args):
+    """Decode with the backbone linears of layers >= k in pinned host memory:
+    tokens/s at tau (the exit copies in HBM serve the layers past the exit)
+    and with every layer forced onto its backbone (E = L: every offloaded
+    layer crosses the host link each step), plus device memory in use."""
+    import torch
+    import synth
+    from early_exit_kv_amd import river as rv
+    wl = synth.WORKLOADS[args.workload]
+    shape, B, T = wl.shape, wl.batch, wl.prompt
+    tau = 0.5 if args.tau is None else args.tau
+    k, K, W = args.offload_from, args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.make_weights(shape, seed=0, device=dev)
+    wo = rv.offload_layers(w, k)
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    tokens = synth.make_tokens(shape, B, T, seed=0).to(dev)
+    r = rv.River(shape, wo, B, T + W + K + 8)
+    r.build_exit_layers("int4")
+    torch.cuda.synchronize()
+    dev_bytes = torch.cuda.memory_allocated(dev)
+    weights_dev = sum(t.numel() * 2 for t in r._all_weight_tensors() if t.is_cuda)
+    weights_host = sum(t.numel() * 2 for t in r._all_weight_tensors() if not t.is_cuda)
+    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    out = {"what": "backbone offloading", "workload": wl.name, "offload_from_layer": k, "tau": tau,
+           "device_weight_bytes": weights_dev, "host_weight_bytes": weights_host,
+           "exit_bank_bytes": r.sizes.exit_bank_bytes, "kv_cache_bytes": r.sizes.kv_cache_bytes,
+           "workspace_bytes": r.sizes.workspace_bytes, "torch_allocated_bytes": dev_bytes}
+    for name, fe, n in (("decide", -1, K), ("all_backbone", shape.n_layers, max(2, K // 64))):
+        r.force_exit_layer(fe)
+        r.reset()
+        _, nxt = r.prefill(tokens, tau, want_logits=False)
+        bufs[0].copy_(nxt)
+        el, hist = timed_steps(r, bufs, logits, tau, min(W, n), n)
+        out[name] = {"steps": n, "decode_tok_s": round(B * n / el, 3), "ms_per_step": round(el / n * 1e3, 3),
+                     "exit_hist": {str(e): c for e, c in enumerate(hist) if c}}
+        print(f"[offload] {name}: {out[name]}", file=sys.stderr, flush=True)
+    r.force_exit_layer(-1)
+    r.close()
+    print(json.dumps(out))
+
+
 def tau_sweep(args):
     """Per tau: exit histogram, decode tokens/s; then the exit-decision share
     of the step, exit/backbone layer time and exit/backbone K/V cosine."""
@@ -339,6 +389,9 @@ def main():
             print("the tau sweep runs on one GPU", file=sys.stderr)
             sys.exit(2)
         tau_sweep(args)
+        return
+    if args.offload_from is not None:
+        offload_measure(args)
         return
     if args.exit_gemm_only:
         import torch

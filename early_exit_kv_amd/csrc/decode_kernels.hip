@@ -191,6 +191,9 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   bool ex = flag0 != 0 || (p.layer >= 0 && force0 >= 0 && p.layer >= force0);
   if (p.layer < 0) ex = false;
   if (p.path != kPathDevice) ex = p.path == kPathExit;
+  // with the test pending the weights start streaming on a guess: the
+  // backbone, unless it lives in host memory (then the exit copy in HBM)
+  if (pending) ex = p.remote_bb != 0;
   bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
 
   // Rows of the current task: row indices plus at most two segment bases (the
@@ -440,7 +443,9 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
         mcos = fminf(mcos, cs);
       }
     }
-    const bool fired = mcos > ctl->tau;
+    // (the same value in every lane; readfirstlane lets the compiler know it,
+    // so the weight choice that follows stays in scalar registers)
+    const bool fired = __builtin_amdgcn_readfirstlane(mcos > ctl->tau ? 1 : 0) != 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       ctl->trace[p.layer - 1] = mcos;
       if (fired) {
@@ -448,9 +453,9 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
         __hip_atomic_store(&ctl->flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (fired) {  // the guess was the backbone: fetch the exit layer instead
-      ex = true;
-      q4 = p.exit_mode == RIVER_EXIT_INT4;
+    if (fired != ex) {  // the guess was wrong: fetch the other weights instead
+      ex = fired;
+      q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
       setup_rows(task);
       load_batch(Buf<0>{}, 0, nchunks(min(kslab, K)), lane);
     }
@@ -887,6 +892,9 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   bool ex = flag0 != 0 || (p.layer >= 0 && force0 >= 0 && p.layer >= force0);
   if (p.layer < 0) ex = false;
   if (p.path != kPathDevice) ex = p.path == kPathExit;
+  // while the test is pending the backbone units start streaming on a guess;
+  // with the backbone in host memory the weights wait for the decision
+  const bool defer = pending && p.remote_bb != 0;
   const bool int4_mode = p.exit_mode == RIVER_EXIT_INT4;
   const int pos = ctl->pos;
 
@@ -1160,12 +1168,15 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         }
       }
     }
-    for_slots<0, kMvD>(fetch);
+    if (!defer || restart) for_slots<0, kMvD>(fetch);
 
     if (!restart && !XR) {
       if constexpr (kDmaRow) {
-        wait_vm<kMvD * NDMA>();   // this wavefront's row DMAs have landed
-        __syncthreads();          // and every other wavefront's
+        // this wavefront's row DMAs have landed (the units issued after them
+        // may still be in flight), then every other wavefront's
+        if (defer) wait_vm<0>();
+        else wait_vm<kMvD * NDMA>();
+        __syncthreads();
       }
       float4 hv[kMvHold][2];
       uint4 gv[kMvHold], bv[kMvHold];
@@ -1284,7 +1295,9 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
             mcos = fminf(mcos, cs);
           }
         }
-        fired = mcos > ctl->tau;
+        // (uniform over the workgroup; readfirstlane tells the compiler, so the
+        // weight choice that follows stays in scalar registers)
+        fired = __builtin_amdgcn_readfirstlane(mcos > ctl->tau ? 1 : 0) != 0;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
           ctl->trace[p.layer - 1] = mcos;
           if (fired) {
@@ -1372,6 +1385,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         wait_vm<0>();
         return true;
       }
+      if (defer) for_slots<0, kMvD>(fetch);   // the test kept the (host-resident) backbone
     }
 
     // ---- main loop: unit n of the sequence sits in ring slot n % kMvD; the
@@ -1398,6 +1412,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
     return false;
   };
 
+  // one pass on the weights chosen (or guessed); when the pending test
+  // decides against the guess, a second pass on the other weights
   const bool q4 = ex && int4_mode;
   if (q4) {
     run(Buf<1>{}, false);

@@ -169,6 +169,7 @@ struct river_ctx {
   int attn_chunk = 0;   // positions per decode-attention workgroup (0: chosen per shape)
   int gemv_mode = 0;    // RIVER_OPT_GEMV
   int attn_kind = 0;    // RIVER_OPT_ATTN
+  std::vector<char> remote;   // per layer: backbone linears in host memory (offloaded)
 };
 
 namespace {
@@ -468,6 +469,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
     // the exit test after layer l-1 is decided at the start of this kernel
     q.test_prev = l > 0; q.part = at<float>(ctx->ws, ctx->wl.part); q.part_wgs = down_wgs;
+    q.remote_bb = ctx->remote.empty() ? 0 : ctx->remote[l];
     RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
     TIMED_ONLY(RIVER_K_QKV, launch_gemv(kXNorm, kEpQKV, q, s));
     RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
@@ -772,6 +774,14 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
                            ctx->stream));
   LinearShape sh[7];
   linear_shapes(c, sh);
+  // offloaded backbone layers: their linears live in host memory
+  ctx->remote.assign(c.n_layers, 0);
+  for (int l = 0; l < c.n_layers; ++l) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, ctx->layers[l].wq) == hipSuccess && a.type == hipMemoryTypeHost)
+      ctx->remote[l] = 1;
+  }
+  (void)hipGetLastError();   // a pointer HIP does not know leaves an error behind
   for (int l = 0; l < c.n_layers; ++l) {
     const river_layer_w &L = ctx->layers[l];
     const void *src[7] = {L.wq, L.wk, L.wv, L.wo, L.w_gate, L.w_up, L.w_down};
@@ -779,8 +789,9 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
       size_t co, so;
       bank_offsets(c, l, i, copy, &co, &so);
       if (copy) {
+        // (hipMemcpyDefault: an offloaded backbone layer lives in host memory)
         RV_TRY(hipMemcpyAsync(ctx->bank + co, src[i], (size_t)sh[i].N * sh[i].K * 2,
-                              hipMemcpyDeviceToDevice, ctx->stream));
+                              hipMemcpyDefault, ctx->stream));
       } else {
         RV_TRY(launch_quantize(static_cast<const uint16_t *>(src[i]), sh[i].N, sh[i].K,
                                c.group_size, at<uint32_t>(ctx->bank, co), at<uint32_t>(ctx->bank, so),

@@ -144,6 +144,8 @@ struct GemvParams {
   float *y_out; int64_t y_stride; // kEpPlain: fp32 [B][N]
   float *logits; int32_t *next; int is_prefill; int vocab;// LM head
   int gemv_mode;                  // 0 per-linear choice, 1 dot-product GEMV, 2 MFMA GEMV where it fits
+  int remote_bb;                  // the backbone weights live in host memory: while the exit
+                                  // test is pending, stream the exit copy first
 };
 
 

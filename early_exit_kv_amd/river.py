@@ -194,13 +194,22 @@ class River:
         self.w = weights  # keep the borrowed tensors alive
         c = self.cfg
         for t in self._all_weight_tensors():
-            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-                raise ValueError("weights must be contiguous bf16 CUDA tensors")
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError("weights must be contiguous bf16 tensors")
+            if not t.is_cuda and not t.is_pinned():
+                raise ValueError("weights must be CUDA tensors (or, for offloaded backbone "
+                                 "linears, pinned host tensors)")
+        for t in (weights["embed"], weights["final_norm"], weights.get("lm_head")):
+            if t is not None and not t.is_cuda:
+                raise ValueError("embedding, final norm and LM head must be CUDA tensors")
         n = c.n_layers
         self._layers = (RiverLayerW * n)()
         for i, lw in enumerate(weights["layers"]):
             for name, _ in RiverLayerW._fields_:
-                setattr(self._layers[i], name, lw[name].data_ptr())
+                t = lw[name]
+                if not t.is_cuda and name in ("attn_norm", "mlp_norm"):
+                    raise ValueError("norm gains must be CUDA tensors")
+                setattr(self._layers[i], name, t.data_ptr() if t.is_cuda else device_address(t))
         rw = RiverWeights(weights["embed"].data_ptr(), weights["final_norm"].data_ptr(),
                           weights["lm_head"].data_ptr() if weights.get("lm_head") is not None else None,
                           self._layers)
@@ -410,6 +419,44 @@ class River:
         qd, kd = c.n_q_heads * c.head_dim, c.n_kv_heads * c.head_dim
         return [(qd, c.d_model), (kd, c.d_model), (kd, c.d_model), (c.d_model, qd),
                 (c.ffn_dim, c.d_model), (c.ffn_dim, c.d_model), (c.d_model, c.ffn_dim)][linear]
+
+
+_HIP = None
+
+
+def device_address(t):
+    """Device-side address of a pinned host tensor (hipHostGetDevicePointer)."""
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
+        _HIP.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+    out = ctypes.c_void_p()
+    rc = _HIP.hipHostGetDevicePointer(ctypes.byref(out), ctypes.c_void_p(t.data_ptr()), 0)
+    if rc != 0 or not out.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({rc}): is the tensor pinned?")
+    return out.value
+
+
+def offload_layers(weights, first_layer):
+    """Backbone offloading (lead page, section 5): a copy of the weight dict in
+    which the seven linear matrices of layers >= first_layer are pinned host
+    tensors (the device reads them over the host link only when it runs that
+    layer on its backbone).  Norm gains, embedding and LM head stay where they
+    are.  Drop the caller's references to the original tensors of those
+    layers to release their device memory."""
+    out = {k: v for k, v in weights.items() if k != "layers"}
+    out["layers"] = []
+    for l, lw in enumerate(weights["layers"]):
+        nl = dict(lw)
+        if l >= first_layer:
+            for name in LINEAR_NAMES:
+                h = torch.empty(lw[name].shape, dtype=lw[name].dtype, pin_memory=True)
+                h.copy_(lw[name])
+                nl[name] = h
+        out["layers"].append(nl)
+    return out
 
 
 def unpack_int4(words, sz, group):

@@ -78,9 +78,22 @@ typedef struct {
   int32_t max_seq;         /* positions the shared cache holds per row         */
 } river_config;
 
-/* One decoder layer's backbone weights, device pointers to bf16:
+/* One decoder layer's backbone weights, pointers to bf16 that the device can
+ * read:
  *   attn_norm, mlp_norm [d_model]; wq [Hq*Dh][d]; wk, wv [Hkv*Dh][d];
- *   wo [d][Hq*Dh]; w_gate, w_up [F][d]; w_down [d][F]. */
+ *   wo [d][Hq*Dh]; w_gate, w_up [F][d]; w_down [d][F].
+ * Backbone offloading (lead page, section 5: deep backbone layers leave
+ * device memory, the exit layers stay): the seven linear matrices of a layer
+ * may live in pinned host memory mapped into the device's address space
+ * (hipHostMalloc, or a pinned allocation made by the caller's framework; pass
+ * the device-side address hipHostGetDevicePointer gives).  The kernels then
+ * read them over the host link, and only when the device-side decision runs
+ * that layer on its backbone: once the exit has fired, the step reads the
+ * int4 exit copy in HBM instead.  The exit bank, the norm gains, the
+ * embedding, the LM head and the KV cache stay in device memory.  The first
+ * kernel after a pending exit test starts streaming the backbone weights
+ * before the test is decided, so an offloaded layer right after a tested one
+ * is touched (a few KB) even when the exit fires. */
 typedef struct {
   const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
 } river_layer_w;
