@@ -529,7 +529,238 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
   }
 }
 
+// ===========================================================================
+// Causal GQA attention over the prompt on the matrix cores (flash-style).
+//   Workgroup: 64 query positions x the GQ query heads of one kv head x row b;
+//   wavefront w takes query positions q0 + 16 w .. +15 for all GQ heads, so
+//   every K/V tile is loaded once for 4 * 16 * GQ query rows.  Tiles of 32
+//   key positions sit in LDS, double-buffered: K row-major with its 16-byte
+//   chunks XOR-swizzled by the row, V transposed (V^T[dim][key]).
+//   Scores as S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys x queries: each
+//   lane then holds one query's scores, 4 keys of each 16-key half); online
+//   softmax in fp32 in the base-2 domain; O^T = V^T P^T, with P split exactly
+//   into three bf16 terms (p = p1 + p2 + p3, each the top 8 significant bits
+//   of what is left), so the probabilities enter the products with all 24
+//   bits and every sum is fp32.  The lanes' key order inside a k-step
+//   ({4q..4q+3} and {16+4q..16+4q+3} for lane quarter q) is the same in the
+//   A operand (V^T) and in the B operand (P^T), so the products pair up.
+// ===========================================================================
+template <int DH>
+__device__ __forceinline__ int flash_swz(int r) {
+  return DH == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int DH, int GQ>
+__global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
+  constexpr int KT = 32;                // key positions per tile
+  constexpr int CPR = DH / 8;           // 16-byte chunks per key row
+  constexpr int NS = DH / 32;           // k-steps of a score MFMA
+  constexpr int NO = DH / 16;           // output tiles of 16 dims
+  constexpr int VST = KT + 4;           // V^T row stride (bf16): 72 bytes
+  constexpr int NCH = KT * CPR / 256;   // 16-byte chunks per thread per tile
+  __shared__ __align__(16) uint16_t Ks[2][KT * DH];
+  __shared__ __align__(16) uint16_t Vt[2][DH * VST];
+
+  const int qb = (int)gridDim.x - 1 - (int)blockIdx.x;   // longest rows first
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, c16 = lane & 15;
+  const int q0 = qb * 64;
+  const int my_q = q0 + 16 * wid + c16;         // this lane's query position
+  const int kend = min(p.T, q0 + 64);           // key positions the workgroup needs
+  const int ntiles = (kend + KT - 1) / KT;
+  const int64_t kvbase = ((int64_t)b * p.Hkv + kvh) * p.S * DH;
+  const uint16_t *Kg = p.k_cache + kvbase, *Vg = p.v_cache + kvbase;
+  const float scale2 = p.scale * 1.4426950408889634f;
+
+  // Q^T operands: lane (q, c16) holds dims 32 s + 8 q .. +7 of query my_q
+  bf16x8_t qf[GQ][NS];
+  {
+    const int row = min(my_q, p.T - 1);
+    const uint16_t *qp = p.q + ((int64_t)b * p.T + row) * (int64_t)(p.Hq * DH) + (int64_t)kvh * GQ * DH + 8 * q;
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        qf[h][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qp + h * DH + 32 * st));
+  }
+
+  // one tile: thread tid moves 16-byte chunks tid + 256 u of K and of V
+  uint4 kr[NCH], vr[NCH];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int ch = tid + 256 * u, r = ch / CPR, cc = ch % CPR;
+      const int pos = min(kt * KT + r, p.T - 1);   // past the prompt: masked below
+      kr[u] = *reinterpret_cast<const uint4 *>(Kg + (int64_t)pos * DH + 8 * cc);
+      vr[u] = *reinterpret_cast<const uint4 *>(Vg + (int64_t)pos * DH + 8 * cc);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int ch = tid + 256 * u, r = ch / CPR, cc = ch % CPR;
+      *reinterpret_cast<uint4 *>(&Ks[buf][(r * CPR + (cc ^ flash_swz<DH>(r))) * 8]) = kr[u];
+      const uint32_t w4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[buf][(8 * cc + 2 * e) * VST + r] = (uint16_t)(w4[e] & 0xFFFFu);
+        Vt[buf][(8 * cc + 2 * e + 1) * VST + r] = (uint16_t)(w4[e] >> 16);
+      }
+    }
+  };
+
+  float m[GQ], lsum[GQ];
+  f32x4_t o[GQ][NO];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NO; ++j) o[h][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);   // in flight while this tile is reduced
+    const uint16_t *K = Ks[buf];
+    const uint16_t *V = Vt[buf];
+    // K operands of both 16-key halves: lane (q, c16) = key 16 kk + c16, dims 32 s + 8 q
+    bf16x8_t ka[2][NS];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int r = 16 * kk + c16;
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        ka[kk][st] = *reinterpret_cast<const bf16x8_t *>(&K[(r * CPR + ((4 * st + q) ^ flash_swz<DH>(r))) * 8]);
+    }
+    // scores, online softmax and the three-term split of P, per head
+    uint32_t pt[GQ][3][4];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+          sc[kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk][st], qf[h][st], sc[kk], 0, 0, 0);
+      // this lane: query my_q against keys kt KT + 16 kk + 4 q + i
+      float sv[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt * KT + 16 * kk + 4 * q + i;
+          const bool ok = key <= my_q && key < p.T;
+          sv[4 * kk + i] = ok ? sc[kk][i] * scale2 : -INFINITY;
+          mx = fmaxf(mx, sv[4 * kk + i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m[h], mx);
+      float corr = 1.f, part = 0.f;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+      if (mnew != -INFINITY) {
+        corr = exp2_fast(m[h] - mnew);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = exp2_fast(sv[e] - mnew);
+          part += pv[e];
+        }
+      }
+      lsum[h] = lsum[h] * corr + part;   // this lane's share of the row sum
+      m[h] = mnew;
+#pragma unroll
+      for (int j = 0; j < NO; ++j) o[h][j] *= corr;
+      // p = p1 + p2 + p3 exactly: each term keeps the top 16 bits of what is
+      // left (a bf16 value), the subtractions are exact
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t t1[2], t2[2], t3[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const float v = pv[2 * e + x];
+          const float v1 = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+          const float r1 = v - v1;
+          const float v2 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+          const float v3 = r1 - v2;          // has at most 8 significant bits: a bf16 value
+          t1[x] = __float_as_uint(v1);
+          t2[x] = __float_as_uint(v2);
+          t3[x] = __float_as_uint(v3);
+        }
+        pt[h][0][e] = __builtin_amdgcn_perm(t1[1], t1[0], 0x07060302u);
+        pt[h][1][e] = __builtin_amdgcn_perm(t2[1], t2[0], 0x07060302u);
+        pt[h][2][e] = __builtin_amdgcn_perm(t3[1], t3[0], 0x07060302u);
+      }
+    }
+    // O^T += V^T P^T: lane (q, c16) reads dim 16 j + c16 at keys {4q..4q+3} and {16+4q..16+4q+3}
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const uint16_t *vrow = V + (16 * j + c16) * VST + 4 * q;
+      const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+      const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
+      const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int h = 0; h < GQ; ++h)
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          o[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              va, __builtin_bit_cast(bf16x8_t, make_uint4(pt[h][t][0], pt[h][t][1], pt[h][t][2], pt[h][t][3])),
+              o[h][j], 0, 0, 0);
+    }
+    if (kt + 1 < ntiles) {
+      // the other buffer was last read in the previous iteration, which every
+      // wavefront finished before the barrier that ended it
+      lstore((kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // row sums over the four lane quarters; O^T lane (q, c16): dims 16 j + 4 q + i of query my_q
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float lt = lsum[h];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = 1.0f / lt;
+    if (my_q < p.T) {
+      uint16_t *op = p.out + ((int64_t)b * p.T + my_q) * (int64_t)(p.Hq * DH) + ((int64_t)kvh * GQ + h) * DH + 4 * q;
+#pragma unroll
+      for (int j = 0; j < NO; ++j) {
+        const f32x4_t v = o[h][j];
+        *reinterpret_cast<uint2 *>(op + 16 * j) =
+            make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
+      }
+    }
+  }
+}
+
+template <int DH>
+static hipError_t attn_flash_launch(const AttnPrefillParams &p, hipStream_t s) {
+  dim3 grid((p.T + 63) / 64, p.Hkv, p.B);
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_1(attn_flash_kernel<DH, 1>, grid, dim3(256), p, s);
+    case 2: return launch_1(attn_flash_kernel<DH, 2>, grid, dim3(256), p, s);
+    case 4: return launch_1(attn_flash_kernel<DH, 4>, grid, dim3(256), p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
+  if (p.mfma) {
+    switch (p.Dh) {
+      case 64: return attn_flash_launch<64>(p, s);
+      case 128: return attn_flash_launch<128>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   dim3 grid((p.T + 63) / 64, p.Hq, p.B);
   switch (p.Dh) {
     case 64: return launch_1(attn_prefill_kernel<64>, grid, dim3(256), p, s);

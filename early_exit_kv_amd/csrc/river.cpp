@@ -567,6 +567,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     ap.out = at<uint16_t>(ctx->ws, ctx->wl.attn); ap.B = B; ap.T = T; ap.Hq = c.n_q_heads;
     ap.Hkv = c.n_kv_heads; ap.Dh = c.head_dim; ap.S = c.max_seq;
     ap.scale = 1.0f / std::sqrt((float)c.head_dim);
+    ap.mfma = ctx->attn_kind == 0;
     TIMED(RIVER_K_P_ATTN, launch_attn_prefill(ap, s));
     RV_TRY(rec.put(l, rec.lay.attn, ap.out, qbytes));
 

@@ -254,6 +254,7 @@ struct AttnPrefillParams {
   uint16_t *out;           // [B*T][Hq*Dh]
   int B, T, Hq, Hkv, Dh, S;
   float scale;
+  int mfma;                // 1: the matrix-core (flash-style) kernel, 0: the vector-ALU one
 };
 hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s);
 

@@ -314,7 +314,7 @@ class River:
         self.set_option(RIVER_OPT_GEMV, {"auto": 0, "dot": 1, "mfma": 2}[mode])
 
     def attn_kind(self, kind):
-        """Decode attention: "mfma" (scores on the matrix cores) or "valu"."""
+        """Attention kernels (decode and prefill): "mfma" (matrix cores) or "valu"."""
         self.set_option(RIVER_OPT_ATTN, {"mfma": 0, "valu": 1}[kind])
 
     def profile(self, on=True):

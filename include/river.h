@@ -232,9 +232,11 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     every linear it fits but the LM head at four rows).
  *                     All give the same results up to the fp32 summation
  *                     order;
- *   RIVER_OPT_ATTN    decode attention: 0 (default) scores on the matrix
- *                     cores, 1 all on the vector ALUs (same results up to
- *                     the fp32 summation order). */
+ *   RIVER_OPT_ATTN    attention kernels: 0 (default) on the matrix cores
+ *                     (decode: scores by MFMA; prefill: flash-style causal
+ *                     attention with the probabilities split exactly into
+ *                     three bf16 terms), 1 all on the vector ALUs (same
+ *                     results up to the fp32 summation order). */
 enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4,
        RIVER_OPT_GEMV = 5, RIVER_OPT_ATTN = 6 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);

@@ -103,6 +103,23 @@ def rope_allowance(y, b, pos, D, theta):
     return e, rb
 
 
+def attention_row(q, k, v, scale):
+    """Exact softmax(q k^T scale) v of one query row over the stored keys and
+    values k, v [n][Dh] (float64), and its fp32 evaluation allowance: the
+    score error (accumulation bound plus the exponential's few ulps) carried
+    through the softmax, the accumulation of the n products, the final
+    rounding."""
+    n = k.shape[0]
+    sc = (k @ q) * scale
+    m = sc.max()
+    w = np.exp(sc - m)
+    pr = w / w.sum()
+    o = pr @ v
+    ds = C_ACC * np.sqrt(k.shape[1]) * U32 * scale * (np.abs(k) @ np.abs(q)) + 4e-6 * (1.0 + np.abs(sc - m))
+    b = 2.0 * (pr * ds) @ np.abs(v - o) + C_ACC * np.sqrt(n) * U32 * (pr @ np.abs(v)) + 2 * U32 * np.abs(o)
+    return o, b
+
+
 def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, trace, tau,
                logits, nxt, final_norm, w_lm, report=None):
     """Check one prefill (n = T rows per sequence, start = 0) or decode step
@@ -152,18 +169,7 @@ def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, 
             b, p = bidx[r], pos[r]
             for h in range(s.Hq):
                 j = (h * s.Hkv) // s.Hq
-                k = kc[l, b, j, :p + 1]
-                v = vc[l, b, j, :p + 1]
-                sc = (k @ q[r, h]) * scale
-                m = sc.max()
-                w = np.exp(sc - m)
-                pr = w / w.sum()
-                o = pr @ v
-                ds = C_ACC * np.sqrt(s.Dh) * U32 * scale * (np.abs(k) @ np.abs(q[r, h])) + \
-                    4e-6 * (1.0 + np.abs(sc - m))
-                eo[r, h] = o
-                bo[r, h] = 2.0 * (pr * ds) @ np.abs(v - o) + \
-                    C_ACC * np.sqrt(p + 1) * U32 * (pr @ np.abs(v)) + 2 * U32 * np.abs(o)
+                eo[r, h], bo[r, h] = attention_row(q[r, h], kc[l, b, j, :p + 1], vc[l, b, j, :p + 1], scale)
         rep.bf16(f"attn[{tag}]", st["attn"].reshape(R, s.Hq, s.Dh), eo, bo)
 
         # o projection + residual (fp32 stored)
