@@ -40,6 +40,7 @@ import numpy as np
 
 EXIT_INT4 = "int4"
 EXIT_COPY = "copy"
+EXIT_HQQ = "hqq"
 
 
 # --------------------------------------------------------------------------
@@ -102,6 +103,73 @@ def quantize_int4(w, group):
     t = t + z[..., None]
     q = np.clip(np.rint(t), 0, 15).astype(np.uint8)
     return q.reshape(n, k), s, z
+
+
+# HQQ-style refinement of the zero point.  The page names HQQ as its default
+# quantiser but gives none of its steps; these are the published defaults of
+# the half-quadratic solver (beta 10, growth kappa 1.01, 20 rounds), with the
+# l1 norm (p = 1) as the sparsity-promoting error norm: its proximal step is a
+# plain soft threshold, so every step is a separately rounded float32
+# operation and both sides reach the same codes bit for bit (HQQ's p < 1 needs
+# a power function, which no two math libraries round alike).
+HQQ_ITERS = 20
+HQQ_BETA = 10.0
+HQQ_KAPPA = 1.01
+
+
+def tree_sum_f32(x):
+    """Sum over the last axis (a power of two) in a fixed pairwise order, in
+    float32: the two halves are added element-wise, then the two halves of
+    that, down to a single value."""
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[-1]
+    if n & (n - 1):
+        raise ValueError("the tree sum takes a power-of-two length")
+    while n > 1:
+        n //= 2
+        x = x[..., :n] + x[..., n:2 * n]
+    return x[..., 0]
+
+
+def quantize_int4_hqq(w, group, iters=HQQ_ITERS, beta=HQQ_BETA, kappa=HQQ_KAPPA):
+    """4-bit quantisation with an HQQ-style refinement of the zero point.
+
+    Starts from the min-max quantiser (quantize_int4: scale s and zero z), then
+    alternates, for ``iters`` rounds, per (row, group), in float32 with every
+    operation separately rounded and zf = z to begin with:
+        q  = clamp(round_half_even(fl(fl(w / s) + zf)), 0, 15)   quantise
+        e  = fl(w - fl(fl(q - zf) * s))                          residual
+        we = sign(e) * max(fl(|e| - fl(1 / beta)), 0)            proximal step of |.|_1
+        zf = fl(tree_sum(fl(q - fl(fl(w - we) / s))) / G)        closed-form zero
+        beta = fl(beta * kappa)
+    (half-quadratic splitting: the error variable we absorbs the sparse large
+    residuals, the zero is the least-squares fit of the rest).  The scale keeps
+    its min-max value; the zero is stored as bf16(zf) and the codes are taken
+    once more with the stored scale and zero.  iters = 0 is quantize_int4.
+    Returns (q uint8 [N,K], s float32 [N,K/G], z float32 [N,K/G]).
+    """
+    q0, s, z = quantize_int4(w, group)
+    if iters == 0:
+        return q0, s, z
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    wg = w.reshape(n, k // group, group)
+    sg = s[..., None]
+    zf = z.astype(np.float32)
+    b = np.float32(beta)
+    kap = np.float32(kappa)
+    inv_g = np.float32(1.0) / np.float32(group)       # a power of two: exact
+    for _ in range(iters):
+        q = np.clip(np.rint((wg / sg) + zf[..., None]), 0, 15).astype(np.float32)
+        e = wg - (q - zf[..., None]) * sg
+        thr = np.float32(1.0) / b
+        we = np.sign(e) * np.maximum(np.abs(e) - thr, np.float32(0.0))
+        t = q - (wg - we) / sg
+        zf = (tree_sum_f32(t) * inv_g).astype(np.float32)
+        b = np.float32(b * kap)
+    zb = bf16_from_f32(zf)
+    q = np.clip(np.rint((wg / sg) + zb[..., None]), 0, 15).astype(np.uint8)
+    return q.reshape(n, k), s, zb
 
 
 def dequantize_int4(q, s, z, group):
@@ -267,16 +335,18 @@ class RiverOracle:
     # -- build ------------------------------------------------------------
     def build_exit_layers(self, mode=EXIT_INT4):
         """One exit layer per decoder layer: a copy of all its parameters,
-        with the seven linear matrices quantised in int4 mode (norm gains are
-        copied as they are).  Embedding, final norm and LM head get no copy."""
-        if mode not in (EXIT_INT4, EXIT_COPY):
+        with the seven linear matrices quantised in int4 mode (min-max) or hqq
+        mode (min-max, then the HQQ-style zero refinement); norm gains are
+        copied as they are.  Embedding, final norm and LM head get no copy."""
+        if mode not in (EXIT_INT4, EXIT_COPY, EXIT_HQQ):
             raise ValueError(mode)
+        quant = quantize_int4_hqq if mode == EXIT_HQQ else quantize_int4
         self.exit_layers, self.exit_codes = [], []
         for lw in self.w["layers"]:
             ex, codes = {}, {}
             for name, arr in lw.items():
-                if name in self.LINEARS and mode == EXIT_INT4:
-                    q, sc, z = quantize_int4(arr, self.s.G)
+                if name in self.LINEARS and mode in (EXIT_INT4, EXIT_HQQ):
+                    q, sc, z = quant(arr, self.s.G)
                     codes[name] = (q, sc, z)
                     ex[name] = dequantize_int4(q, sc, z, self.s.G)
                 else:
