@@ -43,6 +43,8 @@ def parse():
                          "the exit histogram, decode tokens/s, the exit-decision share of the step, "
                          "exit/backbone layer time and exit/backbone K/V cosine, as one JSON line")
     ap.add_argument("--taus", type=str, default=None, help="comma-separated taus for --tau-sweep")
+    ap.add_argument("--exit-mode", default="int4", choices=["int4", "hqq"],
+                    help="exit bank of --tau-sweep: min-max int4, or int4 with the HQQ-style zero refinement")
     ap.add_argument("--offload-from", type=int, default=None,
                     help="backbone offloading: the linears of layers >= this one in pinned host "
                          "memory; prints decode tokens/s at --tau and with every layer on its "
@@ -313,7 +315,11 @@ def tau_sweep(args):
     weights = synth.make_weights(shape, seed=0, device=dev)
     tokens = synth.make_tokens(shape, B, T, seed=0).to(dev)
     r = rv.River(shape, weights, B, T + W + K + 2)
-    r.build_exit_layers("int4")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r.build_exit_layers(args.exit_mode)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
     bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
     rows = []
@@ -375,7 +381,8 @@ def tau_sweep(args):
     Tk = min(T, 128)
     x8 = kv_cosines(r, tokens[:, :Tk].contiguous(), shape, B)
     r.close()
-    out = {"what": "tau sweep", "workload": wl.name, "batch": B, "prompt": T, "steps": K, "warmup": W,
+    out = {"what": "tau sweep", "workload": wl.name, "exit_mode": args.exit_mode,
+           "build_exit_layers_s": round(build_s, 4), "batch": B, "prompt": T, "steps": K, "warmup": W,
            "config": f"decoder L={L} d={d} {shape.n_q_heads}q/{shape.n_kv_heads}kv heads x {shape.head_dim} "
                      f"FFN {F} vocab {shape.vocab}, int4 g{G} exit layers",
            "sweep": rows, "x6_exit_decision": x6, "x7_layer_time": x7, "x8_kv_cosine": x8}

@@ -763,7 +763,8 @@ int river_init(const river_config *cfg, const river_weights *w, void *exit_bank,
 
 int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
   if (!ctx) return RIVER_E_INVALID_ARG;
-  if (mode != RIVER_EXIT_INT4 && mode != RIVER_EXIT_COPY) return RIVER_E_INVALID_ARG;
+  if (mode != RIVER_EXIT_INT4 && mode != RIVER_EXIT_COPY && mode != RIVER_EXIT_HQQ)
+    return RIVER_E_INVALID_ARG;
   const bool copy = mode == RIVER_EXIT_COPY;
   if (ctx->bank_size < bank_bytes(ctx->cfg, copy)) return RIVER_E_BAD_SIZE;
   const river_config &c = ctx->cfg;
@@ -793,6 +794,10 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
         // (hipMemcpyDefault: an offloaded backbone layer lives in host memory)
         RV_TRY(hipMemcpyAsync(ctx->bank + co, src[i], (size_t)sh[i].N * sh[i].K * 2,
                               hipMemcpyDefault, ctx->stream));
+      } else if (mode == RIVER_EXIT_HQQ) {
+        RV_TRY(launch_quantize_hqq(static_cast<const uint16_t *>(src[i]), sh[i].N, sh[i].K,
+                                   c.group_size, at<uint32_t>(ctx->bank, co), at<uint32_t>(ctx->bank, so),
+                                   kHqqIters, kHqqBeta, kHqqKappa, ctx->stream));
       } else {
         RV_TRY(launch_quantize(static_cast<const uint16_t *>(src[i]), sh[i].N, sh[i].K,
                                c.group_size, at<uint32_t>(ctx->bank, co), at<uint32_t>(ctx->bank, so),
@@ -801,7 +806,8 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
     }
   }
   ctx->built = true;
-  ctx->exit_mode = mode;
+  // (the kernels see the bank's form: an HQQ-refined bank is an int4 bank)
+  ctx->exit_mode = copy ? RIVER_EXIT_COPY : RIVER_EXIT_INT4;
   ctx->pos = 0;
   ctx->batch = 0;
   return RIVER_OK;

@@ -193,6 +193,13 @@ hipError_t launch_1(void (*kernel)(P), dim3 grid, dim3 block, const P &p, hipStr
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
                            hipStream_t s);
+// the min-max quantiser followed by `iters` HQQ-style rounds on the zero point
+hipError_t launch_quantize_hqq(const uint16_t *w, int N, int K, int G, uint32_t *codes, uint32_t *sz,
+                               int iters, float beta, float kappa, hipStream_t s);
+// defaults of those rounds (the half-quadratic solver's published settings)
+constexpr int kHqqIters = 20;
+constexpr float kHqqBeta = 10.0f;
+constexpr float kHqqKappa = 1.01f;
 hipError_t launch_begin(const BeginParams &p, hipStream_t s);
 // one thread writes tau into the control block
 hipError_t launch_set_tau(Control *c, float tau, hipStream_t s);

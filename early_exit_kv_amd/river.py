@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libriver.so")
 
 RIVER_OK, RIVER_E_INVALID_ARG, RIVER_E_BAD_SIZE, RIVER_E_STATE = 0, 1, 2, 3
 RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
-RIVER_EXIT_INT4, RIVER_EXIT_COPY = 1, 2
+RIVER_EXIT_INT4, RIVER_EXIT_COPY, RIVER_EXIT_HQQ = 1, 2, 3
 RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK, RIVER_OPT_GEMV = 1, 2, 3, 4, 5
 RIVER_OPT_ATTN = 6
 KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
@@ -249,7 +249,7 @@ class River:
 
     # -- API -----------------------------------------------------------------
     def build_exit_layers(self, mode="int4"):
-        m = {"int4": RIVER_EXIT_INT4, "copy": RIVER_EXIT_COPY}[mode]
+        m = {"int4": RIVER_EXIT_INT4, "copy": RIVER_EXIT_COPY, "hqq": RIVER_EXIT_HQQ}[mode]
         self._call(self.lib.river_build_exit_layers, "river_build_exit_layers", m)
         self.mode = mode
 

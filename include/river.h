@@ -58,8 +58,10 @@ enum {
 /* ---- exit-bank construction modes -------------------------------------- */
 enum {
   RIVER_EXIT_INT4 = 1, /* copy + 4-bit group quantisation (the method)         */
-  RIVER_EXIT_COPY = 2  /* exact bf16 copy: exit layers equal the backbone; used
+  RIVER_EXIT_COPY = 2, /* exact bf16 copy: exit layers equal the backbone; used
                           to check that the exit plumbing changes nothing      */
+  RIVER_EXIT_HQQ = 3   /* RIVER_EXIT_INT4 followed by an HQQ-style refinement
+                          of every group's zero point (same bank layout)       */
 };
 
 #define RIVER_MAX_LAYERS 256
@@ -173,6 +175,16 @@ int river_init(const river_config *cfg, const river_weights *w, void *exit_bank,
  * columns), in float32 with every operation separately rounded:
  *   s = bf16((max - min) / 15), s = 1 if that is 0;  z = bf16(-min / s);
  *   code = clamp(round_half_even(w / s + z), 0, 15).
+ * mode RIVER_EXIT_HQQ then refines each group's zero point in the manner of
+ * HQQ, the quantiser the lead page names as its default (section 6; the page
+ * gives none of its steps): with zf = z, 20 rounds of
+ *   q = clamp(round_half_even(w / s + zf), 0, 15);  e = w - (q - zf) s;
+ *   we = sign(e) max(|e| - 1/beta, 0);  zf = sum_group(q - (w - we) / s) / G;
+ *   beta = beta * 1.01   (beta = 10 to begin with),
+ * every operation float32 and separately rounded, the group sum a fixed
+ * pairwise tree (the two halves added element-wise, then their halves, down
+ * to one value); s stays, z = bf16(zf), and the codes are taken again with
+ * the stored s and z.
  * mode RIVER_EXIT_COPY stores exact bf16 copies instead and needs a bank of
  * exit_bank_copy_bytes (else RIVER_E_BAD_SIZE).  Clears the control block and
  * resets the cache position to 0.  May be called again to rebuild. */
