@@ -237,12 +237,14 @@ class Shape:
         self.eps, self.theta = float(rms_eps), float(rope_theta)
 
 
-def attention(q, kc, vc, start, n):
+def attention(q, kc, vc, start, n, present=None):
     """Causal GQA attention for n new rows at positions start..start+n-1.
 
     q [B, n, Hq, D]; kc/vc [B, Hkv, S, D] already hold the new keys/values.
     Query head h reads kv head floor(h * Hkv / Hq).  Scores q.k / sqrt(D),
     softmax with its maximum subtracted, float64.  Returns [B, n, Hq, D].
+    ``present`` (bool per position, or None for all): earlier positions whose
+    keys/values this layer does not hold are left out (the KV-mask strategy).
     """
     B, _, Hq, D = q.shape
     Hkv = kc.shape[1]
@@ -251,6 +253,8 @@ def attention(q, kc, vc, start, n):
     rows = np.arange(n)[:, None] + start
     cols = np.arange(end)[None, :]
     masked = cols > rows
+    if present is not None:
+        masked = masked | ~np.asarray(present[:end], dtype=bool)[None, :]
     for b in range(B):
         for h in range(Hq):
             j = (h * Hkv) // Hq
@@ -265,7 +269,22 @@ def attention(q, kc, vc, start, n):
     return out
 
 
-def decoder_layer(shape, lw, h, start, kc, vc, rec=None):
+def layer_kv(shape, lw, h, start, kc, vc):
+    """Keys and values of one layer for h [B, n, d] at positions
+    start..start+n-1 (RMSNorm, the k and v projections, RoPE on k), written
+    into this layer's cache slots; the layer's attention and MLP do not run
+    (the state-propagation strategy's deeper layers)."""
+    B, n, d = h.shape
+    Hkv, D = shape.Hkv, shape.Dh
+    x = bf16_from_f64(rmsnorm(h, lw["attn_norm"], shape.eps))
+    k = linear(x, lw["wk"]).reshape(B, n, Hkv, D)
+    v = linear(x, lw["wv"]).reshape(B, n, Hkv, D)
+    cos, sin = rope_tables(np.arange(start, start + n), D, shape.theta)
+    kc[:, :, start:start + n] = bf16_from_f64(apply_rope(k, cos, sin)).transpose(0, 2, 1, 3)
+    vc[:, :, start:start + n] = bf16_from_f64(v).transpose(0, 2, 1, 3)
+
+
+def decoder_layer(shape, lw, h, start, kc, vc, rec=None, present=None):
     """One decoder layer on h [B, n, d] at positions start..start+n-1.
 
     ``lw`` holds float32 copies of the layer weights (backbone or exit copy).
@@ -286,7 +305,7 @@ def decoder_layer(shape, lw, h, start, kc, vc, rec=None):
     v = bf16_from_f64(v)
     kc[:, :, start:start + n] = k.transpose(0, 2, 1, 3)
     vc[:, :, start:start + n] = v.transpose(0, 2, 1, 3)
-    o = bf16_from_f64(attention(q, kc, vc, start, n)).reshape(B, n, Hq * D)
+    o = bf16_from_f64(attention(q, kc, vc, start, n, present)).reshape(B, n, Hq * D)
     h1 = h + linear(o, lw["wo"])
     x2 = bf16_from_f64(rmsnorm(h1, lw["mlp_norm"], shape.eps))
     u = bf16_from_f64(silu(linear(x2, lw["w_gate"])) * linear(x2, lw["w_up"]))
@@ -329,8 +348,8 @@ class RiverOracle:
         kv_shape = (s.L, self.max_batch, s.Hkv, self.max_seq, s.Dh)
         self.k_cache = np.zeros(kv_shape, dtype=np.float64)
         self.v_cache = np.zeros(kv_shape, dtype=np.float64)
-        self.pos = 0
-        self.batch = None
+        self.strategy = "river"
+        self.reset()
 
     # -- build ------------------------------------------------------------
     def build_exit_layers(self, mode=EXIT_INT4):
@@ -354,15 +373,42 @@ class RiverOracle:
             self.exit_layers.append(ex)
             self.exit_codes.append(codes)
 
+    # What happens to the layers at and past the exit (E .. L-1):
+    #   river      they run as their exit layers and write K/V into the shared
+    #              cache (the method of the lead page, section 3);
+    #   and, as speed comparators, three of the prior fixes the page's
+    #   section 2 describes for the missing K/V of early-exited tokens:
+    #   kv_mask    they are skipped; deeper layers of later tokens leave out
+    #              the positions whose K/V they do not hold;
+    #   propagate  they only compute their K/V from the exit state (their own
+    #              RMSNorm gain, k and v projections and RoPE), no attention
+    #              and no MLP;
+    #   mono       they are skipped, and the exit layer never increases along
+    #              the sequence: a decode step also exits on reaching the
+    #              previous pass's E, so every layer a token runs holds K/V
+    #              for all earlier positions.
+    #   In every strategy but river the logits come from the exit state.
+    KV_STRATEGIES = ("river", "kv_mask", "propagate", "mono")
+
+    def set_kv_strategy(self, name):
+        if name not in self.KV_STRATEGIES:
+            raise ValueError(name)
+        self.strategy = name
+
     def reset(self):
         self.pos = 0
         self.batch = None
+        self.last_E = self.s.L
+        self.pos_E = np.full(self.max_seq, self.s.L, dtype=np.int64)
 
     # -- one pass over all layers ------------------------------------------
     def _run(self, tokens, start, tau, force_E, record):
         s = self.s
         B, n = tokens.shape
         h = self.w["embed"][tokens].astype(np.float64)        # [B, n, d]
+        strat = getattr(self, "strategy", "river")
+        # mono: a decode step exits at the latest on reaching the previous E
+        cap = self.last_E if (strat == "mono" and start > 0) else s.L
         exited = False
         E = s.L
         trace = []
@@ -372,9 +418,19 @@ class RiverOracle:
                 use_exit = l >= force_E
             else:
                 use_exit = exited
+            if use_exit and strat != "river":
+                # past the exit: skipped, or (propagate) only this layer's K/V
+                # from the exit state; the residual stream stays as it is
+                if strat == "propagate":
+                    layer_kv(s, self.w["layers"][l], h, start, self.k_cache[l, :B], self.v_cache[l, :B])
+                continue
             lw = self.exit_layers[l] if use_exit else self.w["layers"][l]
             rec = {} if record else None
-            h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B], rec)
+            present = None
+            if strat == "kv_mask":
+                present = self.pos_E > l                       # earlier positions holding layer l
+                present[start:] = True
+            h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B], rec, present)
             if record:
                 inputs.append(rec)
             if force_E is None:
@@ -383,12 +439,14 @@ class RiverOracle:
                     m = float(cosine_rows(h.reshape(-1, s.d), h_out.reshape(-1, s.d)).min())
                     trace.append(m)
                     # the decision is taken in float32, like the device's
-                    if np.float32(m) > np.float32(tau):
+                    if np.float32(m) > np.float32(tau) or l + 1 >= cap:
                         exited = True
                         E = l + 1
             h = h_out
         if force_E is not None:
             E = int(force_E)
+        self.last_E = E
+        self.pos_E[start:start + n] = E
         w_lm = self.w["embed"] if self.w["lm_head"] is None else self.w["lm_head"]
         logits = lm_head(s, h[:, -1], self.w["final_norm"], w_lm)
         res = {"logits": logits, "next": greedy(logits), "E": E, "trace": trace, "h_final": h}
