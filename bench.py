@@ -42,7 +42,12 @@ def parse():
                     help="instead of the benchmark line: for each tau of the workload (or --taus) "
                          "the exit histogram, decode tokens/s, the exit-decision share of the step, "
                          "exit/backbone layer time and exit/backbone K/V cosine, as one JSON line")
-    ap.add_argument("--taus", type=str, default=None, help="comma-separated taus for --tau-sweep")
+    ap.add_argument("--taus", type=str, default=None,
+                    help="comma-separated taus for --tau-sweep and --kv-strategies")
+    ap.add_argument("--kv-strategies", action="store_true",
+                    help="instead of the benchmark line: decode tokens/s and exit histogram of the "
+                         "method and of the three earlier K/V fixes it is compared with (kv mask, "
+                         "state propagation, mono-decreasing exit) at each tau, as one JSON line")
     ap.add_argument("--exit-mode", default="int4", choices=["int4", "hqq"],
                     help="exit bank of --tau-sweep: min-max int4, or int4 with the HQQ-style zero refinement")
     ap.add_argument("--offload-from", type=int, default=None,
@@ -154,9 +159,10 @@ def cpu_baseline(shape, weights, B, T, mean_E):
     step = mean_E * t_bb + (s.L - mean_E) * t_ex + t_lm
     return {
         "value": round(B / step, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-        "sample": (f"one decode position at context {T}: 1 backbone layer ({t_bb:.2f} s), 1 int4 exit "
-                   f"layer ({t_ex:.2f} s), LM head ({t_lm:.2f} s); step = {mean_E:.2f} x backbone + "
-                   f"{s.L - mean_E:.2f} x exit + LM head = {step:.2f} s"),
+        "sample": (f"float64 numpy oracle, extrapolated: one decode position at context {T}, timed on 1 "
+                   f"backbone layer ({t_bb:.2f} s), 1 int4 exit layer ({t_ex:.2f} s) and the LM head "
+                   f"({t_lm:.2f} s); step = {mean_E:.2f} x backbone + {s.L - mean_E:.2f} x exit + "
+                   f"LM head = {step:.2f} s; cores = the BLAS thread pool's size"),
     }
 
 
@@ -389,8 +395,56 @@ def tau_sweep(args):
     print(json.dumps(out))
 
 
+def strategy_sweep(args):
+    """Per tau and per K/V strategy of the layers past the exit: decode
+    tokens/s, the exit histogram and the mean exit layer."""
+    import torch
+    import synth
+    from early_exit_kv_amd import river as rv
+
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    B, T = wl.batch, wl.prompt
+    taus = [float(t) for t in args.taus.split(",")] if args.taus else list(wl.taus)
+    K, W = args.steps, args.warmup
+    print(f"[strategies] workload {wl.name} B={B} T={T} steps={K} warmup={W} taus={taus}", file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = synth.make_weights(shape, seed=0, device=dev)
+    tokens = synth.make_tokens(shape, B, T, seed=0).to(dev)
+    r = rv.River(shape, weights, B, T + W + K + 2)
+    r.build_exit_layers("int4")
+    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    rows = []
+    for tau in taus:
+        for strategy in rv.KV_STRATEGIES:
+            r.kv_strategy(strategy)
+            r.reset()
+            _, nxt = r.prefill(tokens, tau, want_logits=False)
+            pE = r.exit_stats()["last_E"]
+            bufs[0].copy_(nxt)
+            el, hist = timed_steps(r, bufs, logits, tau, W, K)
+            mean_E = sum(e * n for e, n in enumerate(hist)) / max(1, sum(hist))
+            rows.append({"tau": tau, "strategy": strategy, "prefill_E": pE,
+                         "decode_tok_s": round(B * K / el, 2), "ms_per_step": round(el / K * 1e3, 4),
+                         "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
+                         "mean_exit_layer": round(mean_E, 3)})
+            print(f"[strategies] {rows[-1]}", file=sys.stderr, flush=True)
+    r.close()
+    print(json.dumps({"what": "K/V strategies past the exit", "workload": wl.name, "batch": B, "prompt": T,
+                      "steps": K, "warmup": W, "rows": rows}))
+
+
 def main():
     args = parse()
+    if args.kv_strategies:
+        if args.gpus != 1:
+            print("the strategy sweep runs on one GPU", file=sys.stderr)
+            sys.exit(2)
+        strategy_sweep(args)
+        return
     if args.tau_sweep:
         if args.gpus != 1:
             print("the tau sweep runs on one GPU", file=sys.stderr)

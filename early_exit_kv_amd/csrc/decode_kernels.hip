@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void begin_kernel(BeginParams p) {
       c->force_E = p.force_E;
       c->E = p.force_E >= 0 ? p.force_E : p.n_layers;
       if (p.write_tau) c->tau = p.tau;
+      c->strategy = p.strategy;
       if (p.set_pos >= 0) c->pos = p.set_pos;
     }
     for (int l = threadIdx.x; l < kMaxLayers; l += blockDim.x) c->trace[l] = __builtin_nanf("");
@@ -63,6 +64,21 @@ __global__ void set_tau_kernel(Control *c, float tau) { c->tau = tau; }
 
 hipError_t launch_set_tau(Control *c, float tau, hipStream_t s) {
   hipLaunchKernelGGL(set_tau_kernel, dim3(1), dim3(1), 0, s, c, tau);
+  return hipGetLastError();
+}
+
+__global__ void set_pos_E_kernel(Control *c, int32_t *pos_E, int n) {
+  const int E = c->last_E;
+  if (n > 0) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) pos_E[i] = E;
+  } else if (blockIdx.x == 0 && threadIdx.x == 0) {
+    pos_E[c->pos - 1] = E;   // the position the step wrote (pos was advanced)
+  }
+}
+
+hipError_t launch_set_pos_E(Control *c, int32_t *pos_E, int n, hipStream_t s) {
+  const int blocks = n > 0 ? std::min(64, (n + 255) / 256) : 1;
+  hipLaunchKernelGGL(set_pos_E_kernel, dim3(blocks), dim3(256), 0, s, c, pos_E, n);
   return hipGetLastError();
 }
 
@@ -194,6 +210,30 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
   // with the test pending the weights start streaming on a guess: the
   // backbone, unless it lives in host memory (then the exit copy in HBM)
   if (pending) ex = p.remote_bb != 0;
+  // past the exit under a comparator strategy: skipped, or (q|k|v) the k and
+  // v rows only, from the backbone weights
+  const int strat = ctl->strategy;
+  const int action = past_exit_action(ctl, p.layer, p.path);
+  if constexpr (EP == kEpResid || EP == kEpSwiGLU || EP == kEpResidExit) {
+    if (action != kRun) {
+      if constexpr (EP == kEpResid) {   // the residual stream passes through
+        for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < (int64_t)p.B * p.N;
+             idx += (int64_t)gridDim.x * 256) {
+          const int64_t o = (idx / p.N) * p.h_io_stride + idx % p.N;
+          p.h_out[o] = p.h_in[o];
+        }
+      }
+      return;
+    }
+  }
+  bool kv_only = false;
+  if constexpr (EP == kEpQKV) {
+    if (action == kSkip) return;
+    if (action == kKvOnly) {
+      kv_only = true;
+      ex = false;
+    }
+  }
   bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
 
   // Rows of the current task: row indices plus at most two segment bases (the
@@ -350,7 +390,9 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
       for (int i = 0; i < 3 * M; ++i) pv[j][i] = pp[i];
     }
   }
-  int task = blockIdx.x * 4 + wid;
+  // (k|v rows only: the tasks start past the query rows)
+  const int kv_task0 = EP == kEpQKV ? (p.Hq * p.Dh) / R : 0;
+  int task = blockIdx.x * 4 + wid + (kv_only ? kv_task0 : 0);
   setup_rows(task);
   load_batch(Buf<0>{}, 0, nchunks(min(kslab, K)), lane);
 
@@ -445,7 +487,9 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
     }
     // (the same value in every lane; readfirstlane lets the compiler know it,
     // so the weight choice that follows stays in scalar registers)
-    const bool fired = __builtin_amdgcn_readfirstlane(mcos > ctl->tau ? 1 : 0) != 0;
+    // (mono: a step also exits on reaching the previous pass's E)
+    const bool fired = __builtin_amdgcn_readfirstlane(
+                           (mcos > ctl->tau || (strat == kStratMono && p.layer >= ctl->last_E)) ? 1 : 0) != 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       ctl->trace[p.layer - 1] = mcos;
       if (fired) {
@@ -453,7 +497,19 @@ void gemv_kernel(GemvParams p, int kslab, int ntask) {
         __hip_atomic_store(&ctl->flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (fired != ex) {  // the guess was wrong: fetch the other weights instead
+    if (fired && strat != kStratRiver) {
+      // this layer is the first past the exit under a comparator strategy
+      if (strat != kStratPropagate) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the guessed loads land first
+        return;
+      }
+      kv_only = true;   // k and v rows only, from the backbone weights
+      ex = false;
+      q4 = false;
+      task += kv_task0;
+      setup_rows(task);
+      load_batch(Buf<0>{}, 0, nchunks(min(kslab, K)), lane);
+    } else if (fired != ex) {  // the guess was wrong: fetch the other weights instead
       ex = fired;
       q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
       setup_rows(task);
@@ -897,6 +953,31 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   const bool defer = pending && p.remote_bb != 0;
   const bool int4_mode = p.exit_mode == RIVER_EXIT_INT4;
   const int pos = ctl->pos;
+  // past the exit under a comparator strategy: skipped, or (q|k|v) the k and
+  // v tiles only, from the backbone weights
+  const int strat = ctl->strategy;
+  const int action = past_exit_action(ctl, p.layer, p.path);
+  if constexpr (EP == kEpResid || EP == kEpSwiGLU || EP == kEpResidExit) {
+    if (action != kRun) {
+      if constexpr (EP == kEpResid) {   // the residual stream passes through
+        for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < (int64_t)p.B * p.N;
+             idx += (int64_t)gridDim.x * 256) {
+          const int64_t o = (idx / p.N) * p.h_io_stride + idx % p.N;
+          p.h_out[o] = p.h_in[o];
+        }
+      }
+      return;
+    }
+  }
+  int tbase = 0;   // first tile (k|v only: past the query rows)
+  const int kv_tile0 = EP == kEpQKV ? (p.Hq * p.Dh) / 16 : 0;
+  if constexpr (EP == kEpQKV) {
+    if (action == kSkip) return;
+    if (action == kKvOnly) {
+      tbase = kv_tile0;
+      ex = false;
+    }
+  }
 
   // ---- per-thread epilogue state kept across tiles (the down projection has
   // no pending test, so its weight choice is final here)
@@ -925,7 +1006,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
     constexpr int NDMA = 2 + (Q4 ? 1 : 0) + NEPI + NX;  // DMAs per unit
     constexpr int UKB = Q4 ? 256 : 64;             // K columns per unit
     const int KU = K / UKB, U = (KU + 3) >> 2;     // units per tile row, per wavefront
-    const int my_tiles = (ntile - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int my_tiles = (ntile - tbase - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    if (my_tiles <= 0) return false;               // (k|v only: fewer tiles than workgroups)
 
     // ---- fetch side: the tile being fetched (this lane's two weight rows,
     // its scale row, its epilogue operands) and the next unit (lti, ls)
@@ -977,7 +1059,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
       constexpr int d = decltype(dc)::value;
       const bool past = lti >= my_tiles;             // past the last unit: the last unit again
       const int ti = past ? my_tiles - 1 : lti, s = past ? U - 1 : ls;
-      const int t = (int)blockIdx.x + ti * (int)gridDim.x;
+      const int t = tbase + (int)blockIdx.x + ti * (int)gridDim.x;
       if (t != ltile) {
         set_tile(t);
         ltile = t;
@@ -1072,7 +1154,7 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
     auto end_tile = [&](auto dc, int ti) {
       constexpr int d = decltype(dc)::value;
       const int par = ti & 1;
-      const int t = (int)blockIdx.x + ti * (int)gridDim.x;
+      const int t = tbase + (int)blockIdx.x + ti * (int)gridDim.x;
 #pragma unroll
       for (int i = 0; i < IM; ++i) {
         const int m = 4 * qq + i;
@@ -1297,7 +1379,9 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
         }
         // (uniform over the workgroup; readfirstlane tells the compiler, so the
         // weight choice that follows stays in scalar registers)
-        fired = __builtin_amdgcn_readfirstlane(mcos > ctl->tau ? 1 : 0) != 0;
+        // (mono: a step also exits on reaching the previous pass's E)
+        fired = __builtin_amdgcn_readfirstlane(
+                    (mcos > ctl->tau || (strat == kStratMono && p.layer >= ctl->last_E)) ? 1 : 0) != 0;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
           ctl->trace[p.layer - 1] = mcos;
           if (fired) {
@@ -1418,9 +1502,16 @@ __global__ __launch_bounds__(256) void mgemv_kernel(GemvParams p, int ntile) {
   if (q4) {
     run(Buf<1>{}, false);
   } else if (run(Buf<0>{}, false)) {
-    ex = true;   // the pending test fired: the exit weights instead
-    if (int4_mode) run(Buf<1>{}, true);
-    else run(Buf<0>{}, true);
+    // the pending test fired: the exit weights instead; under a comparator
+    // strategy this layer is the first past the exit (k|v only, or nothing)
+    bool again = true;
+    if (strat == kStratRiver) ex = true;
+    else if (strat == kStratPropagate) tbase = kv_tile0;
+    else again = false;
+    if (again) {
+      if (ex && int4_mode) run(Buf<1>{}, true);
+      else run(Buf<0>{}, true);
+    }
   }
 
   // ---- per-workgroup tails
@@ -1710,6 +1801,7 @@ int attn_chunk(int max_seq, int batch, int n_kv_heads) {
 
 template <int DH, int GQ>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
+  if (past_exit_action(p.ctrl, p.layer, kPathDevice) != kRun) return;   // (comparators)
   constexpr int LPP = DH / 8;        // lanes per position (8 bf16 each)
   constexpr int PPW = 64 / LPP;      // positions per wavefront per pass (slots)
   constexpr int PPP = 4 * PPW;       // positions per workgroup per pass
@@ -1948,12 +2040,16 @@ __device__ __forceinline__ int attn_swz(int r) {
   return DH == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
-template <int DH, int GQ>
+// MASK (the kv-mask comparator): positions whose pass exited at or before this
+// layer hold no K/V here and are left out; their pos_E words come in by DMA
+// with each block.
+template <int DH, int GQ, bool MASK>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
+  if (past_exit_action(p.ctrl, p.layer, kPathDevice) != kRun) return;   // (comparators)
   constexpr int CPR = DH * 2 / 16;             // 16-byte chunks per position
   constexpr int BLK = 16 * DH * 2;             // bytes of a 16-position K (or V) block
   constexpr int NDK = BLK / 1024;              // DMAs per block
-  constexpr int NDMA = 2 * NDK;                // K and V DMAs per sub-chunk per wavefront
+  constexpr int NDMA = 2 * NDK + (MASK ? 1 : 0);   // DMAs per sub-chunk per wavefront
   constexpr int LPP = DH / 8;                  // P V lanes per position
   constexpr int PPW = 64 / LPP;                // positions per P V pass
   constexpr int NPASS = 16 / PPW;              // passes per block
@@ -1964,6 +2060,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   __shared__ __align__(16) float pl[4][16][GQ];
   __shared__ float wm[4][GQ], wl[4][GQ];
   __shared__ int last_flag;
+  __shared__ int32_t pe[4][2][64];                 // MASK: pos_E of a wavefront's block
   static_assert(4 * PPW * GQ * DH * 4 <= 4 * 2 * KVB, "the partial results fit the K/V buffers");
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -1989,6 +2086,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       const uint32_t dst = kvw_lds + bi * KVB + 1024 * h;
       dma16_nt(dst, Kc + off);
       dma16_nt(dst + BLK, Vc + off);
+    }
+    if constexpr (MASK) {
+      const uint32_t pl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)&pe[wid][bi][0]);
+      dma4(pl, p.pos_E + min(base + lane, p.S - 1));
     }
   };
 
@@ -2031,7 +2132,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(kb + 16 * (cl * CPR + ((4 * j + qq) ^ rs)));
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kf, sc, 0, 0, 0);
     }
-    const bool vis = base + cl < t1;
+    bool vis = base + cl < t1;
+    // (MASK: an earlier position keeps its K/V at this layer only if its
+    // pass ran the layer; the current position always does)
+    if constexpr (MASK) vis = vis && (base + cl >= n - 1 || pe[wid][bi][cl] > p.layer);
     float corr[GQ];
 #pragma unroll
     for (int i = 0; i < GQ; ++i) {
@@ -2059,7 +2163,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = ps * PPW + slot;
       uint4 v = *reinterpret_cast<const uint4 *>(vb + 16 * (r * CPR + (ln ^ attn_swz<DH>(r))));
-      if (base + r >= t1) v = make_uint4(0, 0, 0, 0);
+      bool rv = base + r < t1;
+      if constexpr (MASK) rv = rv && (base + r >= n - 1 || pe[wid][bi][r] > p.layer);
+      if (!rv) v = make_uint4(0, 0, 0, 0);
       const float vf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
                            bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
       float pr[GQ];
@@ -2174,11 +2280,20 @@ template <int DH>
 static hipError_t attn_launch_dh(const AttnParams &p, hipStream_t s) {
   dim3 grid(p.splits, p.Hkv, p.B);
   const int gq = p.Hq / p.Hkv;
+  if (p.mfma && p.pos_E) {
+    switch (gq) {
+      case 1: return launch_1(attn_mfma_kernel<DH, 1, true>, grid, dim3(256), p, s);
+      case 2: return launch_1(attn_mfma_kernel<DH, 2, true>, grid, dim3(256), p, s);
+      case 4: return launch_1(attn_mfma_kernel<DH, 4, true>, grid, dim3(256), p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (p.pos_E) return hipErrorInvalidValue;   // the vector-ALU kernel has no mask
   if (p.mfma) {
     switch (gq) {
-      case 1: return launch_1(attn_mfma_kernel<DH, 1>, grid, dim3(256), p, s);
-      case 2: return launch_1(attn_mfma_kernel<DH, 2>, grid, dim3(256), p, s);
-      case 4: return launch_1(attn_mfma_kernel<DH, 4>, grid, dim3(256), p, s);
+      case 1: return launch_1(attn_mfma_kernel<DH, 1, false>, grid, dim3(256), p, s);
+      case 2: return launch_1(attn_mfma_kernel<DH, 2, false>, grid, dim3(256), p, s);
+      case 4: return launch_1(attn_mfma_kernel<DH, 4, false>, grid, dim3(256), p, s);
       default: return hipErrorInvalidValue;
     }
   }

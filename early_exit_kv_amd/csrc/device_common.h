@@ -189,6 +189,18 @@ __device__ __forceinline__ bool layer_uses_exit(const Control *c, int layer) {
   return c->flag != 0;
 }
 
+// Under the prior-art comparators (KvStrategy other than the river) a layer
+// at or past the exit does not run as an exit layer: what its kernels do.
+enum PastExit { kRun = 0, kSkip = 1, kKvOnly = 2 };
+__device__ __forceinline__ int past_exit_action(const Control *c, int layer, int path) {
+  if (layer < 0) return kRun;
+  const int st = c->strategy;
+  if (st == kStratRiver) return kRun;
+  const bool past = path == kPathDevice ? layer_uses_exit(c, layer) : path == kPathExit;
+  if (!past) return kRun;
+  return st == kStratPropagate ? kKvOnly : kSkip;
+}
+
 // Monotone map of fp32 to uint32 (larger float -> larger integer).
 __device__ __forceinline__ uint32_t float_order(float f) {
   uint32_t u = __float_as_uint(f);

@@ -287,6 +287,32 @@ __device__ void tile_epilogue(const GemmParams &p, const float *Cs, int cs, int 
   }
 }
 
+// Prefill GEMMs of a layer at or past the exit under a comparator strategy:
+// o passes the residual stream through, gate|up and down do nothing, q|k|v
+// computes the k and v column blocks only, from the backbone weights (ex is
+// set to false for them).  Returns true when the workgroup has nothing to do.
+template <int EP, int BN>
+__device__ __forceinline__ bool past_exit_skip(const GemmParams &p, int colblk, bool &ex) {
+  if constexpr (EP != kEpQKV && EP != kEpResid && EP != kEpSwiGLU) return false;
+  const int action = past_exit_action(p.ctrl, p.layer, p.path);
+  if (action == kRun) return false;
+  if constexpr (EP == kEpResid) {
+    const int64_t nb = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    const int64_t i0 = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int64_t idx = i0; idx < (int64_t)p.M * p.N; idx += nb) {
+      const int64_t o = (idx / p.N) * p.h_io_stride + idx % p.N;
+      if (p.h_out != p.h_in) p.h_out[o] = p.h_in[o];
+    }
+    return true;
+  } else if constexpr (EP == kEpQKV) {
+    if (action == kSkip) return true;
+    ex = false;
+    return (colblk + 1) * BN <= p.Hq * p.Dh;   // a block of query columns only
+  } else {
+    return true;
+  }
+}
+
 template <int BM, int BN, int EP>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   constexpr int LDSK = kBK + kLdsPad;
@@ -297,7 +323,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   __shared__ uint32_t szs[BN];
   __shared__ float xsg[BM];
 
-  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
+  bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
+  if (past_exit_skip<EP, BN>(p, blockIdx.y, ex)) return;   // (comparators)
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -453,6 +480,7 @@ hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 // ===========================================================================
 template <int DH>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) {
+  if (past_exit_action(p.ctrl, p.layer, p.path) != kRun) return;   // (comparators)
   constexpr int SL = DH / 4;    // elements per thread
   constexpr int KT = 16;        // keys per tile (measured: 16 beats 8, 32 and 64)
   __shared__ __align__(16) uint16_t Ks[KT][DH];
@@ -552,6 +580,7 @@ __device__ __forceinline__ int flash_swz(int r) {
 
 template <int DH, int GQ>
 __global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
+  if (past_exit_action(p.ctrl, p.layer, p.path) != kRun) return;   // (comparators)
   constexpr int KT = 32;                // key positions per tile
   constexpr int CPR = DH / 8;           // 16-byte chunks per key row
   constexpr int NS = DH / 32;           // k-steps of a score MFMA
@@ -1512,8 +1541,7 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   __shared__ __align__(16) uint4 smem[psmem_slots<BN>()];
   uint4 *xs = smem, *cs = smem + kPBufs * kPTileSlots, *zs = cs + kPBufs * pcode_slots<BN>();
   constexpr int AF = ptm<BN>() / 16;
-  const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
-  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+  bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   // grouped order: kPGroupRows row blocks share the weights of each column block
   const int per_group = kPGroupRows * ncolblk;
   const int grp = blockIdx.x / per_group;
@@ -1521,6 +1549,8 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   const int gm = min(nrowblk - first, kPGroupRows);
   const int in_grp = blockIdx.x - grp * per_group;
   const int rowblk = first + in_grp % gm, colblk = in_grp / gm;
+  if (past_exit_skip<EP, BN>(p, colblk, ex)) return;   // (comparators)
+  const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
 
   f32x4_t tot[AF][4];
 #pragma unroll

@@ -170,6 +170,7 @@ struct river_ctx {
   int gemv_mode = 0;    // RIVER_OPT_GEMV
   int attn_kind = 0;    // RIVER_OPT_ATTN
   std::vector<char> remote;   // per layer: backbone linears in host memory (offloaded)
+  int strategy = kStratRiver; // RIVER_OPT_KV_STRATEGY
 };
 
 namespace {
@@ -354,7 +355,7 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
-  bp.tau = tau; bp.write_tau = 0; bp.is_prefill = 0; bp.set_pos = -1;
+  bp.tau = tau; bp.write_tau = 0; bp.is_prefill = 0; bp.set_pos = -1; bp.strategy = ctx->strategy;
   TIMED_ONLY(RIVER_K_BEGIN, launch_begin(bp, s));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -384,6 +385,8 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
     a.mfma = ctx->attn_kind == 0;
+    a.layer = l;
+    a.pos_E = ctx->strategy == kStratMask ? control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads) : nullptr;
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
@@ -442,7 +445,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = B; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
-  bp.tau = tau; bp.write_tau = 0; bp.is_prefill = 0; bp.set_pos = -1;
+  bp.tau = tau; bp.write_tau = 0; bp.is_prefill = 0; bp.set_pos = -1; bp.strategy = ctx->strategy;
   TIMED_ONLY(RIVER_K_BEGIN, launch_begin(bp, s));
 
   int down_wgs = 0;
@@ -483,6 +486,8 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     a.splits = (c.max_seq + a.chunk - 1) / a.chunk;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
     a.mfma = ctx->attn_kind == 0;
+    a.layer = l;
+    a.pos_E = ctx->strategy == kStratMask ? control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads) : nullptr;
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
@@ -521,6 +526,8 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   lm.h_src = hA; lm.h_stride = c.d_model; lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
   lm.logits = logits; lm.next = next; lm.is_prefill = 0; lm.vocab = c.vocab;
   TIMED_ONLY(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
+  if (ctx->strategy == kStratMask && only < 0)
+    RV_TRY(launch_set_pos_E(ctx->ctrl, control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads), 0, s));
   return RIVER_OK;
 }
 
@@ -538,7 +545,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
   BeginParams bp{};
   bp.ctrl = ctx->ctrl; bp.tokens = tok; bp.rows = R; bp.B = B; bp.embed = ctx->embed; bp.h = hA;
   bp.d = c.d_model; bp.vocab = c.vocab; bp.n_layers = c.n_layers; bp.force_E = ctx->force_E;
-  bp.tau = tau; bp.write_tau = 1; bp.is_prefill = 1; bp.set_pos = T;
+  bp.tau = tau; bp.write_tau = 1; bp.is_prefill = 1; bp.set_pos = T; bp.strategy = ctx->strategy;
   TIMED(RIVER_K_BEGIN, launch_begin(bp, s));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -568,6 +575,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     ap.Hkv = c.n_kv_heads; ap.Dh = c.head_dim; ap.S = c.max_seq;
     ap.scale = 1.0f / std::sqrt((float)c.head_dim);
     ap.mfma = ctx->attn_kind == 0;
+    ap.ctrl = ctx->ctrl; ap.layer = l; ap.path = g.path;
     TIMED(RIVER_K_P_ATTN, launch_attn_prefill(ap, s));
     RV_TRY(rec.put(l, rec.lay.attn, ap.out, qbytes));
 
@@ -602,9 +610,15 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     std::swap(hA, hB);
   }
   RV_TRY(rec.put(-1, 0, hA, hbytes));
-  if (B > 8)
-    return enqueue_lm_head_rows(ctx, hA + (int64_t)(T - 1) * c.d_model, (int64_t)T * c.d_model, B,
-                                logits, next, 1);
+  if (B > 8) {
+    const int st = enqueue_lm_head_rows(ctx, hA + (int64_t)(T - 1) * c.d_model, (int64_t)T * c.d_model, B,
+                                        logits, next, 1);
+    if (st != RIVER_OK) return st;
+    // (kv mask: every prompt position holds K/V up to the prompt's exit)
+    if (ctx->strategy == kStratMask)
+      RV_TRY(launch_set_pos_E(ctx->ctrl, control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads), T, s));
+    return RIVER_OK;
+  }
   GemvParams lm{};
   lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
   lm.gemv_mode = ctx->gemv_mode;
@@ -615,6 +629,8 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
   lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
   lm.logits = logits; lm.next = next; lm.is_prefill = 1; lm.vocab = c.vocab;
   TIMED(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
+  if (ctx->strategy == kStratMask)
+    RV_TRY(launch_set_pos_E(ctx->ctrl, control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads), T, s));
   return RIVER_OK;
 }
 
@@ -709,7 +725,7 @@ int river_query_sizes(const river_config *cfg, river_sizes *out) {
   out->kv_cache_bytes = (size_t)2 * cfg->n_layers * cfg->max_batch * cfg->n_kv_heads *
                         cfg->max_seq * cfg->head_dim * 2;
   out->workspace_bytes = workspace_layout(*cfg).total;
-  out->control_bytes = control_bytes(cfg->max_batch, cfg->n_kv_heads);
+  out->control_bytes = control_bytes(cfg->max_batch, cfg->n_kv_heads, cfg->max_seq);
   return RIVER_OK;
 }
 
@@ -770,7 +786,7 @@ int river_build_exit_layers(river_ctx *ctx, int32_t mode) {
   const river_config &c = ctx->cfg;
   drop_graphs(ctx);
   ctx->built = false;
-  RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads), ctx->stream));
+  RV_TRY(launch_clear(ctx->ctrl, control_bytes(c.max_batch, c.n_kv_heads, c.max_seq), ctx->stream));
   ctx->ctrl_tau_bits = 0;   // the cleared block holds tau = +0.0
   RV_TRY(launch_rope_table(at<float2>(ctx->ws, ctx->wl.rope), c.max_seq, c.head_dim, c.rope_theta,
                            ctx->stream));
@@ -842,6 +858,10 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
   if (ctx->pos + 1 > ctx->cfg.max_seq) return RIVER_E_RANGE;
   if (ctx->rec && record_layout(ctx->cfg, ctx->batch).total > ctx->rec_bytes)
     return RIVER_E_BAD_SIZE;
+  // the comparator strategies run on the decode kernels of up to 8 rows; the
+  // kv mask on the matrix-core attention
+  if (ctx->strategy != kStratRiver && ctx->batch > 8) return RIVER_E_UNIMPLEMENTED;
+  if (ctx->strategy == kStratMask && ctx->attn_kind != 0) return RIVER_E_UNIMPLEMENTED;
   // the step reads tau from the control block: write it when it changes
   uint32_t tau_bits;
   std::memcpy(&tau_bits, &tau, 4);
@@ -926,6 +946,11 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
     case RIVER_OPT_GEMV:
       if (value < 0 || value > 2) return RIVER_E_INVALID_ARG;
       ctx->gemv_mode = (int)value;
+      drop_graphs(ctx);
+      return RIVER_OK;
+    case RIVER_OPT_KV_STRATEGY:
+      if (value < kStratRiver || value > kStratMono) return RIVER_E_INVALID_ARG;
+      ctx->strategy = (int)value;
       drop_graphs(ctx);
       return RIVER_OK;
     case RIVER_OPT_PROFILE:

@@ -35,7 +35,7 @@ struct Control {
   int32_t force_E;   // -1: decide with tau; e >= 0: layers >= e are exit layers
   int32_t bad_token; // a token id outside [0, vocab) was seen (and clamped)
   int32_t last_E;
-  int32_t pad0;
+  int32_t strategy;  // KvStrategy of the current pass
   int64_t n_decode, n_prefill;
   int64_t decode_hist[kMaxLayers + 1];
   int64_t prefill_hist[kMaxLayers + 1];
@@ -43,13 +43,23 @@ struct Control {
   uint32_t counters[kNumCounters];
   // followed by: uint64_t argmax_key[max_batch];
   //              uint32_t attn_counters[max_batch * n_kv_heads];
+  //              int32_t pos_E[max_seq]  (E of the pass that wrote each position)
 };
 
-__host__ __device__ inline size_t control_bytes(int max_batch, int n_kv_heads) {
+// What the layers at and past the exit do (RIVER_OPT_KV_STRATEGY): run as
+// exit layers (the method), or, as comparators, three prior fixes of the
+// missing K/V of early-exited tokens: skipped with later tokens leaving out
+// the K/V that are missing (kv mask), only their K/V computed from the exit
+// state (state propagation), skipped with the exit layer never increasing
+// along the sequence (mono-decreasing).
+enum KvStrategy { kStratRiver = 0, kStratMask = 1, kStratPropagate = 2, kStratMono = 3 };
+
+__host__ __device__ inline size_t control_bytes(int max_batch, int n_kv_heads, int max_seq) {
   size_t b = sizeof(Control);
   b = (b + 7) & ~size_t(7);
   b += sizeof(uint64_t) * (size_t)max_batch;
   b += sizeof(uint32_t) * (size_t)max_batch * n_kv_heads;
+  b += sizeof(int32_t) * (size_t)max_seq;
   return (b + 255) & ~size_t(255);
 }
 __host__ __device__ inline uint64_t *control_keys(Control *c) {
@@ -58,6 +68,9 @@ __host__ __device__ inline uint64_t *control_keys(Control *c) {
 }
 __host__ __device__ inline uint32_t *control_attn_counters(Control *c, int max_batch) {
   return reinterpret_cast<uint32_t *>(control_keys(c) + max_batch);
+}
+__host__ __device__ inline int32_t *control_pos_E(Control *c, int max_batch, int n_kv_heads) {
+  return reinterpret_cast<int32_t *>(control_attn_counters(c, max_batch) + (size_t)max_batch * n_kv_heads);
 }
 
 // ---------------------------------------------------------------------------
@@ -159,6 +172,9 @@ struct AttnParams {
   int B, Hq, Hkv, Dh, S, splits, chunk;
   float scale;
   int mfma;               // 1: scores on the matrix cores
+  int layer;              // the layer (kernels past the exit return at once in the comparators)
+  const int32_t *pos_E;   // kv mask: E per earlier position (positions whose E <= layer
+                          // hold no K/V here); nullptr: every position
 };
 // positions per decode-attention workgroup for a cache of max_seq positions
 int attn_chunk(int max_seq, int batch, int n_kv_heads);
@@ -177,6 +193,7 @@ struct BeginParams {
                       // recorded step serves every tau
   int is_prefill;
   int set_pos;        // >= 0: write this position into the control block
+  int strategy;       // KvStrategy of the pass
 };
 
 // ---- launchers (each returns hipGetLastError() after the launch) ----------
@@ -203,6 +220,9 @@ constexpr float kHqqKappa = 1.01f;
 hipError_t launch_begin(const BeginParams &p, hipStream_t s);
 // one thread writes tau into the control block
 hipError_t launch_set_tau(Control *c, float tau, hipStream_t s);
+// after a pass (kv mask): pos_E of the positions it wrote = its E (n > 0: the
+// first n positions, a prefill; n = 0: position pos - 1, a decode step)
+hipError_t launch_set_pos_E(Control *c, int32_t *pos_E, int n, hipStream_t s);
 // RoPE table: rope[t][i] = (cos, sin)(t * theta^(-2i/Dh)), angles in float64
 hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float theta, hipStream_t s);
 hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s);
@@ -262,6 +282,7 @@ struct AttnPrefillParams {
   int B, T, Hq, Hkv, Dh, S;
   float scale;
   int mfma;                // 1: the matrix-core (flash-style) kernel, 0: the vector-ALU one
+  Control *ctrl; int layer; int path;   // past the exit in the comparators: return at once
 };
 hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s);
 

@@ -17,7 +17,8 @@ RIVER_OK, RIVER_E_INVALID_ARG, RIVER_E_BAD_SIZE, RIVER_E_STATE = 0, 1, 2, 3
 RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
 RIVER_EXIT_INT4, RIVER_EXIT_COPY, RIVER_EXIT_HQQ = 1, 2, 3
 RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK, RIVER_OPT_GEMV = 1, 2, 3, 4, 5
-RIVER_OPT_ATTN = 6
+RIVER_OPT_ATTN, RIVER_OPT_KV_STRATEGY = 6, 7
+KV_STRATEGIES = ("river", "kv_mask", "propagate", "mono")
 KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
                 "p_norm", "p_gemm", "p_attn", "p_cos")
 RIVER_MAX_LAYERS = 256
@@ -312,6 +313,11 @@ class River:
         """Kernel of decode linears of <= 8 rows: "auto" (per linear), "dot"
         (dot-product GEMV) or "mfma" (matrix-core GEMV where it fits)."""
         self.set_option(RIVER_OPT_GEMV, {"auto": 0, "dot": 1, "mfma": 2}[mode])
+
+    def kv_strategy(self, name):
+        """Layers at and past the exit: "river" (exit layers, the method) or a
+        comparator: "kv_mask", "propagate", "mono" (see include/river.h)."""
+        self.set_option(RIVER_OPT_KV_STRATEGY, KV_STRATEGIES.index(name))
 
     def attn_kind(self, kind):
         """Attention kernels (decode and prefill): "mfma" (matrix cores) or "valu"."""

@@ -250,7 +250,24 @@ int river_exit_stats(river_ctx *ctx, river_exit_stats_t *host_out);
  *                     three bf16 terms), 1 all on the vector ALUs (same
  *                     results up to the fp32 summation order). */
 enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_OPT_ATTN_CHUNK = 4,
-       RIVER_OPT_GEMV = 5, RIVER_OPT_ATTN = 6 };
+       RIVER_OPT_GEMV = 5, RIVER_OPT_ATTN = 6, RIVER_OPT_KV_STRATEGY = 7 };
+/* RIVER_OPT_KV_STRATEGY: what the layers at and past the exit (E .. L-1) do.
+ *   RIVER_KV_RIVER (default): they run as their exit layers and write their
+ *     K/V into the shared cache (the method, lead page section 3);
+ *   speed comparators, three of the earlier fixes for the K/V that an
+ *   early-exited token leaves missing (section 2), the logits then coming
+ *   from the exit state:
+ *   RIVER_KV_MASK: they are skipped; deeper layers of later tokens leave out
+ *     the positions whose K/V they do not hold (matrix-core attention only);
+ *   RIVER_KV_PROPAGATE: they only compute their K/V from the exit state (their
+ *     RMSNorm gain, backbone k and v projections, RoPE), no attention, no MLP;
+ *   RIVER_KV_MONO: they are skipped, and a decode step also exits on reaching
+ *     the previous pass's E, so the exit layer never increases along the
+ *     sequence.
+ * Decode steps of more than 8 rows take only RIVER_KV_RIVER
+ * (RIVER_E_UNIMPLEMENTED); the activation record of a skipped layer holds
+ * nothing of the pass. */
+enum { RIVER_KV_RIVER = 0, RIVER_KV_MASK = 1, RIVER_KV_PROPAGATE = 2, RIVER_KV_MONO = 3 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
 
 /* Kernel classes timed when RIVER_OPT_PROFILE is 1 (decode steps then launch

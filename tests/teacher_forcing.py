@@ -121,7 +121,8 @@ def attention_row(q, k, v, scale):
 
 
 def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, trace, tau,
-               logits, nxt, final_norm, w_lm, report=None):
+               logits, nxt, final_norm, w_lm, report=None, strategy="river", pos_E=None, forced=False,
+               cap=None):
     """Check one prefill (n = T rows per sequence, start = 0) or decode step
     (n = 1, start = position) of the implementation under test.
 
@@ -129,6 +130,14 @@ def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, 
     or exit copy); rec_layers / h_out: the stored activations (rows ordered
     b-major, float64); kc, vc: the stored cache [L][B][Hkv][S][D] (float64);
     trace: the per-layer batch-min cosines the implementation recorded.
+
+    strategy: what the layers from E on did.  "river": ran as exit layers;
+    "kv_mask" / "mono": skipped (nothing stored, the final state is the exit
+    state), and under "kv_mask" the attention of layer l leaves out the
+    earlier positions p with pos_E[p] <= l; "propagate": only their K/V,
+    from the exit state with the backbone's norm gain and k/v projections.
+    forced: E was forced (no exit test ran); cap: under "mono", the E at which
+    the pass exits whatever the cosine (the previous pass's E).
     """
     s = shape
     rep = report or Report()
@@ -138,12 +147,27 @@ def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, 
     pos = np.tile(np.arange(start, start + n), B)           # position of each row
     bidx = np.repeat(np.arange(B), n)
     end = start + n
+    skip = strategy != "river"
+    last_run = E if skip else L                              # layers that ran in full
     for l in range(L):
         use_exit = l >= E
+        if skip and use_exit:
+            if strategy == "propagate":
+                lw = layer_weights(l, False)
+                xr, fl = flip_size(ro.rmsnorm(h_out, lw["attn_norm"], s.eps))
+                yk, bk = product(xr, lw["wk"], fl)
+                yv, bv = product(xr, lw["wv"], fl)
+                ek, rk = rope_allowance(yk.reshape(R, s.Hkv, s.Dh), bk.reshape(R, s.Hkv, s.Dh), pos, s.Dh,
+                                        s.theta)
+                tag = f"layer {l} (propagated K/V)"
+                rep.bf16(f"k[{tag}]", kc[l, bidx, :, pos], ek, rk)
+                rep.bf16(f"v[{tag}]", vc[l, bidx, :, pos], yv.reshape(R, s.Hkv, s.Dh),
+                         bv.reshape(R, s.Hkv, s.Dh) + 2 * U32 * np.abs(yv.reshape(R, s.Hkv, s.Dh)))
+            continue
         lw = layer_weights(l, use_exit)
         st = rec_layers[l]
         h_in = st["h_in"]
-        h_next = rec_layers[l + 1]["h_in"] if l + 1 < L else h_out
+        h_next = rec_layers[l + 1]["h_in"] if l + 1 < last_run else h_out
         tag = f"layer {l} ({'exit' if use_exit else 'backbone'})"
 
         # RMSNorm -> q|k|v -> RoPE; q stored, k/v in the cache slot of layer l
@@ -167,9 +191,12 @@ def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, 
         bo = np.empty((R, s.Hq, s.Dh))
         for r in range(R):
             b, p = bidx[r], pos[r]
+            keep = np.arange(p + 1)
+            if strategy == "kv_mask":
+                keep = keep[(keep >= start) | (np.asarray(pos_E)[:p + 1] > l)]
             for h in range(s.Hq):
                 j = (h * s.Hkv) // s.Hq
-                eo[r, h], bo[r, h] = attention_row(q[r, h], kc[l, b, j, :p + 1], vc[l, b, j, :p + 1], scale)
+                eo[r, h], bo[r, h] = attention_row(q[r, h], kc[l, b, j, keep], vc[l, b, j, keep], scale)
         rep.bf16(f"attn[{tag}]", st["attn"].reshape(R, s.Hq, s.Dh), eo, bo)
 
         # o projection + residual (fp32 stored)
@@ -194,17 +221,17 @@ def check_pass(shape, layer_weights, E, rec_layers, h_out, kc, vc, B, n, start, 
         rep.f32(f"h_out[{tag}]", h_next, e2, bd + 2 * U32 * (np.abs(st["h_mid"]) + np.abs(e2)))
 
         # exit test after backbone layers except the last
-        if l < L - 1 and l < E:
+        if l < L - 1 and l < E and not forced:
             cos = ro.cosine_rows(h_in, h_next)
             m = float(cos.min())
             gm = float(trace[l])
             assert abs(gm - m) <= COS_TOL, f"{tag}: recorded min cos {gm} vs {m} from the stored states"
             exited = l == E - 1
-            if exited:
+            if exited and E != cap:
                 assert m > tau - COS_TOL, f"{tag}: exited with min cos {m} <= tau {tau}"
             else:
                 assert m <= tau + COS_TOL, f"{tag}: did not exit with min cos {m} > tau {tau}"
-    if E < L:
+    if E < L and not forced:
         assert E >= 1 and (E - 1) < len(trace), f"exit layer E={E} without a test before it"
 
     # final RMSNorm + LM head on the last row of every sequence
