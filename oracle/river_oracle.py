@@ -387,8 +387,16 @@ class RiverOracle:
     #              the sequence: a decode step also exits on reaching the
     #              previous pass's E, so every layer a token runs holds K/V
     #              for all earlier positions.
+    #   recompute  they are skipped; each position keeps its state at its
+    #              exit, and when a later pass runs layer l, the earlier
+    #              positions that lack layer l's K/V run layer l (backbone)
+    #              as extra rows of that pass, their state advancing with it.
+    #              A position's depth (the layers it holds K/V for) is the
+    #              largest E of the passes from its own on, so it never grows
+    #              along the sequence and the rows missing at layer l are the
+    #              last positions before the current one.
     #   In every strategy but river the logits come from the exit state.
-    KV_STRATEGIES = ("river", "kv_mask", "propagate", "mono")
+    KV_STRATEGIES = ("river", "kv_mask", "propagate", "mono", "recompute")
 
     def set_kv_strategy(self, name):
         if name not in self.KV_STRATEGIES:
@@ -400,6 +408,10 @@ class RiverOracle:
         self.batch = None
         self.last_E = self.s.L
         self.pos_E = np.full(self.max_seq, self.s.L, dtype=np.int64)
+        # recompute: each position's depth and its state at the input of
+        # that depth's layer
+        self.depth = np.full(self.max_seq, self.s.L, dtype=np.int64)
+        self.h_state = np.zeros((self.max_batch, self.max_seq, self.s.d), dtype=np.float64)
 
     # -- one pass over all layers ------------------------------------------
     def _run(self, tokens, start, tau, force_E, record):
@@ -430,7 +442,21 @@ class RiverOracle:
             if strat == "kv_mask":
                 present = self.pos_E > l                       # earlier positions holding layer l
                 present[start:] = True
-            h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B], rec, present)
+            pend = np.nonzero(self.depth[:start] <= l)[0] if strat == "recompute" else ()
+            if len(pend):
+                # the earlier positions without layer l's K/V go through layer
+                # l together with this pass's rows
+                q0 = int(pend[0])
+                assert np.array_equal(pend, np.arange(q0, start)), "missing rows are not a suffix"
+                rows = np.concatenate([self.h_state[:B, q0:start], h], axis=1)
+                out = decoder_layer(s, lw, rows, q0, self.k_cache[l, :B], self.v_cache[l, :B], rec)
+                self.h_state[:B, q0:start] = out[:, :start - q0]
+                self.depth[q0:start] = l + 1
+                h_out = out[:, start - q0:]
+                if record:
+                    rec = {k: v[:, start - q0:] for k, v in rec.items()}
+            else:
+                h_out = decoder_layer(s, lw, h, start, self.k_cache[l, :B], self.v_cache[l, :B], rec, present)
             if record:
                 inputs.append(rec)
             if force_E is None:
@@ -447,6 +473,8 @@ class RiverOracle:
             E = int(force_E)
         self.last_E = E
         self.pos_E[start:start + n] = E
+        self.depth[start:start + n] = E
+        self.h_state[:B, start:start + n] = h
         w_lm = self.w["embed"] if self.w["lm_head"] is None else self.w["lm_head"]
         logits = lm_head(s, h[:, -1], self.w["final_norm"], w_lm)
         res = {"logits": logits, "next": greedy(logits), "E": E, "trace": trace, "h_final": h}

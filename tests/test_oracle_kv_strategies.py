@@ -3,7 +3,8 @@ KV-shared exit; the lead page's section 2 describes them in a sentence each):
 kv_mask (layers past the exit are skipped, later tokens leave out the K/V
 that are missing), propagate (layers past the exit only compute their K/V
 from the exit state), mono (skipped as well, the exit layer never increases
-along the sequence)."""
+along the sequence), recompute (skipped, and the missing K/V are computed by
+running the earlier positions through a layer when a later pass reaches it)."""
 import math
 
 import numpy as np
@@ -13,7 +14,7 @@ import synth
 from oracle import river_oracle as ro
 from test_oracle_invariants import B, T, prompt, textbook_last_logits
 
-STRATS = ("kv_mask", "propagate", "mono")
+STRATS = ("kv_mask", "propagate", "mono", "recompute")
 
 
 def make(tiny_np, strat, max_seq=T + 6):
@@ -123,3 +124,52 @@ def test_mono_exit_layer_never_increases(tiny_np):
     # the river with the same taus goes back to the full depth
     rr = run(make(tiny_np, "river"), [0.5, 1.5, 1.5, -1.5, 1.5])
     assert rr[1]["E"] == o.s.L
+
+
+def test_recompute_completes_to_the_backbone(tiny_np):
+    """recompute with forced exits: after every pass, each (layer, position)
+    that the position's depth covers holds exactly the K/V of the plain
+    backbone decoder fed the same tokens, the depth never grows along the
+    sequence, and a pass that runs every layer completes the whole cache and
+    gives the backbone's logits."""
+    L = synth.TINY.n_layers
+    plan = [2, 1, 3, 1, 2, L]
+    o = make(tiny_np, "recompute", max_seq=T + len(plan) + 1)
+    bb = make(tiny_np, "river", max_seq=T + len(plan) + 1)
+    r = o.prefill(prompt(), 0.5, force_E=1)
+    rb = bb.prefill(prompt(), 0.5, force_E=L)
+    nxt = r["next"]
+
+    def same_where_deep(upto):
+        for p in range(upto):
+            for l in range(int(o.depth[p])):
+                for a, b in ((o.k_cache, bb.k_cache), (o.v_cache, bb.v_cache)):
+                    assert np.allclose(a[l, :, :, p], b[l, :, :, p], rtol=1e-12, atol=1e-12), (l, p)
+
+    same_where_deep(T)
+    assert np.all(o.depth[:T] == 1)
+    for i, fe in enumerate(plan):
+        r = o.decode_step(nxt, 0.5, force_E=fe)
+        rb = bb.decode_step(nxt, 0.5, force_E=L)
+        pos = T + i
+        assert o.depth[pos] == fe
+        assert np.all(np.diff(o.depth[:pos + 1]) <= 0), o.depth[:pos + 1]
+        # every earlier position now holds at least this pass's depth
+        assert np.all(o.depth[:pos + 1] >= fe)
+        same_where_deep(pos + 1)
+        nxt = r["next"]
+    assert np.all(o.depth[:T + len(plan)] == L)
+    assert np.allclose(r["logits"], rb["logits"], rtol=1e-12, atol=1e-12)
+
+
+def test_recompute_batches_only_missing_rows(tiny_np):
+    """After a prompt that exits at 2, a pass that runs 3 layers recomputes
+    layer 2 for every prompt position and nothing at layers 0 and 1 (their
+    cached K/V stay bit for bit); the positions' depth becomes 3."""
+    o = make(tiny_np, "recompute")
+    r = o.prefill(prompt(), 0.5, force_E=2)
+    k0 = o.k_cache.copy()
+    o.decode_step(r["next"], 0.5, force_E=3)
+    assert np.array_equal(o.k_cache[:2, :, :, :T], k0[:2, :, :, :T])
+    assert not np.array_equal(o.k_cache[2, :, :, :T], k0[2, :, :, :T])
+    assert np.all(o.depth[:T + 1] == 3)
