@@ -46,8 +46,9 @@ def parse():
                     help="comma-separated taus for --tau-sweep and --kv-strategies")
     ap.add_argument("--kv-strategies", action="store_true",
                     help="instead of the benchmark line: decode tokens/s and exit histogram of the "
-                         "method and of the three earlier K/V fixes it is compared with (kv mask, "
-                         "state propagation, mono-decreasing exit) at each tau, as one JSON line")
+                         "method and of the four earlier K/V fixes it is compared with (kv mask, "
+                         "state propagation, mono-decreasing exit, batching recompute) at each tau, "
+                         "as one JSON line")
     ap.add_argument("--exit-mode", default="int4", choices=["int4", "hqq"],
                     help="exit bank of --tau-sweep: min-max int4, or int4 with the HQQ-style zero refinement")
     ap.add_argument("--offload-from", type=int, default=None,
@@ -427,10 +428,23 @@ def strategy_sweep(args):
             bufs[0].copy_(nxt)
             el, hist = timed_steps(r, bufs, logits, tau, W, K)
             mean_E = sum(e * n for e, n in enumerate(hist)) / max(1, sum(hist))
-            rows.append({"tau": tau, "strategy": strategy, "prefill_E": pE,
-                         "decode_tok_s": round(B * K / el, 2), "ms_per_step": round(el / K * 1e3, 4),
-                         "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
-                         "mean_exit_layer": round(mean_E, 3)})
+            row = {"tau": tau, "strategy": strategy, "prefill_E": pE,
+                   "decode_tok_s": round(B * K / el, 2), "ms_per_step": round(el / K * 1e3, 4),
+                   "exit_hist": {str(e): n for e, n in enumerate(hist) if n},
+                   "mean_exit_layer": round(mean_E, 3)}
+            if strategy == "recompute":
+                row["launch"] = "eager, exit layer read back after every step"
+            else:
+                # the same steps launched eagerly (the recompute comparator's mode)
+                r.use_graph(False)
+                r.reset()
+                _, nxt = r.prefill(tokens, tau, want_logits=False)
+                bufs[0].copy_(nxt)
+                el2, _ = timed_steps(r, bufs, logits, tau, W, K)
+                r.use_graph(True)
+                row["launch"] = "graph"
+                row["decode_tok_s_eager"] = round(B * K / el2, 2)
+            rows.append(row)
             print(f"[strategies] {rows[-1]}", file=sys.stderr, flush=True)
     r.close()
     print(json.dumps({"what": "K/V strategies past the exit", "workload": wl.name, "batch": B, "prompt": T,

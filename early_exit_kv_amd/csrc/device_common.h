@@ -196,7 +196,8 @@ __device__ __forceinline__ int past_exit_action(const Control *c, int layer, int
   if (layer < 0) return kRun;
   const int st = c->strategy;
   if (st == kStratRiver) return kRun;
-  const bool past = path == kPathDevice ? layer_uses_exit(c, layer) : path == kPathExit;
+  const bool past = (path == kPathDevice || path == kPathPending) ? layer_uses_exit(c, layer)
+                                                                  : path == kPathExit;
   if (!past) return kRun;
   return st == kStratPropagate ? kKvOnly : kSkip;
 }

@@ -21,6 +21,8 @@ namespace river {
 constexpr int kNormHeld = 8;   // float4 per thread held in registers (d <= 8192)
 
 __global__ __launch_bounds__(256) void rows_norm_kernel(RowsNormParams p) {
+  // (state propagation still normalises the exit state for its k and v)
+  if (p.ctrl && past_exit_action(p.ctrl, p.layer, p.path) == kSkip) return;
   __shared__ float red[4];
   const int64_t r = blockIdx.x;
   const float *h = p.h + r * (p.h_stride ? p.h_stride : (int64_t)p.d);
@@ -53,6 +55,24 @@ __global__ __launch_bounds__(256) void rows_norm_kernel(RowsNormParams p) {
 hipError_t launch_rows_norm(const RowsNormParams &p, hipStream_t s) {
   if (p.d % 4 || p.d > 4 * 256 * kNormHeld) return hipErrorInvalidValue;
   return launch_1(rows_norm_kernel, dim3((unsigned)p.rows), dim3(256), p, s);
+}
+
+__global__ __launch_bounds__(256) void rows_copy_run_kernel(float4 *__restrict__ dst, const float4 *__restrict__ src,
+                                                            int64_t n4, const Control *ctrl, int layer, int path) {
+  if (past_exit_action(ctrl, layer, path) != kRun) return;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_rows_copy_run(float *dst, const float *src, int64_t n, const Control *ctrl, int layer,
+                                int path, hipStream_t s) {
+  if (n % 4 || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16)
+    return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
+  hipLaunchKernelGGL(rows_copy_run_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<float4 *>(dst),
+                     reinterpret_cast<const float4 *>(src), n4, ctrl, layer, path);
+  return hipGetLastError();
 }
 
 // ===========================================================================
@@ -233,7 +253,7 @@ __device__ void tile_epilogue(const GemmParams &p, const float *Cs, int cs, int 
       const int L0 = colblk * BN + 2 * pp;
       if (m >= p.M || L0 >= p.N) continue;
       int b, t;
-      if (p.T > 0) { b = (int)(m / p.T); t = (int)(m % p.T); }
+      if (p.T > 0) { b = (int)(m / p.T); t = (int)(m % p.T) + p.start; }
       else { b = (int)m; t = p.ctrl->pos; }
       const int P = L0 >> 1;
       const int hh = P / half, i = P % half;
@@ -297,11 +317,14 @@ __device__ __forceinline__ bool past_exit_skip(const GemmParams &p, int colblk, 
   const int action = past_exit_action(p.ctrl, p.layer, p.path);
   if (action == kRun) return false;
   if constexpr (EP == kEpResid) {
+    // the residual stream passes through (rows of earlier positions under the
+    // recompute comparator: nothing is written back past the exit)
+    if (p.path == kPathPending || p.h_out == p.h_in) return true;
     const int64_t nb = (int64_t)gridDim.x * gridDim.y * blockDim.x;
     const int64_t i0 = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
     for (int64_t idx = i0; idx < (int64_t)p.M * p.N; idx += nb) {
       const int64_t o = (idx / p.N) * p.h_io_stride + idx % p.N;
-      if (p.h_out != p.h_in) p.h_out[o] = p.h_in[o];
+      p.h_out[o] = p.h_in[o];
     }
     return true;
   } else if constexpr (EP == kEpQKV) {
@@ -491,6 +514,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
   const int t = qb * 64 + r;
   const bool live = t < p.T;
   const int64_t qrow = (int64_t)b * p.T + t;
+  const int tpos = p.start + t;               // the query's position
   float q[SL], acc[SL];
 #pragma unroll
   for (int e = 0; e < SL; ++e) { q[e] = 0.f; acc[e] = 0.f; }
@@ -504,7 +528,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
     }
   }
   float mrun = -INFINITY, lrun = 0.f;
-  const int kend = min(p.T, qb * 64 + 64);  // keys needed by this block
+  const int kend = p.start + min(p.T, qb * 64 + 64);  // keys needed by this block
   const int64_t kvbase = (((int64_t)b * p.Hkv + kvh) * p.S) * DH;
   for (int k0 = 0; k0 < kend; k0 += KT) {
     __syncthreads();
@@ -528,7 +552,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
       for (int e = 0; e < SL; ++e) d = fmaf(q[e], bf2f(Ks[j][part * SL + e]), d);
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
-      const bool ok = live && (k0 + j) <= t;
+      const bool ok = live && (k0 + j) <= tpos;
       sc[j] = ok ? d * p.scale : -INFINITY;
       tmax = fmaxf(tmax, sc[j]);
     }
@@ -596,8 +620,10 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, c16 = lane & 15;
   const int q0 = qb * 64;
-  const int my_q = q0 + 16 * wid + c16;         // this lane's query position
-  const int kend = min(p.T, q0 + 64);           // key positions the workgroup needs
+  const int my_q = q0 + 16 * wid + c16;         // this lane's query row
+  const int qpos = p.start + my_q;              // and its position
+  const int kall = p.start + p.T;               // key positions in the cache
+  const int kend = p.start + min(p.T, q0 + 64); // key positions the workgroup needs
   const int ntiles = (kend + KT - 1) / KT;
   const int64_t kvbase = ((int64_t)b * p.Hkv + kvh) * p.S * DH;
   const uint16_t *Kg = p.k_cache + kvbase, *Vg = p.v_cache + kvbase;
@@ -621,7 +647,7 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int ch = tid + 256 * u, r = ch / CPR, cc = ch % CPR;
-      const int pos = min(kt * KT + r, p.T - 1);   // past the prompt: masked below
+      const int pos = min(kt * KT + r, kall - 1);  // past the last key: masked below
       kr[u] = *reinterpret_cast<const uint4 *>(Kg + (int64_t)pos * DH + 8 * cc);
       vr[u] = *reinterpret_cast<const uint4 *>(Vg + (int64_t)pos * DH + 8 * cc);
     }
@@ -685,7 +711,7 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kt * KT + 16 * kk + 4 * q + i;
-          const bool ok = key <= my_q && key < p.T;
+          const bool ok = key <= qpos && key < kall;
           sv[4 * kk + i] = ok ? sc[kk][i] * scale2 : -INFINITY;
           mx = fmaxf(mx, sv[4 * kk + i]);
         }

@@ -171,6 +171,11 @@ struct river_ctx {
   int attn_kind = 0;    // RIVER_OPT_ATTN
   std::vector<char> remote;   // per layer: backbone linears in host memory (offloaded)
   int strategy = kStratRiver; // RIVER_OPT_KV_STRATEGY
+  // recompute comparator (one sequence): per position, its state at the
+  // input of the first layer it holds no K/V for (caller-owned, fp32
+  // [max_seq][d_model]), and that depth (non-increasing along the sequence)
+  float *kv_state = nullptr;
+  std::vector<int> depth;
 };
 
 namespace {
@@ -249,6 +254,11 @@ uint16_t *v_layer(river_ctx *ctx, int l) {
   do {                                       \
     hipError_t e_ = (expr);                  \
     if (e_ != hipSuccess) return RIVER_E_HIP; \
+  } while (0)
+#define RV_TRY_RC(expr)                 \
+  do {                                  \
+    const int rc_ = (expr);             \
+    if (rc_ != RIVER_OK) return rc_;    \
   } while (0)
 
 hipEvent_t take_event(river_ctx *ctx) {
@@ -427,6 +437,68 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
   return RIVER_OK;
 }
 
+// Recompute comparator: layer l (backbone) for the n earlier positions
+// q0 .. q0+n-1 that hold no K/V at l, as rows of one prefill-style pass
+// (positions offset by q0, causal attention over the cache), their states
+// read from and written back to kv_state.  Every launch does nothing once
+// the current pass is past its exit at l.  Rows 1.. of the workspace (row 0
+// is the current token's).
+int enqueue_pending_rows(river_ctx *ctx, int l, int q0, int n) {
+  const river_config &c = ctx->cfg;
+  hipStream_t s = ctx->stream;
+  const river_layer_w &L = ctx->layers[l];
+  const int qd = c.n_q_heads * c.head_dim;
+  float *H = ctx->kv_state + (int64_t)q0 * c.d_model;
+  float *hC = at<float>(ctx->ws, ctx->wl.hB) + c.d_model;
+  uint16_t *x = at<uint16_t>(ctx->ws, ctx->wl.x) + c.d_model;
+  GemmParams g{};
+  g.M = n; g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl;
+  g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim; g.max_seq = c.max_seq;
+  g.max_batch = c.max_batch; g.T = n; g.start = q0; g.rope_theta = c.rope_theta;
+  g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
+  g.path = kPathPending;
+
+  RowsNormParams rn{H, x, static_cast<const uint16_t *>(L.attn_norm), n, c.d_model, c.rms_eps, 0,
+                    ctx->ctrl, l, kPathPending};
+  TIMED(RIVER_K_P_NORM, launch_rows_norm(rn, s));
+  GemmParams q = g;
+  fill_weights(ctx, l, 0, 3, q.w);
+  q.N = qd + 2 * c.n_kv_heads * c.head_dim; q.K = c.d_model; q.x = x; q.ldx = c.d_model;
+  q.q_out = at<uint16_t>(ctx->ws, ctx->wl.q) + qd;
+  q.k_cache = k_layer(ctx, l); q.v_cache = v_layer(ctx, l);
+  TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpQKV, q, s));
+
+  AttnPrefillParams ap{};
+  ap.q = q.q_out; ap.k_cache = q.k_cache; ap.v_cache = q.v_cache;
+  ap.out = at<uint16_t>(ctx->ws, ctx->wl.attn) + qd; ap.B = 1; ap.T = n; ap.start = q0;
+  ap.Hq = c.n_q_heads; ap.Hkv = c.n_kv_heads; ap.Dh = c.head_dim; ap.S = c.max_seq;
+  ap.scale = 1.0f / std::sqrt((float)c.head_dim);
+  ap.mfma = ctx->attn_kind == 0;
+  ap.ctrl = ctx->ctrl; ap.layer = l; ap.path = kPathPending;
+  TIMED(RIVER_K_P_ATTN, launch_attn_prefill(ap, s));
+
+  GemmParams o = g;
+  fill_weights(ctx, l, 3, 1, o.w);
+  o.N = c.d_model; o.K = qd; o.x = ap.out; o.ldx = qd;
+  o.h_in = H; o.h_out = hC; o.h_io_stride = c.d_model;
+  TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, o, s));
+  RowsNormParams rn2{hC, x, static_cast<const uint16_t *>(L.mlp_norm), n, c.d_model, c.rms_eps, 0,
+                     ctx->ctrl, l, kPathPending};
+  TIMED(RIVER_K_P_NORM, launch_rows_norm(rn2, s));
+  GemmParams gu = g;
+  fill_weights(ctx, l, 4, 2, gu.w);
+  gu.N = 2 * c.ffn_dim; gu.K = c.d_model; gu.x = x; gu.ldx = c.d_model;
+  gu.u_out = at<uint16_t>(ctx->ws, ctx->wl.u) + c.ffn_dim;
+  TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpSwiGLU, gu, s));
+  GemmParams dn = g;
+  fill_weights(ctx, l, 6, 1, dn.w);
+  dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
+  dn.h_in = hC; dn.h_out = hC; dn.h_io_stride = c.d_model;
+  TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, dn, s));
+  RV_TRY(launch_rows_copy_run(H, hC, (int64_t)n * c.d_model, ctx->ctrl, l, kPathPending, s));
+  return RIVER_OK;
+}
+
 // Enqueue one decode step (B <= 8 rows): GEMV linears + split-K attention.
 //
 // only >= 0 (a RIVER_K_* layer kernel class) enqueues nothing but that class's
@@ -476,6 +548,15 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
     TIMED_ONLY(RIVER_K_QKV, launch_gemv(kXNorm, kEpQKV, q, s));
     RV_TRY(rec.put(l, rec.lay.q, q.q_out, qbytes));
+    if (ctx->strategy == kStratRecompute && only < 0) {
+      // (this layer's exit decision is taken by now: the launch above made it)
+      const int pos = ctx->pos;
+      const int q0 = (int)(std::partition_point(ctx->depth.begin(), ctx->depth.begin() + pos,
+                                                [l](int d) { return d > l; }) - ctx->depth.begin());
+      // (with the exit forced the host knows which layers run)
+      if (q0 < pos && (ctx->force_E < 0 || l < ctx->force_E))
+        RV_TRY_RC(enqueue_pending_rows(ctx, l, q0, pos - q0));
+    }
 
     AttnParams a{};
     a.q = q.q_out; a.k_cache = q.k_cache; a.v_cache = q.v_cache;
@@ -528,6 +609,9 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
   TIMED_ONLY(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
   if (ctx->strategy == kStratMask && only < 0)
     RV_TRY(launch_set_pos_E(ctx->ctrl, control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads), 0, s));
+  if (ctx->strategy == kStratRecompute && only < 0)   // this position's state at its exit
+    RV_TRY(hipMemcpyAsync(ctx->kv_state + (int64_t)ctx->pos * c.d_model, hA, (size_t)c.d_model * 4,
+                          hipMemcpyDeviceToDevice, s));
   return RIVER_OK;
 }
 
@@ -558,7 +642,8 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     if (ctx->force_E >= 0) g.path = l >= ctx->force_E ? kPathExit : kPathBackbone;
 
     RV_TRY(rec.put(l, rec.lay.h_in, hA, hbytes));
-    RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), R, c.d_model, c.rms_eps};
+    RowsNormParams rn{hA, x, static_cast<const uint16_t *>(L.attn_norm), R, c.d_model, c.rms_eps, 0,
+                      ctx->ctrl, l, g.path};
     TIMED(RIVER_K_P_NORM, launch_rows_norm(rn, s));
 
     GemmParams q = g;
@@ -586,7 +671,8 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, o, s));
     RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
-    RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), R, c.d_model, c.rms_eps};
+    RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), R, c.d_model, c.rms_eps, 0,
+                       ctx->ctrl, l, g.path};
     TIMED(RIVER_K_P_NORM, launch_rows_norm(rn2, s));
 
     GemmParams gu = g;
@@ -610,6 +696,8 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     std::swap(hA, hB);
   }
   RV_TRY(rec.put(-1, 0, hA, hbytes));
+  if (ctx->strategy == kStratRecompute)   // (one sequence) every prompt position's state at the exit
+    RV_TRY(hipMemcpyAsync(ctx->kv_state, hA, (size_t)T * c.d_model * 4, hipMemcpyDeviceToDevice, s));
   if (B > 8) {
     const int st = enqueue_lm_head_rows(ctx, hA + (int64_t)(T - 1) * c.d_model, (int64_t)T * c.d_model, B,
                                         logits, next, 1);
@@ -631,6 +719,19 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
   TIMED(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
   if (ctx->strategy == kStratMask)
     RV_TRY(launch_set_pos_E(ctx->ctrl, control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads), T, s));
+  return RIVER_OK;
+}
+
+// Recompute comparator: the pass just enqueued exited at E (read back: the
+// next pass's launches depend on it); positions up to `last` hold at least
+// E layers now, `first` .. `last` exactly E if they held fewer.
+int note_depth(river_ctx *ctx, int first, int last) {
+  int32_t E = 0;
+  RV_TRY(hipMemcpyAsync(&E, &ctx->ctrl->last_E, sizeof(E), hipMemcpyDeviceToHost, ctx->stream));
+  RV_TRY(hipStreamSynchronize(ctx->stream));
+  if ((int)ctx->depth.size() < ctx->cfg.max_seq) ctx->depth.assign(ctx->cfg.max_seq, ctx->cfg.n_layers);
+  for (int p = first; p <= last; ++p) ctx->depth[p] = E;
+  for (int p = first - 1; p >= 0 && ctx->depth[p] < E; --p) ctx->depth[p] = E;
   return RIVER_OK;
 }
 
@@ -837,6 +938,8 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
   if (B < 1 || T < 1 || B > ctx->cfg.max_batch || T > ctx->cfg.max_seq) return RIVER_E_RANGE;
   if (ctx->rec && record_layout(ctx->cfg, (int64_t)B * T).total > ctx->rec_bytes)
     return RIVER_E_BAD_SIZE;
+  if (ctx->strategy == kStratRecompute && B != 1) return RIVER_E_UNIMPLEMENTED;
+  if (ctx->strategy == kStratRecompute && !ctx->kv_state) return RIVER_E_STATE;
   const int st = enqueue_prefill(ctx, d_tokens, B, T, tau, d_logits, d_next);
   // its begin kernel wrote tau (after a failure the value is unknown: a bit
   // pattern no finite tau has makes the next decode step write it again)
@@ -847,6 +950,10 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
   if (st != RIVER_OK) return st;
   ctx->pos = T;
   ctx->batch = B;
+  if (ctx->strategy == kStratRecompute) {
+    ctx->depth.assign(ctx->cfg.max_seq, ctx->cfg.n_layers);
+    RV_TRY_RC(note_depth(ctx, 0, T - 1));
+  }
   return RIVER_OK;
 }
 
@@ -862,6 +969,11 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
   // kv mask on the matrix-core attention
   if (ctx->strategy != kStratRiver && ctx->batch > 8) return RIVER_E_UNIMPLEMENTED;
   if (ctx->strategy == kStratMask && ctx->attn_kind != 0) return RIVER_E_UNIMPLEMENTED;
+  // the recompute comparator: one sequence, a state buffer, and a prefill
+  // under the same strategy before its steps
+  const bool recompute = ctx->strategy == kStratRecompute;
+  if (recompute && ctx->batch != 1) return RIVER_E_UNIMPLEMENTED;
+  if (recompute && (!ctx->kv_state || (int)ctx->depth.size() < ctx->cfg.max_seq)) return RIVER_E_STATE;
   // the step reads tau from the control block: write it when it changes
   uint32_t tau_bits;
   std::memcpy(&tau_bits, &tau, 4);
@@ -869,7 +981,9 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
     RV_TRY(launch_set_tau(ctx->ctrl, tau, ctx->stream));
     ctx->ctrl_tau_bits = tau_bits;
   }
-  if (ctx->use_graph && !ctx->profiling && !ctx->rec && ctx->stream != nullptr) {
+  // (recompute: the launches of a step depend on the exits of the earlier
+  // passes, so its steps run eagerly)
+  if (ctx->use_graph && !ctx->profiling && !ctx->rec && ctx->stream != nullptr && !recompute) {
     const river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E};
     auto it = ctx->graphs.find(key);
     if (it == ctx->graphs.end()) {
@@ -892,6 +1006,7 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
     const int st = enqueue_decode(ctx, d_tokens, tau, d_logits, d_next);
     if (st != RIVER_OK) return st;
   }
+  if (recompute) RV_TRY_RC(note_depth(ctx, ctx->pos, ctx->pos));
   ctx->pos += 1;
   return RIVER_OK;
 }
@@ -949,8 +1064,9 @@ int river_set_option(river_ctx *ctx, int32_t option, int64_t value) {
       drop_graphs(ctx);
       return RIVER_OK;
     case RIVER_OPT_KV_STRATEGY:
-      if (value < kStratRiver || value > kStratMono) return RIVER_E_INVALID_ARG;
+      if (value < kStratRiver || value > kStratRecompute) return RIVER_E_INVALID_ARG;
       ctx->strategy = (int)value;
+      ctx->depth.clear();   // (a recompute sequence starts at its prefill)
       drop_graphs(ctx);
       return RIVER_OK;
     case RIVER_OPT_PROFILE:
@@ -1016,10 +1132,21 @@ int river_set_record(river_ctx *ctx, void *d_buf, size_t bytes) {
   return RIVER_OK;
 }
 
+int river_set_kv_state(river_ctx *ctx, void *d_buf, size_t bytes) {
+  if (!ctx) return RIVER_E_INVALID_ARG;
+  if (d_buf && (bytes < (size_t)ctx->cfg.max_seq * ctx->cfg.d_model * 4 ||
+                reinterpret_cast<uintptr_t>(d_buf) % 16))
+    return RIVER_E_BAD_SIZE;
+  ctx->kv_state = static_cast<float *>(d_buf);
+  ctx->depth.clear();
+  return RIVER_OK;
+}
+
 int river_reset(river_ctx *ctx) {
   if (!ctx) return RIVER_E_INVALID_ARG;
   ctx->pos = 0;
   ctx->batch = 0;
+  ctx->depth.clear();
   return RIVER_OK;
 }
 

@@ -47,12 +47,13 @@ struct Control {
 };
 
 // What the layers at and past the exit do (RIVER_OPT_KV_STRATEGY): run as
-// exit layers (the method), or, as comparators, three prior fixes of the
+// exit layers (the method), or, as comparators, four prior fixes of the
 // missing K/V of early-exited tokens: skipped with later tokens leaving out
 // the K/V that are missing (kv mask), only their K/V computed from the exit
 // state (state propagation), skipped with the exit layer never increasing
-// along the sequence (mono-decreasing).
-enum KvStrategy { kStratRiver = 0, kStratMask = 1, kStratPropagate = 2, kStratMono = 3 };
+// along the sequence (mono-decreasing), skipped with the missing K/V computed
+// when a later pass reaches the layer (batching recompute).
+enum KvStrategy { kStratRiver = 0, kStratMask = 1, kStratPropagate = 2, kStratMono = 3, kStratRecompute = 4 };
 
 __host__ __device__ inline size_t control_bytes(int max_batch, int n_kv_heads, int max_seq) {
   size_t b = sizeof(Control);
@@ -117,8 +118,11 @@ constexpr int kPartFloatsPerWG = 3 * 64;  // B <= 64 rows x (dot, |a|^2, |b|^2)
 // ---------------------------------------------------------------------------
 enum XSource { kXNorm = 0, kXBf16 = 1 };
 enum Epilogue { kEpQKV = 0, kEpResid = 1, kEpResidExit = 2, kEpSwiGLU = 3, kEpLogits = 4, kEpPlain = 5 };
-// weight path of a launch: decided on the device, or fixed (debug entry point)
-enum PathChoice { kPathDevice = 0, kPathBackbone = 1, kPathExit = 2 };
+// weight path of a launch: decided on the device, or fixed (debug entry point,
+// forced exit).  kPathPending (the recompute comparator's rows of earlier
+// positions): backbone weights, and the launch does nothing once the current
+// pass is past its exit at this layer.
+enum PathChoice { kPathDevice = 0, kPathBackbone = 1, kPathExit = 2, kPathPending = 3 };
 
 struct LinearWeights {
   const uint16_t *bf[3];   // backbone bf16 segments (or exit bf16 copies)
@@ -237,8 +241,13 @@ hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 struct RowsNormParams {
   const float *h; uint16_t *x; const uint16_t *gain; int64_t rows; int d; float eps;
   int64_t h_stride;   // floats between input rows (0: d)
+  const Control *ctrl; int layer; int path;   // ctrl set: nothing where the layer is skipped past the exit
 };
 hipError_t launch_rows_norm(const RowsNormParams &p, hipStream_t s);
+// dst[i] = src[i] for i < n, unless the current pass is past its exit at
+// `layer` (the path's rule; the recompute comparator's state write-back)
+hipError_t launch_rows_copy_run(float *dst, const float *src, int64_t n, const Control *ctrl, int layer,
+                                int path, hipStream_t s);
 
 struct GemmParams {
   LinearWeights w;
@@ -250,6 +259,7 @@ struct GemmParams {
   const float *h_in; float *h_out; int64_t h_io_stride;
   uint16_t *q_out; uint16_t *k_cache; uint16_t *v_cache;
   int Hq, Hkv, Dh, max_seq, max_batch, T; float rope_theta;
+  int start;                       // T > 0: row t of a sequence sits at position start + t
   const float2 *rope;
   uint16_t *u_out;
   int path;                        // PathChoice
@@ -283,6 +293,7 @@ struct AttnPrefillParams {
   float scale;
   int mfma;                // 1: the matrix-core (flash-style) kernel, 0: the vector-ALU one
   Control *ctrl; int layer; int path;   // past the exit in the comparators: return at once
+  int start;               // query row t sits at position start + t and sees keys 0 .. start + t
 };
 hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s);
 

@@ -18,7 +18,7 @@ RIVER_E_RANGE, RIVER_E_HIP, RIVER_E_UNIMPLEMENTED = 4, 5, 6
 RIVER_EXIT_INT4, RIVER_EXIT_COPY, RIVER_EXIT_HQQ = 1, 2, 3
 RIVER_OPT_GRAPH, RIVER_OPT_FORCE_E, RIVER_OPT_PROFILE, RIVER_OPT_ATTN_CHUNK, RIVER_OPT_GEMV = 1, 2, 3, 4, 5
 RIVER_OPT_ATTN, RIVER_OPT_KV_STRATEGY = 6, 7
-KV_STRATEGIES = ("river", "kv_mask", "propagate", "mono")
+KV_STRATEGIES = ("river", "kv_mask", "propagate", "mono", "recompute")
 KERNEL_KINDS = ("begin", "qkv", "attn", "o", "gateup", "down", "lm_head",
                 "p_norm", "p_gemm", "p_attn", "p_cos")
 RIVER_MAX_LAYERS = 256
@@ -30,7 +30,7 @@ EXPORTS = (
     "river_prefill", "river_decode_step", "river_exit_stats", "river_set_option",
     "river_reset", "river_destroy", "river_strerror", "river_profile_read",
     "river_debug_linear", "river_record_bytes", "river_set_record", "river_time_kernel",
-    "river_debug_linear_noalloc",
+    "river_debug_linear_noalloc", "river_set_kv_state",
 )
 
 
@@ -115,6 +115,7 @@ def load_library(path=LIB_PATH):
         "river_record_bytes": (ctypes.c_int, [ctypes.POINTER(RiverConfig), i32, ctypes.POINTER(ctypes.c_size_t)]),
         "river_set_record": (ctypes.c_int, [P, P, ctypes.c_size_t]),
         "river_time_kernel": (ctypes.c_int, [P, i32, i32, ctypes.POINTER(ctypes.c_double)]),
+        "river_set_kv_state": (ctypes.c_int, [P, P, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -316,7 +317,13 @@ class River:
 
     def kv_strategy(self, name):
         """Layers at and past the exit: "river" (exit layers, the method) or a
-        comparator: "kv_mask", "propagate", "mono" (see include/river.h)."""
+        comparator: "kv_mask", "propagate", "mono", "recompute" (see
+        include/river.h; "recompute" attaches a state buffer of max_seq rows)."""
+        if name == "recompute" and getattr(self, "kv_state", None) is None:
+            c = self.cfg
+            self.kv_state = torch.empty(c.max_seq * c.d_model, dtype=torch.float32, device=self.ws.device)
+            _check(self.lib.river_set_kv_state(self.ctx, _ptr(self.kv_state), self.kv_state.numel() * 4),
+                   "river_set_kv_state")
         self.set_option(RIVER_OPT_KV_STRATEGY, KV_STRATEGIES.index(name))
 
     def attn_kind(self, kind):

@@ -254,7 +254,7 @@ enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_
 /* RIVER_OPT_KV_STRATEGY: what the layers at and past the exit (E .. L-1) do.
  *   RIVER_KV_RIVER (default): they run as their exit layers and write their
  *     K/V into the shared cache (the method, lead page section 3);
- *   speed comparators, three of the earlier fixes for the K/V that an
+ *   speed comparators, four of the earlier fixes for the K/V that an
  *   early-exited token leaves missing (section 2), the logits then coming
  *   from the exit state:
  *   RIVER_KV_MASK: they are skipped; deeper layers of later tokens leave out
@@ -263,11 +263,19 @@ enum { RIVER_OPT_GRAPH = 1, RIVER_OPT_FORCE_E = 2, RIVER_OPT_PROFILE = 3, RIVER_
  *     RMSNorm gain, backbone k and v projections, RoPE), no attention, no MLP;
  *   RIVER_KV_MONO: they are skipped, and a decode step also exits on reaching
  *     the previous pass's E, so the exit layer never increases along the
- *     sequence.
+ *     sequence;
+ *   RIVER_KV_RECOMPUTE: they are skipped; when a later decode step runs a
+ *     layer, the earlier positions that hold no K/V there run that layer
+ *     (backbone) first, as rows of one prefill-style pass, their states kept
+ *     in the buffer river_set_kv_state attaches.  One sequence (batch 1); its
+ *     steps run eagerly and read the exit layer back to the host (the next
+ *     step's launches depend on it).
  * Decode steps of more than 8 rows take only RIVER_KV_RIVER
  * (RIVER_E_UNIMPLEMENTED); the activation record of a skipped layer holds
- * nothing of the pass. */
-enum { RIVER_KV_RIVER = 0, RIVER_KV_MASK = 1, RIVER_KV_PROPAGATE = 2, RIVER_KV_MONO = 3 };
+ * nothing of the pass.  Setting the option starts no sequence: a prefill
+ * under the strategy comes before its decode steps. */
+enum { RIVER_KV_RIVER = 0, RIVER_KV_MASK = 1, RIVER_KV_PROPAGATE = 2, RIVER_KV_MONO = 3,
+       RIVER_KV_RECOMPUTE = 4 };
 int river_set_option(river_ctx *ctx, int32_t option, int64_t value);
 
 /* Kernel classes timed when RIVER_OPT_PROFILE is 1 (decode steps then launch
@@ -356,6 +364,15 @@ int river_debug_linear_noalloc(river_ctx *ctx, int32_t layer, int32_t linear, in
  * RIVER_E_BAD_SIZE before launching anything. */
 int river_record_bytes(const river_config *cfg, int32_t rows, size_t *bytes);
 int river_set_record(river_ctx *ctx, void *d_buf, size_t bytes);
+
+/* State buffer of the recompute comparator (RIVER_KV_RECOMPUTE): device
+ * memory of at least max_seq * d_model * 4 bytes, 16-byte aligned, owned by
+ * the caller and used until it is replaced or the context is destroyed.  It
+ * holds, per position of the one sequence, the fp32 residual stream at the
+ * input of the first layer that position holds no K/V for.  NULL detaches it.
+ * A prefill or decode step under RIVER_KV_RECOMPUTE without it returns
+ * RIVER_E_STATE; RIVER_E_BAD_SIZE for a smaller or misaligned buffer. */
+int river_set_kv_state(river_ctx *ctx, void *d_buf, size_t bytes);
 
 /* Start a new sequence: position back to 0 (statistics are kept). */
 int river_reset(river_ctx *ctx);

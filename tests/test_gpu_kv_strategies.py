@@ -33,6 +33,24 @@ class _Sub:
         self.v_cache = orc.v_cache[l:l + 1]
 
 
+def snapshot(orc):
+    """The oracle's sequence state (a replayed pass must start from it: the
+    recompute strategy moves earlier positions' states and depths)."""
+    return {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in vars(orc).items()
+            if k in ("k_cache", "v_cache", "depth", "h_state", "pos_E", "pos", "last_E")}
+
+
+def restore(orc, snap):
+    for k, v in snap.items():
+        setattr(orc, k, v.copy() if isinstance(v, np.ndarray) else v)
+
+
+def compare_kv_deep(gk, gv, orc, L, B, upto):
+    """Every (layer, position) the oracle's depth covers (recompute)."""
+    for p in range(upto):
+        compare_kv_layers(gk, gv, orc, range(int(orc.depth[p])), B, [p])
+
+
 def run_strategy(tiny, strategy, tau, steps, B=2, T=32, gemv="auto", graph=True):
     rv = _river()
     s = synth.TINY
@@ -65,9 +83,10 @@ def run_strategy(tiny, strategy, tau, steps, B=2, T=32, gemv="auto", graph=True)
         tok.copy_(torch.from_numpy(nxt.astype(np.int32)))
         gl, gn = r.decode_step(tok, tau)
         st = r.exit_stats()
+        snap = snapshot(orc)
         o = orc.decode_step(nxt, tau)
         if check_decision(st["last_E"], st["last_trace"], o, tau, L):
-            orc.pos -= 1
+            restore(orc, snap)
             o = orc.decode_step(nxt, tau, force_E=st["last_E"])
         compare_logits(gl.cpu().numpy(), o["logits"])
         for b in range(B):
@@ -78,6 +97,8 @@ def run_strategy(tiny, strategy, tau, steps, B=2, T=32, gemv="auto", graph=True)
         written = range(L) if strategy in ("river", "propagate") else range(E)
         gk, gv = kv_numpy(r, L, B, pos + 1)
         compare_kv_layers(gk, gv, orc, written, B, [pos])
+        if strategy == "recompute":
+            compare_kv_deep(gk, gv, orc, L, B, pos + 1)
         Es.append(E)
         nxt = o["next"]
     r.close()
@@ -95,6 +116,17 @@ def test_strategy_parity_tiny(tiny, strategy, tau):
         assert all(e == 1 for e in Es)
     if strategy == "mono":
         assert all(a >= b for a, b in zip(Es[1:], Es[2:])), Es
+
+
+@pytest.mark.parametrize("tau", [0.5, -1.5, 1.5, 0.9])
+def test_recompute_parity_tiny(tiny, tau):
+    """One sequence (the recompute comparator runs batch 1)."""
+    L = synth.TINY.n_layers
+    Es = run_strategy(tiny, "recompute", tau, steps=12, B=1, T=33)
+    if tau > 1:
+        assert all(e == L for e in Es)
+    if tau < -1:
+        assert all(e == 1 for e in Es)
 
 
 @pytest.mark.parametrize("strategy", ["kv_mask", "propagate", "mono"])
@@ -140,17 +172,20 @@ def test_kv_mask_varied_exits(tiny):
     r.close()
 
 
-def test_strategies_agree_without_exit(tiny):
+@pytest.mark.parametrize("B", [1, 2])
+def test_strategies_agree_without_exit(tiny, B):
     """With no exit (tau above 1) every strategy runs the same layers: the
-    logits are bitwise those of the method."""
+    logits are bitwise those of the method (recompute: one sequence)."""
     rv = _river()
     s = synth.TINY
     outs = []
     for strategy in rv.KV_STRATEGIES:
-        r = rv.River(s, tiny["cuda"], 2, 40)
+        if strategy == "recompute" and B != 1:
+            continue
+        r = rv.River(s, tiny["cuda"], B, 40)
         r.kv_strategy(strategy)
         r.build_exit_layers("int4")
-        lg, nx = r.prefill(synth.make_tokens(s, 2, 32, seed=0).cuda(), 1.5)
+        lg, nx = r.prefill(synth.make_tokens(s, B, 32, seed=0).cuda(), 1.5)
         seq = [lg.clone()]
         for _ in range(4):
             lg, nx = r.decode_step(nx.clone(), 1.5)
@@ -167,16 +202,21 @@ def test_strategy_option_rejects(tiny):
     r = rv.River(s, tiny["cuda"], 2, 40)
     r.build_exit_layers("int4")
     with pytest.raises(rv.RiverError):
-        r.set_option(rv.RIVER_OPT_KV_STRATEGY, 4)
+        r.set_option(rv.RIVER_OPT_KV_STRATEGY, 5)
     r.kv_strategy("kv_mask")
     r.attn_kind("valu")
     _, nx = r.prefill(synth.make_tokens(s, 2, 32, seed=0).cuda(), 0.5)
     with pytest.raises(rv.RiverError):
         r.decode_step(nx.clone(), 0.5)
+    # recompute: one sequence only
+    r.attn_kind("mfma")
+    r.kv_strategy("recompute")
+    with pytest.raises(rv.RiverError):
+        r.prefill(synth.make_tokens(s, 2, 32, seed=0).cuda(), 0.5)
     r.close()
 
 
-def run_forced(shape, w_dev, w_np, strategy, B, T, plan, chunk=0, prefill_E=None):
+def run_forced(shape, w_dev, w_np, strategy, B, T, plan, chunk=0, prefill_E=None, attn="mfma"):
     """Exits forced per pass (prefill at prefill_E, then plan[i] at decode step
     i) on both sides; logits and the K/V slots the strategy writes compared."""
     rv = _river()
@@ -187,6 +227,7 @@ def run_forced(shape, w_dev, w_np, strategy, B, T, plan, chunk=0, prefill_E=None
           flush=True)
     r = rv.River(sh, w_dev, B, max_seq)
     r.kv_strategy(strategy)
+    r.attn_kind(attn)
     if chunk:
         r.set_option(rv.RIVER_OPT_ATTN_CHUNK, chunk)
     r.build_exit_layers("int4")
@@ -210,8 +251,20 @@ def run_forced(shape, w_dev, w_np, strategy, B, T, plan, chunk=0, prefill_E=None
         written = range(L) if strategy == "propagate" else range(fe)
         gk, gv = kv_numpy(r, L, B, T + step + 1)
         compare_kv_layers(gk, gv, orc, written, B, [T + step])
+        if strategy == "recompute":
+            compare_kv_deep(gk, gv, orc, L, B, T + step + 1)
         nxt = o["next"]
     r.close()
+
+
+@pytest.mark.parametrize("attn", ["mfma", "valu"])
+def test_recompute_forced_exits_tiny(tiny, attn):
+    """A prompt that exits after layer 0, then passes deeper and shallower:
+    150 pending rows at once (every prompt position through layers 1..3),
+    then a few rows at a time, on both attention kernels."""
+    L = synth.TINY.n_layers
+    run_forced(synth.TINY, tiny["cuda"], tiny["np"], "recompute", 1, 150, [2, L, 1, 3, 2, 1, 1, L],
+               prefill_E=1, attn=attn)
 
 
 @pytest.mark.parametrize("strategy", ["kv_mask", "propagate"])
@@ -276,6 +329,10 @@ def run_forced_tf(shape, w_dev, hw, strategy, B, T, plan, chunk=0, prefill_E=Non
         orc.decode_step(nxt, 0.5, force_E=fe)
         written = L if strategy == "propagate" else fe
         kv_cos(kc[:written], vc[:written], orc, written, B, pos, pos + 1)
+        if strategy == "recompute":
+            for p in range(pos + 1):
+                dp = int(orc.depth[p])
+                kv_cos(kc[:dp], vc[:dp], orc, dp, B, p, p + 1)
         nxt = gn.cpu().numpy().astype(np.int64)
     print(f"[kv-strategy] worst: {rep.worst}", flush=True)
     r.close()
@@ -288,12 +345,13 @@ def w8b3():
     return w, host_weights(w)
 
 
-@pytest.mark.parametrize("strategy", ["kv_mask", "propagate", "mono"])
+@pytest.mark.parametrize("strategy", ["kv_mask", "propagate", "mono", "recompute"])
 def test_forced_exits_8b_layer_shapes(w8b3, strategy):
     """Head dim 128, 4 query heads per K/V head, the full vocabulary: the
     decode kernels at the benchmark's launch shapes under each strategy."""
     w, hw = w8b3
-    run_forced_tf(synth.LLAMA_8B, w, hw, strategy, 1, 40, [3, 1, 2, 1, 3], chunk=0, prefill_E=3)
+    plan, pe = ([1, 3, 2, 1, 1, 3], 1) if strategy == "recompute" else ([3, 1, 2, 1, 3], 3)
+    run_forced_tf(synth.LLAMA_8B, w, hw, strategy, 1, 40, plan, chunk=0, prefill_E=pe)
 
 
 def test_forced_exits_8b_split_mask(w8b3):
