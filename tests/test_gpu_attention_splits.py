@@ -62,3 +62,20 @@ def test_attention_splits_8b_batch1(w8b_2, chunk, attn):
 def test_attention_default_chunk_8b_batch32(w8b_2, attn):
     parity_run(synth.LLAMA_8B, w8b_2, B=32, T=1100, steps=2, tau=0.5, attn=attn,
                check_prefill=False, free_running=False)
+
+
+# The long-context workload's shape: 8 rows, 16,384-token prompts, the 8B
+# layer shapes (2 layers), the library's own split (about 1,088 positions,
+# 17 sub-chunks, per workgroup).  Decode steps checked stage by stage against
+# the cache the GPU's prefill wrote (the float64 oracle cannot prefill
+# 131,072 rows in seconds).
+def test_decode_parity_8b_long_context_batch8(w8b_2):
+    parity_run(synth.LLAMA_8B, w8b_2, B=8, T=16384, steps=2, tau=0.5, check_prefill=False,
+               free_running=False)
+
+
+# The 1B workload's prompt length (256 tokens, one row, tied embeddings),
+# prefill and decode checked stage by stage, a free-running oracle beside.
+def test_parity_1b_layer_shapes_prompt256():
+    w = synth.make_weights(synth.LLAMA_1B, seed=0, device="cuda", n_layers=2)
+    parity_run(synth.LLAMA_1B, w, B=1, T=256, steps=3, tau=0.5)
