@@ -1289,7 +1289,6 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
                                            int rowblk, int colblk, f32x4_t (&tot)[ptm<BN>() / 16][4]) {
   constexpr int STEPS = G / 32, GW = G / 32;
   constexpr int WN = pwn<BN>(), TM = ptm<BN>(), AF = TM / 16, CSL = pcode_slots<BN>();
-  typedef typename WordsT<GW>::T WT;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
   const int wm = wid / WN, wn = wid % WN;
@@ -1452,51 +1451,48 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
     const int kl = k0 % kPKT;
     const int r0 = wm * TM + cl;
     if constexpr (Q4) {
-      // this lane's GW code words of the group, for each of its 4 column tiles
+      // this lane's code words of the group, for each of its 4 column tiles:
+      // word j of column tile t at cb[cslot[t] + j] (read per step, so that no
+      // register array is indexed by the step)
       const uint32_t *cb = reinterpret_cast<const uint32_t *>(cs + ((k0 / kPKT) % kPBufs) * CSL);
       const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
-      WT wq[4];
+      int cslot[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int col = wn * 64 + t * 16 + cl;
-        const int slot = col * 4 + ((wo >> 2) ^ ((col >> 2) & 3));
-        wq[t] = *reinterpret_cast<const WT *>(cb + slot * 4 + (wo & 3));
+        cslot[t] = (col * 4 + ((wo >> 2) ^ ((col >> 2) & 3))) * 4 + (wo & 3);
       }
       // the group sums of the rows come from one more MFMA per row block
       // against a B operand of ones (row sums in every column)
       const bf16x8_t ones =
           __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+      const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
       if (defer) fold();                           // the previous group's
-#pragma unroll
-      for (int a = 0; a < AF; ++a) {
-        as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-      // (64-row wavefronts: two steps per trip, so that the compiler does not
-      // hoist every step's operand reads at once and run out of registers)
-#pragma unroll(AF == 4 ? 2 : STEPS)
-      for (int j = 0; j < STEPS; ++j) {
+      // one k-step of 32: the row fragments, then one column tile at a time
+      // (its unpacked operand feeds the AF MFMAs of the step and is dead
+      // after them); the first step of a group starts its sums from zero
+      auto kstep = [&](int j, bool first) {
         bf16x8_t af[AF];
 #pragma unroll
         for (int a = 0; a < AF; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + qq * (G / 4) + 8 * j);
-        // one column tile at a time: its unpacked operand feeds the AF MFMAs
-        // of the step and is dead after them
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          uint32_t w;
-          if constexpr (GW == 1) w = wq[t];
-          else w = wq[t][j];
           uint32_t pr[4];
-          unpack_word(w, pr);
+          unpack_word(cb[cslot[t] + j], pr);
           const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
 #pragma unroll
           for (int a = 0; a < AF; ++a)
-            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, ag[a][t], 0, 0, 0);
+            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, first ? zero4 : ag[a][t], 0, 0, 0);
         }
 #pragma unroll
-        for (int a = 0; a < AF; ++a) as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, as[a], 0, 0, 0);
-      }
+        for (int a = 0; a < AF; ++a)
+          as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, first ? zero4 : as[a], 0, 0, 0);
+      };
+      kstep(0, true);
+      // (64-row wavefronts: one step per trip, so that the compiler does not
+      // hoist every step's operand reads at once and run out of registers)
+#pragma unroll(AF == 4 ? 1 : STEPS)
+      for (int j = 1; j < STEPS; ++j) kstep(j, false);
       // this group's scale/zero words (read now: the buffer is refilled
       // after the next barrier)
       const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs + ((k0 / kPKT) % kPBufs) * kPSzSlots) +
