@@ -1489,9 +1489,7 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
           as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, first ? zero4 : as[a], 0, 0, 0);
       };
       kstep(0, true);
-      // (64-row wavefronts: one step per trip, so that the compiler does not
-      // hoist every step's operand reads at once and run out of registers)
-#pragma unroll(AF == 4 ? 1 : STEPS)
+#pragma unroll
       for (int j = 1; j < STEPS; ++j) kstep(j, false);
       // this group's scale/zero words (read now: the buffer is refilled
       // after the next barrier)
