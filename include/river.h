@@ -370,7 +370,9 @@ int river_set_record(river_ctx *ctx, void *d_buf, size_t bytes);
  * the caller and used until it is replaced or the context is destroyed.  It
  * holds, per position of the one sequence, the fp32 residual stream at the
  * input of the first layer that position holds no K/V for.  NULL detaches it.
- * A prefill or decode step under RIVER_KV_RECOMPUTE without it returns
+ * Attaching or detaching ends the current sequence for the strategy: decode
+ * steps under it return RIVER_E_STATE until a prefill under it.  A prefill
+ * or decode step under RIVER_KV_RECOMPUTE without a buffer returns
  * RIVER_E_STATE; RIVER_E_BAD_SIZE for a smaller or misaligned buffer. */
 int river_set_kv_state(river_ctx *ctx, void *d_buf, size_t bytes);
 
