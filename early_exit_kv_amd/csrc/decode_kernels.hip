@@ -1788,6 +1788,11 @@ hipError_t launch_rope_table(float2 *rope, int max_seq, int head_dim, float thet
 // ===========================================================================
 int attn_chunk(int max_seq, int batch, int n_kv_heads) {
   const int pairs = batch * n_kv_heads;
+  // a workgroup per CU already at one split per (b, kv head): one split,
+  // which the matrix-core kernel runs with eight wavefronts and no merge
+  // (measured on the 8B shapes at B=32 with 1.2K positions: 29.8 us against
+  // 31.9 with two splits)
+  if (pairs >= 256) return (max_seq + 2 * kAttnSub - 1) / (2 * kAttnSub) * (2 * kAttnSub);
   // splits per (b, kv head): enough for about 512 workgroups (two per CU),
   // and at least one per 1024 positions so that long caches stream through
   // many workgroups at once; at most 16, as merging more costs more than the
@@ -2043,8 +2048,8 @@ __device__ __forceinline__ int attn_swz(int r) {
 // MASK (the kv-mask comparator): positions whose pass exited at or before this
 // layer hold no K/V here and are left out; their pos_E words come in by DMA
 // with each block.
-template <int DH, int GQ, bool MASK>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
+template <int DH, int GQ, bool MASK, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnParams p) {
   if (past_exit_action(p.ctrl, p.layer, kPathDevice) != kRun) return;   // (comparators)
   constexpr int CPR = DH * 2 / 16;             // 16-byte chunks per position
   constexpr int BLK = 16 * DH * 2;             // bytes of a 16-position K (or V) block
@@ -2055,13 +2060,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   constexpr int NPASS = 16 / PPW;              // passes per block
   constexpr int NJ = DH / 32;                  // score MFMAs per block
   constexpr int KVB = 2 * BLK;                 // one buffer: K block then V block
+  constexpr int SUB = 16 * NW;                 // positions per sub-chunk (16 per wavefront)
+  constexpr int NT = 64 * NW;                  // threads
   // per wavefront two buffers; the split's partial results reuse the space
-  __shared__ __align__(16) char kvs[4 * 2 * KVB];
-  __shared__ __align__(16) float pl[4][16][GQ];
-  __shared__ float wm[4][GQ], wl[4][GQ];
+  __shared__ __align__(16) char kvs[NW * 2 * KVB];
+  __shared__ __align__(16) float pl[NW][16][GQ];
+  __shared__ float wm[NW][GQ], wl[NW][GQ];
   __shared__ int last_flag;
-  __shared__ int32_t pe[4][2][64];                 // MASK: pos_E of a wavefront's block
-  static_assert(4 * PPW * GQ * DH * 4 <= 4 * 2 * KVB, "the partial results fit the K/V buffers");
+  __shared__ int32_t pe[NW][2][64];                // MASK: pos_E of a wavefront's block
+  static_assert(NW * PPW * GQ * DH * 4 <= NW * 2 * KVB, "the partial results fit the K/V buffers");
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -2179,9 +2186,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   };
 
   int bi = 0;
-  for (int sb = t0; sb < t1; sb += kAttnSub) {
-    if (sb + kAttnSub < t1) {
-      fetch(bi ^ 1, sb + kAttnSub);
+  for (int sb = t0; sb < t1; sb += SUB) {
+    if (sb + SUB < t1) {
+      fetch(bi ^ 1, sb + SUB);
       wait_vm<NDMA>();
     } else {
       wait_vm<0>();
@@ -2200,7 +2207,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     }
   }
   __syncthreads();                               // every wavefront is done with its buffers
-  float *wo = reinterpret_cast<float *>(kvs);    // [4][PPW][GQ][DH]
+  float *wo = reinterpret_cast<float *>(kvs);    // [NW][PPW][GQ][DH]
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
     float4 *dst = reinterpret_cast<float4 *>(wo + ((wid * PPW + slot) * GQ + h) * DH + ln * 8);
@@ -2210,15 +2217,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   __syncthreads();
   const bool direct = p.splits == 1;
   float *part_base = p.part + ((int64_t)b * p.Hq + kvh * GQ) * p.splits * (DH + 2);
-  for (int idx = tid; idx < GQ * DH; idx += 256) {
+  for (int idx = tid; idx < GQ * DH; idx += NT) {
     const int h = idx / DH, e = idx % DH;
     float M = -INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, wm[wv][h]);
+    for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, wm[wv][h]);
     float L = 0.f, o = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int wv = 0; wv < 4; ++wv) {
+      for (int wv = 0; wv < NW; ++wv) {
         const float f = exp2_fast(wm[wv][h] - M);
         float ow = 0.f;
 #pragma unroll
@@ -2242,7 +2249,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   if (arrive_last(&p.counters[b * p.Hkv + kvh], gridDim.x, &last_flag)) {
     // merge the splits that hold positions, 16 splits per round of loads
     const int nval = (n + p.chunk - 1) / p.chunk;
-    for (int idx = tid; idx < GQ * DH; idx += 256) {
+    for (int idx = tid; idx < GQ * DH; idx += NT) {
       const int h = idx / DH, e = idx % DH;
       const float *base = part_base + (int64_t)h * p.splits * (DH + 2);
       float M = -INFINITY, L = 0.f, O = 0.f;
@@ -2276,27 +2283,36 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   }
 }
 
+template <int DH, int GQ, bool MASK>
+static hipError_t attn_mfma_launch(const AttnParams &p, dim3 grid, hipStream_t s) {
+  // one split per (row, kv head) and few of them: eight wavefronts, so that
+  // a workgroup keeps twice the positions in flight and no split merge runs
+  if (p.nw8) return launch_1(attn_mfma_kernel<DH, GQ, MASK, 8>, grid, dim3(512), p, s);
+  return launch_1(attn_mfma_kernel<DH, GQ, MASK, 4>, grid, dim3(256), p, s);
+}
+
 template <int DH>
 static hipError_t attn_launch_dh(const AttnParams &p, hipStream_t s) {
   dim3 grid(p.splits, p.Hkv, p.B);
   const int gq = p.Hq / p.Hkv;
   if (p.mfma && p.pos_E) {
     switch (gq) {
-      case 1: return launch_1(attn_mfma_kernel<DH, 1, true>, grid, dim3(256), p, s);
-      case 2: return launch_1(attn_mfma_kernel<DH, 2, true>, grid, dim3(256), p, s);
-      case 4: return launch_1(attn_mfma_kernel<DH, 4, true>, grid, dim3(256), p, s);
+      case 1: return attn_mfma_launch<DH, 1, true>(p, grid, s);
+      case 2: return attn_mfma_launch<DH, 2, true>(p, grid, s);
+      case 4: return attn_mfma_launch<DH, 4, true>(p, grid, s);
       default: return hipErrorInvalidValue;
     }
   }
   if (p.pos_E) return hipErrorInvalidValue;   // the vector-ALU kernel has no mask
   if (p.mfma) {
     switch (gq) {
-      case 1: return launch_1(attn_mfma_kernel<DH, 1, false>, grid, dim3(256), p, s);
-      case 2: return launch_1(attn_mfma_kernel<DH, 2, false>, grid, dim3(256), p, s);
-      case 4: return launch_1(attn_mfma_kernel<DH, 4, false>, grid, dim3(256), p, s);
+      case 1: return attn_mfma_launch<DH, 1, false>(p, grid, s);
+      case 2: return attn_mfma_launch<DH, 2, false>(p, grid, s);
+      case 4: return attn_mfma_launch<DH, 4, false>(p, grid, s);
       default: return hipErrorInvalidValue;
     }
   }
+  if (p.nw8) return hipErrorInvalidValue;
   switch (gq) {
     case 1: return launch_1(attn_decode_kernel<DH, 1>, grid, dim3(256), p, s);
     case 2: return launch_1(attn_decode_kernel<DH, 2>, grid, dim3(256), p, s);
@@ -2307,6 +2323,7 @@ static hipError_t attn_launch_dh(const AttnParams &p, hipStream_t s) {
 
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
   if (p.chunk % kAttnSub || p.splits < 1 || p.splits > kMaxAttnSplits) return hipErrorInvalidValue;
+  if (p.nw8 && (p.splits != 1 || p.chunk % (2 * kAttnSub))) return hipErrorInvalidValue;
   switch (p.Dh) {
     case 64: return attn_launch_dh<64>(p, s);
     case 128: return attn_launch_dh<128>(p, s);

@@ -397,6 +397,7 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     a.mfma = ctx->attn_kind == 0;
     a.layer = l;
     a.pos_E = ctx->strategy == kStratMask ? control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads) : nullptr;
+    a.nw8 = a.mfma && a.splits == 1 && a.chunk % (2 * kAttnSub) == 0;
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
@@ -569,6 +570,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     a.mfma = ctx->attn_kind == 0;
     a.layer = l;
     a.pos_E = ctx->strategy == kStratMask ? control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads) : nullptr;
+    a.nw8 = a.mfma && a.splits == 1 && a.chunk % (2 * kAttnSub) == 0;
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 

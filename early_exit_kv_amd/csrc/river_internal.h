@@ -179,6 +179,7 @@ struct AttnParams {
   int layer;              // the layer (kernels past the exit return at once in the comparators)
   const int32_t *pos_E;   // kv mask: E per earlier position (positions whose E <= layer
                           // hold no K/V here); nullptr: every position
+  int nw8;                // matrix-core kernel with eight wavefronts (one split, chunk a multiple of 128)
 };
 // positions per decode-attention workgroup for a cache of max_seq positions
 int attn_chunk(int max_seq, int batch, int n_kv_heads);

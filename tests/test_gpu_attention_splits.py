@@ -45,9 +45,11 @@ def test_attention_sub_chunks_tiny(tiny_w, chunk, attn):
 # 8B layer shapes (head dim 128, 32 q / 8 kv heads), one row, a 500-token
 # prompt (cache of 503): the library's own choice is 8 splits of one
 # sub-chunk merged by the last workgroup; chunk 256 gives 2 splits of 4
-# sub-chunks with positions 500..502 in the last one.
+# sub-chunks with positions 500..502 in the last one; chunk 1024 one split
+# (the matrix-core kernel then runs eight wavefronts, 128 positions per
+# sub-chunk, no merge).
 @pytest.mark.parametrize("attn", ["mfma", "valu"])
-@pytest.mark.parametrize("chunk", [0, 256])
+@pytest.mark.parametrize("chunk", [0, 256, 1024])
 def test_attention_splits_8b_batch1(w8b_2, chunk, attn):
     parity_run(synth.LLAMA_8B, w8b_2, B=1, T=500, steps=3, tau=0.5, attn=attn, chunk=chunk,
                check_prefill=False)
