@@ -2027,8 +2027,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
 
 // ===========================================================================
 // Decode attention with the scores on the matrix cores.  Same work split as
-// attn_decode_kernel (workgroup = split x kv head x row, sub-chunks of 64
-// positions, the last workgroup of a (row, kv head) merges the splits).
+// attn_decode_kernel (workgroup = split x kv head x row, the last workgroup
+// of a (row, kv head) merges the splits), with NW wavefronts per workgroup
+// and sub-chunks of 16 NW positions (NW = 4: 64, as the vector-ALU kernel;
+// NW = 8 for a single split, which then writes its result directly).
 // Inside a sub-chunk each wavefront owns a block of 16 consecutive positions:
 // their K and V rows (16 x Dh bf16, contiguous in the cache) land in LDS by
 // DMA, the next sub-chunk's while this one is reduced, each row's 16-byte
