@@ -1741,8 +1741,14 @@ int gemv_grid(Epilogue ep, const GemvParams &p) {
 }
 
 hipError_t launch_gemv(XSource xs, Epilogue ep, const GemvParams &p, hipStream_t s) {
-  (void)xs;
   if (p.B < 1 || p.B > 8 || ep > kEpPlain) return hipErrorInvalidValue;
+  // the input form is fixed by the epilogue: q|k|v, gate|up and the LM head
+  // normalise fp32 rows (h_src, gain) on the way in; the others read bf16
+  // rows (x_src).  A call that asks for the other form, or leaves its input
+  // unset, is refused before anything is launched.
+  const XSource want = (ep == kEpQKV || ep == kEpSwiGLU || ep == kEpLogits) ? kXNorm : kXBf16;
+  if (xs != want) return hipErrorInvalidValue;
+  if (want == kXNorm ? (!p.h_src || !p.gain) : !p.x_src) return hipErrorInvalidValue;
   if (use_mgemv(ep, p)) {
     const MvPlan g = mgemv_plan(ep, p);
     int ntile = g.ntile;
