@@ -602,6 +602,8 @@ __device__ __forceinline__ int flash_swz(int r) {
   return DH == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
+constexpr float kLazyLog2 = 8.0f;   // largest probability taken against a stale maximum: 2^8
+
 template <int DH, int GQ>
 __global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
   if (past_exit_action(p.ctrl, p.layer, p.path) != kRun) return;   // (comparators)
@@ -717,23 +719,33 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(AttnPrefillParams p) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m[h], mx);
-      float corr = 1.f, part = 0.f;
+      // lazy rescaling: the reference maximum moves only when a score
+      // exceeds it by more than 2^kLazyLog2; below that the probabilities are
+      // taken against the old reference (at most 2^kLazyLog2, exact in fp32,
+      // and the same reference divides out of O and the row sum), so the
+      // output tiles are rescaled only in the rare tiles where some lane's
+      // reference moved (the four lanes of a query agree: mx is their common
+      // maximum)
+      const bool bump = mx > m[h] + kLazyLog2;
+      const float mref = bump ? mx : m[h];
+      const float corr = bump ? exp2_fast(m[h] - mx) : 1.f;
+      float part = 0.f;
       float pv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-      if (mnew != -INFINITY) {
-        corr = exp2_fast(m[h] - mnew);
+      if (mref != -INFINITY) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2_fast(sv[e] - mnew);
+          pv[e] = exp2_fast(sv[e] - mref);
           part += pv[e];
         }
       }
       lsum[h] = lsum[h] * corr + part;   // this lane's share of the row sum
-      m[h] = mnew;
+      m[h] = mref;
+      if (__any(bump)) {
 #pragma unroll
-      for (int j = 0; j < NO; ++j) o[h][j] *= corr;
+        for (int j = 0; j < NO; ++j) o[h][j] *= corr;
+      }
       // p = p1 + p2 + p3 exactly: each term keeps the top 16 bits of what is
       // left (a bf16 value), the subtractions are exact
 #pragma unroll
