@@ -357,3 +357,68 @@ def test_forced_exits_8b_layer_shapes(w8b3, strategy):
 def test_forced_exits_8b_split_mask(w8b3):
     w, hw = w8b3
     run_forced_tf(synth.LLAMA_8B, w, hw, "kv_mask", 2, 140, [1, 3, 2, 3], chunk=64, prefill_E=2)
+
+
+@pytest.mark.parametrize("strategy", ["kv_mask", "propagate", "mono"])
+def test_strategy_prefill_batch16_tiny(strategy):
+    """Prefill of more than 8 rows per position (the batched-row path) under
+    each comparator: logits and the written K/V against the oracle's same
+    strategy (decode steps of more than 8 rows take only the method)."""
+    rv = _river()
+    s = synth.TINY
+    L = s.n_layers
+    B, T = 16, 20
+    w = synth.make_weights(s, seed=0)
+    from conftest import np_weights
+    from test_gpu_parity import to_cuda
+    r = rv.River(s, to_cuda(w), B, T + 2)
+    r.kv_strategy(strategy)
+    r.build_exit_layers("int4")
+    orc = ro.RiverOracle(s.as_dict(), np_weights(w), B, T + 2)
+    orc.set_kv_strategy(strategy)
+    orc.build_exit_layers("int4")
+    toks = synth.make_tokens(s, B, T, seed=3)
+    for fe in (None, 1, 2):
+        r.force_exit_layer(-1 if fe is None else fe)
+        r.reset()
+        gl, _ = r.prefill(toks.cuda(), 0.5)
+        st = r.exit_stats()
+        o = orc.prefill(toks.numpy(), 0.5, force_E=fe)
+        if fe is None and check_decision(st["last_E"], st["last_trace"], o, 0.5, L):
+            o = orc.prefill(toks.numpy(), 0.5, force_E=st["last_E"])
+        compare_logits(gl.cpu().numpy(), o["logits"])
+        E = st["last_E"]
+        written = range(L) if strategy == "propagate" else range(E)
+        gk, gv = kv_numpy(r, L, B, T)
+        compare_kv_layers(gk, gv, orc, written, B, range(T))
+    with pytest.raises(rv.RiverError):
+        r.decode_step(torch.zeros(B, dtype=torch.int32, device="cuda"), 0.5)
+    r.close()
+
+
+def test_recompute_state_buffer_rules(tiny):
+    """The recompute comparator's state buffer: too small or misaligned ->
+    RIVER_E_BAD_SIZE; no buffer, or a decode step after the buffer was
+    replaced without a new prefill -> RIVER_E_STATE."""
+    import ctypes
+    rv = _river()
+    s = synth.TINY
+    r = rv.River(s, tiny["cuda"], 1, 40)
+    r.build_exit_layers("int4")
+    lib = r.lib
+    small = torch.empty(40 * s.d_model - 1, dtype=torch.float32, device="cuda")
+    assert lib.river_set_kv_state(r.ctx, ctypes.c_void_p(small.data_ptr()), small.numel() * 4) == \
+        rv.RIVER_E_BAD_SIZE
+    big = torch.empty(40 * s.d_model + 8, dtype=torch.float32, device="cuda")
+    assert lib.river_set_kv_state(r.ctx, ctypes.c_void_p(big.data_ptr() + 4), 40 * s.d_model * 4) == \
+        rv.RIVER_E_BAD_SIZE
+    r.set_option(rv.RIVER_OPT_KV_STRATEGY, rv.KV_STRATEGIES.index("recompute"))
+    with pytest.raises(rv.RiverError):      # no buffer attached
+        r.prefill(synth.make_tokens(s, 1, 16, seed=0).cuda(), 0.5)
+    r.kv_strategy("recompute")              # attaches one
+    _, nx = r.prefill(synth.make_tokens(s, 1, 16, seed=0).cuda(), 0.5)
+    r.decode_step(nx.clone(), 0.5)
+    assert lib.river_set_kv_state(r.ctx, ctypes.c_void_p(big.data_ptr()), big.numel() * 4) == 0
+    with pytest.raises(rv.RiverError):      # a new buffer starts no sequence
+        r.decode_step(nx.clone(), 0.5)
+    r.close()
