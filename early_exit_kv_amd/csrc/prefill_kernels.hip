@@ -1260,30 +1260,39 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 // Prefill GEMM for many rows: Y[m][n] = sum_k X[m][k] W[n][k] on
 // v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 rows x BN columns, eight
 // wavefronts of 64 columns each: BN = 128 as 4 x 2 wavefronts of 32 x 64, BN
-// = 256 (from 4,096 rows) as 2 x 4 of 64 x 64, where every unpacked int4
-// operand feeds four MFMAs instead of two; two wavefronts per SIMD so that
-// one's waits overlap the other's MFMAs.
-//   Rows X: k-tiles of 128 columns copied straight from memory into LDS
-//   (global_load_lds, no registers), three buffers, so two tiles are in
-//   flight while one feeds the MFMAs; 16-byte chunks are XOR-swizzled within a
-//   row (chunk c of row r at slot c ^ (r mod 16)) so that the 16 rows one
-//   fragment read touches fall in distinct banks.
-//   int4 weights: the k-tile's codes and scale/zero words are copied into LDS
-//   with the rows (same int4 conventions as the batched-row GEMM: per-group
+// = 256 (from 4,096 rows) as 2 x 4 of 64 x 64, where every B operand feeds
+// four MFMAs instead of two; two wavefronts per SIMD so that one's waits
+// overlap the other's MFMAs.
+//   Every operand goes straight from memory into LDS (global_load_lds, no
+//   registers), three k-tile buffers, so two tiles are in flight while one
+//   feeds the MFMAs.  Rows (and bf16 weight rows) are stored whole, their
+//   16-byte chunks XOR-swizzled (chunk c of row r at slot r * CH + (c ^ (r mod
+//   CH)), CH chunks per row), so that one copy instruction reads whole rows
+//   from memory.  A 16-byte LDS read runs at the full rate only when each
+//   quarter wavefront (16 lanes) reads one contiguous 256-byte block; the
+//   fragment reads here (16 rows at one chunk) take about 1.45x that, but a
+//   layout with conflict-free fragment reads needs copies of 64 bytes per row
+//   and measured slower overall (int4 -8%, bf16 -20%).
+//   int4 weights: k-tiles of 128; the codes of 16 columns stored as 4 blocks
+//   of (one quarter's 4 words of each column), so that each quarter of a code
+//   read is one 256-byte block; the scale/zero words beside them (per-group
 //   accumulation, lane quarters over G/4 codes, group fold
 //   tot += s * (acc - (128 + z) * sum_k x), the row sums of each group from
-//   one more MFMA per row block against a B operand of ones).  bf16 weights
-//   go from memory straight into B operands, every lane loading its own column
-//   several k-steps ahead.
+//   one more MFMA per row block against a B operand of ones).
+//   bf16 weights: k-tiles of 64 (rows and weights of three tiles then fit
+//   the same LDS).
 //   Workgroups are ordered in groups of 8 row blocks so that the rows and
 //   weights they share stay in L2.
 // ===========================================================================
-constexpr int kPBM = 128, kPKT = 128, kPGroupRows = 8;
+constexpr int kPBM = 128, kPGroupRows = 8;
 constexpr int kPThreads = 512, kPBufs = 3;
 constexpr int kPWideRows = 4096;                  // rows from which column blocks are 256 wide
-constexpr int kPTileSlots = kPBM * kPKT / 8;      // 16-byte slots of rows per k-tile (2048)
-// 16-byte slots of int4 codes per k-tile of BN columns
-template <int BN> constexpr int pcode_slots() { return BN * kPKT / 32; }
+// k-tile: 128 columns for int4 weights, 64 for bf16 weights
+template <bool Q4> constexpr int pkt() { return Q4 ? 128 : 64; }
+// 16-byte slots of rows per k-tile
+template <bool Q4> constexpr int prow_slots() { return kPBM * pkt<Q4>() / 8; }
+// 16-byte slots of weights per k-tile of BN columns (int4 codes or bf16)
+template <bool Q4, int BN> constexpr int pw_slots() { return Q4 ? BN * pkt<Q4>() / 32 : BN * pkt<Q4>() / 8; }
 // wavefronts along N (each 64 columns wide) and along M, rows per wavefront
 template <int BN> constexpr int pwn() { return BN / 64; }
 template <int BN> constexpr int pwm() { return 8 / pwn<BN>(); }
@@ -1291,61 +1300,66 @@ template <int BN> constexpr int ptm() { return kPBM / pwm<BN>(); }
 // 16-byte slots of int4 scale/zero words per k-tile: one word for each of
 // the 512 lanes of the workgroup (at most 2 groups x 256 columns are used)
 constexpr int kPSzSlots = 128;
-// LDS of a workgroup: row buffers, code buffers, scale/zero buffers (the
+// LDS of a workgroup: row buffers, weight buffers, scale/zero buffers (the
 // results reuse them all)
-template <int BN> constexpr int psmem_slots() { return kPBufs * (kPTileSlots + pcode_slots<BN>() + kPSzSlots); }
+template <bool Q4, int BN> constexpr int pstage_slots() {
+  return prow_slots<Q4>() + pw_slots<Q4, BN>() + (Q4 ? kPSzSlots : 0);
+}
+template <int BN> constexpr int psmem_slots() {
+  return kPBufs * (pstage_slots<true, BN>() > pstage_slots<false, BN>() ? pstage_slots<true, BN>()
+                                                                          : pstage_slots<false, BN>());
+}
 
 
 template <int G, int EP, bool Q4, int BN>
-__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4 *cs, uint4 *zs, bool ex,
-                                           int rowblk, int colblk, f32x4_t (&tot)[ptm<BN>() / 16][4]) {
+__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *smem, bool ex, int rowblk, int colblk,
+                                           f32x4_t (&tot)[ptm<BN>() / 16][4]) {
+  constexpr int KT = pkt<Q4>(), CH = KT / 8;               // k columns and 16-byte chunks per row
+  constexpr int ASL = prow_slots<Q4>(), WSL = pw_slots<Q4, BN>();
+  constexpr int NA = ASL / kPThreads;                      // row copies per wavefront per k-tile
+  constexpr int NW = WSL / kPThreads;                      // weight copies per wavefront per k-tile
+  static_assert(ASL % kPThreads == 0 && WSL % kPThreads == 0, "whole copies");
   constexpr int STEPS = G / 32, GW = G / 32;
-  constexpr int WN = pwn<BN>(), TM = ptm<BN>(), AF = TM / 16, CSL = pcode_slots<BN>();
+  constexpr int WN = pwn<BN>(), TM = ptm<BN>(), AF = TM / 16;
+  uint4 *xs = smem, *ws = smem + kPBufs * ASL, *zs = ws + kPBufs * WSL;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
   const int wm = wid / WN, wn = wid % WN;
   const int64_t m0 = (int64_t)rowblk * kPBM;
   const int KG = p.K / G;
-  const int ntile = p.K / kPKT;
+  const int ntile = p.K / KT;
 
-  // segment bases are uniform over a 16-column tile (scalar registers); only
-  // the 32-bit row offsets live in vector registers
-  const uint16_t *bbase[4];
-  int roff[4];
+  // ---- weights of a k-tile, copy i of this wavefront covers slots
+  //      s = (8 i + wid) * 64 + lane.  int4: column c's quarter q (its words
+  //      4q..4q+3) at slot ((c / 16) * 4 + q) * 16 + c % 16; bf16: chunk q
+  //      of column n at slot n * CH + (q ^ (n mod CH))
+  const void *wsrc[NW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int i = 0; i < NW; ++i) {
+    const int s = (i * 8 + wid) * 64 + lane;
+    int c, q;
+    if constexpr (Q4) { c = (s >> 6) * 16 + (s & 15); q = (s >> 4) & 3; }
+    else { c = s / CH; q = (s % CH) ^ (c & (CH - 1)); }
     int seg, row;
     bool valid;
-    map_col<EP>(p, colblk, BN, wn * 64 + t * 16 + cl, seg, row, valid);
-    if (!valid) row = 0;
-    seg = __builtin_amdgcn_readfirstlane(seg);
-    roff[t] = row;
-    if constexpr (!Q4) bbase[t] = ex ? p.w.ex_bf[seg] : p.w.bf[seg];
-  }
-
-  // ---- int4 codes of a k-tile: BN columns x 64 bytes, one 16-byte slot per
-  //      lane of every wavefront per BN / 128; column c's chunk q sits at
-  //      slot 4c + (q ^ ((c >> 2) & 3)), so the 16 columns one B-fragment read
-  //      touches fall in distinct banks
-  constexpr int NCD = BN / 128;                 // code copies per wavefront per k-tile
-  const uint32_t *crow[NCD];
-#pragma unroll
-  for (int i = 0; i < NCD; ++i) {
-    crow[i] = nullptr;
+    map_col<EP>(p, colblk, BN, c, seg, row, valid);
+    if (!valid) { seg = 0; row = 0; }
+    // the segment is picked by selects, not by indexing the parameter arrays
+    // with a per-lane value (that would copy them to scratch memory)
     if constexpr (Q4) {
-      const int slot = (i * 8 + wid) * 64 + lane;
-      const int c = slot >> 2, q = (slot & 3) ^ ((c >> 2) & 3);
-      int seg, row;
-      bool valid;
-      map_col<EP>(p, colblk, BN, c, seg, row, valid);
-      if (!valid) { seg = 0; row = 0; }
-      crow[i] = p.w.q4[seg] + (int64_t)row * (p.K / 8) + 4 * q;
+      const uint32_t *b = seg == 0 ? p.w.q4[0] : seg == 1 ? p.w.q4[1] : p.w.q4[2];
+      wsrc[i] = b + (int64_t)row * (p.K / 8) + 4 * q;
+    } else {
+      const uint16_t *b0 = ex ? p.w.ex_bf[0] : p.w.bf[0], *b1 = ex ? p.w.ex_bf[1] : p.w.bf[1],
+                     *b2 = ex ? p.w.ex_bf[2] : p.w.bf[2];
+      const uint16_t *b = seg == 0 ? b0 : seg == 1 ? b1 : b2;
+      wsrc[i] = b + (int64_t)row * p.K + 8 * q;
     }
   }
-  // ---- their scale/zero words: entry e = 64 wid + lane of a k-tile is
+  // ---- int4 scale/zero words: entry e = 64 wid + lane of a k-tile is
   //      group e / BN of the k-tile for column e % BN (entries past the
   //      tile's groups repeat the last group)
-  constexpr int GPT = kPKT / G;                 // groups per k-tile
+  constexpr int GPT = KT / G;                   // groups per k-tile
   const uint32_t *zrow = nullptr;
   if constexpr (Q4) {
     const int e = wid * 64 + lane;
@@ -1354,19 +1368,21 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
     bool valid;
     map_col<EP>(p, colblk, BN, c, seg, row, valid);
     if (!valid) { seg = 0; row = 0; }
-    zrow = p.w.sz[seg] + (int64_t)row * KG + gi;
+    const uint32_t *b = seg == 0 ? p.w.sz[0] : seg == 1 ? p.w.sz[1] : p.w.sz[2];
+    zrow = b + (int64_t)row * KG + gi;
   }
 
-  // ---- rows: each wavefront copies 4 x 64 slots of a k-tile into LDS
-  const uint16_t *arow[4];
-  int acol[4];
+  // ---- rows: copy i of this wavefront covers slots s = (wid * NA + i) * 64 +
+  //      lane, i.e. row s / CH, chunk (s mod CH) ^ (row mod CH)
+  const uint16_t *arow[NA];
+  int acol[NA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = (wid * 4 + i) * 64 + lane;
-    const int r = slot >> 4, sc = slot & 15;
+  for (int i = 0; i < NA; ++i) {
+    const int s = (wid * NA + i) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ (r & (CH - 1));
     const int64_t m = min(m0 + r, (int64_t)p.M - 1);      // rows past M: any valid row
     arow[i] = p.x + m * p.ldx;
-    acol[i] = 8 * (sc ^ (r & 15));
+    acol[i] = 8 * c;
   }
   // The copies are issued from inline assembly: the compiler then does not
   // treat every later LDS read as possibly overlapping them (it would wait for
@@ -1374,57 +1390,42 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
   // copies it needs with an explicit s_waitcnt.  m0 holds the LDS destination
   // of a copy (each lane writes 16 bytes at m0 + 16 * lane).
   const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_ptr_t)xs;
-  const int uwid = __builtin_amdgcn_readfirstlane(wid);
-  const uint32_t cs_base = (uint32_t)(uintptr_t)(lds_ptr_t)cs;
+  const uint32_t ws_base = (uint32_t)(uintptr_t)(lds_ptr_t)ws;
   const uint32_t zs_base = (uint32_t)(uintptr_t)(lds_ptr_t)zs;
-  auto load_a = [&](int kt) {
+  const int uwid = __builtin_amdgcn_readfirstlane(wid);
+  auto load_tile = [&](int kt) {
     const int ktc = min(kt, ntile - 1);                    // unconditional: fixed load count
-    const uint32_t buf = xs_base + (uint32_t)((kt % kPBufs) * kPTileSlots * 16);
+    const int buf = kt % kPBufs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(buf + (uint32_t)((uwid * 4 + i) * 64 * 16));
-      const uint16_t *src = arow[i] + ktc * kPKT + acol[i];
+    for (int i = 0; i < NA; ++i) {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(xs_base + (uint32_t)((buf * ASL + (uwid * NA + i) * 64) * 16));
+      const uint16_t *src = arow[i] + ktc * KT + acol[i];
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                   : "memory", "m0");
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(ws_base + (uint32_t)((buf * WSL + (i * 8 + uwid) * 64) * 16));
+      const void *src;
+      if constexpr (Q4) src = static_cast<const uint32_t *>(wsrc[i]) + ktc * (KT / 8);
+      else src = static_cast<const uint16_t *>(wsrc[i]) + ktc * KT;
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
                    : "memory", "m0");
     }
     if constexpr (Q4) {
-#pragma unroll
-      for (int i = 0; i < NCD; ++i) {
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(
-            cs_base + (uint32_t)(((kt % kPBufs) * CSL + (i * 8 + uwid) * 64) * 16));
-        const uint32_t *src = crow[i] + ktc * (kPKT / 8);
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
-                     : "memory", "m0");
-      }
       // scale/zero words: each lane writes 4 bytes at m0 + 4 * lane
-      const uint32_t zdst = __builtin_amdgcn_readfirstlane(
-          zs_base + (uint32_t)(((kt % kPBufs) * kPSzSlots) * 16 + uwid * 256));
+      const uint32_t zdst =
+          __builtin_amdgcn_readfirstlane(zs_base + (uint32_t)((buf * kPSzSlots) * 16 + uwid * 256));
       const uint32_t *zsrc = zrow + ktc * GPT;
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(zdst), "v"(zsrc)
                    : "memory", "m0");
     }
   };
-  auto a_frag = [&](const uint4 *buf, int r, int k) -> bf16x8_t {
-    const int c = k >> 3;
-    return __builtin_bit_cast(bf16x8_t, buf[r * 16 + (c ^ (r & 15))]);
-  };
-
-  // ---- weights: int4 codes and their scale/zero words come through LDS with
-  //      the rows, so that no load the compiler tracks sits in the int4 loop
-  //      (its wait for such a load would also wait for every copy issued
-  //      after it); bf16 weights one k-step of 32 per chunk into registers
-  constexpr int D = Q4 ? 2 : AF == 4 ? 4 : 8;   // chunks per pass (bf16: 4 loads each in flight)
-  constexpr int CK = Q4 ? G : 32;              // k columns per chunk
-  v4u wb[D][4];
-  const int nchunk = p.K / CK;
-  auto load_w = [&](int c, int u) {
-    if constexpr (!Q4) {
-      const int k0 = min(c, nchunk - 1) * CK;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        wb[u][t] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u *>(bbase[t] + (uint32_t)(roff[t] * p.K + k0 + 8 * qq)));
-    }
+  // row fragment: row 16 (wm * AF + a) + cl, chunk c of the k-tile
+  auto a_frag = [&](const uint4 *buf, int a, int c) -> bf16x8_t {
+    return __builtin_bit_cast(bf16x8_t, buf[((wm * AF + a) * 16 + cl) * CH + (c ^ (cl & (CH - 1)))]);
   };
 
   // int4: raw sums of a group (against the codes as 128+q per column tile,
@@ -1457,106 +1458,94 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
     }
   };
 
-  auto compute = [&](int c, int u) {
-    const int k0 = c * CK;
-    const uint4 *buf = xs + ((k0 / kPKT) % kPBufs) * kPTileSlots;
-    const int kl = k0 % kPKT;
-    const int r0 = wm * TM + cl;
-    if constexpr (Q4) {
-      // this lane's code words of the group, for each of its 4 column tiles:
-      // word j of column tile t at cb[cslot[t] + j] (read per step, so that no
-      // register array is indexed by the step)
-      const uint32_t *cb = reinterpret_cast<const uint32_t *>(cs + ((k0 / kPKT) % kPBufs) * CSL);
-      const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
-      int cslot[4];
+  // one group of G columns of int4 weights (kl: its first column in the k-tile)
+  auto group_q4 = [&](int buf, int kl) {
+    const uint4 *xb = xs + buf * ASL;
+    // this lane's code words of the group, for each of its 4 column tiles:
+    // word j of column tile t at cb[cslot[t] + j] (read per step, so that no
+    // register array is indexed by the step)
+    const uint32_t *cb = reinterpret_cast<const uint32_t *>(ws + buf * WSL);
+    const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
+    int cslot[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int col = wn * 64 + t * 16 + cl;
-        cslot[t] = (col * 4 + ((wo >> 2) ^ ((col >> 2) & 3))) * 4 + (wo & 3);
-      }
-      // the group sums of the rows come from one more MFMA per row block
-      // against a B operand of ones (row sums in every column)
-      const bf16x8_t ones =
-          __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-      const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-      if (defer) fold();                           // the previous group's
-      // one k-step of 32: the row fragments, then one column tile at a time
-      // (its unpacked operand feeds the AF MFMAs of the step and is dead
-      // after them); the first step of a group starts its sums from zero
-      auto kstep = [&](int j, bool first) {
-        bf16x8_t af[AF];
-#pragma unroll
-        for (int a = 0; a < AF; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + qq * (G / 4) + 8 * j);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint32_t pr[4];
-          unpack_word(cb[cslot[t] + j], pr);
-          const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
-#pragma unroll
-          for (int a = 0; a < AF; ++a)
-            ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, first ? zero4 : ag[a][t], 0, 0, 0);
-        }
-#pragma unroll
-        for (int a = 0; a < AF; ++a)
-          as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, first ? zero4 : as[a], 0, 0, 0);
-      };
-      kstep(0, true);
-#pragma unroll
-      for (int j = 1; j < STEPS; ++j) kstep(j, false);
-      // this group's scale/zero words (read now: the buffer is refilled
-      // after the next barrier)
-      const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs + ((k0 / kPKT) % kPBufs) * kPSzSlots) +
-                           (kl / G) * BN + wn * 64 + cl;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) pz[t] = zb[t * 16];
-      if (!defer) fold();
-    } else {
+    for (int t = 0; t < 4; ++t) cslot[t] = (((wn * 4 + t) * 4 + (wo >> 2)) * 16 + cl) * 4 + (wo & 3);
+    // the group sums of the rows come from one more MFMA per row block
+    // against a B operand of ones (row sums in every column)
+    const bf16x8_t ones =
+        __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    if (defer) fold();                           // the previous group's
+    // one k-step of 32: the row fragments (lane quarter qq takes chunk
+    // (kl + qq G/4) / 8 + j), then one column tile at a time (its unpacked
+    // operand feeds the AF MFMAs of the step and is dead after them); the
+    // first step of a group starts its sums from zero
+    auto kstep = [&](int j, bool first) {
       bf16x8_t af[AF];
 #pragma unroll
-      for (int a = 0; a < AF; ++a) af[a] = a_frag(buf, r0 + a * 16, kl + 8 * qq);
+      for (int a = 0; a < AF; ++a) af[a] = a_frag(xb, a, kl / 8 + qq * (G / 32) + j);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t pr[4];
+        unpack_word(cb[cslot[t] + j], pr);
+        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+          ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, first ? zero4 : ag[a][t], 0, 0, 0);
+      }
 #pragma unroll
       for (int a = 0; a < AF; ++a)
+        as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, first ? zero4 : as[a], 0, 0, 0);
+    };
+    kstep(0, true);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], __builtin_bit_cast(bf16x8_t, wb[u][t]),
-                                                              tot[a][t], 0, 0, 0);
+    for (int j = 1; j < STEPS; ++j) kstep(j, false);
+    // this group's scale/zero words (read now: the buffer is refilled
+    // after the next barrier)
+    const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs + buf * kPSzSlots) + (kl / G) * BN + wn * 64 + cl;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pz[t] = zb[t * 16];
+    if (!defer) fold();
+  };
+
+  // a k-tile of bf16 weights: two k-steps of 32 in the natural order (lane
+  // quarter qq takes chunk 4 j + qq)
+  auto tile_bf16 = [&](int buf) {
+    const uint4 *xb = xs + buf * ASL, *wb = ws + buf * WSL;
+#pragma unroll
+    for (int j = 0; j < KT / 32; ++j) {
+      bf16x8_t af[AF];
+#pragma unroll
+      for (int a = 0; a < AF; ++a) af[a] = a_frag(xb, a, 4 * j + qq);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sl = ((wn * 4 + t) * 16 + cl) * CH + ((4 * j + qq) ^ (cl & (CH - 1)));
+        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, wb[sl]);
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+          tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, tot[a][t], 0, 0, 0);
+      }
     }
   };
 
-  constexpr int CPT = kPKT / CK;                // chunks per k-tile
-  static_assert(D % CPT == 0, "the ring holds whole k-tiles");
-  constexpr int UT = D / CPT;                   // k-tiles per pass of the ring
 #pragma unroll
-  for (int t = 0; t < kPBufs - 1; ++t) load_a(t);
+  for (int t = 0; t < kPBufs - 1; ++t) load_tile(t);
+  for (int kt = 0; kt < ntile; ++kt) {
+    // tile kt has landed once no more than the copies of the next
+    // kPBufs - 2 k-tiles are outstanding (every copy is unconditional, so the
+    // count holds throughout)
+    constexpr int per_tile = NA + NW + (Q4 ? 1 : 0);
+    constexpr int later = (kPBufs - 2) * per_tile;
+    static_assert(later < 64, "vmcnt field");
+    // s_waitcnt: vmcnt = later, expcnt and lgkmcnt not waited for
+    __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
+    __syncthreads();                        // tile kt visible; tile kt-1 done everywhere
+    load_tile(kt + kPBufs - 1);             // into the buffer tile kt-1 used
+    const int buf = kt % kPBufs;
+    if constexpr (Q4) {
 #pragma unroll
-  for (int u = 0; u < D; ++u) load_w(u, u);
-  for (int kt0 = 0; kt0 < ntile; kt0 += UT) {
-#pragma unroll
-    for (int ti = 0; ti < UT; ++ti) {
-      const int kt = kt0 + ti;              // ntile is a multiple of UT (checked at launch)
-      {
-        // tile kt has landed once no more than `later` vector-memory operations
-        // are outstanding: after its 4 copies came those of the next 2 k-tiles
-        // and at least min(the first D refills, 3 k-tiles of refills) weight
-        // loads (every load is unconditional, so the count holds throughout)
-        // (a k-tile is 4 copies of rows, plus for int4 BN / 128 of codes and
-        // 1 of scale/zero words; a bf16 weight refill is 4 loads per chunk,
-        // int4 has none)
-        constexpr int per_tile = Q4 ? 4 + NCD + 1 : 4;
-        constexpr int ring = (kPBufs - 1) * CPT;
-        constexpr int later = (kPBufs - 2) * per_tile + (Q4 ? 0 : (D < ring ? D : ring) * 4);
-        static_assert(later < 64, "vmcnt field");
-        // s_waitcnt: vmcnt = later, expcnt and lgkmcnt not waited for
-        __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
-        __syncthreads();                        // tile kt visible; tile kt-1 done everywhere
-        load_a(kt + kPBufs - 1);                // into the buffer tile kt-1 used
-#pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-          const int c = kt * CPT + cc;
-          compute(c, ti * CPT + cc);            // ring slot known at compile time
-          load_w(c + D, ti * CPT + cc);
-        }
-      }
+      for (int g = 0; g < GPT; ++g) group_q4(buf, g * G);
+    } else {
+      tile_bf16(buf);
     }
   }
   if (defer) fold();                             // the last group's
@@ -1568,10 +1557,9 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *xs, uint4
 
 template <int G, int EP, int BN>
 __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
-  // 96 KB of row buffers, then 24 (BN 128) or 48 KB (BN 256) of int4 codes;
-  // the results reuse both
+  // three stages of rows and weights (and int4 scale/zero words); the
+  // results reuse them
   __shared__ __align__(16) uint4 smem[psmem_slots<BN>()];
-  uint4 *xs = smem, *cs = smem + kPBufs * kPTileSlots, *zs = cs + kPBufs * pcode_slots<BN>();
   constexpr int AF = ptm<BN>() / 16;
   bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   // grouped order: kPGroupRows row blocks share the weights of each column block
@@ -1589,8 +1577,8 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true, BN>(p, xs, cs, zs, ex, rowblk, colblk, tot);
-  else pgemm_body<G, EP, false, BN>(p, xs, cs, zs, ex, rowblk, colblk, tot);
+  if (q4) pgemm_body<G, EP, true, BN>(p, smem, ex, rowblk, colblk, tot);
+  else pgemm_body<G, EP, false, BN>(p, smem, ex, rowblk, colblk, tot);
 
   // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -1637,8 +1625,8 @@ static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s
 }
 
 bool pgemm_fits(int K, int G) {
-  // K in whole passes of the weight ring (2 k-tiles)
-  return (G == 64 || G == 128) && K % (2 * kPKT) == 0;
+  // K in whole k-tiles of either weight form
+  return (G == 64 || G == 128) && K % pkt<true>() == 0;
 }
 
 hipError_t launch_pgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
