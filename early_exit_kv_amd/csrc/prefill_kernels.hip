@@ -838,6 +838,320 @@ hipError_t launch_attn_prefill(const AttnPrefillParams &p, hipStream_t s) {
 
 
 // ===========================================================================
+// Prefill GEMM for many rows: Y[m][n] = sum_k X[m][k] W[n][k] on
+// v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 rows x BN columns, eight
+// wavefronts of 64 columns each: BN = 128 as 4 x 2 wavefronts of 32 x 64, BN
+// = 256 (from 4,096 rows) as 2 x 4 of 64 x 64, where every B operand feeds
+// four MFMAs instead of two; two wavefronts per SIMD so that one's waits
+// overlap the other's MFMAs.
+//   Every operand goes straight from memory into LDS (global_load_lds, no
+//   registers), three k-tile buffers, so two tiles are in flight while one
+//   feeds the MFMAs.  Rows (and bf16 weight rows) are stored whole, their
+//   16-byte chunks XOR-swizzled (chunk c of row r at slot r * CH + (c ^ (r mod
+//   CH)), CH chunks per row), so that one copy instruction reads whole rows
+//   from memory.  A 16-byte LDS read runs at the full rate only when each
+//   quarter wavefront (16 lanes) reads one contiguous 256-byte block; the
+//   fragment reads here (16 rows at one chunk) take about 1.45x that, but a
+//   layout with conflict-free fragment reads needs copies of 64 bytes per row
+//   and measured slower overall (int4 -8%, bf16 -20%).
+//   int4 weights: k-tiles of 128; the codes of 16 columns stored as 4 blocks
+//   of (one quarter's 4 words of each column), so that each quarter of a code
+//   read is one 256-byte block; the scale/zero words beside them (per-group
+//   accumulation, lane quarters over G/4 codes, group fold
+//   tot += s * (acc - (128 + z) * sum_k x), the row sums of each group from
+//   one more MFMA per row block against a B operand of ones).
+//   bf16 weights: k-tiles of 64 (rows and weights of three tiles then fit
+//   the same LDS).
+//   Workgroups are ordered in groups of 8 row blocks so that the rows and
+//   weights they share stay in L2.
+// ===========================================================================
+constexpr int kPBM = 128, kPGroupRows = 8;
+constexpr int kPThreads = 512, kPBufs = 3;
+constexpr int kPWideRows = 4096;                  // rows from which column blocks are 256 wide
+// k-tile: 128 columns for int4 weights, 64 for bf16 weights
+template <bool Q4> constexpr int pkt() { return Q4 ? 128 : 64; }
+// 16-byte slots of BM rows per k-tile
+template <bool Q4, int BM> constexpr int prow_slots() { return BM * pkt<Q4>() / 8; }
+// 16-byte slots of weights per k-tile of BN columns (int4 codes or bf16)
+template <bool Q4, int BN> constexpr int pw_slots() { return Q4 ? BN * pkt<Q4>() / 32 : BN * pkt<Q4>() / 8; }
+// wavefronts along N (each 64 columns wide) and along M, rows per wavefront
+// (NTH threads, BM rows per workgroup)
+template <int BN> constexpr int pwn() { return BN / 64; }
+template <int BN, int NTH = kPThreads> constexpr int pwm() { return NTH / 64 / pwn<BN>(); }
+template <int BN, int NTH = kPThreads, int BM = kPBM> constexpr int ptm() { return BM / pwm<BN, NTH>(); }
+// int4 scale/zero words per k-tile: one for each thread, or one for each
+// (group, column) of the tile when there are more of those
+template <int G, int BN, int NTH> constexpr int psz_words() {
+  return NTH > (pkt<true>() / G) * BN ? NTH : (pkt<true>() / G) * BN;
+}
+// LDS of a workgroup: row buffers, weight buffers, scale/zero buffers (the
+// results reuse them all)
+template <bool Q4, int G, int BN, int NTH, int BM> constexpr int pstage_slots() {
+  return prow_slots<Q4, BM>() + pw_slots<Q4, BN>() + (Q4 ? psz_words<G, BN, NTH>() / 4 : 0);
+}
+template <int G, int BN, int NTH = kPThreads, int BM = kPBM> constexpr int psmem_slots() {
+  return kPBufs * (pstage_slots<true, G, BN, NTH, BM>() > pstage_slots<false, G, BN, NTH, BM>()
+                       ? pstage_slots<true, G, BN, NTH, BM>()
+                       : pstage_slots<false, G, BN, NTH, BM>());
+}
+
+
+// NTH threads take a BM x BN tile over the k-tiles kt0 .. kt0 + ntile - 1
+// (k-tiles of this weight form); with C128 the columns are mapped as 128-column
+// blocks (block colblk * BN / 128 + c / 128, column c mod 128), the layout of
+// the batched-row GEMM's partial tiles.
+template <int G, int EP, bool Q4, int BN, int NTH = kPThreads, int BM = kPBM, bool C128 = false>
+__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *smem, bool ex, int rowblk, int colblk,
+                                           int kt0, int ntile, f32x4_t (&tot)[ptm<BN, NTH, BM>() / 16][4]) {
+  constexpr int KT = pkt<Q4>(), CH = KT / 8;               // k columns and 16-byte chunks per row
+  constexpr int ASL = prow_slots<Q4, BM>(), WSL = pw_slots<Q4, BN>();
+  constexpr int NA = ASL / NTH;                            // row copies per wavefront per k-tile
+  constexpr int NW = WSL / NTH;                            // weight copies per wavefront per k-tile
+  static_assert(ASL % NTH == 0 && WSL % NTH == 0, "whole copies");
+  constexpr int SZW = psz_words<G, BN, NTH>(), NZ = Q4 ? SZW / NTH : 0;   // scale/zero copies
+  constexpr int STEPS = G / 32, GW = G / 32;
+  constexpr int NWAV = NTH / 64, WN = pwn<BN>(), TM = ptm<BN, NTH, BM>(), AF = TM / 16;
+  static_assert(TM % 16 == 0 && pwm<BN, NTH>() * WN * 64 == NTH, "wavefront grid");
+  uint4 *xs = smem, *ws = smem + kPBufs * ASL, *zs = ws + kPBufs * WSL;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, cl = lane & 15;
+  const int wm = wid / WN, wn = wid % WN;
+  const int64_t m0 = (int64_t)rowblk * BM;
+  const int KG = p.K / G;
+  auto col_of = [&](int c, int &seg, int &row, bool &valid) {
+    if constexpr (C128) map_col<EP>(p, colblk * (BN / 128) + c / 128, 128, c % 128, seg, row, valid);
+    else map_col<EP>(p, colblk, BN, c, seg, row, valid);
+  };
+
+  // ---- weights of a k-tile, copy i of this wavefront covers slots
+  //      s = (NWAV i + wid) * 64 + lane (NWAV wavefronts).  int4: column c's quarter q (its words
+  //      4q..4q+3) at slot ((c / 16) * 4 + q) * 16 + c % 16; bf16: chunk q
+  //      of column n at slot n * CH + (q ^ (n mod CH))
+  const void *wsrc[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int s = (i * NWAV + wid) * 64 + lane;
+    int c, q;
+    if constexpr (Q4) { c = (s >> 6) * 16 + (s & 15); q = (s >> 4) & 3; }
+    else { c = s / CH; q = (s % CH) ^ (c & (CH - 1)); }
+    int seg, row;
+    bool valid;
+    col_of(c, seg, row, valid);
+    if (!valid) { seg = 0; row = 0; }
+    // the segment is picked by selects, not by indexing the parameter arrays
+    // with a per-lane value (that would copy them to scratch memory)
+    if constexpr (Q4) {
+      const uint32_t *b = seg == 0 ? p.w.q4[0] : seg == 1 ? p.w.q4[1] : p.w.q4[2];
+      wsrc[i] = b + (int64_t)row * (p.K / 8) + 4 * q;
+    } else {
+      const uint16_t *b0 = ex ? p.w.ex_bf[0] : p.w.bf[0], *b1 = ex ? p.w.ex_bf[1] : p.w.bf[1],
+                     *b2 = ex ? p.w.ex_bf[2] : p.w.bf[2];
+      const uint16_t *b = seg == 0 ? b0 : seg == 1 ? b1 : b2;
+      wsrc[i] = b + (int64_t)row * p.K + 8 * q;
+    }
+  }
+  // ---- int4 scale/zero words: entry e = NTH z + 64 wid + lane of a k-tile
+  //      is group e / BN of the k-tile for column e % BN (entries past the
+  //      tile's groups repeat the last group)
+  constexpr int GPT = KT / G;                   // groups per k-tile
+  const uint32_t *zrow[NZ > 0 ? NZ : 1];
+#pragma unroll
+  for (int z = 0; z < NZ; ++z) {
+    const int e = z * NTH + wid * 64 + lane;
+    const int gi = min(e / BN, GPT - 1), c = e % BN;
+    int seg, row;
+    bool valid;
+    col_of(c, seg, row, valid);
+    if (!valid) { seg = 0; row = 0; }
+    const uint32_t *b = seg == 0 ? p.w.sz[0] : seg == 1 ? p.w.sz[1] : p.w.sz[2];
+    zrow[z] = b + (int64_t)row * KG + gi;
+  }
+
+  // ---- rows: copy i of this wavefront covers slots s = (wid * NA + i) * 64 +
+  //      lane, i.e. row s / CH, chunk (s mod CH) ^ (row mod CH)
+  const uint16_t *arow[NA];
+  int acol[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int s = (wid * NA + i) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ (r & (CH - 1));
+    const int64_t m = min(m0 + r, (int64_t)p.M - 1);      // rows past M: any valid row
+    arow[i] = p.x + m * p.ldx;
+    acol[i] = 8 * c;
+  }
+  // The copies are issued from inline assembly: the compiler then does not
+  // treat every later LDS read as possibly overlapping them (it would wait for
+  // all memory operations before each one); the loop waits for exactly the
+  // copies it needs with an explicit s_waitcnt.  m0 holds the LDS destination
+  // of a copy (each lane writes 16 bytes at m0 + 16 * lane).
+  const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_ptr_t)xs;
+  const uint32_t ws_base = (uint32_t)(uintptr_t)(lds_ptr_t)ws;
+  const uint32_t zs_base = (uint32_t)(uintptr_t)(lds_ptr_t)zs;
+  const int uwid = __builtin_amdgcn_readfirstlane(wid);
+  auto load_tile = [&](int kt) {
+    const int ktc = kt0 + min(kt, ntile - 1);              // unconditional: fixed load count
+    const int buf = kt % kPBufs;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(xs_base + (uint32_t)((buf * ASL + (uwid * NA + i) * 64) * 16));
+      const uint16_t *src = arow[i] + ktc * KT + acol[i];
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                   : "memory", "m0");
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(ws_base + (uint32_t)((buf * WSL + (i * NWAV + uwid) * 64) * 16));
+      const void *src;
+      if constexpr (Q4) src = static_cast<const uint32_t *>(wsrc[i]) + ktc * (KT / 8);
+      else src = static_cast<const uint16_t *>(wsrc[i]) + ktc * KT;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                   : "memory", "m0");
+    }
+#pragma unroll
+    for (int z = 0; z < NZ; ++z) {
+      // scale/zero words: each lane writes 4 bytes at m0 + 4 * lane
+      const uint32_t zdst =
+          __builtin_amdgcn_readfirstlane(zs_base + (uint32_t)(buf * SZW * 4 + (z * NTH + uwid * 64) * 4));
+      const uint32_t *zsrc = zrow[z] + ktc * GPT;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(zdst), "v"(zsrc)
+                   : "memory", "m0");
+    }
+  };
+  // row fragment: row 16 (wm * AF + a) + cl, chunk c of the k-tile
+  auto a_frag = [&](const uint4 *buf, int a, int c) -> bf16x8_t {
+    return __builtin_bit_cast(bf16x8_t, buf[((wm * AF + a) * 16 + cl) * CH + (c ^ (cl & (CH - 1)))]);
+  };
+
+  // int4: raw sums of a group (against the codes as 128+q per column tile,
+  // and the row sums against ones) and its scale/zero words, kept across
+  // k-tiles.  The two wavefronts of a SIMD (waves w and w + 4 of the
+  // workgroup) fold a group at different times: the first right after its
+  // MFMAs, the second after the next k-tile's barrier, before its next MFMAs.
+  // Each fold (VALU only) then runs beside the other wavefront's MFMAs
+  // instead of both folding at once while the matrix core idles.
+  f32x4_t ag[AF][4], as[AF];
+  uint32_t pz[4];
+#pragma unroll
+  for (int a = 0; a < AF; ++a) {
+    as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pz[t] = 0u;        // scale 0: a fold before any group adds nothing
+  const bool defer = Q4 && NWAV == 8 && wid >= 4;   // the second wavefront of each SIMD
+  // the group's fold: tot += s * (acc - (128 + z) * sum_k x)
+  auto fold = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float sc = bf_lo(pz[t]), zo = 128.0f + bf_hi(pz[t]);
+#pragma unroll
+      for (int a = 0; a < AF; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * as[a][v], tot[a][t][v]);
+    }
+  };
+
+  // one group of G columns of int4 weights (kl: its first column in the k-tile)
+  auto group_q4 = [&](int buf, int kl) {
+    const uint4 *xb = xs + buf * ASL;
+    // this lane's code words of the group, for each of its 4 column tiles:
+    // word j of column tile t at cb[cslot[t] + j] (read per step, so that no
+    // register array is indexed by the step)
+    const uint32_t *cb = reinterpret_cast<const uint32_t *>(ws + buf * WSL);
+    const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
+    int cslot[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cslot[t] = (((wn * 4 + t) * 4 + (wo >> 2)) * 16 + cl) * 4 + (wo & 3);
+    // the group sums of the rows come from one more MFMA per row block
+    // against a B operand of ones (row sums in every column)
+    const bf16x8_t ones =
+        __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    if (defer) fold();                           // the previous group's
+    // one k-step of 32: the row fragments (lane quarter qq takes chunk
+    // (kl + qq G/4) / 8 + j), then one column tile at a time (its unpacked
+    // operand feeds the AF MFMAs of the step and is dead after them); the
+    // first step of a group starts its sums from zero
+    auto kstep = [&](int j, bool first) {
+      bf16x8_t af[AF];
+#pragma unroll
+      for (int a = 0; a < AF; ++a) af[a] = a_frag(xb, a, kl / 8 + qq * (G / 32) + j);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t pr[4];
+        unpack_word(cb[cslot[t] + j], pr);
+        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+          ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, first ? zero4 : ag[a][t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int a = 0; a < AF; ++a)
+        as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, first ? zero4 : as[a], 0, 0, 0);
+    };
+    kstep(0, true);
+#pragma unroll
+    for (int j = 1; j < STEPS; ++j) kstep(j, false);
+    // this group's scale/zero words (read now: the buffer is refilled
+    // after the next barrier)
+    const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs) + buf * SZW + (kl / G) * BN + wn * 64 + cl;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pz[t] = zb[t * 16];
+    if (!defer) fold();
+  };
+
+  // a k-tile of bf16 weights: two k-steps of 32 in the natural order (lane
+  // quarter qq takes chunk 4 j + qq)
+  auto tile_bf16 = [&](int buf) {
+    const uint4 *xb = xs + buf * ASL, *wb = ws + buf * WSL;
+#pragma unroll
+    for (int j = 0; j < KT / 32; ++j) {
+      bf16x8_t af[AF];
+#pragma unroll
+      for (int a = 0; a < AF; ++a) af[a] = a_frag(xb, a, 4 * j + qq);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sl = ((wn * 4 + t) * 16 + cl) * CH + ((4 * j + qq) ^ (cl & (CH - 1)));
+        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, wb[sl]);
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+          tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, tot[a][t], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < kPBufs - 1; ++t) load_tile(t);
+  for (int kt = 0; kt < ntile; ++kt) {
+    // tile kt has landed once no more than the copies of the next
+    // kPBufs - 2 k-tiles are outstanding (every copy is unconditional, so the
+    // count holds throughout)
+    constexpr int per_tile = NA + NW + NZ;
+    constexpr int later = (kPBufs - 2) * per_tile;
+    static_assert(later < 64, "vmcnt field");
+    // s_waitcnt: vmcnt = later, expcnt and lgkmcnt not waited for
+    __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
+    __syncthreads();                        // tile kt visible; tile kt-1 done everywhere
+    load_tile(kt + kPBufs - 1);             // into the buffer tile kt-1 used
+    const int buf = kt % kPBufs;
+    if constexpr (Q4) {
+#pragma unroll
+      for (int g = 0; g < GPT; ++g) group_q4(buf, g * G);
+    } else {
+      tile_bf16(buf);
+    }
+  }
+  if (defer) fold();                             // the last group's
+  // the last k-tiles' spare copies may still be landing in LDS, which the
+  // results reuse: wait for every memory operation, then for every wavefront
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// ===========================================================================
 // Batched-row GEMM for 9..64 rows: Y[m][n] = sum_k X[m][k] W[n][k].
 //   A workgroup (4 wavefronts x 2 column tiles of 16 = 128 columns) takes one
 //   split of K.  Every lane loads the weights of its own output column straight
@@ -945,11 +1259,15 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
     bool valid;
     map_col<EP>(p, colblk, BN, wid * (NT * 16) + t * 16 + cl, seg, row, valid);
     if (!valid) { seg = 0; row = 0; }      // a valid row; its results are dropped
+    // segments picked by selects (a per-lane index into the parameter arrays
+    // would copy them to scratch memory)
     if constexpr (Q4) {
-      qrow[t] = p.w.q4[seg] + (int64_t)row * (p.K / 8);
-      zrow[t] = p.w.sz[seg] + (int64_t)row * KG;
+      qrow[t] = (seg == 0 ? p.w.q4[0] : seg == 1 ? p.w.q4[1] : p.w.q4[2]) + (int64_t)row * (p.K / 8);
+      zrow[t] = (seg == 0 ? p.w.sz[0] : seg == 1 ? p.w.sz[1] : p.w.sz[2]) + (int64_t)row * KG;
     } else {
-      brow[t] = (ex ? p.w.ex_bf[seg] : p.w.bf[seg]) + (int64_t)row * p.K;
+      const uint16_t *b0 = ex ? p.w.ex_bf[0] : p.w.bf[0], *b1 = ex ? p.w.ex_bf[1] : p.w.bf[1],
+                     *b2 = ex ? p.w.ex_bf[2] : p.w.bf[2];
+      brow[t] = (seg == 0 ? b0 : seg == 1 ? b1 : b2) + (int64_t)row * p.K;
     }
   }
 
@@ -1092,11 +1410,54 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
   }
 }
 
+// int4 layers through the copy ring (p.ring): 256-column blocks of the rows
+// (ROWS = 16 MB of them) over one K split, on the prefill GEMM's body with 256
+// threads (4 wavefronts of 64 columns); rows, codes and scale/zero words
+// reach LDS by DMA, three k-tiles deep.  The partial tile goes out in the
+// 128-column layout that the reduce kernel adds (the plan always splits K).
+template <int MB> constexpr int mgemm_ring_bm() { return MB * 16; }
+template <int MB, int G> constexpr int mgemm_ring_bytes() {
+  return kPBufs * pstage_slots<true, G, 256, 256, mgemm_ring_bm<MB>()>() * 16;   // int4 stages only
+}
+
+template <int MB, int G, int EP>
+__device__ void mgemm_ring(const GemmParams &p, uint4 *smem, bool ex) {
+  constexpr int BM = mgemm_ring_bm<MB>(), AF = ptm<256, 256, BM>() / 16;
+  static_assert(AF == MB, "one wavefront row: MB row blocks");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, cl = lane & 15;
+  const int nsplit = p.nsplit;
+  const int cb = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+  const int ncols = EP == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
+  if (cb * 256 >= ncols) return;                 // the grid is laid out for 128-column blocks
+  const int ncb128 = (ncols + kMgemmBN - 1) / kMgemmBN;
+  f32x4_t tot[AF][4];
+#pragma unroll
+  for (int a = 0; a < AF; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kpt = p.ks / pkt<true>();           // k-tiles per split
+  pgemm_body<G, EP, true, 256, 256, BM, true>(p, smem, ex, 0, cb, split * kpt, kpt, tot);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = wid * 64 + t * 16 + cl;
+    const int cb128 = cb * 2 + (col >> 7);
+    if (cb128 >= ncb128) continue;
+    float *mine = p.part + ((int64_t)cb128 * nsplit + split) * (BM * kMgemmBN) + (col & (kMgemmBN - 1));
+#pragma unroll
+    for (int a = 0; a < AF; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mine[(a * 16 + 4 * qq + v) * kMgemmBN] = tot[a][t][v];
+  }
+}
+
 template <int MB, int G, int EP>
 __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
   typedef MgemmShape<MB, G> S;
   constexpr int NT = S::NT, BN = S::BN, ROWS = S::ROWS, KS = S::KS;
-  __shared__ __align__(16) char smem[S::SMEM];
+  // LDS: the staged rows of the register path, or the ring of the int4 path
+  constexpr int SM = S::SMEM > mgemm_ring_bytes<MB, G>() ? S::SMEM : mgemm_ring_bytes<MB, G>();
+  __shared__ __align__(16) char smem[SM];
   __shared__ float xsg[ROWS * (KS / G)];
   __shared__ uint64_t rowkey[ROWS];
   __shared__ int last_flag;
@@ -1105,6 +1466,12 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
 
   const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
+  if constexpr (EP != kEpLogits) {
+    if (q4 && p.ring) {
+      mgemm_ring<MB, G, EP>(p, reinterpret_cast<uint4 *>(smem), ex);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
   const int split = blockIdx.x % p.nsplit, colblk = blockIdx.x / p.nsplit;
@@ -1198,8 +1565,43 @@ MgemmPlan mgemm_plan(int M, int ncols, int K, bool allow_split) {
 }
 MgemmPlan mgemm_plan(int M, int ncols, int K) { return mgemm_plan(M, ncols, K, true); }
 
+// Plan of a linear whose layer may run on its int4 copy: the int4 path goes
+// through the copy ring in 256-column blocks, and K is split into whole
+// k-tiles of 128, at least two splits, the fewest that give a workgroup per CU
+// (256 on this chip); the register path of the bf16 layers takes the same
+// split (the weight form is chosen on the device), so a split also stays
+// within the rows it can stage.
+static bool mgemm_ring_ok(Epilogue ep, const GemmParams &p) {
+  return ep != kEpLogits && p.layer >= 0 && p.exit_mode == RIVER_EXIT_INT4 && p.path != kPathBackbone &&
+         p.K % (2 * pkt<true>()) == 0;
+}
+static MgemmPlan mgemm_ring_plan(int M, int ncols, int K) {
+  MgemmPlan pl{};
+  pl.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  pl.ncolblk = (ncols + kMgemmBN - 1) / kMgemmBN;
+  const int KS = pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512;
+  const int nt = K / pkt<true>(), ncb = (ncols + 255) / 256;
+  constexpr int kMinKs = 512;                   // K columns per split at least (measured best)
+  int best = 0;
+  for (int d = 2; d <= nt; ++d) {
+    if (nt % d != 0 || K / d > KS) continue;
+    if (best && K / d < kMinKs) break;
+    best = d;
+    if (ncb * d >= 256) break;
+  }
+  pl.nsplit = best;
+  pl.ks = best ? K / best : 0;
+  return pl;
+}
+
 int64_t mgemm_part_floats(const MgemmPlan &pl) {
   return pl.nsplit > 1 ? (int64_t)pl.ncolblk * pl.nsplit * (pl.mb * 16) * kMgemmBN : 0;
+}
+
+int64_t mgemm_part_floats_max(int M, int ncols, int K) {
+  int64_t f = mgemm_part_floats(mgemm_plan(M, ncols, K));
+  if (K % (2 * pkt<true>()) == 0) f = std::max(f, mgemm_part_floats(mgemm_ring_plan(M, ncols, K)));
+  return f;
 }
 
 template <int MB>
@@ -1242,12 +1644,15 @@ static hipError_t mgemm_launch_mb(Epilogue ep, const GemmParams &p, int ncolblk,
 hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
   if (p.M < 1 || p.M > 64 || p.K % p.G || (p.G != 64 && p.G != 128)) return hipErrorInvalidValue;
   const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
-  const MgemmPlan pl = mgemm_plan(p.M, ncols, p.K, ep != kEpLogits);
+  const bool ring = mgemm_ring_ok(ep, p);
+  const MgemmPlan pl = ring ? mgemm_ring_plan(p.M, ncols, p.K) : mgemm_plan(p.M, ncols, p.K, ep != kEpLogits);
+  if (ring && pl.nsplit < 2) return hipErrorInvalidValue;
   if (pl.nsplit > 1 && (!p.part || mgemm_part_floats(pl) > p.part_cap)) return hipErrorInvalidValue;
   if (pl.ks > (pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512)) return hipErrorInvalidValue;
   GemmParams q = p;
   q.nsplit = pl.nsplit;
   q.ks = pl.ks;
+  q.ring = ring ? 1 : 0;
   switch (pl.mb) {
     case 1: return mgemm_launch_mb<1>(ep, q, pl.ncolblk, s);
     case 2: return mgemm_launch_mb<2>(ep, q, pl.ncolblk, s);
@@ -1256,310 +1661,11 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 }
 
 
-// ===========================================================================
-// Prefill GEMM for many rows: Y[m][n] = sum_k X[m][k] W[n][k] on
-// v_mfma_f32_16x16x32_bf16.  Workgroup tile 128 rows x BN columns, eight
-// wavefronts of 64 columns each: BN = 128 as 4 x 2 wavefronts of 32 x 64, BN
-// = 256 (from 4,096 rows) as 2 x 4 of 64 x 64, where every B operand feeds
-// four MFMAs instead of two; two wavefronts per SIMD so that one's waits
-// overlap the other's MFMAs.
-//   Every operand goes straight from memory into LDS (global_load_lds, no
-//   registers), three k-tile buffers, so two tiles are in flight while one
-//   feeds the MFMAs.  Rows (and bf16 weight rows) are stored whole, their
-//   16-byte chunks XOR-swizzled (chunk c of row r at slot r * CH + (c ^ (r mod
-//   CH)), CH chunks per row), so that one copy instruction reads whole rows
-//   from memory.  A 16-byte LDS read runs at the full rate only when each
-//   quarter wavefront (16 lanes) reads one contiguous 256-byte block; the
-//   fragment reads here (16 rows at one chunk) take about 1.45x that, but a
-//   layout with conflict-free fragment reads needs copies of 64 bytes per row
-//   and measured slower overall (int4 -8%, bf16 -20%).
-//   int4 weights: k-tiles of 128; the codes of 16 columns stored as 4 blocks
-//   of (one quarter's 4 words of each column), so that each quarter of a code
-//   read is one 256-byte block; the scale/zero words beside them (per-group
-//   accumulation, lane quarters over G/4 codes, group fold
-//   tot += s * (acc - (128 + z) * sum_k x), the row sums of each group from
-//   one more MFMA per row block against a B operand of ones).
-//   bf16 weights: k-tiles of 64 (rows and weights of three tiles then fit
-//   the same LDS).
-//   Workgroups are ordered in groups of 8 row blocks so that the rows and
-//   weights they share stay in L2.
-// ===========================================================================
-constexpr int kPBM = 128, kPGroupRows = 8;
-constexpr int kPThreads = 512, kPBufs = 3;
-constexpr int kPWideRows = 4096;                  // rows from which column blocks are 256 wide
-// k-tile: 128 columns for int4 weights, 64 for bf16 weights
-template <bool Q4> constexpr int pkt() { return Q4 ? 128 : 64; }
-// 16-byte slots of rows per k-tile
-template <bool Q4> constexpr int prow_slots() { return kPBM * pkt<Q4>() / 8; }
-// 16-byte slots of weights per k-tile of BN columns (int4 codes or bf16)
-template <bool Q4, int BN> constexpr int pw_slots() { return Q4 ? BN * pkt<Q4>() / 32 : BN * pkt<Q4>() / 8; }
-// wavefronts along N (each 64 columns wide) and along M, rows per wavefront
-template <int BN> constexpr int pwn() { return BN / 64; }
-template <int BN> constexpr int pwm() { return 8 / pwn<BN>(); }
-template <int BN> constexpr int ptm() { return kPBM / pwm<BN>(); }
-// 16-byte slots of int4 scale/zero words per k-tile: one word for each of
-// the 512 lanes of the workgroup (at most 2 groups x 256 columns are used)
-constexpr int kPSzSlots = 128;
-// LDS of a workgroup: row buffers, weight buffers, scale/zero buffers (the
-// results reuse them all)
-template <bool Q4, int BN> constexpr int pstage_slots() {
-  return prow_slots<Q4>() + pw_slots<Q4, BN>() + (Q4 ? kPSzSlots : 0);
-}
-template <int BN> constexpr int psmem_slots() {
-  return kPBufs * (pstage_slots<true, BN>() > pstage_slots<false, BN>() ? pstage_slots<true, BN>()
-                                                                          : pstage_slots<false, BN>());
-}
-
-
-template <int G, int EP, bool Q4, int BN>
-__device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *smem, bool ex, int rowblk, int colblk,
-                                           f32x4_t (&tot)[ptm<BN>() / 16][4]) {
-  constexpr int KT = pkt<Q4>(), CH = KT / 8;               // k columns and 16-byte chunks per row
-  constexpr int ASL = prow_slots<Q4>(), WSL = pw_slots<Q4, BN>();
-  constexpr int NA = ASL / kPThreads;                      // row copies per wavefront per k-tile
-  constexpr int NW = WSL / kPThreads;                      // weight copies per wavefront per k-tile
-  static_assert(ASL % kPThreads == 0 && WSL % kPThreads == 0, "whole copies");
-  constexpr int STEPS = G / 32, GW = G / 32;
-  constexpr int WN = pwn<BN>(), TM = ptm<BN>(), AF = TM / 16;
-  uint4 *xs = smem, *ws = smem + kPBufs * ASL, *zs = ws + kPBufs * WSL;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int qq = lane >> 4, cl = lane & 15;
-  const int wm = wid / WN, wn = wid % WN;
-  const int64_t m0 = (int64_t)rowblk * kPBM;
-  const int KG = p.K / G;
-  const int ntile = p.K / KT;
-
-  // ---- weights of a k-tile, copy i of this wavefront covers slots
-  //      s = (8 i + wid) * 64 + lane.  int4: column c's quarter q (its words
-  //      4q..4q+3) at slot ((c / 16) * 4 + q) * 16 + c % 16; bf16: chunk q
-  //      of column n at slot n * CH + (q ^ (n mod CH))
-  const void *wsrc[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int s = (i * 8 + wid) * 64 + lane;
-    int c, q;
-    if constexpr (Q4) { c = (s >> 6) * 16 + (s & 15); q = (s >> 4) & 3; }
-    else { c = s / CH; q = (s % CH) ^ (c & (CH - 1)); }
-    int seg, row;
-    bool valid;
-    map_col<EP>(p, colblk, BN, c, seg, row, valid);
-    if (!valid) { seg = 0; row = 0; }
-    // the segment is picked by selects, not by indexing the parameter arrays
-    // with a per-lane value (that would copy them to scratch memory)
-    if constexpr (Q4) {
-      const uint32_t *b = seg == 0 ? p.w.q4[0] : seg == 1 ? p.w.q4[1] : p.w.q4[2];
-      wsrc[i] = b + (int64_t)row * (p.K / 8) + 4 * q;
-    } else {
-      const uint16_t *b0 = ex ? p.w.ex_bf[0] : p.w.bf[0], *b1 = ex ? p.w.ex_bf[1] : p.w.bf[1],
-                     *b2 = ex ? p.w.ex_bf[2] : p.w.bf[2];
-      const uint16_t *b = seg == 0 ? b0 : seg == 1 ? b1 : b2;
-      wsrc[i] = b + (int64_t)row * p.K + 8 * q;
-    }
-  }
-  // ---- int4 scale/zero words: entry e = 64 wid + lane of a k-tile is
-  //      group e / BN of the k-tile for column e % BN (entries past the
-  //      tile's groups repeat the last group)
-  constexpr int GPT = KT / G;                   // groups per k-tile
-  const uint32_t *zrow = nullptr;
-  if constexpr (Q4) {
-    const int e = wid * 64 + lane;
-    const int gi = min(e / BN, GPT - 1), c = e % BN;
-    int seg, row;
-    bool valid;
-    map_col<EP>(p, colblk, BN, c, seg, row, valid);
-    if (!valid) { seg = 0; row = 0; }
-    const uint32_t *b = seg == 0 ? p.w.sz[0] : seg == 1 ? p.w.sz[1] : p.w.sz[2];
-    zrow = b + (int64_t)row * KG + gi;
-  }
-
-  // ---- rows: copy i of this wavefront covers slots s = (wid * NA + i) * 64 +
-  //      lane, i.e. row s / CH, chunk (s mod CH) ^ (row mod CH)
-  const uint16_t *arow[NA];
-  int acol[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int s = (wid * NA + i) * 64 + lane;
-    const int r = s / CH, c = (s % CH) ^ (r & (CH - 1));
-    const int64_t m = min(m0 + r, (int64_t)p.M - 1);      // rows past M: any valid row
-    arow[i] = p.x + m * p.ldx;
-    acol[i] = 8 * c;
-  }
-  // The copies are issued from inline assembly: the compiler then does not
-  // treat every later LDS read as possibly overlapping them (it would wait for
-  // all memory operations before each one); the loop waits for exactly the
-  // copies it needs with an explicit s_waitcnt.  m0 holds the LDS destination
-  // of a copy (each lane writes 16 bytes at m0 + 16 * lane).
-  const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_ptr_t)xs;
-  const uint32_t ws_base = (uint32_t)(uintptr_t)(lds_ptr_t)ws;
-  const uint32_t zs_base = (uint32_t)(uintptr_t)(lds_ptr_t)zs;
-  const int uwid = __builtin_amdgcn_readfirstlane(wid);
-  auto load_tile = [&](int kt) {
-    const int ktc = min(kt, ntile - 1);                    // unconditional: fixed load count
-    const int buf = kt % kPBufs;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const uint32_t dst =
-          __builtin_amdgcn_readfirstlane(xs_base + (uint32_t)((buf * ASL + (uwid * NA + i) * 64) * 16));
-      const uint16_t *src = arow[i] + ktc * KT + acol[i];
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
-                   : "memory", "m0");
-    }
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint32_t dst =
-          __builtin_amdgcn_readfirstlane(ws_base + (uint32_t)((buf * WSL + (i * 8 + uwid) * 64) * 16));
-      const void *src;
-      if constexpr (Q4) src = static_cast<const uint32_t *>(wsrc[i]) + ktc * (KT / 8);
-      else src = static_cast<const uint16_t *>(wsrc[i]) + ktc * KT;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
-                   : "memory", "m0");
-    }
-    if constexpr (Q4) {
-      // scale/zero words: each lane writes 4 bytes at m0 + 4 * lane
-      const uint32_t zdst =
-          __builtin_amdgcn_readfirstlane(zs_base + (uint32_t)((buf * kPSzSlots) * 16 + uwid * 256));
-      const uint32_t *zsrc = zrow + ktc * GPT;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(zdst), "v"(zsrc)
-                   : "memory", "m0");
-    }
-  };
-  // row fragment: row 16 (wm * AF + a) + cl, chunk c of the k-tile
-  auto a_frag = [&](const uint4 *buf, int a, int c) -> bf16x8_t {
-    return __builtin_bit_cast(bf16x8_t, buf[((wm * AF + a) * 16 + cl) * CH + (c ^ (cl & (CH - 1)))]);
-  };
-
-  // int4: raw sums of a group (against the codes as 128+q per column tile,
-  // and the row sums against ones) and its scale/zero words, kept across
-  // k-tiles.  The two wavefronts of a SIMD (waves w and w + 4 of the
-  // workgroup) fold a group at different times: the first right after its
-  // MFMAs, the second after the next k-tile's barrier, before its next MFMAs.
-  // Each fold (VALU only) then runs beside the other wavefront's MFMAs
-  // instead of both folding at once while the matrix core idles.
-  f32x4_t ag[AF][4], as[AF];
-  uint32_t pz[4];
-#pragma unroll
-  for (int a = 0; a < AF; ++a) {
-    as[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ag[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) pz[t] = 0u;        // scale 0: a fold before any group adds nothing
-  const bool defer = Q4 && wid >= 4;             // the second wavefront of each SIMD
-  // the group's fold: tot += s * (acc - (128 + z) * sum_k x)
-  auto fold = [&]() {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float sc = bf_lo(pz[t]), zo = 128.0f + bf_hi(pz[t]);
-#pragma unroll
-      for (int a = 0; a < AF; ++a)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tot[a][t][v] = fmaf(sc, ag[a][t][v] - zo * as[a][v], tot[a][t][v]);
-    }
-  };
-
-  // one group of G columns of int4 weights (kl: its first column in the k-tile)
-  auto group_q4 = [&](int buf, int kl) {
-    const uint4 *xb = xs + buf * ASL;
-    // this lane's code words of the group, for each of its 4 column tiles:
-    // word j of column tile t at cb[cslot[t] + j] (read per step, so that no
-    // register array is indexed by the step)
-    const uint32_t *cb = reinterpret_cast<const uint32_t *>(ws + buf * WSL);
-    const int wo = (kl / G) * (G / 8) + qq * GW;        // first word within the column's 16
-    int cslot[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) cslot[t] = (((wn * 4 + t) * 4 + (wo >> 2)) * 16 + cl) * 4 + (wo & 3);
-    // the group sums of the rows come from one more MFMA per row block
-    // against a B operand of ones (row sums in every column)
-    const bf16x8_t ones =
-        __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    if (defer) fold();                           // the previous group's
-    // one k-step of 32: the row fragments (lane quarter qq takes chunk
-    // (kl + qq G/4) / 8 + j), then one column tile at a time (its unpacked
-    // operand feeds the AF MFMAs of the step and is dead after them); the
-    // first step of a group starts its sums from zero
-    auto kstep = [&](int j, bool first) {
-      bf16x8_t af[AF];
-#pragma unroll
-      for (int a = 0; a < AF; ++a) af[a] = a_frag(xb, a, kl / 8 + qq * (G / 32) + j);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t pr[4];
-        unpack_word(cb[cslot[t] + j], pr);
-        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, make_uint4(pr[0], pr[1], pr[2], pr[3]));
-#pragma unroll
-        for (int a = 0; a < AF; ++a)
-          ag[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, first ? zero4 : ag[a][t], 0, 0, 0);
-      }
-#pragma unroll
-      for (int a = 0; a < AF; ++a)
-        as[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], ones, first ? zero4 : as[a], 0, 0, 0);
-    };
-    kstep(0, true);
-#pragma unroll
-    for (int j = 1; j < STEPS; ++j) kstep(j, false);
-    // this group's scale/zero words (read now: the buffer is refilled
-    // after the next barrier)
-    const uint32_t *zb = reinterpret_cast<const uint32_t *>(zs + buf * kPSzSlots) + (kl / G) * BN + wn * 64 + cl;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) pz[t] = zb[t * 16];
-    if (!defer) fold();
-  };
-
-  // a k-tile of bf16 weights: two k-steps of 32 in the natural order (lane
-  // quarter qq takes chunk 4 j + qq)
-  auto tile_bf16 = [&](int buf) {
-    const uint4 *xb = xs + buf * ASL, *wb = ws + buf * WSL;
-#pragma unroll
-    for (int j = 0; j < KT / 32; ++j) {
-      bf16x8_t af[AF];
-#pragma unroll
-      for (int a = 0; a < AF; ++a) af[a] = a_frag(xb, a, 4 * j + qq);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int sl = ((wn * 4 + t) * 16 + cl) * CH + ((4 * j + qq) ^ (cl & (CH - 1)));
-        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, wb[sl]);
-#pragma unroll
-        for (int a = 0; a < AF; ++a)
-          tot[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr, tot[a][t], 0, 0, 0);
-      }
-    }
-  };
-
-#pragma unroll
-  for (int t = 0; t < kPBufs - 1; ++t) load_tile(t);
-  for (int kt = 0; kt < ntile; ++kt) {
-    // tile kt has landed once no more than the copies of the next
-    // kPBufs - 2 k-tiles are outstanding (every copy is unconditional, so the
-    // count holds throughout)
-    constexpr int per_tile = NA + NW + (Q4 ? 1 : 0);
-    constexpr int later = (kPBufs - 2) * per_tile;
-    static_assert(later < 64, "vmcnt field");
-    // s_waitcnt: vmcnt = later, expcnt and lgkmcnt not waited for
-    __builtin_amdgcn_s_waitcnt((later & 0xF) | (0x7 << 4) | (0xF << 8) | ((later >> 4) << 14));
-    __syncthreads();                        // tile kt visible; tile kt-1 done everywhere
-    load_tile(kt + kPBufs - 1);             // into the buffer tile kt-1 used
-    const int buf = kt % kPBufs;
-    if constexpr (Q4) {
-#pragma unroll
-      for (int g = 0; g < GPT; ++g) group_q4(buf, g * G);
-    } else {
-      tile_bf16(buf);
-    }
-  }
-  if (defer) fold();                             // the last group's
-  // the last k-tiles' spare copies may still be landing in LDS, which the
-  // results reuse: wait for every memory operation, then for every wavefront
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-}
-
 template <int G, int EP, int BN>
 __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
   // three stages of rows and weights (and int4 scale/zero words); the
   // results reuse them
-  __shared__ __align__(16) uint4 smem[psmem_slots<BN>()];
+  __shared__ __align__(16) uint4 smem[psmem_slots<G, BN>()];
   constexpr int AF = ptm<BN>() / 16;
   bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   // grouped order: kPGroupRows row blocks share the weights of each column block
@@ -1577,15 +1683,15 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true, BN>(p, smem, ex, rowblk, colblk, tot);
-  else pgemm_body<G, EP, false, BN>(p, smem, ex, rowblk, colblk, tot);
+  if (q4) pgemm_body<G, EP, true, BN>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<true>(), tot);
+  else pgemm_body<G, EP, false, BN>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<false>(), tot);
 
   // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
   const int wm = wid / pwn<BN>(), wn = wid % pwn<BN>();
   float *Cs = reinterpret_cast<float *>(smem);
-  static_assert(kPBM * (BN + 1) * 4 <= psmem_slots<BN>() * 16, "the results fit the buffers");
+  static_assert(kPBM * (BN + 1) * 4 <= psmem_slots<G, BN>() * 16, "the results fit the buffers");
 #pragma unroll
   for (int a = 0; a < AF; ++a)
 #pragma unroll

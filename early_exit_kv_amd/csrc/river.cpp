@@ -92,7 +92,7 @@ Workspace workspace_layout(const river_config &c) {
     const int rows[3] = {std::min(c.max_batch, 16), std::min(c.max_batch, 32), c.max_batch};
     for (int M : rows)
       for (auto &sh : shapes)
-        mg = std::max<int64_t>(mg, mgemm_part_floats(mgemm_plan(M, sh[0], sh[1])));
+        mg = std::max<int64_t>(mg, mgemm_part_floats_max(M, sh[0], sh[1]));
   }
   w.mg_part_floats = std::max<int64_t>(mg, 1);
   w.mg_part = take((size_t)w.mg_part_floats * 4);
@@ -1223,8 +1223,7 @@ int debug_linear(river_ctx *ctx, int32_t layer, int32_t linear, int32_t use_exit
       // the decode core of 9..64 rows
       g.part = part;
       g.part_cap = part_cap;
-      const MgemmPlan pl = mgemm_plan(M, sh[linear].N, sh[linear].K);
-      if (pl.nsplit > 1 && mgemm_part_floats(pl) > part_cap) return RIVER_E_BAD_SIZE;
+      if (mgemm_part_floats_max(M, sh[linear].N, sh[linear].K) > part_cap) return RIVER_E_BAD_SIZE;
       RV_TRY(launch_mgemm(kEpPlain, g, ctx->stream));
     } else {
       RV_TRY(launch_prefill_gemm(kEpPlain, g, ctx->stream));   // the prefill core

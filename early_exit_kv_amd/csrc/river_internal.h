@@ -270,6 +270,7 @@ struct GemmParams {
   float *part;                                               // split-K partial tiles
   int64_t part_cap;                                          // floats at part
   int nsplit, ks;                                            // K splits, K per split
+  int ring;                                                  // int4 through the copy ring (set at launch)
 };
 
 // Batched-row GEMM for 9..64 rows (decode of larger batches, LM head of
@@ -280,6 +281,9 @@ constexpr int kMgemmBN = 128;
 struct MgemmPlan { int mb, ncolblk, nsplit, ks; };
 MgemmPlan mgemm_plan(int M, int ncols, int K);
 int64_t mgemm_part_floats(const MgemmPlan &pl);
+// split-K partial floats the launch of a linear of ncols x K at M rows may
+// need (either plan)
+int64_t mgemm_part_floats_max(int M, int ncols, int K);
 hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 hipError_t launch_gemm(Epilogue ep, const GemmParams &p, hipStream_t s);
 // Prefill GEMM for many rows (128 x 128 tiles; shapes where pgemm_fits holds).
