@@ -8,6 +8,7 @@
 // sequence-level exit in prefill, token-level exit in generation).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -61,6 +62,11 @@ void bank_offsets(const river_config &c, int layer, int linear, bool copy, size_
   *sz = copy ? 0 : off + szo;
 }
 
+// Decode steps of at least this many rows run RMSNorm and the exit test as
+// row kernels and the normalised-input linears on the batched-row GEMM.
+constexpr int kRowsPathMin = 5;
+
+
 size_t bank_bytes(const river_config &c, bool copy) { return (size_t)c.n_layers * layer_region(c, copy); }
 
 Workspace workspace_layout(const river_config &c) {
@@ -83,9 +89,9 @@ Workspace workspace_layout(const river_config &c) {
   w.attn_splits = (c.max_seq + kAttnSub - 1) / kAttnSub;  // the most any batch size uses
   w.attn_part = take((size_t)c.max_batch * c.n_q_heads * w.attn_splits * (c.head_dim + 2) * 4);
   w.rope = take((size_t)c.max_seq * (c.head_dim / 2) * 8);
-  // split-K partials of the batched-row GEMM (decode steps of more than 8 rows)
+  // split-K partials of the batched-row GEMM (decode steps on the row-kernel path)
   int64_t mg = 0;
-  if (c.max_batch > 8) {
+  if (c.max_batch >= kRowsPathMin) {
     const int kd = c.n_kv_heads * c.head_dim;
     const int shapes[5][2] = {{qd + 2 * kd, c.d_model}, {c.d_model, qd}, {2 * c.ffn_dim, c.d_model},
                               {c.d_model, c.ffn_dim}, {c.vocab, c.d_model}};
@@ -209,7 +215,7 @@ int supported(const river_config *c) {
   if (gq != 1 && gq != 2 && gq != 4) return RIVER_E_UNIMPLEMENTED;
   if (c->max_batch > 64) return RIVER_E_UNIMPLEMENTED;
   // more than 8 rows per decode step run on the batched-row MFMA GEMM
-  if (c->max_batch > 8 && G != 64 && G != 128) return RIVER_E_UNIMPLEMENTED;
+  if (c->max_batch >= kRowsPathMin && G != 64 && G != 128) return RIVER_E_UNIMPLEMENTED;
   if (c->ffn_dim % 32) return RIVER_E_UNIMPLEMENTED;
   return RIVER_OK;
 }
@@ -348,13 +354,63 @@ int enqueue_lm_head_rows(river_ctx *ctx, const float *h, int64_t stride, int B, 
   return RIVER_OK;
 }
 
-// Decode step of more than 8 rows: every linear on the batched-row MFMA GEMM,
-// RMSNorm and the exit test as row kernels (the test is the same batch-min
-// rule; its flag is read by the next layer's GEMMs).
+// Whether a decode step takes the row-kernel path (see below): always above 8
+// rows; from kRowsPathMin rows unless a comparator other than the method
+// itself runs, the backbone sits in host memory or a GEMV kind is forced
+// (those keep the fused GEMVs up to 8 rows).
+bool use_rows_path(const river_ctx *ctx) {
+  if (ctx->batch > 8) return true;
+  return ctx->batch >= kRowsPathMin && ctx->strategy == kStratRiver && ctx->gemv_mode == 0 &&
+         std::none_of(ctx->remote.begin(), ctx->remote.end(), [](char r) { return r != 0; });
+}
+
+// Common fields of a decode GEMV of layer l over B rows.
+GemvParams gemv_base(river_ctx *ctx, int l, int B) {
+  const river_config &c = ctx->cfg;
+  GemvParams g{};
+  g.G = c.group_size; g.layer = l; g.exit_mode = ctx->exit_mode; g.ctrl = ctx->ctrl; g.B = B;
+  g.gemv_mode = ctx->gemv_mode;
+  g.gshift = __builtin_ctz((unsigned)c.group_size);
+  g.eps = c.rms_eps; g.Hq = c.n_q_heads; g.Hkv = c.n_kv_heads; g.Dh = c.head_dim;
+  g.max_seq = c.max_seq; g.max_batch = c.max_batch; g.rope_theta = c.rope_theta;
+  g.rope = at<const float2>(ctx->ws, ctx->wl.rope);
+  g.n_layers = c.n_layers;
+  // a forced exit layer fixes every weight choice on the host: no kernel
+  // then waits for the device flag before streaming its weights
+  if (ctx->force_E >= 0 && l >= 0) g.path = l >= ctx->force_E ? kPathExit : kPathBackbone;
+  return g;
+}
+
+// Final RMSNorm + LM head + argmax of B <= 8 decode rows on the GEMV.
+int enqueue_lm_head_gemv(river_ctx *ctx, const float *h, int B, float *logits, int32_t *next,
+                         hipStream_t s) {
+  const river_config &c = ctx->cfg;
+  GemvParams lm{};
+  lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
+  lm.gemv_mode = ctx->gemv_mode;
+  lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
+  lm.gshift = __builtin_ctz((unsigned)c.group_size);
+  lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
+  lm.h_src = h; lm.h_stride = c.d_model; lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
+  lm.logits = logits; lm.next = next; lm.is_prefill = 0; lm.vocab = c.vocab;
+  TIMED(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
+  return RIVER_OK;
+}
+
+// Decode step on row kernels: RMSNorm and the exit test as row kernels (the
+// test is the same batch-min rule; its flag is read by the next layer's
+// GEMMs), the linears with normalised inputs (q|k|v, gate|up) on the
+// batched-row MFMA GEMM.  More than 8 rows: o and down there too.  5..8 rows
+// (kRowsPathMin): o and down on the matrix-core GEMV with the bf16 rows
+// through its load ring, and the LM head on the GEMV; normalising the rows
+// once per layer here beats staging them normalised in every workgroup of
+// the fused GEMVs (8B shape, 8 rows: q|k|v 26.0 -> 14.5 us, gate|up 35.3 ->
+// 29.5 us), while o and down stay faster on the GEMV.
 int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next,
                         int only) {
   const river_config &c = ctx->cfg;
   const int B = ctx->batch;
+  const bool few = B <= 8;
   hipStream_t s = ctx->stream;
   float *hA = at<float>(ctx->ws, ctx->wl.hA), *hB = at<float>(ctx->ws, ctx->wl.hB);
   uint16_t *x = at<uint16_t>(ctx->ws, ctx->wl.x);
@@ -401,11 +457,19 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     TIMED_ONLY(RIVER_K_ATTN, launch_attn_decode(a, s));
     RV_TRY(rec.put(l, rec.lay.attn, a.out, qbytes));
 
-    GemmParams o = mgemm_base(ctx, l, B);
-    fill_weights(ctx, l, 3, 1, o.w);
-    o.N = c.d_model; o.K = qd; o.x = a.out; o.ldx = qd;
-    o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
-    TIMED_ONLY(RIVER_K_O, launch_mgemm(kEpResid, o, s));
+    if (few) {
+      GemvParams o = gemv_base(ctx, l, B);
+      fill_weights(ctx, l, 3, 1, o.w);
+      o.N = c.d_model; o.K = qd; o.x_src = a.out; o.x_stride = qd;
+      o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
+      TIMED_ONLY(RIVER_K_O, launch_gemv(kXBf16, kEpResid, o, s));
+    } else {
+      GemmParams o = mgemm_base(ctx, l, B);
+      fill_weights(ctx, l, 3, 1, o.w);
+      o.N = c.d_model; o.K = qd; o.x = a.out; o.ldx = qd;
+      o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
+      TIMED_ONLY(RIVER_K_O, launch_mgemm(kEpResid, o, s));
+    }
     RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
     RowsNormParams rn2{hB, x, static_cast<const uint16_t *>(L.mlp_norm), B, c.d_model, c.rms_eps, 0};
@@ -417,11 +481,19 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     TIMED_ONLY(RIVER_K_GATEUP, launch_mgemm(kEpSwiGLU, gu, s));
     RV_TRY(rec.put(l, rec.lay.u, gu.u_out, (size_t)B * c.ffn_dim * 2));
 
-    GemmParams dn = mgemm_base(ctx, l, B);
-    fill_weights(ctx, l, 6, 1, dn.w);
-    dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
-    dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
-    TIMED_ONLY(RIVER_K_DOWN, launch_mgemm(kEpResid, dn, s));
+    if (few) {
+      GemvParams dn = gemv_base(ctx, l, B);
+      fill_weights(ctx, l, 6, 1, dn.w);
+      dn.N = c.d_model; dn.K = c.ffn_dim; dn.x_src = gu.u_out; dn.x_stride = c.ffn_dim;
+      dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
+      TIMED_ONLY(RIVER_K_DOWN, launch_gemv(kXBf16, kEpResid, dn, s));
+    } else {
+      GemmParams dn = mgemm_base(ctx, l, B);
+      fill_weights(ctx, l, 6, 1, dn.w);
+      dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
+      dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
+      TIMED_ONLY(RIVER_K_DOWN, launch_mgemm(kEpResid, dn, s));
+    }
 
     if (l < c.n_layers - 1) {
       // the exit test after this layer and the next layer's input RMSNorm
@@ -434,6 +506,7 @@ int enqueue_decode_rows(river_ctx *ctx, const int32_t *tok, float tau, float *lo
     std::swap(hA, hB);
   }
   RV_TRY(rec.put(-1, 0, hA, hbytes));
+  if (only < 0 && few) return enqueue_lm_head_gemv(ctx, hA, B, logits, next, s);
   if (only < 0) return enqueue_lm_head_rows(ctx, hA, c.d_model, B, logits, next, 0);
   return RIVER_OK;
 }
@@ -506,7 +579,7 @@ int enqueue_pending_rows(river_ctx *ctx, int l, int q0, int n) {
 // launch for every layer, with the same parameters (kernel timing).
 int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits, int32_t *next,
                    int only = -1) {
-  if (ctx->batch > 8) return enqueue_decode_rows(ctx, tok, tau, logits, next, only);
+  if (use_rows_path(ctx)) return enqueue_decode_rows(ctx, tok, tau, logits, next, only);
   const river_config &c = ctx->cfg;
   const int B = ctx->batch;
   hipStream_t s = ctx->stream;
@@ -600,15 +673,7 @@ int enqueue_decode(river_ctx *ctx, const int32_t *tok, float tau, float *logits,
     std::swap(hA, hB);
   }
   RV_TRY(rec.put(-1, 0, hA, hbytes));
-  GemvParams lm{};
-  lm.w.bf[0] = ctx->lm_head; lm.w.seg_rows[0] = c.vocab; lm.w.nseg = 1;
-  lm.gemv_mode = ctx->gemv_mode;
-  lm.N = c.vocab; lm.K = c.d_model; lm.G = c.group_size; lm.layer = -1;
-  lm.gshift = __builtin_ctz((unsigned)c.group_size);
-  lm.exit_mode = ctx->exit_mode; lm.ctrl = ctx->ctrl; lm.B = B;
-  lm.h_src = hA; lm.h_stride = c.d_model; lm.gain = ctx->final_norm; lm.eps = c.rms_eps;
-  lm.logits = logits; lm.next = next; lm.is_prefill = 0; lm.vocab = c.vocab;
-  TIMED_ONLY(RIVER_K_LMHEAD, launch_gemv(kXNorm, kEpLogits, lm, s));
+  if (only < 0) RV_TRY_RC(enqueue_lm_head_gemv(ctx, hA, B, logits, next, s));
   if (ctx->strategy == kStratMask && only < 0)
     RV_TRY(launch_set_pos_E(ctx->ctrl, control_pos_E(ctx->ctrl, c.max_batch, c.n_kv_heads), 0, s));
   if (ctx->strategy == kStratRecompute && only < 0)   // this position's state at its exit
