@@ -180,9 +180,23 @@ def test_decode_parity_1b_layer_shapes_tied(w1b):
 
 
 def test_decode_parity_8b_layer_shapes_batch8(w8b):
+    """8 rows per step: RMSNorm and the exit test as row kernels, q|k|v and
+    gate|up on the batched-row GEMM, o and down on the matrix-core GEMV."""
     w = dict(w8b)
     w["layers"] = w8b["layers"][:2]
     parity_run(synth.LLAMA_8B, w, B=8, T=6, steps=2, tau=0.3)
+
+
+@pytest.mark.parametrize("tau", [0.5, -1.5])
+def test_decode_parity_row_path_ragged(tau):
+    """5 and 7 rows per step, the fewest and a ragged count on the row-kernel
+    path (the batched-row GEMM's 16-row tile mostly padding), on the tiny
+    decoder (group size 64) with the exit taken and never taken."""
+    w = synth.make_weights(synth.TINY, seed=0, device="cuda")
+    for B in (5, 7):
+        Es = parity_run(synth.TINY, w, B=B, T=6, steps=3, tau=tau)
+        if tau < -1:
+            assert all(e == 1 for e in Es)
 
 
 def test_decode_parity_8b_layer_shapes_batch32(w8b):
