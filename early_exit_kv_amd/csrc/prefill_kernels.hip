@@ -1661,12 +1661,12 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
 }
 
 
-template <int G, int EP, int BN>
-__global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
+template <int G, int EP, int BN, int NTH = kPThreads, int BM = kPBM>
+__global__ __launch_bounds__(NTH, 1) void pgemm_kernel(GemmParams p, int nrowblk, int ncolblk) {
   // three stages of rows and weights (and int4 scale/zero words); the
   // results reuse them
-  __shared__ __align__(16) uint4 smem[psmem_slots<G, BN>()];
-  constexpr int AF = ptm<BN>() / 16;
+  __shared__ __align__(16) uint4 smem[psmem_slots<G, BN, NTH, BM>()];
+  constexpr int TM = ptm<BN, NTH, BM>(), AF = TM / 16;
   bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   // grouped order: kPGroupRows row blocks share the weights of each column block
   const int per_group = kPGroupRows * ncolblk;
@@ -1683,50 +1683,58 @@ __global__ __launch_bounds__(kPThreads, 1) void pgemm_kernel(GemmParams p, int n
   for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true, BN>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<true>(), tot);
-  else pgemm_body<G, EP, false, BN>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<false>(), tot);
+  if (q4) pgemm_body<G, EP, true, BN, NTH, BM>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<true>(), tot);
+  else pgemm_body<G, EP, false, BN, NTH, BM>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<false>(), tot);
 
   // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
   const int wm = wid / pwn<BN>(), wn = wid % pwn<BN>();
   float *Cs = reinterpret_cast<float *>(smem);
-  static_assert(kPBM * (BN + 1) * 4 <= psmem_slots<G, BN>() * 16, "the results fit the buffers");
+  static_assert(BM * (BN + 1) * 4 <= psmem_slots<G, BN, NTH, BM>() * 16, "the results fit the buffers");
 #pragma unroll
   for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        Cs[(wm * ptm<BN>() + a * 16 + 4 * qq + v) * (BN + 1) + wn * 64 + t * 16 + cl] = tot[a][t][v];
+        Cs[(wm * TM + a * 16 + 4 * qq + v) * (BN + 1) + wn * 64 + t * 16 + cl] = tot[a][t][v];
   __syncthreads();
-  tile_epilogue<EP, BN, kPThreads>(p, Cs, BN + 1, kPBM, (int64_t)rowblk * kPBM, colblk);
+  tile_epilogue<EP, BN, NTH>(p, Cs, BN + 1, BM, (int64_t)rowblk * BM, colblk);
 }
 
-template <int G, int BN>
+template <int G, int BN, int NTH = kPThreads, int BM = kPBM>
 static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t s) {
   const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
-  int nrowblk = (p.M + kPBM - 1) / kPBM, ncolblk = (ncols + BN - 1) / BN;
+  int nrowblk = (p.M + BM - 1) / BM, ncolblk = (ncols + BN - 1) / BN;
   GemmParams q = p;
   void *args[] = {&q, &nrowblk, &ncolblk};
   const dim3 grid((unsigned)(nrowblk * ncolblk));
   const void *fn;
   switch (ep) {
-    case kEpQKV: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpQKV, BN>); break;
-    case kEpSwiGLU: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpSwiGLU, BN>); break;
-    case kEpResid: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpResid, BN>); break;
-    case kEpPlain: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpPlain, BN>); break;
+    case kEpQKV: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpQKV, BN, NTH, BM>); break;
+    case kEpSwiGLU: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpSwiGLU, BN, NTH, BM>); break;
+    case kEpResid: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpResid, BN, NTH, BM>); break;
+    case kEpPlain: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpPlain, BN, NTH, BM>); break;
     default: return hipErrorInvalidValue;
   }
-  return launch_kernel(fn, grid, dim3(kPThreads), args, 0, s);
+  return launch_kernel(fn, grid, dim3(NTH), args, 0, s);
 }
 
 // 256-column blocks (64 x 64 per wavefront: half the int4 unpacking per
 // MFMA of 128-column blocks) once there are enough rows to fill the chip
-// with them; 128-column blocks for short prompts
+// with them; 128-column blocks for shorter prompts.  Up to kPSmallRows rows a
+// layer that may run on its int4 copy takes 64-row x 128-column tiles of 256
+// threads instead (twice the workgroups, two per CU): at 256 and 512 rows
+// the int4 GEMMs ran 16-17% faster so, while bf16 weights, read twice as often
+// per flop, ran 4-17% slower (and from 1,024 rows int4 gained <= 6%, bf16 lost
+// up to 27%), so a layer known to run on its backbone keeps the larger tile.
+constexpr int kPSmallRows = 512;
 template <int G>
 static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s) {
   if (p.M >= kPWideRows) return pgemm_launch_gb<G, 256>(ep, p, s);
+  const bool may_q4 = p.exit_mode == RIVER_EXIT_INT4 && p.layer >= 0 && p.path != kPathBackbone;
+  if (p.M <= kPSmallRows && may_q4) return pgemm_launch_gb<G, 128, 256, 64>(ep, p, s);
   return pgemm_launch_gb<G, 128>(ep, p, s);
 }
 
