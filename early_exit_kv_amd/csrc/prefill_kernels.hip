@@ -1572,8 +1572,8 @@ MgemmPlan mgemm_plan(int M, int ncols, int K) { return mgemm_plan(M, ncols, K, t
 // split (the weight form is chosen on the device), so a split also stays
 // within the rows it can stage.
 static bool mgemm_ring_ok(Epilogue ep, const GemmParams &p) {
-  return ep != kEpLogits && p.layer >= 0 && p.exit_mode == RIVER_EXIT_INT4 && p.path != kPathBackbone &&
-         p.K % (2 * pkt<true>()) == 0;
+  return ep != kEpLogits && p.layer >= 0 && p.exit_mode == RIVER_EXIT_INT4 &&
+         (p.path == kPathDevice || p.path == kPathExit) && p.K % (2 * pkt<true>()) == 0;
 }
 static MgemmPlan mgemm_ring_plan(int M, int ncols, int K) {
   MgemmPlan pl{};
@@ -1728,12 +1728,15 @@ static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t 
 // threads instead (twice the workgroups, two per CU): at 256 and 512 rows
 // the int4 GEMMs ran 16-17% faster so, while bf16 weights, read twice as often
 // per flop, ran 4-17% slower (and from 1,024 rows int4 gained <= 6%, bf16 lost
-// up to 27%), so a layer known to run on its backbone keeps the larger tile.
+// up to 27%), so a layer known to run on its backbone (a backbone path, or a
+// pending-row pass) keeps the larger tile.
 constexpr int kPSmallRows = 512;
 template <int G>
 static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s) {
   if (p.M >= kPWideRows) return pgemm_launch_gb<G, 256>(ep, p, s);
-  const bool may_q4 = p.exit_mode == RIVER_EXIT_INT4 && p.layer >= 0 && p.path != kPathBackbone;
+  // (a pending-row pass runs the backbone, as a backbone path does)
+  const bool may_q4 =
+      p.exit_mode == RIVER_EXIT_INT4 && p.layer >= 0 && (p.path == kPathDevice || p.path == kPathExit);
   if (p.M <= kPSmallRows && may_q4) return pgemm_launch_gb<G, 128, 256, 64>(ep, p, s);
   return pgemm_launch_gb<G, 128>(ep, p, s);
 }
