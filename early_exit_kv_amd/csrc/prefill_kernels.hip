@@ -1410,26 +1410,29 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
   }
 }
 
-// int4 layers through the copy ring (p.ring): 256-column blocks of the rows
-// (ROWS = 16 MB of them) over one K split, on the prefill GEMM's body with 256
-// threads (4 wavefronts of 64 columns); rows, codes and scale/zero words
-// reach LDS by DMA, three k-tiles deep.  The partial tile goes out in the
-// 128-column layout that the reduce kernel adds (the plan always splits K).
+// int4 layers through the copy ring (p.ring = RBN, the column block): RBN =
+// 256 or 128 columns of the rows (ROWS = 16 MB of them) over one K split, on
+// the prefill GEMM's body with 256 threads (4 wavefronts of 64 columns: 1 x 4,
+// or 2 x 2 for 128-column blocks of 32 or more rows); rows, codes and
+// scale/zero words reach LDS by DMA, three k-tiles deep.  The partial tile
+// goes out in the 128-column layout that the reduce kernel adds (the plan
+// always splits K).
 template <int MB> constexpr int mgemm_ring_bm() { return MB * 16; }
 template <int MB, int G> constexpr int mgemm_ring_bytes() {
   return kPBufs * pstage_slots<true, G, 256, 256, mgemm_ring_bm<MB>()>() * 16;   // int4 stages only
 }
 
-template <int MB, int G, int EP>
+template <int MB, int G, int EP, int RBN>
 __device__ void mgemm_ring(const GemmParams &p, uint4 *smem, bool ex) {
-  constexpr int BM = mgemm_ring_bm<MB>(), AF = ptm<256, 256, BM>() / 16;
-  static_assert(AF == MB, "one wavefront row: MB row blocks");
+  constexpr int BM = mgemm_ring_bm<MB>(), WN = RBN / 64, TM = ptm<RBN, 256, BM>(), AF = TM / 16;
+  static_assert(RBN == 256 || RBN == 128, "column block");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
+  const int wm = wid / WN, wn = wid % WN;
   const int nsplit = p.nsplit;
   const int cb = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
   const int ncols = EP == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
-  if (cb * 256 >= ncols) return;                 // the grid is laid out for 128-column blocks
+  if (cb * RBN >= ncols) return;                 // the grid is laid out for 128-column blocks
   const int ncb128 = (ncols + kMgemmBN - 1) / kMgemmBN;
   f32x4_t tot[AF][4];
 #pragma unroll
@@ -1437,17 +1440,17 @@ __device__ void mgemm_ring(const GemmParams &p, uint4 *smem, bool ex) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int kpt = p.ks / pkt<true>();           // k-tiles per split
-  pgemm_body<G, EP, true, 256, 256, BM, true>(p, smem, ex, 0, cb, split * kpt, kpt, tot);
+  pgemm_body<G, EP, true, RBN, 256, BM, true>(p, smem, ex, 0, cb, split * kpt, kpt, tot);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int col = wid * 64 + t * 16 + cl;
-    const int cb128 = cb * 2 + (col >> 7);
+    const int col = wn * 64 + t * 16 + cl;
+    const int cb128 = cb * (RBN / kMgemmBN) + (col >> 7);
     if (cb128 >= ncb128) continue;
     float *mine = p.part + ((int64_t)cb128 * nsplit + split) * (BM * kMgemmBN) + (col & (kMgemmBN - 1));
 #pragma unroll
     for (int a = 0; a < AF; ++a)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) mine[(a * 16 + 4 * qq + v) * kMgemmBN] = tot[a][t][v];
+      for (int v = 0; v < 4; ++v) mine[(wm * TM + a * 16 + 4 * qq + v) * kMgemmBN] = tot[a][t][v];
   }
 }
 
@@ -1468,7 +1471,13 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
   if constexpr (EP != kEpLogits) {
     if (q4 && p.ring) {
-      mgemm_ring<MB, G, EP>(p, reinterpret_cast<uint4 *>(smem), ex);
+      if constexpr (MB >= 2) {
+        if (p.ring == 128) {
+          mgemm_ring<MB, G, EP, 128>(p, reinterpret_cast<uint4 *>(smem), ex);
+          return;
+        }
+      }
+      mgemm_ring<MB, G, EP, 256>(p, reinterpret_cast<uint4 *>(smem), ex);
       return;
     }
   }
@@ -1575,12 +1584,13 @@ static bool mgemm_ring_ok(Epilogue ep, const GemmParams &p) {
   return ep != kEpLogits && p.layer >= 0 && p.exit_mode == RIVER_EXIT_INT4 &&
          (p.path == kPathDevice || p.path == kPathExit) && p.K % (2 * pkt<true>()) == 0;
 }
-static MgemmPlan mgemm_ring_plan(int M, int ncols, int K) {
+static MgemmPlan mgemm_ring_plan_bn(int M, int ncols, int K, int rbn) {
   MgemmPlan pl{};
   pl.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   pl.ncolblk = (ncols + kMgemmBN - 1) / kMgemmBN;
+  pl.rbn = rbn;
   const int KS = pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512;
-  const int nt = K / pkt<true>(), ncb = (ncols + 255) / 256;
+  const int nt = K / pkt<true>(), ncb = (ncols + rbn - 1) / rbn;
   constexpr int kMinKs = 512;                   // K columns per split at least (measured best)
   int best = 0;
   for (int d = 2; d <= nt; ++d) {
@@ -1591,6 +1601,19 @@ static MgemmPlan mgemm_ring_plan(int M, int ncols, int K) {
   }
   pl.nsplit = best;
   pl.ks = best ? K / best : 0;
+  return pl;
+}
+// 256-column blocks, or 128-column ones (from 32 rows) where the 256-column
+// plan fills at most half the CUs: at 32 rows the o projection (4,096 x
+// 4,096) 13.4 -> 11.7 us, while q|k|v (192 workgroups) and down (256) were
+// slower with 128 (the rows tile read by twice the workgroups, each unpacked
+// B operand feeding half the MFMAs)
+static MgemmPlan mgemm_ring_plan(int M, int ncols, int K) {
+  MgemmPlan pl = mgemm_ring_plan_bn(M, ncols, K, 256);
+  if (pl.mb >= 2 && pl.nsplit && ((ncols + 255) / 256) * pl.nsplit <= 128) {
+    const MgemmPlan narrow = mgemm_ring_plan_bn(M, ncols, K, 128);
+    if (narrow.nsplit >= 2) pl = narrow;
+  }
   return pl;
 }
 
@@ -1652,7 +1675,7 @@ hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
   GemmParams q = p;
   q.nsplit = pl.nsplit;
   q.ks = pl.ks;
-  q.ring = ring ? 1 : 0;
+  q.ring = ring ? pl.rbn : 0;
   switch (pl.mb) {
     case 1: return mgemm_launch_mb<1>(ep, q, pl.ncolblk, s);
     case 2: return mgemm_launch_mb<2>(ep, q, pl.ncolblk, s);

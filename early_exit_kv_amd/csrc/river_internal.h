@@ -270,7 +270,7 @@ struct GemmParams {
   float *part;                                               // split-K partial tiles
   int64_t part_cap;                                          // floats at part
   int nsplit, ks;                                            // K splits, K per split
-  int ring;                                                  // int4 through the copy ring (set at launch)
+  int ring;                                                  // int4 ring column block, 0: none (set at launch)
 };
 
 // Batched-row GEMM for 9..64 rows (decode of larger batches, LM head of
@@ -278,7 +278,7 @@ struct GemmParams {
 // in LDS.  Plan: 16-row blocks, 128-column workgroups, K split over nsplit
 // workgroups whose partial tiles a second kernel adds up.
 constexpr int kMgemmBN = 128;
-struct MgemmPlan { int mb, ncolblk, nsplit, ks; };
+struct MgemmPlan { int mb, ncolblk, nsplit, ks, rbn; };   // rbn: int4 ring column block (0: none)
 MgemmPlan mgemm_plan(int M, int ncols, int K);
 int64_t mgemm_part_floats(const MgemmPlan &pl);
 // split-K partial floats the launch of a linear of ncols x K at M rows may
