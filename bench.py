@@ -489,8 +489,9 @@ def main():
         r.close()
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the decode path is single-GPU; see the sharding design note).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path runs on a single GPU; sharding across GPUs is designed, not built).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import synth
