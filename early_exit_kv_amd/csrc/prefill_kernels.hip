@@ -1161,25 +1161,18 @@ __device__ __forceinline__ void pgemm_body(const GemmParams &p, uint4 *smem, boo
 //   the epilogue.
 // ===========================================================================
 
-// LM head epilogue of one column block: logits out, per-row argmax keys
-// (value order, then lowest index), and in the last workgroup of the launch
-// the next tokens and the pass bookkeeping (E histogram, position).
-template <int ROWS, int BN>
-__device__ void logits_epilogue(const GemmParams &p, const float *Cs, int m0, int colblk,
-                                uint64_t *rowkey, int *last_flag) {
+// LM head argmax key of logit v in column n: value order, then lowest index
+__device__ __forceinline__ uint64_t logit_key(float v, int n) {
+  return ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+}
+
+// End of an LM head workgroup: its per-row keys (rows m0 .. m0 + ROWS, in
+// LDS, complete) go to the launch-wide maxima, and the last workgroup of the
+// launch writes the next tokens and the pass bookkeeping (E histogram,
+// position).
+template <int ROWS>
+__device__ void logits_finish(const GemmParams &p, int m0, uint64_t *rowkey, int *last_flag) {
   Control *ctl = p.ctrl;
-  if (threadIdx.x < ROWS) rowkey[threadIdx.x] = 0;
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
-    const int r = idx / BN, j = idx % BN;
-    const int n = colblk * BN + j;
-    if (m0 + r >= p.M || n >= p.N) continue;
-    const float v = Cs[r * (BN + 1) + j];
-    if (p.logits) p.logits[(int64_t)(m0 + r) * p.vocab + n] = v;
-    const uint64_t key = ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
-    __hip_atomic_fetch_max(&rowkey[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  __syncthreads();
   if (threadIdx.x < ROWS && m0 + (int)threadIdx.x < p.M)
     __hip_atomic_fetch_max(control_keys(ctl) + m0 + threadIdx.x, rowkey[threadIdx.x], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -1202,6 +1195,25 @@ __device__ void logits_epilogue(const GemmParams &p, const float *Cs, int m0, in
       }
     }
   }
+}
+
+// LM head epilogue of one column block: logits out, per-row argmax keys, then
+// logits_finish.
+template <int ROWS, int BN>
+__device__ void logits_epilogue(const GemmParams &p, const float *Cs, int m0, int colblk,
+                                uint64_t *rowkey, int *last_flag) {
+  if (threadIdx.x < ROWS) rowkey[threadIdx.x] = 0;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ROWS * BN; idx += 256) {
+    const int r = idx / BN, j = idx % BN;
+    const int n = colblk * BN + j;
+    if (m0 + r >= p.M || n >= p.N) continue;
+    const float v = Cs[r * (BN + 1) + j];
+    if (p.logits) p.logits[(int64_t)(m0 + r) * p.vocab + n] = v;
+    __hip_atomic_fetch_max(&rowkey[r], logit_key(v, n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  logits_finish<ROWS>(p, m0, rowkey, last_flag);
 }
 
 template <int MB, int G> struct MgemmShape {
@@ -1525,6 +1537,7 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
 constexpr int kReduceRows = 8;
 template <int MB, int EP>
 __global__ __launch_bounds__(256) void mgemm_reduce_kernel(GemmParams p) {
+  static_assert(EP != kEpLogits, "the LM head has its own reduce kernel");
   constexpr int BN = kMgemmBN, ROWS = MB * 16, RG = kReduceRows;
   __shared__ float Cs[RG * (BN + 1)];
   const int colblk = blockIdx.x / (ROWS / RG), rg = blockIdx.x % (ROWS / RG);
@@ -1540,13 +1553,60 @@ __global__ __launch_bounds__(256) void mgemm_reduce_kernel(GemmParams p) {
   float *c = Cs + r * (BN + 1) + j;
   c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
   __syncthreads();
-  if constexpr (EP == kEpLogits) {
-    __shared__ uint64_t rowkey[RG];
-    __shared__ int last_flag;
-    logits_epilogue<RG, BN>(p, Cs, rg * RG, colblk, rowkey, &last_flag);
-  } else {
-    tile_epilogue<EP, BN>(p, Cs, BN + 1, RG, rg * RG, colblk);
+  tile_epilogue<EP, BN>(p, Cs, BN + 1, RG, rg * RG, colblk);
+}
+
+// The same for the LM head, kLogitsBlocks column blocks per workgroup: the
+// per-row maxima go out once per workgroup, so a vocabulary of ~1,000 column
+// blocks makes 1/kLogitsBlocks of the agent-scope atomics and arrivals (each
+// of which serialises on its address) that one workgroup per block would.
+constexpr int kLogitsBlocks = 8;
+template <int MB>
+__global__ __launch_bounds__(256) void mgemm_reduce_logits_kernel(GemmParams p) {
+  constexpr int BN = kMgemmBN, ROWS = MB * 16, RG = kReduceRows, C = kLogitsBlocks;
+  __shared__ uint64_t rowkey[RG];
+  __shared__ int last_flag;
+  const int ncolblk = (p.N + BN - 1) / BN;
+  const int cg = blockIdx.x / (ROWS / RG), rg = blockIdx.x % (ROWS / RG);
+  const int i4 = threadIdx.x;                       // RG * BN / 4 == 256 float4
+  const int r = (4 * i4) / BN, j = (4 * i4) % BN, m = rg * RG + r;
+  if (threadIdx.x < RG) rowkey[threadIdx.x] = 0;
+  // C column blocks of this row group: every split of all of them is loaded
+  // before the sums are used (plain loads, C independent streams per thread)
+  float4 v[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int cb = min(cg * C + c, ncolblk - 1);
+    v[c] = *reinterpret_cast<const float4 *>(p.part + (int64_t)cb * p.nsplit * (ROWS * BN) + r * BN +
+                                             rg * RG * BN + j);
   }
+  for (int sp = 1; sp < p.nsplit; ++sp) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int cb = min(cg * C + c, ncolblk - 1);
+      const float4 t = *reinterpret_cast<const float4 *>(
+          p.part + ((int64_t)cb * p.nsplit + sp) * (ROWS * BN) + r * BN + rg * RG * BN + j);
+      v[c].x += t.x; v[c].y += t.y; v[c].z += t.z; v[c].w += t.w;
+    }
+  }
+  uint64_t best = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int cb = cg * C + c;
+    const float e[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = cb * BN + j + q;
+      if (cb >= ncolblk || m >= p.M || n >= p.N) continue;
+      if (p.logits) p.logits[(int64_t)m * p.vocab + n] = e[q];
+      const uint64_t key = logit_key(e[q], n);
+      best = key > best ? key : best;
+    }
+  }
+  __syncthreads();   // rowkey cleared
+  if (best) __hip_atomic_fetch_max(&rowkey[r], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  logits_finish<RG>(p, rg * RG, rowkey, &last_flag);
 }
 
 MgemmPlan mgemm_plan(int M, int ncols, int K, bool allow_split) {
@@ -1628,7 +1688,6 @@ static hipError_t mgemm_reduce(Epilogue ep, const GemmParams &p, int grid, hipSt
     case kEpResid: return launch_1(mgemm_reduce_kernel<MB, kEpResid>, dim3(grid), dim3(256), p, s);
     case kEpSwiGLU: return launch_1(mgemm_reduce_kernel<MB, kEpSwiGLU>, dim3(grid), dim3(256), p, s);
     case kEpPlain: return launch_1(mgemm_reduce_kernel<MB, kEpPlain>, dim3(grid), dim3(256), p, s);
-    case kEpLogits: return launch_1(mgemm_reduce_kernel<MB, kEpLogits>, dim3(grid), dim3(256), p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1655,6 +1714,10 @@ static hipError_t mgemm_launch_mb(Epilogue ep, const GemmParams &p, int ncolblk,
   }
   if (e != hipSuccess || p.nsplit == 1) return e;
   static_assert(kReduceRows * kMgemmBN / 4 == 256, "one float4 per thread");
+  if (ep == kEpLogits)
+    return launch_1(mgemm_reduce_logits_kernel<MB>,
+                    dim3(((ncolblk + kLogitsBlocks - 1) / kLogitsBlocks) * (MB * 16 / kReduceRows)), dim3(256),
+                    p, s);
   return mgemm_reduce<MB>(ep, p, ncolblk * (MB * 16 / kReduceRows), s);
 }
 

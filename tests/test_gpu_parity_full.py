@@ -224,6 +224,18 @@ def test_decode_parity_tiny_batch64_max_rows():
     parity_run(synth.TINY, w, B=37, T=5, steps=2, tau=0.5)
 
 
+def test_decode_parity_lm_head_split_reduce():
+    """The batched LM head with K split: a 2,048-wide decoder with a
+    1,100-token vocabulary (nine 128-column blocks, the last partial) at 24
+    rows (two splits) and 40 rows (four splits); the reduce kernel takes eight
+    column blocks per workgroup, so one full group of blocks and one ragged
+    group of a single partial block."""
+    sh = synth.shrink(synth.LLAMA_1B, name="1b-layers-small-vocab", n_layers=2, vocab=1100)
+    w = synth.make_weights(sh, seed=3, device="cuda")
+    parity_run(sh, w, B=24, T=4, steps=2, tau=0.5)
+    parity_run(sh, w, B=40, T=4, steps=2, tau=0.5)
+
+
 def test_split_attention_long_context_tiny():
     """A context of several hundred positions splits the decode attention over
     workgroups and merges the splits in the last one; B=8 fills the GEMV's
