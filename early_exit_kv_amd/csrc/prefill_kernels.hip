@@ -1422,13 +1422,16 @@ __device__ __forceinline__ void mgemm_body(const GemmParams &p, const MgemmLds &
 // or 2 x 2 for 128-column blocks of 32 or more rows); rows, codes and
 // scale/zero words reach LDS by DMA, three k-tiles deep.  The partial tile
 // goes out in the 128-column layout that the reduce kernel adds (the plan
-// always splits K).
+// always splits K).  The LM head (bf16 weights, Q4 false) takes the same ring
+// from 17 rows on: every k-tile then reads whole 128-byte lines of 256 weight
+// rows, where the register path reads each row in 64-byte pieces.
 template <int MB> constexpr int mgemm_ring_bm() { return MB * 16; }
-template <int MB, int G> constexpr int mgemm_ring_bytes() {
-  return kPBufs * pstage_slots<true, G, 256, 256, mgemm_ring_bm<MB>()>() * 16;   // int4 stages only
+template <int MB, int G, bool Q4 = true, int RBN = 256> constexpr int mgemm_ring_bytes() {
+  return kPBufs * pstage_slots<Q4, G, RBN, 256, mgemm_ring_bm<MB>()>() * 16;
 }
+constexpr int kLogitsRbn = 128;   // column block of the LM head's ring
 
-template <int MB, int G, int EP, int RBN>
+template <int MB, int G, int EP, int RBN, bool Q4 = true>
 __device__ void mgemm_ring(const GemmParams &p, uint4 *smem, bool ex) {
   constexpr int BM = mgemm_ring_bm<MB>(), WN = RBN / 64, TM = ptm<RBN, 256, BM>(), AF = TM / 16;
   static_assert(RBN == 256 || RBN == 128, "column block");
@@ -1445,8 +1448,8 @@ __device__ void mgemm_ring(const GemmParams &p, uint4 *smem, bool ex) {
   for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int kpt = p.ks / pkt<true>();           // k-tiles per split
-  pgemm_body<G, EP, true, RBN, 256, BM, true>(p, smem, ex, 0, cb, split * kpt, kpt, tot);
+  const int kpt = p.ks / pkt<Q4>();             // k-tiles per split
+  pgemm_body<G, EP, Q4, RBN, 256, BM, true>(p, smem, ex, 0, cb, split * kpt, kpt, tot);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int col = wn * 64 + t * 16 + cl;
@@ -1464,8 +1467,11 @@ template <int MB, int G, int EP>
 __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
   typedef MgemmShape<MB, G> S;
   constexpr int NT = S::NT, BN = S::BN, ROWS = S::ROWS, KS = S::KS;
-  // LDS: the staged rows of the register path, or the ring of the int4 path
-  constexpr int SM = S::SMEM > mgemm_ring_bytes<MB, G>() ? S::SMEM : mgemm_ring_bytes<MB, G>();
+  // LDS: the staged rows of the register path, or the ring (int4 layers;
+  // bf16 for the LM head of 17 rows or more)
+  constexpr int RB =
+      EP == kEpLogits ? (MB >= 2 ? mgemm_ring_bytes<MB, G, false, kLogitsRbn>() : 0) : mgemm_ring_bytes<MB, G>();
+  constexpr int SM = S::SMEM > RB ? S::SMEM : RB;
   __shared__ __align__(16) char smem[SM];
   __shared__ float xsg[ROWS * (KS / G)];
   __shared__ uint64_t rowkey[ROWS];
@@ -1475,7 +1481,14 @@ __global__ __launch_bounds__(256) void mgemm_kernel(GemmParams p) {
 
   const bool ex = p.path == kPathDevice ? layer_uses_exit(p.ctrl, p.layer) : p.path == kPathExit;
   const bool q4 = ex && p.exit_mode == RIVER_EXIT_INT4;
-  if constexpr (EP != kEpLogits) {
+  if constexpr (EP == kEpLogits) {
+    if constexpr (MB >= 2) {
+      if (p.ring) {
+        mgemm_ring<MB, G, EP, kLogitsRbn, false>(p, reinterpret_cast<uint4 *>(smem), false);
+        return;
+      }
+    }
+  } else {
     if (q4 && p.ring) {
       if constexpr (MB >= 2) {
         if (p.ring == 128) {
@@ -1671,6 +1684,23 @@ static MgemmPlan mgemm_ring_plan(int M, int ncols, int K) {
   return pl;
 }
 
+// The LM head from 17 rows on (bf16 weights through the ring): 256-column
+// blocks, K in two halves of whole 64-column k-tiles.  With K >= 2048 the
+// register path's plan for the same rows splits K at least twice as often, so
+// the workspace sized for that plan holds these partials.
+static bool mgemm_logits_ring_ok(Epilogue ep, const GemmParams &p) {
+  return ep == kEpLogits && p.M > 16 && p.K >= 2048 && p.K % (2 * pkt<false>()) == 0;
+}
+static MgemmPlan mgemm_logits_ring_plan(int M, int ncols, int K) {
+  MgemmPlan pl{};
+  pl.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  pl.ncolblk = (ncols + kMgemmBN - 1) / kMgemmBN;
+  pl.rbn = kLogitsRbn;
+  pl.nsplit = 2;
+  pl.ks = K / 2;
+  return pl;
+}
+
 int64_t mgemm_part_floats(const MgemmPlan &pl) {
   return pl.nsplit > 1 ? (int64_t)pl.ncolblk * pl.nsplit * (pl.mb * 16) * kMgemmBN : 0;
 }
@@ -1724,11 +1754,16 @@ static hipError_t mgemm_launch_mb(Epilogue ep, const GemmParams &p, int ncolblk,
 hipError_t launch_mgemm(Epilogue ep, const GemmParams &p, hipStream_t s) {
   if (p.M < 1 || p.M > 64 || p.K % p.G || (p.G != 64 && p.G != 128)) return hipErrorInvalidValue;
   const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
-  const bool ring = mgemm_ring_ok(ep, p);
-  const MgemmPlan pl = ring ? mgemm_ring_plan(p.M, ncols, p.K) : mgemm_plan(p.M, ncols, p.K, ep != kEpLogits);
+  const bool lring = mgemm_logits_ring_ok(ep, p);
+  const bool ring = lring || mgemm_ring_ok(ep, p);
+  const MgemmPlan pl = lring  ? mgemm_logits_ring_plan(p.M, ncols, p.K)
+                       : ring ? mgemm_ring_plan(p.M, ncols, p.K)
+                              : mgemm_plan(p.M, ncols, p.K, ep != kEpLogits);
   if (ring && pl.nsplit < 2) return hipErrorInvalidValue;
   if (pl.nsplit > 1 && (!p.part || mgemm_part_floats(pl) > p.part_cap)) return hipErrorInvalidValue;
-  if (pl.ks > (pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512)) return hipErrorInvalidValue;
+  // (the register path stages a whole split of the rows; the LM head's ring
+  // never takes that path)
+  if (!lring && pl.ks > (pl.mb == 1 ? 2048 : pl.mb == 2 ? 1024 : 512)) return hipErrorInvalidValue;
   GemmParams q = p;
   q.nsplit = pl.nsplit;
   q.ks = pl.ks;
