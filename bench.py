@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch decode steps without HIP graphs")
+    ap.add_argument("--steps-per-launch", type=int, default=1,
+                    help="decode steps per library call (river_decode_steps; with graphs, one "
+                         "recorded graph of that many steps); 1 = one step per call")
     ap.add_argument("--tau-sweep", action="store_true",
                     help="instead of the benchmark line: for each tau of the workload (or --taus) "
                          "the exit histogram, decode tokens/s, the exit-decision share of the step, "
@@ -175,20 +178,48 @@ def cpu_baseline(shape, weights, B, T, mean_E):
     }
 
 
-def timed_steps(r, bufs, logits, tau, W, K):
+class DecodeLoop:
+    """Greedy decode steps with the next tokens fed back on the device, `per`
+    steps per library call (river_decode_steps: with graphs on, one recorded
+    graph of `per` steps, so the graph launch is paid once per `per` steps);
+    a remainder runs one step per call.  Next tokens land in two [per][B]
+    buffers used in turn; a call reads its first tokens from the last row of
+    the other buffer, so the calls hit the same two recorded graphs."""
+
+    def __init__(self, r, B, vocab, dev, per):
+        import torch
+        self.r, self.per = r, max(1, int(per))
+        self.ring = [torch.empty((self.per, B), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.logits = torch.empty((B, vocab), dtype=torch.float32, device=dev)
+        self.cur = 0
+
+    def start(self, first):
+        """The tokens of the next step (e.g. the prefill's next tokens)."""
+        self.ring[0][self.per - 1].copy_(first)
+        self.cur = 0
+
+    def run(self, n, tau):
+        while n > 0:
+            src, dst = self.ring[self.cur][self.per - 1], self.ring[1 - self.cur]
+            if self.per > 1 and n >= self.per:
+                self.r.decode_steps(src, self.per, tau, logits=self.logits, next_tok=dst)
+                n -= self.per
+            else:
+                self.r.decode_step(src, tau, logits=self.logits, next_tok=dst[self.per - 1])
+                n -= 1
+            self.cur = 1 - self.cur
+
+
+def timed_steps(r, loop, tau, W, K):
     """W warm-up and K timed decode steps (graph replays): seconds for the K
     and the histogram of E over the K."""
     import torch
 
-    def run(n, start):
-        for i in range(n):
-            j = start + i
-            r.decode_step(bufs[j % 2], tau, logits=logits, next_tok=bufs[(j + 1) % 2])
-    run(W, 0)
+    loop.run(W, tau)
     h0 = r.exit_stats()["decode_hist"]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run(K, W)
+    loop.run(K, tau)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     h1 = r.exit_stats()["decode_hist"]
@@ -290,8 +321,7 @@ def offload_measure(args):
     dev_bytes = torch.cuda.memory_allocated(dev)
     weights_dev = sum(t.numel() * 2 for t in r._all_weight_tensors() if t.is_cuda)
     weights_host = sum(t.numel() * 2 for t in r._all_weight_tensors() if not t.is_cuda)
-    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    loop = DecodeLoop(r, B, shape.vocab, dev, args.steps_per_launch)
     out = {"what": "backbone offloading", "workload": wl.name, "offload_from_layer": k, "tau": tau,
            "device_weight_bytes": weights_dev, "host_weight_bytes": weights_host,
            "exit_bank_bytes": r.sizes.exit_bank_bytes, "kv_cache_bytes": r.sizes.kv_cache_bytes,
@@ -300,8 +330,8 @@ def offload_measure(args):
         r.force_exit_layer(fe)
         r.reset()
         _, nxt = r.prefill(tokens, tau, want_logits=False)
-        bufs[0].copy_(nxt)
-        el, hist = timed_steps(r, bufs, logits, tau, min(W, n), n)
+        loop.start(nxt)
+        el, hist = timed_steps(r, loop, tau, min(W, n), n)
         out[name] = {"steps": n, "decode_tok_s": round(B * n / el, 3), "ms_per_step": round(el / n * 1e3, 3),
                      "exit_hist": {str(e): c for e, c in enumerate(hist) if c}}
         print(f"[offload] {name}: {out[name]}", file=sys.stderr, flush=True)
@@ -335,8 +365,7 @@ def tau_sweep(args):
     r.build_exit_layers(args.exit_mode)
     torch.cuda.synchronize()
     build_s = time.perf_counter() - t0
-    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    loop = DecodeLoop(r, B, shape.vocab, dev, args.steps_per_launch)
     rows = []
     for tau in taus:
         r.reset()
@@ -346,8 +375,8 @@ def tau_sweep(args):
         torch.cuda.synchronize()
         prefill_s = time.perf_counter() - t0
         pE = r.exit_stats()["last_E"]
-        bufs[0].copy_(nxt)
-        el, hist_all = timed_steps(r, bufs, logits, tau, W, K)
+        loop.start(nxt)
+        el, hist_all = timed_steps(r, loop, tau, W, K)
         mean_E = sum(e * n for e, n in enumerate(hist_all)) / max(1, sum(hist_all))
         pos = T + W + K / 2
         byts = sum(n * step_bytes(shape, B, e, pos) for e, n in enumerate(hist_all)) / max(1, sum(hist_all))
@@ -369,8 +398,8 @@ def tau_sweep(args):
         r.force_exit_layer(fe)
         r.reset()
         _, nxt = r.prefill(tokens, tau_ref, want_logits=False)
-        bufs[0].copy_(nxt)
-        x6[name + "_ms"] = round(timed_steps(r, bufs, logits, tau_ref, W, K)[0] / K * 1e3, 4)
+        loop.start(nxt)
+        x6[name + "_ms"] = round(timed_steps(r, loop, tau_ref, W, K)[0] / K * 1e3, 4)
     r.force_exit_layer(-1)
     x6["tau"] = tau_ref
     x6["E"] = int(E_ref)
@@ -424,8 +453,9 @@ def strategy_sweep(args):
     tokens = synth.make_tokens(shape, B, T, seed=0).to(dev)
     r = rv.River(shape, weights, B, T + W + K + 2)
     r.build_exit_layers("int4")
-    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    # one step per call for every strategy: the recompute comparator sizes
+    # each step's launches on the host, and the others are timed alike
+    loop = DecodeLoop(r, B, shape.vocab, dev, 1)
     rows = []
     for tau in taus:
         for strategy in rv.KV_STRATEGIES:
@@ -433,8 +463,8 @@ def strategy_sweep(args):
             r.reset()
             _, nxt = r.prefill(tokens, tau, want_logits=False)
             pE = r.exit_stats()["last_E"]
-            bufs[0].copy_(nxt)
-            el, hist = timed_steps(r, bufs, logits, tau, W, K)
+            loop.start(nxt)
+            el, hist = timed_steps(r, loop, tau, W, K)
             mean_E = sum(e * n for e, n in enumerate(hist)) / max(1, sum(hist))
             row = {"tau": tau, "strategy": strategy, "prefill_E": pE,
                    "decode_tok_s": round(B * K / el, 2), "ms_per_step": round(el / K * 1e3, 4),
@@ -447,8 +477,8 @@ def strategy_sweep(args):
                 r.use_graph(False)
                 r.reset()
                 _, nxt = r.prefill(tokens, tau, want_logits=False)
-                bufs[0].copy_(nxt)
-                el2, _ = timed_steps(r, bufs, logits, tau, W, K)
+                loop.start(nxt)
+                el2, _ = timed_steps(r, loop, tau, W, K)
                 r.use_graph(True)
                 row["launch"] = "graph"
                 row["decode_tok_s_eager"] = round(B * K / el2, 2)
@@ -537,21 +567,18 @@ def main():
         del src, dst
     r.use_graph(not args.eager)
 
-    bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    bufs[0].copy_(nxt)
-    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    loop = DecodeLoop(r, B, shape.vocab, dev, args.steps_per_launch)
+    loop.start(nxt)
 
-    def run(n, start):
-        for i in range(n):
-            j = start + i
-            r.decode_step(bufs[j % 2], tau, logits=logits, next_tok=bufs[(j + 1) % 2])
+    def run(n):
+        loop.run(n, tau)
 
-    run(W, 0)
+    run(W)
     torch.cuda.synchronize()
     hist0 = r.exit_stats()["decode_hist"]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run(K, W)
+    run(K)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     hist1 = r.exit_stats()["decode_hist"]
@@ -573,18 +600,18 @@ def main():
             r.force_exit_layer(e)
             r.reset()
             _, nxt_b = r.prefill(tokens, tau, want_logits=False)
-            bufs[0].copy_(nxt_b)
-            run(W, 0)                      # same positions as the timed River steps
+            loop.start(nxt_b)
+            run(W)                         # same positions as the timed River steps
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            run(K, W)
+            run(K)
             torch.cuda.synchronize()
             baselines[name] = round(B * K / (time.perf_counter() - t0), 2)
         r.force_exit_layer(-1)
         r.reset()
         _, nxt_b = r.prefill(tokens, tau, want_logits=False)
-        bufs[0].copy_(nxt_b)
-        run(W + K, 0)                      # back to the state the profiling below expects
+        loop.start(nxt_b)
+        run(W + K)                         # back to the state the profiling below expects
         baselines["river_vs_original"] = round(tok_s / baselines["original"], 3)
         baselines["river_vs_full_int4"] = round(tok_s / baselines["full_int4"], 3)
 
@@ -609,7 +636,7 @@ def main():
         r.force_exit_layer(-1)
         r.profile(True)
         r.profile_read()
-        run(1, W + K)
+        run(1)
         times = r.profile_read()
         r.profile(False)
         for kind in ("begin", "lm_head"):
@@ -669,7 +696,7 @@ def main():
                                f"{shape.n_q_heads}q/{shape.n_kv_heads}kv heads x {shape.head_dim} "
                                f"FFN {shape.ffn_dim} vocab {shape.vocab}",
                    "batch": B, "prompt": T, "tau": tau, "exit_layers": "int4 g%d" % shape.group_size,
-                   "graphs": not args.eager},
+                   "graphs": not args.eager, "steps_per_launch": args.steps_per_launch},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_hbm_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

@@ -152,9 +152,10 @@ struct river_ctx {
   // of the key: a step reads it from the control block.
   struct GraphKey {
     const void *tok, *logits, *next;
-    int B, force_E;
+    int B, force_E, steps;
     bool operator<(const GraphKey &o) const {
-      return std::tie(tok, logits, next, B, force_E) < std::tie(o.tok, o.logits, o.next, o.B, o.force_E);
+      return std::tie(tok, logits, next, B, force_E, steps) <
+             std::tie(o.tok, o.logits, o.next, o.B, o.force_E, o.steps);
     }
   };
   std::map<GraphKey, hipGraphExec_t> graphs;
@@ -188,6 +189,7 @@ namespace {
 
 // recorded decode steps kept per context before the cache is emptied
 constexpr size_t kMaxGraphs = 32;
+constexpr int kMaxStepsPerCall = 64;   // decode steps one river_decode_steps call may take
 
 bool valid_config(const river_config *c) {
   if (!c) return false;
@@ -1024,12 +1026,15 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
   return RIVER_OK;
 }
 
-int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float *d_logits,
-                      int32_t *d_next) {
-  if (!ctx || !d_tokens) return RIVER_E_INVALID_ARG;
+// n decode steps enqueued back to back: step i reads its tokens from d_tokens
+// (i = 0) or from the next tokens of step i - 1, d_next + (i - 1) B, and writes
+// its own to d_next + i B (d_next may be null only for n = 1)
+static int decode_steps(river_ctx *ctx, int n, const int32_t *d_tokens, float tau, float *d_logits,
+                        int32_t *d_next) {
+  if (!ctx || !d_tokens || n < 1 || n > kMaxStepsPerCall || (n > 1 && !d_next)) return RIVER_E_INVALID_ARG;
   if (!std::isfinite(tau)) return RIVER_E_INVALID_ARG;
   if (!ctx->built || ctx->batch == 0) return RIVER_E_STATE;
-  if (ctx->pos + 1 > ctx->cfg.max_seq) return RIVER_E_RANGE;
+  if (ctx->pos + n > ctx->cfg.max_seq) return RIVER_E_RANGE;
   if (ctx->rec && record_layout(ctx->cfg, ctx->batch).total > ctx->rec_bytes)
     return RIVER_E_BAD_SIZE;
   // the comparator strategies run on the decode kernels of up to 8 rows; the
@@ -1037,9 +1042,10 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
   if (ctx->strategy != kStratRiver && ctx->batch > 8) return RIVER_E_UNIMPLEMENTED;
   if (ctx->strategy == kStratMask && ctx->attn_kind != 0) return RIVER_E_UNIMPLEMENTED;
   // the recompute comparator: one sequence, a state buffer, and a prefill
-  // under the same strategy before its steps
+  // under the same strategy before its steps; the host sizes each step's
+  // launches from the earlier steps' exits, so one step per call
   const bool recompute = ctx->strategy == kStratRecompute;
-  if (recompute && ctx->batch != 1) return RIVER_E_UNIMPLEMENTED;
+  if (recompute && (ctx->batch != 1 || n != 1)) return RIVER_E_UNIMPLEMENTED;
   if (recompute && (!ctx->kv_state || (int)ctx->depth.size() < ctx->cfg.max_seq)) return RIVER_E_STATE;
   // the step reads tau from the control block: write it when it changes
   uint32_t tau_bits;
@@ -1048,18 +1054,28 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
     RV_TRY(launch_set_tau(ctx->ctrl, tau, ctx->stream));
     ctx->ctrl_tau_bits = tau_bits;
   }
+  const int B = ctx->batch;
+  auto enqueue_all = [&]() -> int {
+    for (int i = 0; i < n; ++i) {
+      const int32_t *tok = i == 0 ? d_tokens : d_next + (int64_t)(i - 1) * B;
+      int32_t *nx = d_next ? d_next + (int64_t)i * B : nullptr;
+      const int st = enqueue_decode(ctx, tok, tau, d_logits, nx);
+      if (st != RIVER_OK) return st;
+    }
+    return RIVER_OK;
+  };
   // (recompute: the launches of a step depend on the exits of the earlier
   // passes, so its steps run eagerly)
   if (ctx->use_graph && !ctx->profiling && !ctx->rec && ctx->stream != nullptr && !recompute) {
-    const river_ctx::GraphKey key{d_tokens, d_logits, d_next, ctx->batch, ctx->force_E};
+    const river_ctx::GraphKey key{d_tokens, d_logits, d_next, B, ctx->force_E, n};
     auto it = ctx->graphs.find(key);
     if (it == ctx->graphs.end()) {
-      // every new (tokens, logits, next) triple records a graph; callers that
-      // reuse their buffers hit the cache, the others are bounded here
+      // every new (tokens, logits, next, steps) key records a graph; callers
+      // that reuse their buffers hit the cache, the others are bounded here
       if (ctx->graphs.size() >= kMaxGraphs) drop_graphs(ctx);
       hipGraph_t graph = nullptr;
       RV_TRY(hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
-      const int st = enqueue_decode(ctx, d_tokens, tau, d_logits, d_next);
+      const int st = enqueue_all();
       hipError_t e = hipStreamEndCapture(ctx->stream, &graph);
       hipGraphExec_t exec = nullptr;
       if (st == RIVER_OK && e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -1070,12 +1086,22 @@ int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float 
     }
     RV_TRY(hipGraphLaunch(it->second, ctx->stream));
   } else {
-    const int st = enqueue_decode(ctx, d_tokens, tau, d_logits, d_next);
+    const int st = enqueue_all();
     if (st != RIVER_OK) return st;
   }
   if (recompute) RV_TRY_RC(note_depth(ctx, ctx->pos, ctx->pos));
-  ctx->pos += 1;
+  ctx->pos += n;
   return RIVER_OK;
+}
+
+int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float *d_logits,
+                      int32_t *d_next) {
+  return decode_steps(ctx, 1, d_tokens, tau, d_logits, d_next);
+}
+
+int river_decode_steps(river_ctx *ctx, int32_t n_steps, const int32_t *d_tokens, float tau,
+                       float *d_logits, int32_t *d_next) {
+  return decode_steps(ctx, n_steps, d_tokens, tau, d_logits, d_next);
 }
 
 int river_exit_stats(river_ctx *ctx, river_exit_stats_t *out) {

@@ -27,7 +27,7 @@ LINEAR_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 # names of every entry point include/river.h declares
 EXPORTS = (
     "river_query_sizes", "river_exit_bank_offsets", "river_init", "river_build_exit_layers",
-    "river_prefill", "river_decode_step", "river_exit_stats", "river_set_option",
+    "river_prefill", "river_decode_step", "river_decode_steps", "river_exit_stats", "river_set_option",
     "river_reset", "river_destroy", "river_strerror", "river_profile_read",
     "river_debug_linear", "river_record_bytes", "river_set_record", "river_time_kernel",
     "river_debug_linear_noalloc", "river_set_kv_state",
@@ -104,6 +104,7 @@ def load_library(path=LIB_PATH):
         "river_build_exit_layers": (ctypes.c_int, [P, i32]),
         "river_prefill": (ctypes.c_int, [P, P, i32, i32, f32, P, P]),
         "river_decode_step": (ctypes.c_int, [P, P, f32, P, P]),
+        "river_decode_steps": (ctypes.c_int, [P, i32, P, f32, P, P]),
         "river_exit_stats": (ctypes.c_int, [P, ctypes.POINTER(RiverExitStats)]),
         "river_set_option": (ctypes.c_int, [P, i32, i64]),
         "river_reset": (ctypes.c_int, [P]),
@@ -284,6 +285,30 @@ class River:
         if next_tok is None:
             next_tok = torch.empty((B,), dtype=torch.int32, device=tokens.device)
         self._call(self.lib.river_decode_step, "river_decode_step", _ptr(tokens), ctypes.c_float(tau),
+                   _ptr(logits), _ptr(next_tok))
+        return logits, next_tok
+
+    def decode_steps(self, tokens, n, tau, want_logits=True, logits=None, next_tok=None):
+        """n decode steps in one call (river_decode_steps), the next tokens fed
+        back on the device: returns (logits of the last step, next tokens
+        [n, B])."""
+        if (not isinstance(tokens, torch.Tensor) or tokens.dtype != torch.int32 or not tokens.is_cuda
+                or tokens.dim() != 1 or not tokens.is_contiguous()):
+            raise ValueError("decode_steps: tokens must be a contiguous int32 CUDA tensor of shape [B]")
+        B = tokens.shape[0]
+        if self.batch is not None and B != self.batch:
+            raise ValueError(f"decode_steps: {B} tokens for a batch of {self.batch}")
+        n = int(n)
+        if next_tok is None:
+            next_tok = torch.empty((n, B), dtype=torch.int32, device=tokens.device)
+        if (next_tok.dtype != torch.int32 or not next_tok.is_cuda or not next_tok.is_contiguous()
+                or tuple(next_tok.shape) != (n, B)):
+            raise ValueError(f"decode_steps: next_tok must be a contiguous int32 CUDA tensor of shape [{n}, {B}]")
+        if logits is None and want_logits:
+            logits = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        if logits is not None and (logits.dtype != torch.float32 or not logits.is_cuda or not logits.is_contiguous()):
+            raise ValueError("decode_steps: logits must be a contiguous float32 CUDA tensor")
+        self._call(self.lib.river_decode_steps, "river_decode_steps", n, _ptr(tokens), ctypes.c_float(tau),
                    _ptr(logits), _ptr(next_tok))
         return logits, next_tok
 

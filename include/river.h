@@ -215,6 +215,20 @@ int river_prefill(river_ctx *ctx, const int32_t *d_tokens, int32_t B, int32_t T,
 int river_decode_step(river_ctx *ctx, const int32_t *d_tokens, float tau, float *d_logits,
                       int32_t *d_next);
 
+/* n_steps decode steps of river_decode_step (section 4) in one call, the
+ * tokens fed back on the device (greedy decoding): step i reads its tokens
+ * from d_tokens [B] (i = 0) or from row i-1 of d_next, and writes its next
+ * tokens to row i of d_next (device int32 [n_steps][B], required).  Every
+ * step writes d_logits [B][vocab] (may be NULL), which so holds the last
+ * step's logits.  Each step takes its own exit decision; the statistics count
+ * every step.  1 <= n_steps <= 64 (else RIVER_E_INVALID_ARG); RIVER_E_RANGE
+ * when the cache has fewer than n_steps free positions; RIVER_E_UNIMPLEMENTED
+ * for n_steps > 1 under the recompute comparator.  With RIVER_OPT_GRAPH on the
+ * n_steps steps are recorded as ONE graph per (buffers, batch, forced E,
+ * n_steps): a replay then pays the graph launch once for n_steps steps. */
+int river_decode_steps(river_ctx *ctx, int32_t n_steps, const int32_t *d_tokens, float tau,
+                       float *d_logits, int32_t *d_next);
+
 /* Copy the statistics to host memory; synchronises the stream.  The
  * histograms of E per prefill and per decode step, and their mean, are the
  * "mean exit layer" statistic the lead page's section 4 reports per tau (E

@@ -157,6 +157,13 @@ def test_call_order_and_argument_errors_enqueue_nothing(lib):
             assert lib.river_prefill(ctx, tok, 2, 8, ctypes.c_float(t), None, None) == rv.RIVER_E_INVALID_ARG
             assert lib.river_decode_step(ctx, tok, ctypes.c_float(t), None, None) == rv.RIVER_E_INVALID_ARG
         assert lib.river_prefill(ctx, None, 2, 8, ctypes.c_float(0.5), None, None) == rv.RIVER_E_INVALID_ARG
+        # several steps per call: 1..64 steps, and a next-token buffer to chain them through
+        nx = ctypes.c_void_p(0x3000)
+        for n in (0, -1, 65):
+            assert lib.river_decode_steps(ctx, n, tok, ctypes.c_float(0.5), None, nx) == rv.RIVER_E_INVALID_ARG
+        assert lib.river_decode_steps(ctx, 2, tok, ctypes.c_float(0.5), None, None) == rv.RIVER_E_INVALID_ARG
+        assert lib.river_decode_steps(ctx, 2, tok, ctypes.c_float(float("nan")), None, nx) == rv.RIVER_E_INVALID_ARG
+        assert lib.river_decode_steps(ctx, 4, tok, ctypes.c_float(0.5), None, nx) == rv.RIVER_E_STATE
         assert lib.river_build_exit_layers(ctx, 7) == rv.RIVER_E_INVALID_ARG
         assert lib.river_exit_stats(ctx, None) == rv.RIVER_E_INVALID_ARG
         st_out = rv.RiverExitStats()

@@ -191,6 +191,63 @@ def test_copy_mode_equals_backbone_on_gpu(tiny):
     assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
 
 
+@pytest.mark.parametrize("B", [2, 16])
+def test_decode_steps_match_single_steps_bitwise(tiny, B):
+    """river_decode_steps (several steps per call, tokens fed back on the
+    device, one recorded graph per call shape) against the same steps one
+    call each: identical next tokens, last logits, K/V cache and exit
+    histogram.  Four calls of two steps over two alternating next-token
+    buffers, so the fourth replays the second's graph; also eager."""
+    rv = _river()
+    s = synth.TINY
+    toks = synth.make_tokens(s, B, 32, seed=0).cuda()
+
+    def single():
+        r = rv.River(s, tiny["cuda"], B, 48)
+        r.build_exit_layers("int4")
+        _, nx = r.prefill(toks, 0.5)
+        outs = []
+        for _ in range(8):
+            lg, nx = r.decode_step(nx.clone(), 0.5)
+            outs.append(nx.clone())
+        torch.cuda.synchronize()
+        k, v = r.kv_views()
+        st = r.exit_stats()
+        res = (torch.stack(outs).cpu(), lg.cpu(), k.clone().cpu(), v.clone().cpu(),
+               (st["decode_hist"], st["pos"], st["n_decode_steps"]))
+        r.close()
+        return res
+
+    def multi(graph):
+        r = rv.River(s, tiny["cuda"], B, 48)
+        r.use_graph(graph)
+        r.build_exit_layers("int4")
+        _, nx = r.prefill(toks, 0.5)
+        ring = [torch.empty((2, B), dtype=torch.int32, device="cuda") for _ in range(2)]
+        logits = torch.empty((B, s.vocab), dtype=torch.float32, device="cuda")
+        ring[1][1].copy_(nx)
+        outs = []
+        for c in range(4):
+            src, dst = ring[(c + 1) % 2][1], ring[c % 2]
+            r.decode_steps(src, 2, 0.5, logits=logits, next_tok=dst)
+            torch.cuda.synchronize()   # eager host work between replays
+            outs.append(dst.clone())
+        k, v = r.kv_views()
+        st = r.exit_stats()
+        res = (torch.cat(outs).cpu(), logits.cpu(), k.clone().cpu(), v.clone().cpu(),
+               (st["decode_hist"], st["pos"], st["n_decode_steps"]))
+        r.close()
+        return res
+
+    ref = single()
+    for graph in (True, False):
+        got = multi(graph)
+        assert torch.equal(got[0], ref[0]), f"graph={graph}: next tokens"
+        assert torch.equal(got[1], ref[1]), f"graph={graph}: last logits"
+        assert torch.equal(got[2], ref[2]) and torch.equal(got[3], ref[3]), f"graph={graph}: K/V cache"
+        assert got[4] == ref[4], f"graph={graph}: exit histogram, position, step count"
+
+
 def test_graph_replay_matches_eager_bitwise(tiny):
     rv = _river()
     s = synth.TINY
