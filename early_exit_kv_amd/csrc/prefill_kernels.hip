@@ -1844,7 +1844,12 @@ static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t 
 // the int4 GEMMs ran 16-17% faster so, while bf16 weights, read twice as often
 // per flop, ran 4-17% slower (and from 1,024 rows int4 gained <= 6%, bf16 lost
 // up to 27%), so a layer known to run on its backbone (a backbone path, or a
-// pending-row pass) keeps the larger tile.
+// pending-row pass) keeps the larger tile.  Where even the 64-row tiles leave
+// fewer workgroups than CUs (256 on this chip), 32-row tiles double them: on
+// the 1B shape at 256 rows (q|k|v, o and down: 96, 64 and 64 workgroups) the
+// int4 prefill GEMMs 179 -> 220 TFLOP/s; on the 8B shape at 512 rows (256 or
+// more everywhere) 32-row tiles for the linears under 512 workgroups were
+// slower (517-524 -> 502-506).
 constexpr int kPSmallRows = 512;
 template <int G>
 static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s) {
@@ -1852,7 +1857,11 @@ static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s
   // (a pending-row pass runs the backbone, as a backbone path does)
   const bool may_q4 =
       p.exit_mode == RIVER_EXIT_INT4 && p.layer >= 0 && (p.path == kPathDevice || p.path == kPathExit);
-  if (p.M <= kPSmallRows && may_q4) return pgemm_launch_gb<G, 128, 256, 64>(ep, p, s);
+  if (p.M <= kPSmallRows && may_q4) {
+    const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
+    if (((p.M + 63) / 64) * ((ncols + 127) / 128) < 256) return pgemm_launch_gb<G, 128, 256, 32>(ep, p, s);
+    return pgemm_launch_gb<G, 128, 256, 64>(ep, p, s);
+  }
   return pgemm_launch_gb<G, 128>(ep, p, s);
 }
 
