@@ -79,6 +79,16 @@ def test_prefill_attention_8b_shape_two_rows():
 
 
 def test_prefill_attention_tiny_1500():
-    """Head dim 64, two query heads per kv head, four prompts of 1,500."""
+    """Head dim 64, two query heads per kv head, four prompts of 1,500 (192
+    workgroups with both heads, so one query head per workgroup)."""
     w = synth.make_weights(synth.TINY, seed=0, device="cuda", n_layers=2)
     check_prefill_attention(synth.TINY, w, B=4, T=1500, attn="mfma", n_random=32)
+
+
+@pytest.mark.parametrize("T", [512, 1100])
+def test_prefill_attention_8b_shape_split_heads(T):
+    """One short prompt: with all four query heads of a kv head per workgroup
+    the grid would hold 64 (T=512) or 144 (T=1,100) workgroups, fewer than
+    CUs, so each workgroup takes one (T=512) or two (T=1,100) of them."""
+    w = synth.make_weights(synth.LLAMA_8B, seed=0, device="cuda", n_layers=1)
+    check_prefill_attention(synth.LLAMA_8B, w, B=1, T=T, attn="mfma", n_random=32)
