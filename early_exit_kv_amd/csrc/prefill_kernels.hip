@@ -1810,13 +1810,37 @@ __global__ __launch_bounds__(NTH, 1) void pgemm_kernel(GemmParams p, int nrowblk
   for (int a = 0; a < AF; ++a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) tot[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (q4) pgemm_body<G, EP, true, BN, NTH, BM>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<true>(), tot);
-  else pgemm_body<G, EP, false, BN, NTH, BM>(p, smem, ex, rowblk, colblk, 0, p.K / pkt<false>(), tot);
+  // K split over gridDim.y in whole 128-column units (one int4 k-tile, two
+  // bf16 ones), so that both weight forms split at the same columns
+  const int nsp = gridDim.y, sp = blockIdx.y;
+  const int units = p.K / pkt<true>(), u0 = units * sp / nsp, u1 = units * (sp + 1) / nsp;
+  if (q4) pgemm_body<G, EP, true, BN, NTH, BM>(p, smem, ex, rowblk, colblk, u0, u1 - u0, tot);
+  else pgemm_body<G, EP, false, BN, NTH, BM>(p, smem, ex, rowblk, colblk, 2 * u0, 2 * (u1 - u0), tot);
 
-  // results through LDS (the body ends with a barrier and no copy in flight)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int qq = lane >> 4, cl = lane & 15;
   const int wm = wid / pwn<BN>(), wn = wid % pwn<BN>();
+  if constexpr (EP == kEpResid) {
+    if (nsp > 1) {
+      // partial tile of split sp: part[sp][row][col], rows of whole blocks;
+      // pgemm_reduce_kernel adds the splits and runs the epilogue
+      float *part = p.part + (int64_t)sp * nrowblk * BM * p.N;
+#pragma unroll
+      for (int a = 0; a < AF; ++a)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int col = colblk * BN + wn * 64 + t * 16 + cl;
+          if (col < p.N) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              part[((int64_t)rowblk * BM + wm * TM + a * 16 + 4 * qq + v) * p.N + col] = tot[a][t][v];
+          }
+        }
+      return;
+    }
+  }
+
+  // results through LDS (the body ends with a barrier and no copy in flight)
   float *Cs = reinterpret_cast<float *>(smem);
   static_assert(BM * (BN + 1) * 4 <= psmem_slots<G, BN, NTH, BM>() * 16, "the results fit the buffers");
 #pragma unroll
@@ -1830,13 +1854,41 @@ __global__ __launch_bounds__(NTH, 1) void pgemm_kernel(GemmParams p, int nrowblk
   tile_epilogue<EP, BN, NTH>(p, Cs, BN + 1, BM, (int64_t)rowblk * BM, colblk);
 }
 
+// Split-K sum of the prefill GEMM (kEpResid) and its epilogue: workgroup
+// (128-column block, group of 8 rows) adds the partial tiles in split order.
+constexpr int kPRedRows = 8;
+template <int EP>
+__global__ __launch_bounds__(256) void pgemm_reduce_kernel(GemmParams p, int mrows, int nsplit) {
+  constexpr int BN = 128, RG = kPRedRows;
+  static_assert(RG * BN / 4 == 256, "one float4 per thread");
+  __shared__ float Cs[RG * (BN + 1)];
+  // (comparators: the GEMM passed the residual stream through already)
+  if (past_exit_action(p.ctrl, p.layer, p.path) != kRun) return;
+  const int ncb = (p.N + BN - 1) / BN;
+  const int colblk = blockIdx.x % ncb, rg = blockIdx.x / ncb;
+  const int r = threadIdx.x / (BN / 4), j = 4 * (threadIdx.x % (BN / 4));
+  const int col = colblk * BN + j;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < p.N) {
+    const float *src = p.part + ((int64_t)rg * RG + r) * p.N + col;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float4 t = *reinterpret_cast<const float4 *>(src + (int64_t)sp * mrows * p.N);
+      v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+    }
+  }
+  float *c = Cs + r * (BN + 1) + j;
+  c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+  __syncthreads();
+  tile_epilogue<EP, BN>(p, Cs, BN + 1, RG, (int64_t)rg * RG, colblk);
+}
+
 template <int G, int BN, int NTH = kPThreads, int BM = kPBM>
-static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t s) {
+static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t s, int nsplit = 1) {
   const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
   int nrowblk = (p.M + BM - 1) / BM, ncolblk = (ncols + BN - 1) / BN;
   GemmParams q = p;
   void *args[] = {&q, &nrowblk, &ncolblk};
-  const dim3 grid((unsigned)(nrowblk * ncolblk));
+  const dim3 grid((unsigned)(nrowblk * ncolblk), (unsigned)nsplit);
   const void *fn;
   switch (ep) {
     case kEpQKV: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpQKV, BN, NTH, BM>); break;
@@ -1845,7 +1897,13 @@ static hipError_t pgemm_launch_gb(Epilogue ep, const GemmParams &p, hipStream_t 
     case kEpPlain: fn = reinterpret_cast<const void *>(pgemm_kernel<G, kEpPlain, BN, NTH, BM>); break;
     default: return hipErrorInvalidValue;
   }
-  return launch_kernel(fn, grid, dim3(NTH), args, 0, s);
+  hipError_t e = launch_kernel(fn, grid, dim3(NTH), args, 0, s);
+  if (e != hipSuccess || nsplit == 1) return e;
+  // (only kEpResid launches split K)
+  int mrows = nrowblk * BM, ns = nsplit;
+  void *rargs[] = {&q, &mrows, &ns};
+  const dim3 rgrid((unsigned)(((p.N + 127) / 128) * (mrows / kPRedRows)));
+  return launch_kernel(reinterpret_cast<const void *>(pgemm_reduce_kernel<kEpResid>), rgrid, dim3(256), rargs, 0, s);
 }
 
 // 256-column blocks (64 x 64 per wavefront: half the int4 unpacking per
@@ -1871,7 +1929,14 @@ static hipError_t pgemm_launch_g(Epilogue ep, const GemmParams &p, hipStream_t s
       p.exit_mode == RIVER_EXIT_INT4 && p.layer >= 0 && (p.path == kPathDevice || p.path == kPathExit);
   if (p.M <= kPSmallRows && may_q4) {
     const int ncols = ep == kEpSwiGLU ? 2 * p.w.seg_rows[0] : p.N;
-    if (((p.M + 63) / 64) * ((ncols + 127) / 128) < 256) return pgemm_launch_gb<G, 128, 256, 32>(ep, p, s);
+    const int wgs = ((p.M + 63) / 64) * ((ncols + 127) / 128);
+    if (wgs < 256) return pgemm_launch_gb<G, 128, 256, 32>(ep, p, s);
+    // o and down with fewer than two workgroups per CU: K in two halves,
+    // partial tiles in the caller's buffer, added up by a second kernel
+    const int64_t part = 2 * (int64_t)((p.M + 63) / 64) * 64 * p.N;
+    if (ep == kEpResid && wgs < 512 && p.part && part <= p.part_cap && p.N % 4 == 0 &&
+        (p.K / pkt<true>()) >= 2)
+      return pgemm_launch_gb<G, 128, 256, 64>(ep, p, s, 2);
     return pgemm_launch_gb<G, 128, 256, 64>(ep, p, s);
   }
   return pgemm_launch_gb<G, 128>(ep, p, s);

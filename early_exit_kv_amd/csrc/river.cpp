@@ -102,6 +102,10 @@ Workspace workspace_layout(const river_config &c) {
   }
   w.mg_part_floats = std::max<int64_t>(mg, 1);
   w.mg_part = take((size_t)w.mg_part_floats * 4);
+  // two K halves of the prefill GEMM's o and down outputs, up to 512 rows in
+  // whole 64-row blocks
+  w.pg_part_floats = 2 * ((std::min<int64_t>(R, 512) + 63) / 64) * 64 * c.d_model;
+  w.pg_part = take((size_t)w.pg_part_floats * 4);
   w.total = off;
   return w;
 }
@@ -737,6 +741,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     fill_weights(ctx, l, 3, 1, o.w);
     o.N = c.d_model; o.K = qd; o.x = ap.out; o.ldx = qd;
     o.h_in = hA; o.h_out = hB; o.h_io_stride = c.d_model;
+    o.part = at<float>(ctx->ws, ctx->wl.pg_part); o.part_cap = ctx->wl.pg_part_floats;
     TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, o, s));
     RV_TRY(rec.put(l, rec.lay.h_mid, hB, hbytes));
 
@@ -755,6 +760,7 @@ int enqueue_prefill(river_ctx *ctx, const int32_t *tok, int B, int T, float tau,
     fill_weights(ctx, l, 6, 1, dn.w);
     dn.N = c.d_model; dn.K = c.ffn_dim; dn.x = gu.u_out; dn.ldx = c.ffn_dim;
     dn.h_in = hB; dn.h_out = hB; dn.h_io_stride = c.d_model;
+    dn.part = o.part; dn.part_cap = o.part_cap;
     TIMED(RIVER_K_P_GEMM, launch_prefill_gemm(kEpResid, dn, s));
 
     if (l < c.n_layers - 1 && ctx->force_E < 0) {

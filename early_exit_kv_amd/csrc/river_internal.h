@@ -101,11 +101,13 @@ struct Workspace {
   size_t attn_part;    // fp32 split-K attention partials
   size_t rope;         // fp32 (cos, sin) of pos * theta^(-2i/Dh), [max_seq][Dh/2]
   size_t mg_part;      // fp32 split-K partials of the batched-row GEMM
+  size_t pg_part;      // fp32 split-K partials of the prefill GEMM (o, down; up to 512 rows)
   size_t total;
   int64_t rows;        // R: rows the buffers hold
   int part_floats;
   int attn_splits;     // split count the decode attention is sized for
   int64_t mg_part_floats;
+  int64_t pg_part_floats;
 };
 Workspace workspace_layout(const river_config &c);
 
