@@ -224,6 +224,17 @@ def test_decode_parity_tiny_batch64_max_rows():
     parity_run(synth.TINY, w, B=37, T=5, steps=2, tau=0.5)
 
 
+def test_prefill_parity_8b_split_k_o_down(w8b):
+    """A 500-token prompt on two 8B-shape layers: the prefill GEMM's o and
+    down run 256 workgroups of 64-row tiles (the last block ragged, 52
+    rows), so K is split in two halves and pgemm_reduce_kernel adds the
+    partial tiles and runs the residual epilogue; every stage of the prefill
+    and one decode step is checked against the oracle."""
+    w = dict(w8b)
+    w["layers"] = w8b["layers"][:2]
+    parity_run(synth.LLAMA_8B, w, B=1, T=500, steps=1, tau=0.5)
+
+
 def test_decode_parity_lm_head_split_reduce():
     """The batched LM head with K split: a 2,048-wide decoder with a
     1,100-token vocabulary (nine 128-column blocks, the last partial) at 24
